@@ -1,0 +1,215 @@
+#!/usr/bin/env python3
+"""Benchmark: one decode step of paged attention at the OPT-13B layer shape.
+
+A step is the whole hot path for one batch: the host block manager's append
+for every sequence (done ahead of the timed region; its inputs are resident
+in HBM before timing starts), the copy-on-write block copies it asks for
+(none in this workload), ``pa_reshape_and_cache`` of the 64 new tokens' K/V,
+and ``pa_paged_decode``.
+
+Workload: 64 sequences, 40 heads, head_dim 128, fp16 K/V/Q ~ N(0,1), scale
+1/sqrt(128), block size 16, history lengths uniform on [1, 2048] drawn from
+SeedSequence(76002), blocks taken from a seeded-shuffled pool sized to the
+blocks needed + 10% (+ room for the steps' growth).  Step i decodes one new
+token per sequence, so its contexts are the drawn lengths + i.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged decode-attn achieved HBM GB/s (% of peak) + seq-steps/s, OPT-13B shape"
+PEAK_HBM_GBS = 8000.0
+S, H, D, B = 64, 40, 128, 16
+DTYPE = "f16"
+ELEM = 2
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_model() -> str:
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name"):
+                return line.split(":", 1)[1].strip()
+    except Exception:
+        pass
+    return platform.processor() or "unknown"
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return 1
+
+
+def cpu_baseline(batch, n_seq: int, repeats: int = 3) -> dict:
+    """The float64 oracle on the first ``n_seq`` sequences of the step (all
+    heads), timed on this host's cores."""
+    import numpy as np
+
+    from oracle import attention as oa
+    from paged_kv_cache_76_amd import workloads
+
+    qs = [batch.q[s].numpy() for s in range(n_seq)]
+    ks = [batch.k_hist[s].numpy() for s in range(n_seq)]
+    vs = [batch.v_hist[s].numpy() for s in range(n_seq)]
+    times = []
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        for s in range(n_seq):
+            oa.decode(qs[s], ks[s], vs[s], batch.scale)
+        times.append(time.perf_counter() - t0)
+    dt = sorted(times)[len(times) // 2]
+    nbytes = workloads.decode_bytes(batch.lens[:n_seq], H, D, ELEM, B)
+    return {
+        "value": nbytes / dt / 1e9, "unit": "GB/s", "cores": blas_threads(),
+        "kind": "oracle",
+        "sample": f"{n_seq} of {S} sequences (all {H} heads, contexts {int(batch.lens[:n_seq].sum())} tokens), "
+                  f"one decode step, median of {repeats}, float64 NumPy on {os.cpu_count()} host cores ({cpu_model()})",
+        "seq_steps_per_s": n_seq / dt, "seconds": dt,
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seqs", type=int, default=64, help="sequences in the CPU-oracle sample (0: skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU layout is a design "
+              "note, not a measured path", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_76_amd import _lib as L
+    from paged_kv_cache_76_amd import inputs, workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    K, W = args.steps, args.warmup
+    n_steps = K + W
+
+    lens0 = workloads.opt13b_decode_lengths(2, S)
+    log(f"building OPT-13B decode workload: S={S} H={H} d={D} B={B} fp16, "
+        f"tokens={int(lens0.sum())}, steps={n_steps}")
+    extra = S * (-(-n_steps // B) + 1)
+    batch = workloads.build_decode_batch(2, lens0, H, D, B, DTYPE, slack=1.10, extra_blocks=extra,
+                                         grow_tokens=n_steps, nan_fill=False)
+    mgr = batch.manager
+    r_step = inputs.streams(2, workloads.STREAMS)[5]   # new tokens' k, v and q, step by step
+
+    # host block-manager steps, done ahead of time; everything lands in HBM
+    steps = []
+    host_ms = []
+    rows = np.arange(S)
+    for i in range(n_steps):
+        t0 = time.perf_counter()
+        slots, pairs = mgr.append_step(rows)
+        tables = mgr.tables.copy()
+        lens = mgr.lens.astype(np.int32).copy()
+        host_ms.append((time.perf_counter() - t0) * 1e3)
+        k_new = inputs.normal(r_step, (S, H, D), DTYPE)
+        v_new = inputs.normal(r_step, (S, H, D), DTYPE)
+        q = inputs.normal(r_step, (S, H, D), DTYPE)
+        steps.append(dict(
+            slots=torch.from_numpy(slots).cuda(), pairs=torch.from_numpy(pairs).cuda(), n_pairs=len(pairs),
+            k=k_new.cuda(), v=v_new.cuda(), q=q.cuda(), tables=torch.from_numpy(tables).cuda(),
+            lens=torch.from_numpy(lens).cuda(), max_ctx=int(lens.max()), lens_host=lens))
+    max_ctx = max(st["max_ctx"] for st in steps)
+    ws = L.decode_workspace(batch.cache, S, max_ctx)
+    out = torch.empty((S, H, D), dtype=torch.float16, device="cuda")
+    scale = 1.0 / math.sqrt(D)
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_steps)]
+
+    def step(i):
+        st = steps[i]
+        if st["n_pairs"]:
+            L.pa_copy_blocks(batch.cache, st["pairs"])
+        L.pa_reshape_and_cache(batch.cache, st["k"], st["v"], st["slots"])
+        ev[i][0].record()
+        L.pa_paged_decode(batch.cache, out, st["q"], st["tables"], st["lens"], max_ctx, scale, ws)
+        ev[i][1].record()
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"warmup done ({W} steps); timing {K} steps")
+    t0 = time.perf_counter()
+    for i in range(W, n_steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    dec_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(W, n_steps)]
+    dec_bytes = [workloads.decode_bytes(steps[i]["lens_host"], H, D, ELEM, B) for i in range(W, n_steps)]
+    write_bytes = 2 * 2 * S * H * D * ELEM          # read + write, keys and values
+    copy_bytes = [2 * 2 * steps[i]["n_pairs"] * H * B * D * ELEM for i in range(W, n_steps)]
+    step_bytes = sum(dec_bytes) + K * write_bytes + sum(copy_bytes)
+    value = step_bytes / elapsed / 1e9
+    ms_per_step = elapsed / K * 1e3
+    dec_avg_ms = sum(dec_ms) / K
+    dec_gbs = (sum(dec_bytes) / K) / (dec_avg_ms * 1e-3) / 1e9
+    log(f"step {ms_per_step:.3f} ms, decode {dec_avg_ms * 1e3:.1f} us -> {dec_gbs:.0f} GB/s")
+
+    cpu = None
+    if args.cpu_seqs > 0:
+        log(f"timing the CPU oracle on {args.cpu_seqs} sequences")
+        cpu = cpu_baseline(batch, args.cpu_seqs)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "OPT-13B-shaped single-layer paged decode step (write + decode)",
+                   "sequences": S, "heads": H, "head_dim": D, "block_size": B, "kv_dtype": "f16",
+                   "context_lens": "uniform[1,2048] + step index", "seed": "SeedSequence(76002)",
+                   "pool_blocks": batch.cache.num_blocks, "parallelism": "none (1 GPU)"},
+        "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
+        "seq_steps_per_s": round(S * K / elapsed, 1),
+        "host_block_manager_ms_per_step": round(sum(host_ms) / len(host_ms), 4),
+        "roofline": {"bound": "hbm", "kernel": "pa_paged_decode", "achieved": round(dec_gbs, 2),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+                     "traffic": None, "avg_launch_us": round(dec_avg_ms * 1e3, 2),
+                     "algorithmic_bytes_per_launch": int(sum(dec_bytes) / K)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,167 @@
+/*
+ * libpagedattn — paged KV-cache attention for AMD Instinct MI355X (gfx950).
+ *
+ * The data-parallel hot path of vLLM's PagedAttention as three web pages
+ * describe it: every sequence keeps its key/value history in fixed-size KV
+ * blocks that need not be adjacent in memory, a per-sequence block table
+ * translates logical block j to a physical block id, and attention reads the
+ * history through that table.  Cache writes and copy-on-write block copies
+ * keep the blocks consistent.
+ *
+ * Sources cited below by page and section:
+ *   [P1] "vLLM / PagedAttention — 把 LLM 服务的瓶颈从显存碎片里救出来"
+ *        (awesome.papernotes.org), "方法详解", key designs 1-5.
+ *   [P2] "vLLM" notes (formulaic.cloudchewie.com), "PagedAttention 原理" and
+ *        "在不同解码策略下的效果".
+ *   [P3] "vLLM / PagedAttention (SOSP 2023)" guide (upskillscore),
+ *        sections 03-04.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All data pointers are DEVICE pointers owned by the caller; the library
+ *   never allocates or frees device memory, never synchronises, and keeps no
+ *   global mutable state except a thread-local "last error" string.
+ * - Every compute call is asynchronous on `stream` (a hipStream_t passed as
+ *   void*; NULL is the default stream).  Buffers must stay alive until the
+ *   stream has executed the call.
+ * - Cache layout: separate key and value pools, each
+ *   [num_blocks][num_heads][block_size][head_dim], row-major, elements of
+ *   `dtype`.  Token offset o of head h in physical block b lives at
+ *   pool[b][h][o][:].  A slot is b * block_size + o (int64).
+ * - Token rows (keys, values, queries, outputs) are contiguous
+ *   [rows][num_heads][head_dim].
+ * - Data pointers (pools, rows, outputs) must be 16-byte aligned, and
+ *   head_dim * sizeof(dtype) must be a multiple of 16.
+ * - Argument checks happen on the host before any launch and return
+ *   PA_ERR_INVALID_ARG / PA_ERR_UNSUPPORTED / PA_ERR_WORKSPACE with a message
+ *   in pa_last_error().  A failed launch returns PA_ERR_LAUNCH.
+ * - Index CONTENTS (slots, block ids, lengths) are preconditions.  The kernels
+ *   skip a slot, a pair or a block id outside the pool instead of touching
+ *   memory outside it, but the numerical result of such a call is undefined.
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1,  /* null pointer, negative size, misalignment, bad dtype */
+  PA_ERR_UNSUPPORTED = 2,  /* valid but not built: (dtype, head_dim, block_size) */
+  PA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required */
+  PA_ERR_LAUNCH = 4        /* the HIP runtime refused a launch */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+
+/* A description of caller-owned cache memory (not owned by the library). */
+typedef struct {
+  void* k;             /* key pool   [num_blocks][num_heads][block_size][head_dim] */
+  void* v;             /* value pool, same shape and dtype                         */
+  int32_t num_blocks;  /* physical blocks in each pool, >= 1                       */
+  int32_t num_heads;   /* attention heads (keys and values have the same count)    */
+  int32_t head_dim;    /* d                                                        */
+  int32_t block_size;  /* B, tokens per block, a power of two                      */
+  pa_dtype dtype;      /* element type of both pools                               */
+} pa_kv_cache;
+
+/*
+ * pa_reshape_and_cache — write new tokens' keys and values into their slots.
+ * [P1] key design 5 (the new K/V of a layer are reshaped into the block-read
+ * layout and written to their positions in one fused operation); [P2]
+ * "PagedAttention 原理" (the K/V of the prompt and of each decoded token go
+ * into the physical-block slots the block table maps to).
+ *
+ *   key, value    [T][num_heads][head_dim], cache dtype, 16-byte aligned.
+ *   slot_mapping  int64 [T]: slot of token t; a negative slot skips the token.
+ *                 Slots are unique within a call (precondition).
+ *   T             number of token rows, >= 0; T == 0 is a no-op.
+ * Effect: k[slot/B][h][slot%B][:] = key[t][h][:] (same for v), bit-exact.
+ */
+pa_status pa_reshape_and_cache(const pa_kv_cache* cache, const void* key, const void* value,
+                               const int64_t* slot_mapping, int32_t T, void* stream);
+
+/*
+ * pa_copy_blocks — batched whole-block copies for copy-on-write.
+ * [P1] key design 3 (a write into a block whose reference count exceeds one
+ * first copies the block into a newly allocated one) and key design 5 (the
+ * many small copies this causes are batched into one kernel instead of one
+ * memcpy per block); [P3] section 04 (copy-on-write copies only one block).
+ *
+ *   pairs  int64 [n][2] = (src, dst) physical ids.  Destinations are distinct
+ *          and no destination is also a source (precondition).
+ *   n      number of pairs, >= 0; n == 0 is a no-op.
+ * Effect: k[dst] = k[src] and v[dst] = v[src] (all heads, all slots), bit-exact.
+ */
+pa_status pa_copy_blocks(const pa_kv_cache* cache, const int64_t* pairs, int32_t n, void* stream);
+
+/*
+ * Workspace of pa_paged_decode, in bytes, for S sequences whose longest
+ * context is max_context_len tokens.  0 means "no workspace needed".
+ * Returns (size_t)-1 for an unsupported cache description.
+ */
+size_t pa_decode_workspace_bytes(const pa_kv_cache* cache, int32_t S, int32_t max_context_len);
+
+/*
+ * pa_paged_decode — one decode step of attention over paged histories.
+ * [P1] key design 1: o = sum_j a_j v_j with a_j = exp(q.k_j * scale) /
+ * sum_t exp(q.k_t * scale), evaluated block by block (eq. 2) with blocks
+ * gathered through the block table; key design 5 (block reads are fused into
+ * the attention kernel).
+ *
+ *   out            [S][num_heads][head_dim] of out_dtype (cache dtype or PA_F32).
+ *   query          [S][num_heads][head_dim], cache dtype.
+ *   block_tables   int32 [S][max_blocks_per_seq]; entry j of row s is the
+ *                  physical id of logical block j.  Entries at or beyond
+ *                  ceil(context_lens[s]/B) are never read.
+ *   context_lens   int32 [S], 1 <= context_lens[s] <= max_context_len; counts
+ *                  the token being decoded (its K/V are already in the cache).
+ *   max_context_len  host-side upper bound of context_lens (sizes the grid).
+ *   scale          score scale, usually 1/sqrt(head_dim).
+ *   workspace      device scratch of >= pa_decode_workspace_bytes() bytes
+ *                  (any content; may be NULL when that size is 0).
+ * Accumulation is fp32; the softmax is exact (no approximation).
+ */
+pa_status pa_paged_decode(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, const void* query,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* context_lens, int32_t S, int32_t max_context_len,
+                          float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_paged_prefill — causal attention for the prompt tokens of S sequences.
+ * [P1] key design 1, eq. 1 (query i attends to positions t <= i, itself
+ * included) with keys/values read through the block table as in eq. 2;
+ * [P2] "PagedAttention 原理" (the prompt's K/V are first written into the
+ * mapped slots — call pa_reshape_and_cache before this).
+ *
+ *   query, out     [sum_s q_len_s][num_heads][head_dim]; rows of sequence s
+ *                  are cu_q_lens[s] .. cu_q_lens[s+1]-1.
+ *   cu_q_lens      int32 [S+1], cu_q_lens[0] = 0, non-decreasing.
+ *   context_lens   int32 [S]; q_len_s <= context_lens[s]; the queries are the
+ *                  last q_len_s logical positions of the sequence.
+ *   max_q_len, max_context_len  host-side upper bounds.
+ */
+pa_status pa_paged_prefill(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, const void* query,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* cu_q_lens, const int32_t* context_lens, int32_t S,
+                           int32_t max_q_len, int32_t max_context_len, float scale, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* pa_status_string(pa_status status);
+/* Detail of the last non-OK status returned on this thread ("" if none). */
+const char* pa_last_error(void);
+/* PA_ABI_VERSION of the built library. */
+int32_t pa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

@@ -1,0 +1,235 @@
+"""Host-side KV block manager: free list, reference counts, lazy append,
+fork, free and copy-on-write, producing the device-ready block tables, slot
+mappings and copy pairs that the kernels consume.
+
+Sources: "vLLM / PagedAttention" (awesome.papernotes.org), "方法详解"
+key design 2 (each sequence's logical blocks map to physical blocks through a
+block table; prefill allocates the prompt's blocks, each decoded token goes
+into the last block, a new block is allocated when that one is full) and key
+design 3 (reference counts per physical block; a write into a shared block
+allocates, copies, decrements and remaps — the ``append_token`` order of
+checks: full first, then shared); "vLLM" notes (formulaic.cloudchewie.com),
+"PagedAttention 原理" and "在不同解码策略下的效果" (parallel sampling shares
+prompt blocks; beam search forks candidates and releases pruned ones);
+"vLLM / PagedAttention (SOSP 2023)" guide, sections 03-04.
+
+Design: state is kept in flat numpy arrays indexed by *row* — the sequence's
+position in the decode batch — so ``tables`` is already the ``[S][max_blocks]``
+int32 array the decode kernel reads, and a decode step over many rows is a
+handful of vectorised operations.  Only rows whose last block is shared take
+a Python-level path (the copy-on-write decision is sequential by nature: the
+i-th appending sharer of a block sees its count lowered by i).
+
+Policies (readings of points the pages leave open):
+
+* lazy allocation: a block is allocated when the token that needs it arrives;
+* a full and shared last block gets a fresh block and no copy;
+* the free list is FIFO: allocation takes the front, release appends to the
+  back; the initial order is an input (a seeded permutation);
+* within a step rows append in ascending order, so the first writer of a
+  shared block copies and the last sharer writes in place; allocations of a
+  step are handed out in ascending row order;
+* a step is all-or-nothing: if the free list cannot cover it, nothing changes
+  and :class:`OutOfBlocks` is raised;
+* slot = physical_id * B + offset (int64); unused table entries hold
+  ``poison`` (default: ``num_blocks``, outside the pool).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+
+class OutOfBlocks(RuntimeError):
+    """The free list cannot cover the request."""
+
+
+class BlockManager:
+    def __init__(self, num_blocks: int, block_size: int, max_rows: int, max_blocks_per_seq: int,
+                 free_order=None, poison: int | None = None):
+        if block_size < 1 or num_blocks < 1:
+            raise ValueError("num_blocks and block_size must be >= 1")
+        self.num_blocks = int(num_blocks)
+        self.B = int(block_size)
+        self.max_rows = int(max_rows)
+        self.max_blocks = int(max_blocks_per_seq)
+        self.poison = self.num_blocks if poison is None else int(poison)
+        order = np.arange(num_blocks, dtype=np.int64) if free_order is None else np.asarray(free_order, np.int64)
+        if order.shape != (num_blocks,) or not np.array_equal(np.sort(order), np.arange(num_blocks)):
+            raise ValueError("free_order must be a permutation of the pool")
+        # FIFO ring of free ids
+        self._ring = order.copy()
+        self._head = 0
+        self._nfree = num_blocks
+        self.ref = np.zeros(num_blocks, dtype=np.int32)
+        self.tables = np.full((max_rows, max_blocks_per_seq), self.poison, dtype=np.int32)
+        self.nblocks = np.zeros(max_rows, dtype=np.int32)
+        self.lens = np.zeros(max_rows, dtype=np.int64)
+        self.cow_copies = 0
+
+    # ---- free list ----------------------------------------------------------
+    @property
+    def num_free(self) -> int:
+        return self._nfree
+
+    def _pop(self, k: int) -> np.ndarray:
+        if k > self._nfree:
+            raise OutOfBlocks(f"{k} blocks needed, {self._nfree} free")
+        idx = (self._head + np.arange(k)) % self.num_blocks
+        ids = self._ring[idx].copy()
+        self._head = (self._head + k) % self.num_blocks
+        self._nfree -= k
+        return ids
+
+    def _push(self, ids: np.ndarray) -> None:
+        k = len(ids)
+        if k == 0:
+            return
+        tail = (self._head + self._nfree) % self.num_blocks
+        self._ring[(tail + np.arange(k)) % self.num_blocks] = ids
+        self._nfree += k
+
+    def free_list(self) -> list[int]:
+        idx = (self._head + np.arange(self._nfree)) % self.num_blocks
+        return self._ring[idx].tolist()
+
+    # ---- sequence operations ------------------------------------------------
+    def _check_row(self, row: int, live: bool) -> None:
+        if not 0 <= row < self.max_rows:
+            raise IndexError(f"row {row} outside [0, {self.max_rows})")
+        if live and self.lens[row] == 0:
+            raise KeyError(f"row {row} holds no sequence")
+        if not live and self.lens[row] != 0:
+            raise KeyError(f"row {row} already holds a sequence")
+
+    def add_prompt(self, row: int, length: int) -> np.ndarray:
+        """Allocate ceil(length/B) blocks for a prompt in ``row``; return the
+        int64 slots of its tokens in logical order."""
+        self._check_row(row, live=False)
+        if length < 1:
+            raise ValueError("a prompt has at least one token")
+        n = -(-int(length) // self.B)
+        if n > self.max_blocks:
+            raise ValueError(f"prompt of {length} tokens needs {n} > {self.max_blocks} table entries")
+        ids = self._pop(n)
+        self.tables[row, :n] = ids
+        self.ref[ids] = 1
+        self.nblocks[row] = n
+        self.lens[row] = length
+        pos = np.arange(length, dtype=np.int64)
+        return ids[pos // self.B] * self.B + pos % self.B
+
+    def append_step(self, rows) -> tuple[np.ndarray, np.ndarray]:
+        """Append one token to each of ``rows`` (processed in ascending order).
+
+        Returns ``(slot_mapping int64 [len(rows)], copy_pairs int64 [P][2])``;
+        ``slot_mapping[i]`` belongs to ``sorted(rows)[i]``.  The copies must be
+        executed before the new tokens are written.
+        """
+        rows = np.sort(np.asarray(rows, dtype=np.int64))
+        if len(rows) == 0:
+            return np.zeros(0, np.int64), np.zeros((0, 2), np.int64)
+        if len(np.unique(rows)) != len(rows):
+            raise ValueError("a row appears twice in one step")
+        if np.any(self.lens[rows] == 0):
+            raise KeyError("append to an empty row")
+        L = self.lens[rows]
+        nb = self.nblocks[rows].astype(np.int64)
+        off = L % self.B
+        need_new = off == 0                                   # last block full
+        if np.any(need_new & (nb >= self.max_blocks)):
+            raise ValueError("a sequence outgrew max_blocks_per_seq")
+        last = self.tables[rows, nb - 1].astype(np.int64)
+        # copy-on-write decision for rows whose partial last block is shared
+        cow = np.zeros(len(rows), dtype=bool)
+        cand = np.nonzero(~need_new & (self.ref[last] > 1))[0]
+        if len(cand):
+            seen: dict[int, int] = {}
+            for i in cand:                                    # ascending rows
+                b = int(last[i])
+                k = seen.get(b, 0)
+                cow[i] = self.ref[b] - k > 1
+                seen[b] = k + 1
+        alloc = need_new | cow
+        n_alloc = int(alloc.sum())
+        ids = self._pop(n_alloc)                              # raises before any change
+        new_ids = np.full(len(rows), -1, dtype=np.int64)
+        new_ids[alloc] = ids
+        # fresh blocks for full last blocks
+        r_new = rows[need_new]
+        self.tables[r_new, nb[need_new]] = new_ids[need_new]
+        self.nblocks[r_new] += 1
+        # copy-on-write: remap the last logical block, move one reference
+        r_cow = rows[cow]
+        src = last[cow]
+        self.tables[r_cow, nb[cow] - 1] = new_ids[cow]
+        np.subtract.at(self.ref, src, 1)
+        self.ref[ids] = 1
+        self.cow_copies += int(cow.sum())
+        phys = np.where(alloc, new_ids, last)
+        slots = phys * self.B + off
+        self.lens[rows] += 1
+        pairs = np.stack([src, new_ids[cow]], axis=1) if len(src) else np.zeros((0, 2), np.int64)
+        return slots.astype(np.int64), pairs.astype(np.int64)
+
+    def fork(self, src_row: int, dst_row: int) -> None:
+        """``dst_row`` shares every block of ``src_row`` (counts + 1)."""
+        self._check_row(src_row, live=True)
+        self._check_row(dst_row, live=False)
+        n = int(self.nblocks[src_row])
+        ids = self.tables[src_row, :n]
+        self.tables[dst_row, :n] = ids
+        self.ref[ids] += 1
+        self.nblocks[dst_row] = n
+        self.lens[dst_row] = self.lens[src_row]
+
+    def free(self, row: int) -> None:
+        """Release every block of ``row`` in logical order."""
+        self._check_row(row, live=True)
+        n = int(self.nblocks[row])
+        ids = self.tables[row, :n].astype(np.int64)
+        self.ref[ids] -= 1
+        self._push(ids[self.ref[ids] == 0])
+        self.tables[row, :] = self.poison
+        self.nblocks[row] = 0
+        self.lens[row] = 0
+
+    # ---- views and accounting -------------------------------------------------
+    def table(self, row: int) -> list[int]:
+        return self.tables[row, : self.nblocks[row]].tolist()
+
+    def slot(self, row: int, pos: int) -> int:
+        return int(self.tables[row, pos // self.B]) * self.B + pos % self.B
+
+    def live_rows(self) -> np.ndarray:
+        return np.nonzero(self.lens > 0)[0]
+
+    def used(self) -> int:
+        return int(np.count_nonzero(self.ref))
+
+    def tail_waste(self, rows=None) -> np.ndarray:
+        """Unused slots in each row's blocks (key design 2, eq. 3, in tokens)."""
+        rows = self.live_rows() if rows is None else np.asarray(rows)
+        return self.nblocks[rows].astype(np.int64) * self.B - self.lens[rows]
+
+    def blocks_saved_by_sharing(self) -> int:
+        """Extra references (key design 3, eq. 4): logical - physical blocks."""
+        r = self.ref[self.ref > 0]
+        return int((r - 1).sum())
+
+    def stats(self) -> dict:
+        live = self.live_rows()
+        waste = self.tail_waste(live)
+        hist = np.bincount(self.ref[self.ref > 0]) if self.used() else np.zeros(1, np.int64)
+        return {
+            "live_sequences": int(len(live)),
+            "used_blocks": self.used(),
+            "free_blocks": self.num_free,
+            "logical_blocks": int(self.nblocks[live].sum()),
+            "blocks_saved_by_sharing": self.blocks_saved_by_sharing(),
+            "tokens": int(self.lens[live].sum()),
+            "tail_waste_slots": int(waste.sum()),
+            "slot_utilisation": float(self.lens[live].sum() / max(1, self.used() * self.B)),
+            "ref_count_histogram": {int(k): int(v) for k, v in enumerate(hist) if k > 0 and v},
+            "cow_copies": self.cow_copies,
+        }

@@ -1,0 +1,196 @@
+// C-ABI of libpagedattn: argument validation, dispatch and error reporting.
+// Every check below runs on the host before any HIP call, so a rejected call
+// touches neither the device nor the stream.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <cmath>
+#include <string>
+
+#include "pa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pa_status fail(pa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+bool valid_dtype(int t) { return t == PA_F32 || t == PA_F16 || t == PA_BF16; }
+bool pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+pa_status check_cache(const char* fn, const pa_kv_cache* c, pa::Cache* out) {
+  if (!c) return fail(PA_ERR_INVALID_ARG, "%s: cache is NULL", fn);
+  if (!valid_dtype((int)c->dtype)) return fail(PA_ERR_INVALID_ARG, "%s: bad cache dtype %d", fn, (int)c->dtype);
+  if (!c->k || !c->v) return fail(PA_ERR_INVALID_ARG, "%s: cache pool pointer is NULL", fn);
+  if (!aligned(c->k, 16) || !aligned(c->v, 16))
+    return fail(PA_ERR_INVALID_ARG, "%s: cache pools must be 16-byte aligned", fn);
+  if (c->num_blocks < 1 || c->num_heads < 1 || c->head_dim < 1 || c->block_size < 1)
+    return fail(PA_ERR_INVALID_ARG, "%s: cache sizes must be >= 1 (blocks %d heads %d dim %d block %d)", fn,
+                c->num_blocks, c->num_heads, c->head_dim, c->block_size);
+  if (!pow2(c->block_size))
+    return fail(PA_ERR_INVALID_ARG, "%s: block_size %d is not a power of two", fn, c->block_size);
+  if ((c->head_dim * pa::dtype_bytes(c->dtype)) % 16 != 0)
+    return fail(PA_ERR_UNSUPPORTED, "%s: head_dim*sizeof(dtype) = %d is not a multiple of 16 bytes", fn,
+                c->head_dim * pa::dtype_bytes(c->dtype));
+  out->k = c->k;
+  out->v = c->v;
+  out->num_blocks = c->num_blocks;
+  out->num_heads = c->num_heads;
+  out->head_dim = c->head_dim;
+  out->block_size = c->block_size;
+  out->dtype = c->dtype;
+  return PA_OK;
+}
+
+pa_status launched(const char* fn, hipError_t err) {
+  if (err != hipSuccess) return fail(PA_ERR_LAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(err));
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_reshape_and_cache(const pa_kv_cache* cache, const void* key, const void* value,
+                               const int64_t* slot_mapping, int32_t T, void* stream) {
+  const char* fn = "pa_reshape_and_cache";
+  pa::Cache c;
+  pa_status st = check_cache(fn, cache, &c);
+  if (st != PA_OK) return st;
+  if (T < 0) return fail(PA_ERR_INVALID_ARG, "%s: T = %d < 0", fn, T);
+  if (T == 0) return PA_OK;
+  if (!key || !value || !slot_mapping) return fail(PA_ERR_INVALID_ARG, "%s: NULL key/value/slot_mapping", fn);
+  if (!aligned(key, 16) || !aligned(value, 16))
+    return fail(PA_ERR_INVALID_ARG, "%s: key/value must be 16-byte aligned", fn);
+  if (!aligned(slot_mapping, 8)) return fail(PA_ERR_INVALID_ARG, "%s: slot_mapping must be 8-byte aligned", fn);
+  return launched(fn, pa::launch_reshape_and_cache(c, key, value, slot_mapping, T, (hipStream_t)stream));
+}
+
+pa_status pa_copy_blocks(const pa_kv_cache* cache, const int64_t* pairs, int32_t n, void* stream) {
+  const char* fn = "pa_copy_blocks";
+  pa::Cache c;
+  pa_status st = check_cache(fn, cache, &c);
+  if (st != PA_OK) return st;
+  if (n < 0) return fail(PA_ERR_INVALID_ARG, "%s: n = %d < 0", fn, n);
+  if (n == 0) return PA_OK;
+  if (!pairs) return fail(PA_ERR_INVALID_ARG, "%s: pairs is NULL", fn);
+  if (!aligned(pairs, 8)) return fail(PA_ERR_INVALID_ARG, "%s: pairs must be 8-byte aligned", fn);
+  if (n > (1 << 30)) return fail(PA_ERR_INVALID_ARG, "%s: n = %d is too large", fn, n);
+  return launched(fn, pa::launch_copy_blocks(c, pairs, n, (hipStream_t)stream));
+}
+
+size_t pa_decode_workspace_bytes(const pa_kv_cache* cache, int32_t S, int32_t max_context_len) {
+  pa::Cache c;
+  if (check_cache("pa_decode_workspace_bytes", cache, &c) != PA_OK) return (size_t)-1;
+  if (S < 0 || max_context_len < 0) {
+    fail(PA_ERR_INVALID_ARG, "pa_decode_workspace_bytes: negative size");
+    return (size_t)-1;
+  }
+  if (pa::decode_partition_tokens(c.dtype, c.head_dim, c.block_size) == 0) {
+    fail(PA_ERR_UNSUPPORTED, "pa_decode_workspace_bytes: (dtype %d, head_dim %d, block_size %d) not built",
+         (int)c.dtype, c.head_dim, c.block_size);
+    return (size_t)-1;
+  }
+  return pa::decode_workspace_bytes(c, S, max_context_len);
+}
+
+pa_status pa_paged_decode(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, const void* query,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* context_lens, int32_t S, int32_t max_context_len, float scale,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "pa_paged_decode";
+  pa::Cache c;
+  pa_status st = check_cache(fn, cache, &c);
+  if (st != PA_OK) return st;
+  if (S < 0) return fail(PA_ERR_INVALID_ARG, "%s: S = %d < 0", fn, S);
+  if (S == 0) return PA_OK;
+  if (out_dtype != c.dtype && out_dtype != PA_F32)
+    return fail(PA_ERR_INVALID_ARG, "%s: out_dtype must be the cache dtype or PA_F32", fn);
+  if (!out || !query || !block_tables || !context_lens)
+    return fail(PA_ERR_INVALID_ARG, "%s: NULL out/query/block_tables/context_lens", fn);
+  if (!aligned(out, 16) || !aligned(query, 16))
+    return fail(PA_ERR_INVALID_ARG, "%s: out/query must be 16-byte aligned", fn);
+  if (!aligned(block_tables, 4) || !aligned(context_lens, 4))
+    return fail(PA_ERR_INVALID_ARG, "%s: block_tables/context_lens must be 4-byte aligned", fn);
+  if (max_context_len < 1) return fail(PA_ERR_INVALID_ARG, "%s: max_context_len = %d < 1", fn, max_context_len);
+  if (max_blocks_per_seq < 1 || (int64_t)max_blocks_per_seq * c.block_size < max_context_len)
+    return fail(PA_ERR_INVALID_ARG, "%s: max_blocks_per_seq = %d cannot hold %d tokens of block %d", fn,
+                max_blocks_per_seq, max_context_len, c.block_size);
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "%s: scale is not finite", fn);
+  const int P = pa::decode_partition_tokens(c.dtype, c.head_dim, c.block_size);
+  if (P == 0)
+    return fail(PA_ERR_UNSUPPORTED, "%s: (dtype %d, head_dim %d, block_size %d) not built", fn, (int)c.dtype,
+                c.head_dim, c.block_size);
+  const int64_t parts = ((int64_t)max_context_len + P - 1) / P;
+  if ((int64_t)S * c.num_heads * parts >= (int64_t)1 << 31)
+    return fail(PA_ERR_INVALID_ARG, "%s: grid of S*H*partitions does not fit", fn);
+  const size_t need = pa::decode_workspace_bytes(c, S, max_context_len);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn,
+                  workspace ? workspace_bytes : (size_t)0, need);
+    if (!aligned(workspace, 16)) return fail(PA_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned", fn);
+  }
+  return launched(fn, pa::launch_paged_decode(c, out, out_dtype, query, block_tables, max_blocks_per_seq,
+                                              context_lens, S, max_context_len, scale,
+                                              need > 0 ? workspace : nullptr, (hipStream_t)stream));
+}
+
+pa_status pa_paged_prefill(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, const void* query,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* cu_q_lens,
+                           const int32_t* context_lens, int32_t S, int32_t max_q_len, int32_t max_context_len,
+                           float scale, void* stream) {
+  const char* fn = "pa_paged_prefill";
+  pa::Cache c;
+  pa_status st = check_cache(fn, cache, &c);
+  if (st != PA_OK) return st;
+  if (S < 0) return fail(PA_ERR_INVALID_ARG, "%s: S = %d < 0", fn, S);
+  if (S == 0) return PA_OK;
+  if (out_dtype != c.dtype && out_dtype != PA_F32)
+    return fail(PA_ERR_INVALID_ARG, "%s: out_dtype must be the cache dtype or PA_F32", fn);
+  if (!out || !query || !block_tables || !cu_q_lens || !context_lens)
+    return fail(PA_ERR_INVALID_ARG, "%s: NULL out/query/block_tables/cu_q_lens/context_lens", fn);
+  if (!aligned(out, 16) || !aligned(query, 16))
+    return fail(PA_ERR_INVALID_ARG, "%s: out/query must be 16-byte aligned", fn);
+  if (!aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(cu_q_lens, 4))
+    return fail(PA_ERR_INVALID_ARG, "%s: index arrays must be 4-byte aligned", fn);
+  if (max_q_len < 1 || max_context_len < max_q_len)
+    return fail(PA_ERR_INVALID_ARG, "%s: need 1 <= max_q_len (%d) <= max_context_len (%d)", fn, max_q_len,
+                max_context_len);
+  if (max_blocks_per_seq < 1 || (int64_t)max_blocks_per_seq * c.block_size < max_context_len)
+    return fail(PA_ERR_INVALID_ARG, "%s: max_blocks_per_seq = %d cannot hold %d tokens of block %d", fn,
+                max_blocks_per_seq, max_context_len, c.block_size);
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "%s: scale is not finite", fn);
+  if (!pa::prefill_supported(c.dtype, c.head_dim, c.block_size))
+    return fail(PA_ERR_UNSUPPORTED, "%s: (dtype %d, head_dim %d, block_size %d) not built", fn, (int)c.dtype,
+                c.head_dim, c.block_size);
+  return launched(fn, pa::launch_paged_prefill(c, out, out_dtype, query, block_tables, max_blocks_per_seq,
+                                               cu_q_lens, context_lens, S, max_q_len, max_context_len, scale,
+                                               (hipStream_t)stream));
+}
+
+const char* pa_status_string(pa_status status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_INVALID_ARG: return "PA_ERR_INVALID_ARG";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE";
+    case PA_ERR_LAUNCH: return "PA_ERR_LAUNCH";
+  }
+  return "PA_ERR_UNKNOWN";
+}
+
+const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+int32_t pa_abi_version(void) { return PA_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,117 @@
+// Device helpers for gfx950: 16-byte chunk arithmetic per element type,
+// 16-lane row reductions with DPP, and output rounding.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/pagedattn.h"
+
+namespace pa {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Storage element tags; the arithmetic is always fp32.
+struct F32 { static constexpr int bytes = 4; static constexpr pa_dtype id = PA_F32; };
+struct F16 { static constexpr int bytes = 2; static constexpr pa_dtype id = PA_F16; };
+struct BF16 { static constexpr int bytes = 2; static constexpr pa_dtype id = PA_BF16; };
+
+template <typename E>
+struct Chunk {
+  static constexpr int elems = 16 / E::bytes;  // elements in 16 bytes
+};
+
+// fp32 sum of the elementwise products of two 16-byte chunks.
+__device__ __forceinline__ float dot_chunk(F32, const u32x4& a, const u32x4& b) {
+  float acc = __uint_as_float(a.x) * __uint_as_float(b.x);
+  acc = __builtin_fmaf(__uint_as_float(a.y), __uint_as_float(b.y), acc);
+  acc = __builtin_fmaf(__uint_as_float(a.z), __uint_as_float(b.z), acc);
+  acc = __builtin_fmaf(__uint_as_float(a.w), __uint_as_float(b.w), acc);
+  return acc;
+}
+__device__ __forceinline__ float dot_chunk(F16, const u32x4& a, const u32x4& b) {
+  // v_dot2_f32_f16: products of 16-bit floats are exact in fp32
+  float acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a.x), __builtin_bit_cast(f16x2, b.x), 0.f, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a.y), __builtin_bit_cast(f16x2, b.y), acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a.z), __builtin_bit_cast(f16x2, b.z), acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a.w), __builtin_bit_cast(f16x2, b.w), acc, false);
+  return acc;
+}
+__device__ __forceinline__ float dot_chunk(BF16, const u32x4& a, const u32x4& b) {
+  float acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.x), __builtin_bit_cast(bf16x2, b.x), 0.f, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.y), __builtin_bit_cast(bf16x2, b.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.z), __builtin_bit_cast(bf16x2, b.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.w), __builtin_bit_cast(bf16x2, b.w), acc, false);
+  return acc;
+}
+
+// Widen the 16-byte chunk to fp32 elements (exact).
+__device__ __forceinline__ void widen(F32, const u32x4& v, float* f) {
+  f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+  f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+}
+__device__ __forceinline__ void widen(F16, const u32x4& v, float* f) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f16x2 h = __builtin_bit_cast(f16x2, w[i]);
+    f[2 * i] = (float)h.x;
+    f[2 * i + 1] = (float)h.y;
+  }
+}
+__device__ __forceinline__ void widen(BF16, const u32x4& v, float* f) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+// ---- DPP lane exchange -------------------------------------------------------
+// Control codes of the GCN/CDNA DPP encoding.
+constexpr int kDppQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141; // lane i <-> 7-i within each 8
+constexpr int kDppRowMirror = 0x140;     // lane i <-> 15-i within each 16
+
+template <int Ctrl>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), Ctrl, 0xf, 0xf, false));
+}
+
+// Sum over each aligned group of N lanes (N a power of two <= 64); every lane
+// of the group receives the same value (each step adds two operands in an
+// order-independent way, so all lanes agree bit for bit).
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (N >= 2) x += dpp<kDppQuadXor1>(x);
+  if constexpr (N >= 4) x += dpp<kDppQuadXor2>(x);
+  if constexpr (N >= 8) x += dpp<kDppRowHalfMirror>(x);
+  if constexpr (N >= 16) x += dpp<kDppRowMirror>(x);
+  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  if constexpr (N >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+// ---- output rounding ---------------------------------------------------------
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ void store_out(void* out, int64_t idx, float val, pa_dtype t) {
+  if (t == PA_F32) {
+    ((float*)out)[idx] = val;
+  } else if (t == PA_F16) {
+    ((_Float16*)out)[idx] = (_Float16)val;
+  } else {
+    ((uint16_t*)out)[idx] = f32_to_bf16_rne(val);
+  }
+}
+
+}  // namespace pa

@@ -1,0 +1,49 @@
+// Internal declarations shared by the HIP translation units of libpagedattn.
+// Nothing here is part of the C-ABI; the public contract is include/pagedattn.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/pagedattn.h"
+
+namespace pa {
+
+// A validated copy of pa_kv_cache with sizes widened for address arithmetic.
+struct Cache {
+  void* k;
+  void* v;
+  int32_t num_blocks;
+  int32_t num_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  pa_dtype dtype;
+};
+
+inline int dtype_bytes(pa_dtype t) { return t == PA_F32 ? 4 : 2; }
+
+// ---- cache writes and copies (cache_ops.hip) ---------------------------------
+hipError_t launch_reshape_and_cache(const Cache& c, const void* key, const void* value,
+                                    const int64_t* slot_mapping, int32_t T, hipStream_t stream);
+hipError_t launch_copy_blocks(const Cache& c, const int64_t* pairs, int32_t n, hipStream_t stream);
+
+// ---- decode (paged_decode.hip) ------------------------------------------------
+// Tokens per context partition for this cache shape, or 0 if the shape is
+// not built.
+int decode_partition_tokens(pa_dtype dtype, int head_dim, int block_size);
+size_t decode_workspace_bytes(const Cache& c, int32_t S, int32_t max_context_len);
+hipError_t launch_paged_decode(const Cache& c, void* out, pa_dtype out_dtype, const void* query,
+                               const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, int32_t S, int32_t max_context_len,
+                               float scale, void* workspace, hipStream_t stream);
+
+// ---- prefill (paged_prefill.hip) ----------------------------------------------
+bool prefill_supported(pa_dtype dtype, int head_dim, int block_size);
+hipError_t launch_paged_prefill(const Cache& c, void* out, pa_dtype out_dtype, const void* query,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* cu_q_lens, const int32_t* context_lens, int32_t S,
+                                int32_t max_q_len, int32_t max_context_len, float scale,
+                                hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,328 @@
+// Paged decode attention: one query token per sequence attends to the
+// sequence's whole key/value history, read block by block through its block
+// table.
+//
+// What is computed ("vLLM / PagedAttention", awesome.papernotes.org, key
+// design 1): o = sum_j a_j v_j, a_j = exp(q.k_j * scale) / sum_t exp(q.k_t *
+// scale) over the logical history, eq. 2 of the same section evaluating it one
+// KV block at a time with each block found through the block table (key
+// design 5 fuses that block read into the attention kernel).
+//
+// gfx950 design (HBM-bound: ~1 flop per byte of K/V):
+// * Work item = (head, sequence, context partition of P tokens).  A
+//   workgroup of NW wave64s owns one item; its waves take interleaved steps of
+//   G tokens.  Long contexts therefore spread over many workgroups, and a
+//   second pass merges the partitions exactly (max-rescaled sums).
+// * Within a wave, LPT = head_dim*bytes/16 lanes hold one token's key or value
+//   row (16 bytes each), so one load instruction moves TPL = 64/LPT whole rows:
+//   1 KiB of consecutive bytes for a (block, head) tile at fp16/d=128.
+// * q.k is a 16-byte dot (v_dot2_f32_f16 / v_dot2_f32_bf16 / fma) followed by
+//   a DPP all-reduce across the LPT lanes of the row.  Each row of the wave
+//   keeps its own running max / sum / output (a log2-domain online softmax),
+//   so no cross-row traffic happens until the partition ends.
+// * The partition's slice of the block table is fetched once, one entry per
+//   lane, and broadcast with readlane: the dependent table read sits off the
+//   per-block critical path.
+// * Entries of the table at or beyond ceil(ctx/B) are never read; a block id
+//   outside the pool contributes nothing (memory stays in bounds).
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+constexpr float kNegBig = -1e30f;  // finite "minus infinity": keeps exp2 free of NaN
+constexpr float kLog2e = 1.44269504088896340736f;
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+struct DecodeArgs {
+  const u32x4* q;      // [S][H][D] as 16-byte chunks
+  const u32x4* kpool;  // [N][H][B][D]
+  const u32x4* vpool;
+  const int32_t* tables;
+  const int32_t* lens;
+  void* out;     // [S][H][D] of out_dtype
+  float* ws_o;   // [S][H][max_parts][D]   unnormalised partial outputs
+  float* ws_ml;  // [S][H][max_parts][2]   (running max in log2 units, sum)
+  int32_t S, H, N, max_blocks, max_parts;
+  float scale_log2;  // scale * log2(e)
+  pa_dtype out_dtype;
+};
+
+constexpr int cmin(int a, int b) { return a < b ? a : b; }
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
+template <typename E, int D, int BS>
+struct DecodeCfg {
+  static constexpr int VEC = 16 / E::bytes;           // elements per 16-byte chunk
+  static constexpr int LPT = D / VEC;                 // lanes per token row
+  static constexpr int TPL = 64 / LPT;                // token rows per wave-wide load
+  static constexpr int G = cmax(TPL, cmin(BS, 4 * TPL));  // tokens per step
+  static constexpr int NCH = G / TPL;                 // loads per lane per step, per pool
+  static constexpr int NW = D >= 64 ? 4 : 1;          // waves per workgroup
+  static constexpr int PT = D >= 64 ? 256 : 64;       // target tokens per partition
+  static constexpr int SPW = cmax(1, PT / (NW * G));  // steps per wave
+  static constexpr int P = NW * SPW * G;              // tokens per partition
+  static constexpr int BPP = P / BS;                  // blocks per partition
+  static_assert(D % VEC == 0 && LPT >= 1 && LPT <= 64, "unsupported head_dim");
+  static_assert(P % BS == 0 && BPP >= 1 && BPP <= 64, "partition must hold 1..64 whole blocks");
+  static_assert(G % TPL == 0 && (BS >= G ? BS % G == 0 : G % BS == 0), "step/block mismatch");
+};
+
+template <typename E, int D, int BS>
+__global__ __launch_bounds__((DecodeCfg<E, D, BS>::NW * 64)) void decode_partition_kernel(DecodeArgs a) {
+  using C = DecodeCfg<E, D, BS>;
+  constexpr int VEC = C::VEC, LPT = C::LPT, TPL = C::TPL, G = C::G, NCH = C::NCH;
+  constexpr int NW = C::NW, SPW = C::SPW, P = C::P, BPP = C::BPP;
+  __shared__ float lds_o[NW][D];
+  __shared__ float lds_m[NW];
+  __shared__ float lds_l[NW];
+
+  const int bid = blockIdx.x;
+  const int h = bid % a.H;
+  const int rest = bid / a.H;
+  const int s = rest % a.S;
+  const int p = rest / a.S;
+  // a length beyond the grid's partitions is clipped (memory stays in bounds)
+  const int ctx = min(a.lens[s], a.max_parts * P);
+  const int nparts = (ctx + P - 1) / P;
+  if (p >= nparts) return;  // uniform for the whole workgroup (also ctx < 1)
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane / LPT;  // token row within a wave-wide load
+  const int c = lane % LPT;  // 16-byte column within the row
+
+  // This partition's slice of the block table: lane k holds logical block
+  // p*BPP + k.  Entries past the sequence's last block stay unread.
+  const int nblk = (ctx + BS - 1) / BS;
+  const int jb = p * BPP;
+  int tbl = -1;
+  if (lane < BPP && jb + lane < nblk && jb + lane < a.max_blocks)
+    tbl = a.tables[(int64_t)s * a.max_blocks + jb + lane];
+
+  const u32x4 qc = a.q[((int64_t)s * a.H + h) * LPT + c];
+
+  float m = kNegBig, l = 0.f;
+  float o[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) o[e] = 0.f;
+
+  for (int g = 0; g < SPW; ++g) {
+    const int step = w + g * NW;
+    const int tb = p * P + step * G;  // first logical token of the step
+    if (tb >= ctx) break;
+    const bool full = tb + G <= ctx;
+
+    u32x4 kc[NCH], vc[NCH];
+    bool valid[NCH];
+    if constexpr (BS >= G) {
+      // the whole step lies in one block: a wave-uniform physical id
+      const int phys = __builtin_amdgcn_readlane(tbl, (step * G) / BS);
+      const bool in_pool = phys >= 0 && phys < a.N;
+      const int off0 = (step * G) % BS;
+      const int64_t base = (((int64_t)phys * a.H + h) * BS + off0 + r) * LPT + c;
+      if (full && in_pool) {
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+          kc[i] = a.kpool[base + i * TPL * LPT];
+          vc[i] = a.vpool[base + i * TPL * LPT];
+          valid[i] = true;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+          valid[i] = in_pool && (tb + i * TPL + r < ctx);
+          kc[i] = valid[i] ? a.kpool[base + i * TPL * LPT] : u32x4{0, 0, 0, 0};
+          vc[i] = valid[i] ? a.vpool[base + i * TPL * LPT] : u32x4{0, 0, 0, 0};
+        }
+      }
+    } else {
+      // several blocks per wave-wide load (B < TPL): per-row physical ids
+      static_assert(NCH == 1, "multi-block steps use one load per pool");
+      const int t = tb + r;
+      const int phys = __shfl(tbl, (t - p * P) / BS);
+      valid[0] = t < ctx && phys >= 0 && phys < a.N;
+      const int64_t idx = (((int64_t)phys * a.H + h) * BS + (t % BS)) * LPT + c;
+      kc[0] = valid[0] ? a.kpool[idx] : u32x4{0, 0, 0, 0};
+      vc[0] = valid[0] ? a.vpool[idx] : u32x4{0, 0, 0, 0};
+    }
+
+    float sc[NCH];
+    float mblk = kNegBig;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const float d = group_sum<LPT>(dot_chunk(E{}, qc, kc[i])) * a.scale_log2;
+      sc[i] = valid[i] ? d : -__builtin_inff();
+      mblk = fmaxf(mblk, sc[i]);
+    }
+    const float m_new = fmaxf(m, mblk);
+    const float alpha = fast_exp2(m - m_new);
+    l *= alpha;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) o[e] *= alpha;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const float pi = fast_exp2(sc[i] - m_new);
+      l += pi;
+      float vf[VEC];
+      widen(E{}, vc[i], vf);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) o[e] = __builtin_fmaf(pi, vf[e], o[e]);
+    }
+    m = m_new;
+  }
+
+  // Merge the TPL row streams of the wave (lanes with equal column c).
+#pragma unroll
+  for (int off = LPT; off < 64; off <<= 1) {
+    const float m2 = __shfl_xor(m, off);
+    const float l2 = __shfl_xor(l, off);
+    const float M = fmaxf(m, m2);
+    const float f1 = fast_exp2(m - M), f2 = fast_exp2(m2 - M);
+    l = l * f1 + l2 * f2;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) o[e] = o[e] * f1 + __shfl_xor(o[e], off) * f2;
+    m = M;
+  }
+  if (lane < LPT) {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) lds_o[w][c * VEC + e] = o[e];
+  }
+  if (lane == 0) {
+    lds_m[w] = m;
+    lds_l[w] = l;
+  }
+  __syncthreads();
+
+  // Merge the waves and write either the final row or this partition's part.
+  float M = kNegBig;
+#pragma unroll
+  for (int k = 0; k < NW; ++k) M = fmaxf(M, lds_m[k]);
+  float L = 0.f;
+  float fw[NW];
+#pragma unroll
+  for (int k = 0; k < NW; ++k) {
+    fw[k] = fast_exp2(lds_m[k] - M);
+    L += lds_l[k] * fw[k];
+  }
+  const int64_t sh = (int64_t)s * a.H + h;
+  for (int d = threadIdx.x; d < D; d += NW * 64) {
+    float O = 0.f;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) O += lds_o[k][d] * fw[k];
+    if (nparts == 1) {
+      store_out(a.out, sh * D + d, O / L, a.out_dtype);
+    } else {
+      a.ws_o[(sh * a.max_parts + p) * D + d] = O;
+    }
+  }
+  if (nparts > 1 && threadIdx.x == 0) {
+    a.ws_ml[(sh * a.max_parts + p) * 2] = M;
+    a.ws_ml[(sh * a.max_parts + p) * 2 + 1] = L;
+  }
+}
+
+// Second pass for sequences split into several partitions:
+// o = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p with M = max_p m_p.
+__global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeArgs a, int32_t D, int32_t P) {
+  const int bid = blockIdx.x;
+  const int h = bid % a.H;
+  const int s = bid / a.H;
+  const int ctx = min(a.lens[s], a.max_parts * P);
+  const int nparts = (ctx + P - 1) / P;
+  if (nparts <= 1) return;
+  const int64_t sh = (int64_t)s * a.H + h;
+  const float* ml = a.ws_ml + sh * a.max_parts * 2;
+  float M = kNegBig;
+  for (int q = 0; q < nparts; ++q) M = fmaxf(M, ml[2 * q]);
+  float L = 0.f;
+  for (int q = 0; q < nparts; ++q) L += ml[2 * q + 1] * fast_exp2(ml[2 * q] - M);
+  const float* po = a.ws_o + sh * a.max_parts * D;
+  for (int d = threadIdx.x; d < D; d += 64) {
+    float O = 0.f;
+    for (int q = 0; q < nparts; ++q) O += po[(int64_t)q * D + d] * fast_exp2(ml[2 * q] - M);
+    store_out(a.out, sh * D + d, O / L, a.out_dtype);
+  }
+}
+
+// ---- instantiation table -------------------------------------------------------
+struct Variant {
+  pa_dtype dtype;
+  int D, BS, P, NW;
+  void (*kernel)(DecodeArgs);
+};
+
+#define PA_DECODE_VARIANT(E, D, BS) \
+  Variant { E::id, D, BS, DecodeCfg<E, D, BS>::P, DecodeCfg<E, D, BS>::NW, decode_partition_kernel<E, D, BS> }
+
+#define PA_DECODE_ALL_TYPES(D, BS) \
+  PA_DECODE_VARIANT(F32, D, BS), PA_DECODE_VARIANT(F16, D, BS), PA_DECODE_VARIANT(BF16, D, BS)
+
+const Variant kVariants[] = {
+    PA_DECODE_ALL_TYPES(8, 4),    PA_DECODE_ALL_TYPES(8, 8),    PA_DECODE_ALL_TYPES(8, 16),
+    PA_DECODE_ALL_TYPES(64, 16),  PA_DECODE_ALL_TYPES(64, 32),
+    PA_DECODE_ALL_TYPES(128, 8),  PA_DECODE_ALL_TYPES(128, 16), PA_DECODE_ALL_TYPES(128, 32),
+    PA_DECODE_ALL_TYPES(128, 64), PA_DECODE_ALL_TYPES(128, 128),
+    PA_DECODE_ALL_TYPES(256, 16), PA_DECODE_ALL_TYPES(256, 32),
+};
+
+const Variant* find_variant(pa_dtype dtype, int D, int BS) {
+  for (const Variant& v : kVariants)
+    if (v.dtype == dtype && v.D == D && v.BS == BS) return &v;
+  return nullptr;
+}
+
+int64_t max_parts_for(const Variant& v, int32_t max_context_len) {
+  return ((int64_t)max_context_len + v.P - 1) / v.P;
+}
+
+}  // namespace
+
+int decode_partition_tokens(pa_dtype dtype, int head_dim, int block_size) {
+  const Variant* v = find_variant(dtype, head_dim, block_size);
+  return v ? v->P : 0;
+}
+
+size_t decode_workspace_bytes(const Cache& c, int32_t S, int32_t max_context_len) {
+  const Variant* v = find_variant(c.dtype, c.head_dim, c.block_size);
+  if (!v) return (size_t)-1;
+  const int64_t mp = max_parts_for(*v, max_context_len);
+  if (mp <= 1) return 0;
+  return (size_t)S * c.num_heads * mp * (c.head_dim + 2) * sizeof(float);
+}
+
+hipError_t launch_paged_decode(const Cache& c, void* out, pa_dtype out_dtype, const void* query,
+                               const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, int32_t S, int32_t max_context_len,
+                               float scale, void* workspace, hipStream_t stream) {
+  const Variant* v = find_variant(c.dtype, c.head_dim, c.block_size);
+  if (!v) return hipErrorInvalidValue;
+  const int64_t mp = max_parts_for(*v, max_context_len);
+  DecodeArgs a;
+  a.q = (const u32x4*)query;
+  a.kpool = (const u32x4*)c.k;
+  a.vpool = (const u32x4*)c.v;
+  a.tables = block_tables;
+  a.lens = context_lens;
+  a.out = out;
+  a.ws_o = (float*)workspace;
+  a.ws_ml = workspace ? (float*)workspace + (size_t)S * c.num_heads * mp * c.head_dim : nullptr;
+  a.S = S;
+  a.H = c.num_heads;
+  a.N = c.num_blocks;
+  a.max_blocks = max_blocks_per_seq;
+  a.max_parts = (int32_t)mp;
+  a.scale_log2 = scale * kLog2e;
+  a.out_dtype = out_dtype;
+  const int64_t grid = (int64_t)S * c.num_heads * mp;
+  hipLaunchKernelGGL(v->kernel, dim3((unsigned)grid), dim3(v->NW * 64), 0, stream, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || mp <= 1) return err;
+  hipLaunchKernelGGL(decode_reduce_kernel, dim3((unsigned)(S * c.num_heads)), dim3(64), 0, stream, a,
+                     (int32_t)c.head_dim, (int32_t)v->P);
+  return hipGetLastError();
+}
+
+}  // namespace pa

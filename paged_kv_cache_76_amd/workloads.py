@@ -1,0 +1,113 @@
+"""Synthetic paged-decode workloads at the pages' shapes, built through the
+host block manager and the C-ABI (the K/V histories are written into the
+pools by ``pa_reshape_and_cache``).
+
+The pages measure on OPT models (OPT-13B: 40 heads of 128, 2-byte KV) with
+ShareGPT/Alpaca length mixes that are not available here; these seeded
+generators stand in for them (see :mod:`paged_kv_cache_76_amd.inputs`).
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from . import inputs
+from ._lib import KVCache, pa_reshape_and_cache
+from .block_manager import BlockManager
+
+TORCH = inputs.DTYPES
+
+# children of a workload's seed: 0 lengths, 1 queries, 2 keys, 3 values,
+# 4 pool order, 5 decode-step tokens, 6 beam choices
+STREAMS = 7
+
+
+@dataclass
+class DecodeBatch:
+    """One layer's paged cache plus one decode step's inputs, resident on the
+    device, with the host copies the checkers read."""
+
+    cache: KVCache
+    manager: BlockManager
+    q: torch.Tensor            # host [S][H][d], storage dtype
+    k_hist: list               # host per sequence [L_s][H][d]
+    v_hist: list
+    q_dev: torch.Tensor
+    tables_dev: torch.Tensor   # int32 [S][max_blocks]
+    lens_dev: torch.Tensor     # int32 [S]
+    lens: np.ndarray
+    max_context_len: int
+    scale: float
+
+    @property
+    def S(self) -> int:
+        return self.q.shape[0]
+
+
+def pool_blocks(lens, block_size: int, slack: float = 1.10, extra: int = 0) -> int:
+    """Physical blocks for the histories plus ``slack`` head-room (and
+    ``extra`` blocks for later growth)."""
+    need = int(sum(-(-int(L) // block_size) for L in lens))
+    return max(1, int(math.ceil(need * slack)) + extra)
+
+
+def build_decode_batch(config_index: int, lens, num_heads: int, head_dim: int, block_size: int,
+                       dtype: str, device: str = "cuda", slack: float = 1.10, extra_blocks: int = 0,
+                       grow_tokens: int = 0, nan_fill: bool = True) -> DecodeBatch:
+    """Histories of ``lens[s]`` tokens each (the last one is the token being
+    decoded), written through seeded-shuffled blocks, plus one query per
+    sequence.
+
+    The device pool has one block more than the manager owns: that block (id
+    ``num_blocks``, the table's poison id) and every slot never written are
+    filled with NaN, so a read of anything outside a sequence's history shows
+    up in the output.
+    """
+    lens = np.asarray(lens, dtype=np.int64)
+    S = len(lens)
+    _, r_q, r_k, r_v, r_pool = inputs.streams(config_index, STREAMS)
+    N = pool_blocks(lens, block_size, slack, extra_blocks)
+    max_blocks = -(-(int(lens.max()) + grow_tokens) // block_size)
+    mgr = BlockManager(N, block_size, max_rows=S, max_blocks_per_seq=max_blocks,
+                       free_order=inputs.pool_order(r_pool, N))
+    total = int(lens.sum())
+    k_all = inputs.normal(r_k, (total, num_heads, head_dim), dtype)
+    v_all = inputs.normal(r_v, (total, num_heads, head_dim), dtype)
+    q = inputs.normal(r_q, (S, num_heads, head_dim), dtype)
+    cuts = np.concatenate([[0], np.cumsum(lens)])
+    k_hist = [k_all[cuts[s]:cuts[s + 1]] for s in range(S)]
+    v_hist = [v_all[cuts[s]:cuts[s + 1]] for s in range(S)]
+    slots = np.concatenate([mgr.add_prompt(s, int(lens[s])) for s in range(S)])
+
+    cache = KVCache.empty(N + 1, num_heads, block_size, head_dim, TORCH[dtype], device)
+    if nan_fill:
+        cache.k.fill_(float("nan"))
+        cache.v.fill_(float("nan"))
+    pa_reshape_and_cache(cache, k_all.to(device), v_all.to(device),
+                         torch.from_numpy(slots).to(device))
+    return DecodeBatch(
+        cache=cache, manager=mgr, q=q, k_hist=k_hist, v_hist=v_hist, q_dev=q.to(device),
+        tables_dev=torch.from_numpy(mgr.tables).to(device),
+        lens_dev=torch.from_numpy(lens.astype(np.int32)).to(device),
+        lens=lens, max_context_len=int(lens.max()), scale=1.0 / math.sqrt(head_dim))
+
+
+def opt13b_decode_lengths(config_index: int = 2, S: int = 64, lo: int = 1, hi: int = 2048) -> np.ndarray:
+    """Context lengths of the OPT-13B decode workload: uniform on [1, 2048]."""
+    r_len = inputs.streams(config_index, STREAMS)[0]
+    return inputs.uniform_lengths(r_len, S, lo, hi)
+
+
+def decode_bytes(lens, num_heads: int, head_dim: int, elem_bytes: int, block_size: int) -> int:
+    """Algorithmic HBM bytes of one decode launch: every valid K and V row
+    once, q and out once, and the table entries in use."""
+    lens = np.asarray(lens, dtype=np.int64)
+    S = len(lens)
+    kv = int(lens.sum()) * 2 * num_heads * head_dim * elem_bytes
+    qo = 2 * S * num_heads * head_dim * elem_bytes
+    tbl = 4 * int(sum(-(-int(L) // block_size) for L in lens))
+    return kv + qo + tbl + 4 * S
