@@ -31,19 +31,26 @@ __device__ __forceinline__ float dot_chunk(F32, const u32x4& a, const u32x4& b) 
   acc = __builtin_fmaf(__uint_as_float(a.w), __uint_as_float(b.w), acc);
   return acc;
 }
+// Reinterpret one 32-bit word as two 16-bit floats.  The word is taken by
+// value: a bit-cast applied directly to an ext_vector element (``v.y``) is
+// compiled as a read of element 0 by this clang, so callers pass ``v.x`` etc.
+// through these helpers instead.
+__device__ __forceinline__ f16x2 as_f16x2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2, u); }
+
 __device__ __forceinline__ float dot_chunk(F16, const u32x4& a, const u32x4& b) {
   // v_dot2_f32_f16: products of 16-bit floats are exact in fp32
-  float acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a.x), __builtin_bit_cast(f16x2, b.x), 0.f, false);
-  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a.y), __builtin_bit_cast(f16x2, b.y), acc, false);
-  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a.z), __builtin_bit_cast(f16x2, b.z), acc, false);
-  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a.w), __builtin_bit_cast(f16x2, b.w), acc, false);
+  float acc = __builtin_amdgcn_fdot2(as_f16x2(a.x), as_f16x2(b.x), 0.f, false);
+  acc = __builtin_amdgcn_fdot2(as_f16x2(a.y), as_f16x2(b.y), acc, false);
+  acc = __builtin_amdgcn_fdot2(as_f16x2(a.z), as_f16x2(b.z), acc, false);
+  acc = __builtin_amdgcn_fdot2(as_f16x2(a.w), as_f16x2(b.w), acc, false);
   return acc;
 }
 __device__ __forceinline__ float dot_chunk(BF16, const u32x4& a, const u32x4& b) {
-  float acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.x), __builtin_bit_cast(bf16x2, b.x), 0.f, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.y), __builtin_bit_cast(bf16x2, b.y), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.z), __builtin_bit_cast(bf16x2, b.z), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.w), __builtin_bit_cast(bf16x2, b.w), acc, false);
+  float acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a.x), as_bf16x2(b.x), 0.f, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a.y), as_bf16x2(b.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a.z), as_bf16x2(b.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a.w), as_bf16x2(b.w), acc, false);
   return acc;
 }
 
@@ -56,7 +63,7 @@ __device__ __forceinline__ void widen(F16, const u32x4& v, float* f) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const f16x2 h = __builtin_bit_cast(f16x2, w[i]);
+    const f16x2 h = as_f16x2(w[i]);
     f[2 * i] = (float)h.x;
     f[2 * i + 1] = (float)h.y;
   }

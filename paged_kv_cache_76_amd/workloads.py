@@ -55,21 +55,29 @@ def pool_blocks(lens, block_size: int, slack: float = 1.10, extra: int = 0) -> i
     return max(1, int(math.ceil(need * slack)) + extra)
 
 
-def build_decode_batch(config_index: int, lens, num_heads: int, head_dim: int, block_size: int,
-                       dtype: str, device: str = "cuda", slack: float = 1.10, extra_blocks: int = 0,
-                       grow_tokens: int = 0, nan_fill: bool = True) -> DecodeBatch:
-    """Histories of ``lens[s]`` tokens each (the last one is the token being
-    decoded), written through seeded-shuffled blocks, plus one query per
-    sequence.
+@dataclass
+class HostHistories:
+    """The host half of a decode batch: histories, queries, block manager and
+    the slots the histories go to."""
 
-    The device pool has one block more than the manager owns: that block (id
-    ``num_blocks``, the table's poison id) and every slot never written are
-    filled with NaN, so a read of anything outside a sequence's history shows
-    up in the output.
-    """
+    manager: BlockManager
+    q: torch.Tensor
+    k_all: torch.Tensor        # [sum L][H][d], sequences back to back
+    v_all: torch.Tensor
+    k_hist: list
+    v_hist: list
+    slots: np.ndarray          # int64 [sum L]
+    lens: np.ndarray
+
+
+def host_histories(config_index: int, lens, num_heads: int, head_dim: int, block_size: int,
+                   dtype: str, slack: float = 1.10, extra_blocks: int = 0,
+                   grow_tokens: int = 0) -> HostHistories:
+    """Seeded histories of ``lens[s]`` tokens, placed by the block manager
+    into a seeded-shuffled pool of ``pool_blocks(lens) + extra_blocks``."""
     lens = np.asarray(lens, dtype=np.int64)
     S = len(lens)
-    _, r_q, r_k, r_v, r_pool = inputs.streams(config_index, STREAMS)
+    _, r_q, r_k, r_v, r_pool = inputs.streams(config_index, STREAMS)[:5]
     N = pool_blocks(lens, block_size, slack, extra_blocks)
     max_blocks = -(-(int(lens.max()) + grow_tokens) // block_size)
     mgr = BlockManager(N, block_size, max_rows=S, max_blocks_per_seq=max_blocks,
@@ -82,18 +90,35 @@ def build_decode_batch(config_index: int, lens, num_heads: int, head_dim: int, b
     k_hist = [k_all[cuts[s]:cuts[s + 1]] for s in range(S)]
     v_hist = [v_all[cuts[s]:cuts[s + 1]] for s in range(S)]
     slots = np.concatenate([mgr.add_prompt(s, int(lens[s])) for s in range(S)])
+    return HostHistories(mgr, q, k_all, v_all, k_hist, v_hist, slots, lens)
 
-    cache = KVCache.empty(N + 1, num_heads, block_size, head_dim, TORCH[dtype], device)
+
+def build_decode_batch(config_index: int, lens, num_heads: int, head_dim: int, block_size: int,
+                       dtype: str, device: str = "cuda", slack: float = 1.10, extra_blocks: int = 0,
+                       grow_tokens: int = 0, nan_fill: bool = True) -> DecodeBatch:
+    """Histories of ``lens[s]`` tokens each (the last one is the token being
+    decoded), written through seeded-shuffled blocks, plus one query per
+    sequence.
+
+    The device pool has one block more than the manager owns: that block (id
+    ``num_blocks``, the table's poison id) and every slot never written are
+    filled with NaN, so a read of anything outside a sequence's history shows
+    up in the output.
+    """
+    h = host_histories(config_index, lens, num_heads, head_dim, block_size, dtype, slack,
+                       extra_blocks, grow_tokens)
+    mgr = h.manager
+    cache = KVCache.empty(mgr.num_blocks + 1, num_heads, block_size, head_dim, TORCH[dtype], device)
     if nan_fill:
         cache.k.fill_(float("nan"))
         cache.v.fill_(float("nan"))
-    pa_reshape_and_cache(cache, k_all.to(device), v_all.to(device),
-                         torch.from_numpy(slots).to(device))
+    pa_reshape_and_cache(cache, h.k_all.to(device), h.v_all.to(device),
+                         torch.from_numpy(h.slots).to(device))
     return DecodeBatch(
-        cache=cache, manager=mgr, q=q, k_hist=k_hist, v_hist=v_hist, q_dev=q.to(device),
+        cache=cache, manager=mgr, q=h.q, k_hist=h.k_hist, v_hist=h.v_hist, q_dev=h.q.to(device),
         tables_dev=torch.from_numpy(mgr.tables).to(device),
-        lens_dev=torch.from_numpy(lens.astype(np.int32)).to(device),
-        lens=lens, max_context_len=int(lens.max()), scale=1.0 / math.sqrt(head_dim))
+        lens_dev=torch.from_numpy(h.lens.astype(np.int32)).to(device),
+        lens=h.lens, max_context_len=int(h.lens.max()), scale=1.0 / math.sqrt(head_dim))
 
 
 def opt13b_decode_lengths(config_index: int = 2, S: int = 64, lo: int = 1, hi: int = 2048) -> np.ndarray:
