@@ -62,7 +62,36 @@ def blas_threads() -> int:
         return 1
 
 
-def cpu_baseline(batch, n_seq: int, repeats: int = 3) -> dict:
+COUNTERS = os.path.join(ROOT, "profiles", "decode_opt13b_fp16_b16_counters.txt")
+DECODE_SOURCES = ("paged_kv_cache_76_amd/csrc/paged_decode.hip", "paged_kv_cache_76_amd/csrc/pa_device.h")
+
+
+def measured_traffic() -> float | None:
+    """HBM bytes per pa_paged_decode launch from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE runs (scaled by the copy-kernel calibration), or
+    None if the decode sources changed since those counters were taken."""
+    import hashlib
+
+    try:
+        kv = {}
+        for line in open(COUNTERS):
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+        h = hashlib.sha256()
+        for f in DECODE_SOURCES:
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+        if h.hexdigest() != kv["kernel_source_sha256"]:
+            return None
+        fs, ws = float(kv["fetch_scale"]), float(kv["write_scale"])
+        kib = (float(kv["decode_partition_kernel_fetch_kib"]) + float(kv["decode_reduce_kernel_fetch_kib"])) * fs \
+            + (float(kv["decode_partition_kernel_write_kib"]) + float(kv["decode_reduce_kernel_write_kib"])) * ws
+        return kib * 1024.0
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(batch, n_seq: int, repeats: int = 10) -> dict:
     """The float64 oracle on the first ``n_seq`` sequences of the step (all
     heads), timed on this host's cores."""
     import numpy as np
@@ -90,12 +119,54 @@ def cpu_baseline(batch, n_seq: int, repeats: int = 3) -> dict:
     }
 
 
+def copy_calibration(args) -> int:
+    """pa_copy_blocks of 2048 (src, dst) pairs of OPT-13B blocks (40 heads x 16
+    tokens x 128 x fp16 = 160 KiB per pool): 640 MiB read + 640 MiB written per
+    launch.  Its HBM counters, divided by these known sizes, give the scale
+    factors applied to the decode kernel's counters."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_76_amd import _lib as L
+
+    n, N = 2048, 4096
+    cache = L.KVCache.empty(N, H, B, D, torch.float16)
+    cache.k.fill_(1.0)
+    cache.v.fill_(2.0)
+    ids = np.random.default_rng(0).permutation(N)
+    pairs = torch.from_numpy(np.stack([ids[:n], ids[n:]], axis=1).astype(np.int64)).cuda()
+    for _ in range(args.warmup):
+        L.pa_copy_blocks(cache, pairs)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record()
+        L.pa_copy_blocks(cache, pairs)
+        b.record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    avg_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    moved = 2 * 2 * n * H * B * D * ELEM           # read + write, keys and values
+    rec = {"metric": "pa_copy_blocks HBM GB/s (read + write), 2048 OPT-13B blocks", "value": round(moved / (avg_ms * 1e-3) / 1e9, 2),
+           "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(elapsed / args.steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+           "config": {"workload": "pa_copy_blocks calibration", "pairs": n, "bytes_read_per_launch": moved // 2,
+                      "bytes_written_per_launch": moved // 2}}
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seqs", type=int, default=64, help="sequences in the CPU-oracle sample (0: skip)")
+    ap.add_argument("--workload", choices=["decode", "copy"], default="decode",
+                    help="decode: the OPT-13B decode step (default); copy: pa_copy_blocks over 2048 "
+                         "OPT-13B blocks, a plain copy of known size used to calibrate HBM counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU layout is a design "
@@ -110,6 +181,8 @@ def main() -> int:
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.workload == "copy":
+        return copy_calibration(args)
     K, W = args.steps, args.warmup
     n_steps = K + W
 
@@ -181,6 +254,7 @@ def main() -> int:
         log(f"timing the CPU oracle on {args.cpu_seqs} sequences")
         cpu = cpu_baseline(batch, args.cpu_seqs)
 
+    traffic = measured_traffic()
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -201,9 +275,9 @@ def main() -> int:
         "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "seq_steps_per_s": round(S * K / elapsed, 1),
         "host_block_manager_ms_per_step": round(sum(host_ms) / len(host_ms), 4),
-        "roofline": {"bound": "hbm", "kernel": "pa_paged_decode", "achieved": round(dec_gbs, 2),
+        "roofline": {"bound": "hbm", "kernel": "pa_paged_decode (partition + merge kernels)", "achieved": round(dec_gbs, 2),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
-                     "traffic": None, "avg_launch_us": round(dec_avg_ms * 1e3, 2),
+                     "traffic": traffic, "avg_launch_us": round(dec_avg_ms * 1e3, 2),
                      "algorithmic_bytes_per_launch": int(sum(dec_bytes) / K)},
         "cpu_baseline": cpu,
     }

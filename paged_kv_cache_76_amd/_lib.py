@@ -49,16 +49,9 @@ class PaKVCache(ctypes.Structure):
 _lib = None
 
 
-def lib() -> ctypes.CDLL:
-    """Load the shared library (once); raise if it has not been built."""
-    global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(
-            f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_76_amd.build` "
-            "(there is no non-HIP fallback)")
-    L = ctypes.CDLL(LIB_PATH)
+def load_library(path: str) -> ctypes.CDLL:
+    """Open a build of libpagedattn at ``path`` and declare its C signatures."""
+    L = ctypes.CDLL(path)
     P, I32, I64P, I32P = ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p
     C = ctypes.POINTER(PaKVCache)
     L.pa_reshape_and_cache.argtypes = [C, P, P, I64P, I32, P]
@@ -77,8 +70,20 @@ def lib() -> ctypes.CDLL:
     L.pa_last_error.restype = ctypes.c_char_p
     L.pa_abi_version.argtypes = []
     L.pa_abi_version.restype = ctypes.c_int32
-    _lib = L
     return L
+
+
+def lib() -> ctypes.CDLL:
+    """Load the in-tree shared library (once); raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_76_amd.build` "
+            "(there is no non-HIP fallback)")
+    _lib = load_library(LIB_PATH)
+    return _lib
 
 
 def _check(status: int) -> None:

@@ -11,8 +11,8 @@
 // gfx950 design (HBM-bound: ~1 flop per byte of K/V):
 // * Work item = (head, sequence, context partition of P tokens).  A
 //   workgroup of NW wave64s owns one item; its waves take interleaved steps of
-//   G tokens.  Long contexts therefore spread over many workgroups, and a
-//   second pass merges the partitions exactly (max-rescaled sums).
+//   G tokens.  Long contexts therefore spread over many workgroups, and the
+//   partitions are merged exactly (max-rescaled sums) afterwards.
 // * Within a wave, LPT = head_dim*bytes/16 lanes hold one token's key or value
 //   row (16 bytes each), so one load instruction moves TPL = 64/LPT whole rows:
 //   1 KiB of consecutive bytes for a (block, head) tile at fp16/d=128.
@@ -20,13 +20,40 @@
 //   a DPP all-reduce across the LPT lanes of the row.  Each row of the wave
 //   keeps its own running max / sum / output (a log2-domain online softmax),
 //   so no cross-row traffic happens until the partition ends.
-// * The partition's slice of the block table is fetched once, one entry per
-//   lane, and broadcast with readlane: the dependent table read sits off the
-//   per-block critical path.
+// * A wave keeps a 64-entry window of the block table in one register (one
+//   entry per lane) and broadcasts entries with readlane, so the dependent
+//   table read sits off the per-block critical path.
 // * Entries of the table at or beyond ceil(ctx/B) are never read; a block id
 //   outside the pool contributes nothing (memory stays in bounds).
 #include "pa_device.h"
 #include "pa_internal.h"
+
+// Tuning knobs.  Defaults are the measured best at the OPT-13B shape (64 x 40
+// heads, d=128, fp16, B=16, contexts U[1,2048]) on MI355X: non-temporal K/V
+// loads are worth ~14% (the K/V stream is read once and must not evict the
+// table, q and partials from L2); 8 waves x 1024-token partitions beat 4 x 256
+// by ~4%.  FUSED (the last partition merges the others after a device-scope
+// fence) is kept as a knob only: the fence costs milliseconds on this part.
+#ifndef PA_DECODE_NW
+#define PA_DECODE_NW 8  // waves per workgroup (head_dim >= 64)
+#endif
+#ifndef PA_DECODE_PT
+#define PA_DECODE_PT 1024  // tokens per context partition (head_dim >= 64)
+#endif
+#ifndef PA_DECODE_NT
+#define PA_DECODE_NT 1  // 1: non-temporal K/V loads
+#endif
+#ifndef PA_DECODE_FUSED
+#define PA_DECODE_FUSED 0  // 1: the last partition of a (sequence, head) merges all of them
+#endif
+#ifndef PA_DECODE_MINW
+#define PA_DECODE_MINW 0  // >0: ask for at least this many waves per SIMD (caps VGPRs)
+#endif
+#if PA_DECODE_MINW > 0
+#define PA_DECODE_OCC __attribute__((amdgpu_waves_per_eu(PA_DECODE_MINW)))
+#else
+#define PA_DECODE_OCC
+#endif
 
 namespace pa {
 namespace {
@@ -35,6 +62,14 @@ constexpr float kNegBig = -1e30f;  // finite "minus infinity": keeps exp2 free o
 constexpr float kLog2e = 1.44269504088896340736f;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ u32x4 load_kv(const u32x4* p) {
+#if PA_DECODE_NT
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
 
 struct DecodeArgs {
   const u32x4* q;      // [S][H][D] as 16-byte chunks
@@ -45,6 +80,7 @@ struct DecodeArgs {
   void* out;     // [S][H][D] of out_dtype
   float* ws_o;   // [S][H][max_parts][D]   unnormalised partial outputs
   float* ws_ml;  // [S][H][max_parts][2]   (running max in log2 units, sum)
+  int32_t* counters;  // [S][H] arrivals per (sequence, head); zero between calls
   int32_t S, H, N, max_blocks, max_parts;
   float scale_log2;  // scale * log2(e)
   pa_dtype out_dtype;
@@ -55,26 +91,59 @@ constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 template <typename E, int D, int BS>
 struct DecodeCfg {
-  static constexpr int VEC = 16 / E::bytes;           // elements per 16-byte chunk
-  static constexpr int LPT = D / VEC;                 // lanes per token row
-  static constexpr int TPL = 64 / LPT;                // token rows per wave-wide load
+  static constexpr int VEC = 16 / E::bytes;               // elements per 16-byte chunk
+  static constexpr int LPT = D / VEC;                     // lanes per token row
+  static constexpr int TPL = 64 / LPT;                    // token rows per wave-wide load
   static constexpr int G = cmax(TPL, cmin(BS, 4 * TPL));  // tokens per step
-  static constexpr int NCH = G / TPL;                 // loads per lane per step, per pool
-  static constexpr int NW = D >= 64 ? 4 : 1;          // waves per workgroup
-  static constexpr int PT = D >= 64 ? 256 : 64;       // target tokens per partition
-  static constexpr int SPW = cmax(1, PT / (NW * G));  // steps per wave
-  static constexpr int P = NW * SPW * G;              // tokens per partition
-  static constexpr int BPP = P / BS;                  // blocks per partition
+  static constexpr int NCH = G / TPL;                     // loads per lane per step, per pool
+  static constexpr bool SMALL = D < 64;
+  static constexpr int NW = SMALL ? 1 : PA_DECODE_NW;     // waves per workgroup
+  static constexpr int PT = SMALL ? 64 : PA_DECODE_PT;    // target tokens per partition
+  static constexpr int STEPS = cmax(1, PT / G);           // steps per partition
+  static constexpr int P = STEPS * G;                     // tokens per partition
   static_assert(D % VEC == 0 && LPT >= 1 && LPT <= 64, "unsupported head_dim");
-  static_assert(P % BS == 0 && BPP >= 1 && BPP <= 64, "partition must hold 1..64 whole blocks");
   static_assert(G % TPL == 0 && (BS >= G ? BS % G == 0 : G % BS == 0), "step/block mismatch");
+  static_assert(P % BS == 0, "a partition holds whole blocks");
+  static_assert(BS >= G || P / BS <= 64, "multi-block steps keep the partition's table in one register");
 };
 
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) x = fmaxf(x, __shfl_xor(x, off));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+// Merge of the partitions of one (sequence, head) split into several:
+// o = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p with M = max_p m_p.
+// Every thread of the block computes M and L (the pairs are few and shared
+// through the cache); thread t then owns dims t, t + nthreads, ...
+__device__ __forceinline__ void merge_partitions(const DecodeArgs& a, int64_t sh, int nparts, int D,
+                                                 int tid, int nthreads) {
+  const float* ml = a.ws_ml + sh * a.max_parts * 2;
+  const float* po = a.ws_o + sh * a.max_parts * D;
+  float M = kNegBig;
+  for (int q = 0; q < nparts; ++q) M = fmaxf(M, ml[2 * q]);
+  float L = 0.f;
+  for (int q = 0; q < nparts; ++q) L += ml[2 * q + 1] * fast_exp2(ml[2 * q] - M);
+  const float inv_L = 1.f / L;
+  for (int d = tid; d < D; d += nthreads) {
+    float O = 0.f;
+#pragma unroll 4
+    for (int q = 0; q < nparts; ++q) O += po[(int64_t)q * D + d] * fast_exp2(ml[2 * q] - M);
+    store_out(a.out, sh * D + d, O * inv_L, a.out_dtype);
+  }
+}
+
 template <typename E, int D, int BS>
-__global__ __launch_bounds__((DecodeCfg<E, D, BS>::NW * 64)) void decode_partition_kernel(DecodeArgs a) {
+__global__ __launch_bounds__((DecodeCfg<E, D, BS>::NW * 64)) PA_DECODE_OCC void decode_partition_kernel(DecodeArgs a) {
   using C = DecodeCfg<E, D, BS>;
   constexpr int VEC = C::VEC, LPT = C::LPT, TPL = C::TPL, G = C::G, NCH = C::NCH;
-  constexpr int NW = C::NW, SPW = C::SPW, P = C::P, BPP = C::BPP;
+  constexpr int NW = C::NW, STEPS = C::STEPS, P = C::P;
   __shared__ float lds_o[NW][D];
   __shared__ float lds_m[NW];
   __shared__ float lds_l[NW];
@@ -94,13 +163,16 @@ __global__ __launch_bounds__((DecodeCfg<E, D, BS>::NW * 64)) void decode_partiti
   const int r = lane / LPT;  // token row within a wave-wide load
   const int c = lane % LPT;  // 16-byte column within the row
 
-  // This partition's slice of the block table: lane k holds logical block
-  // p*BPP + k.  Entries past the sequence's last block stay unread.
-  const int nblk = (ctx + BS - 1) / BS;
-  const int jb = p * BPP;
-  int tbl = -1;
-  if (lane < BPP && jb + lane < nblk && jb + lane < a.max_blocks)
-    tbl = a.tables[(int64_t)s * a.max_blocks + jb + lane];
+  const int nblk = (ctx + BS - 1) / BS;  // logical blocks of the sequence
+  const int jb = p * (P / BS);           // first logical block of the partition
+  const int64_t trow = (int64_t)s * a.max_blocks;
+  // table window: lane k holds logical block jb + wbase + k (-1 past the end)
+  auto window = [&](int wbase) {
+    const int j = jb + wbase + lane;
+    return (j < nblk && j < a.max_blocks) ? a.tables[trow + j] : -1;
+  };
+  int wbase = 0;
+  int tbl = window(0);
 
   const u32x4 qc = a.q[((int64_t)s * a.H + h) * LPT + c];
 
@@ -109,33 +181,37 @@ __global__ __launch_bounds__((DecodeCfg<E, D, BS>::NW * 64)) void decode_partiti
 #pragma unroll
   for (int e = 0; e < VEC; ++e) o[e] = 0.f;
 
-  for (int g = 0; g < SPW; ++g) {
-    const int step = w + g * NW;
+  const int nsteps = min(STEPS, (ctx - p * P + G - 1) / G);
+  for (int step = w; step < nsteps; step += NW) {
     const int tb = p * P + step * G;  // first logical token of the step
-    if (tb >= ctx) break;
     const bool full = tb + G <= ctx;
 
     u32x4 kc[NCH], vc[NCH];
     bool valid[NCH];
     if constexpr (BS >= G) {
       // the whole step lies in one block: a wave-uniform physical id
-      const int phys = __builtin_amdgcn_readlane(tbl, (step * G) / BS);
+      const int jl = (step * G) / BS;
+      if (jl >= wbase + 64) {
+        wbase = jl;
+        tbl = window(wbase);
+      }
+      const int phys = __builtin_amdgcn_readlane(tbl, jl - wbase);
       const bool in_pool = phys >= 0 && phys < a.N;
       const int off0 = (step * G) % BS;
       const int64_t base = (((int64_t)phys * a.H + h) * BS + off0 + r) * LPT + c;
       if (full && in_pool) {
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
-          kc[i] = a.kpool[base + i * TPL * LPT];
-          vc[i] = a.vpool[base + i * TPL * LPT];
+          kc[i] = load_kv(&a.kpool[base + i * TPL * LPT]);
+          vc[i] = load_kv(&a.vpool[base + i * TPL * LPT]);
           valid[i] = true;
         }
       } else {
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
           valid[i] = in_pool && (tb + i * TPL + r < ctx);
-          kc[i] = valid[i] ? a.kpool[base + i * TPL * LPT] : u32x4{0, 0, 0, 0};
-          vc[i] = valid[i] ? a.vpool[base + i * TPL * LPT] : u32x4{0, 0, 0, 0};
+          kc[i] = valid[i] ? load_kv(&a.kpool[base + i * TPL * LPT]) : u32x4{0, 0, 0, 0};
+          vc[i] = valid[i] ? load_kv(&a.vpool[base + i * TPL * LPT]) : u32x4{0, 0, 0, 0};
         }
       }
     } else {
@@ -145,8 +221,8 @@ __global__ __launch_bounds__((DecodeCfg<E, D, BS>::NW * 64)) void decode_partiti
       const int phys = __shfl(tbl, (t - p * P) / BS);
       valid[0] = t < ctx && phys >= 0 && phys < a.N;
       const int64_t idx = (((int64_t)phys * a.H + h) * BS + (t % BS)) * LPT + c;
-      kc[0] = valid[0] ? a.kpool[idx] : u32x4{0, 0, 0, 0};
-      vc[0] = valid[0] ? a.vpool[idx] : u32x4{0, 0, 0, 0};
+      kc[0] = valid[0] ? load_kv(&a.kpool[idx]) : u32x4{0, 0, 0, 0};
+      vc[0] = valid[0] ? load_kv(&a.vpool[idx]) : u32x4{0, 0, 0, 0};
     }
 
     float sc[NCH];
@@ -222,28 +298,68 @@ __global__ __launch_bounds__((DecodeCfg<E, D, BS>::NW * 64)) void decode_partiti
     a.ws_ml[(sh * a.max_parts + p) * 2] = M;
     a.ws_ml[(sh * a.max_parts + p) * 2 + 1] = L;
   }
+#if PA_DECODE_FUSED
+  if (nparts > 1) {
+    // publish this partition, count arrivals; the last one merges them all
+    __shared__ int lds_last;
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) lds_last = atomicAdd(&a.counters[sh], 1) == nparts - 1;
+    __syncthreads();
+    if (!lds_last) return;
+    __threadfence();
+    merge_partitions(a, sh, nparts, D, threadIdx.x, NW * 64);
+    if (threadIdx.x == 0) atomicExch(&a.counters[sh], 0);  // ready for the next call
+  }
+#endif
 }
 
-// Second pass for sequences split into several partitions:
+// Merge of the partitions of each (sequence, head) split into several:
 // o = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p with M = max_p m_p.
+// One wave per (sequence, head): the (m_p, l_p) pairs are read in parallel,
+// one per lane, and the weights go through LDS to the lanes owning the dims.
+constexpr int kReduceChunk = 256;  // partitions whose weights sit in LDS at once
+
 __global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeArgs a, int32_t D, int32_t P) {
+  __shared__ float lds_w[kReduceChunk];
   const int bid = blockIdx.x;
   const int h = bid % a.H;
   const int s = bid / a.H;
   const int ctx = min(a.lens[s], a.max_parts * P);
   const int nparts = (ctx + P - 1) / P;
   if (nparts <= 1) return;
+  const int lane = threadIdx.x;
   const int64_t sh = (int64_t)s * a.H + h;
   const float* ml = a.ws_ml + sh * a.max_parts * 2;
-  float M = kNegBig;
-  for (int q = 0; q < nparts; ++q) M = fmaxf(M, ml[2 * q]);
-  float L = 0.f;
-  for (int q = 0; q < nparts; ++q) L += ml[2 * q + 1] * fast_exp2(ml[2 * q] - M);
   const float* po = a.ws_o + sh * a.max_parts * D;
-  for (int d = threadIdx.x; d < D; d += 64) {
-    float O = 0.f;
-    for (int q = 0; q < nparts; ++q) O += po[(int64_t)q * D + d] * fast_exp2(ml[2 * q] - M);
-    store_out(a.out, sh * D + d, O / L, a.out_dtype);
+  float mloc = kNegBig;
+  for (int q = lane; q < nparts; q += 64) mloc = fmaxf(mloc, ml[2 * q]);
+  const float M = wave_max(mloc);
+  float lloc = 0.f;
+  for (int q = lane; q < nparts; q += 64) lloc += ml[2 * q + 1] * fast_exp2(ml[2 * q] - M);
+  const float inv_L = 1.f / wave_sum(lloc);
+  constexpr int kMaxDimsPerLane = 4;  // head_dim <= 256
+  float O[kMaxDimsPerLane] = {0.f, 0.f, 0.f, 0.f};
+  for (int q0 = 0; q0 < nparts; q0 += kReduceChunk) {
+    const int nq = min(kReduceChunk, nparts - q0);
+    __syncthreads();
+    for (int q = lane; q < nq; q += 64) lds_w[q] = fast_exp2(ml[2 * (q0 + q)] - M);
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kMaxDimsPerLane; ++k) {
+      const int d = lane + 64 * k;
+      if (d < D) {
+        float acc = 0.f;
+#pragma unroll 8
+        for (int q = 0; q < nq; ++q) acc += po[(int64_t)(q0 + q) * D + d] * lds_w[q];
+        O[k] += acc;
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kMaxDimsPerLane; ++k) {
+    const int d = lane + 64 * k;
+    if (d < D) store_out(a.out, sh * D + d, O[k] * inv_L, a.out_dtype);
   }
 }
 
@@ -274,6 +390,10 @@ const Variant* find_variant(pa_dtype dtype, int D, int BS) {
   return nullptr;
 }
 
+size_t counter_bytes(int32_t S, int32_t H) {
+  return ((size_t)S * H * sizeof(int32_t) + 255) / 256 * 256;
+}
+
 int64_t max_parts_for(const Variant& v, int32_t max_context_len) {
   return ((int64_t)max_context_len + v.P - 1) / v.P;
 }
@@ -290,7 +410,7 @@ size_t decode_workspace_bytes(const Cache& c, int32_t S, int32_t max_context_len
   if (!v) return (size_t)-1;
   const int64_t mp = max_parts_for(*v, max_context_len);
   if (mp <= 1) return 0;
-  return (size_t)S * c.num_heads * mp * (c.head_dim + 2) * sizeof(float);
+  return counter_bytes(S, c.num_heads) + (size_t)S * c.num_heads * mp * (c.head_dim + 2) * sizeof(float);
 }
 
 hipError_t launch_paged_decode(const Cache& c, void* out, pa_dtype out_dtype, const void* query,
@@ -307,8 +427,11 @@ hipError_t launch_paged_decode(const Cache& c, void* out, pa_dtype out_dtype, co
   a.tables = block_tables;
   a.lens = context_lens;
   a.out = out;
-  a.ws_o = (float*)workspace;
-  a.ws_ml = workspace ? (float*)workspace + (size_t)S * c.num_heads * mp * c.head_dim : nullptr;
+  // workspace: [counters S*H int32, padded to 256 B][partial o][partial (m, l)]
+  const size_t cbytes = counter_bytes(S, c.num_heads);
+  a.counters = workspace ? (int32_t*)workspace : nullptr;
+  a.ws_o = workspace ? (float*)((char*)workspace + cbytes) : nullptr;
+  a.ws_ml = workspace ? a.ws_o + (size_t)S * c.num_heads * mp * c.head_dim : nullptr;
   a.S = S;
   a.H = c.num_heads;
   a.N = c.num_blocks;
@@ -319,7 +442,7 @@ hipError_t launch_paged_decode(const Cache& c, void* out, pa_dtype out_dtype, co
   const int64_t grid = (int64_t)S * c.num_heads * mp;
   hipLaunchKernelGGL(v->kernel, dim3((unsigned)grid), dim3(v->NW * 64), 0, stream, a);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || mp <= 1) return err;
+  if (err != hipSuccess || mp <= 1 || PA_DECODE_FUSED) return err;
   hipLaunchKernelGGL(decode_reduce_kernel, dim3((unsigned)(S * c.num_heads)), dim3(64), 0, stream, a,
                      (int32_t)c.head_dim, (int32_t)v->P);
   return hipGetLastError();
