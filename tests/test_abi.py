@@ -102,10 +102,10 @@ def test_decode_argument_checks():
     _err(call(maxb=2), "cannot hold")
     _err(call(maxctx=0), "max_context_len")
     _err(call(scale=float("inf")), "scale")
-    need = lib.pa_decode_workspace_bytes(ctypes.byref(d), 4, 600)
+    need = lib.pa_decode_workspace_bytes(ctypes.byref(d), 4, 6000)
     assert need > 0
-    assert call(maxb=64, maxctx=600, ws=FAKE, wsb=need - 1) == L.PA_ERR_WORKSPACE
-    assert call(maxb=64, maxctx=600, ws=None, wsb=need) == L.PA_ERR_WORKSPACE
+    assert call(maxb=400, maxctx=6000, ws=FAKE, wsb=need - 1) == L.PA_ERR_WORKSPACE
+    assert call(maxb=400, maxctx=6000, ws=None, wsb=need) == L.PA_ERR_WORKSPACE
     d2 = _desc(head_dim=48)
     assert lib.pa_paged_decode(ctypes.byref(d2), FAKE, L.PA_F16, FAKE, FAKE, 8, FAKE, 4, 100, 0.1, None, 0,
                                None) == L.PA_ERR_UNSUPPORTED
@@ -116,10 +116,15 @@ def test_workspace_size_formula():
     d = _desc(num_heads=40)
     # a context that fits one partition needs no workspace
     assert lib.pa_decode_workspace_bytes(ctypes.byref(d), 64, 16) == 0
-    n1 = lib.pa_decode_workspace_bytes(ctypes.byref(d), 64, 2048)
-    n2 = lib.pa_decode_workspace_bytes(ctypes.byref(d), 128, 2048)
-    assert n1 > 0 and n2 == 2 * n1
-    assert n1 % (64 * 40 * (128 + 2) * 4) == 0
+    # layout: per-(sequence, head) counters padded to 256 bytes, then one
+    # (d + 2)-float partial per (sequence, head, partition)
+    def counters(S):
+        return -(-(S * 40 * 4) // 256) * 256
+
+    n1 = lib.pa_decode_workspace_bytes(ctypes.byref(d), 64, 8192)
+    n2 = lib.pa_decode_workspace_bytes(ctypes.byref(d), 128, 8192)
+    assert n1 > 0 and n2 - counters(128) == 2 * (n1 - counters(64))
+    assert (n1 - counters(64)) % (64 * 40 * (128 + 2) * 4) == 0
     bad = _desc(head_dim=48)
     assert lib.pa_decode_workspace_bytes(ctypes.byref(bad), 4, 100) == ctypes.c_size_t(-1).value
 
