@@ -158,15 +158,74 @@ def copy_calibration(args) -> int:
     return 0
 
 
+PEAK_BF16_TFLOPS = 2500.0
+
+
+def prefill_bench(args) -> int:
+    """8 prompts x 1024 tokens, 72 heads, d=128, bf16, block 16 (OPT-66B
+    layer shape): one step writes the prompts' K/V through their slots and runs
+    the causal paged prefill."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_76_amd import _lib as L
+    from paged_kv_cache_76_amd import workloads
+
+    S5, H5, L5 = 8, 72, 1024
+    lens = [L5] * S5
+    log(f"building OPT-66B prefill workload: {S5} x {L5} tokens, H={H5}, d={D}, bf16, B={B}")
+    b = workloads.build_prefill_batch(5, lens, lens, H5, D, B, "bf16", nan_fill=False)
+    h = workloads.host_histories(5, lens, H5, D, B, "bf16")
+    k_all, v_all = h.k_all.cuda(), h.v_all.cuda()
+    slots = torch.from_numpy(h.slots).cuda()
+    out = torch.empty((S5 * L5, H5, D), dtype=torch.bfloat16, device="cuda")
+    flops = workloads.prefill_flops(lens, lens, H5, D)
+    wbytes = 2 * 2 * S5 * L5 * H5 * D * 2
+    n = args.steps + args.warmup
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+    for i in range(n):
+        if i == args.warmup:
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+        ev[i][0].record()
+        L.pa_reshape_and_cache(b.cache, k_all, v_all, slots)
+        ev[i][1].record()
+        L.pa_paged_prefill(b.cache, out, b.q_dev, b.tables_dev, b.cu_q_dev, b.lens_dev, L5, L5, b.scale)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    K = args.steps
+    w_ms = sum(ev[i][0].elapsed_time(ev[i][1]) for i in range(args.warmup, n)) / K
+    p_ms = sum(ev[i][1].elapsed_time(ev[i][2]) for i in range(args.warmup, n)) / K
+    tflops = flops / (p_ms * 1e-3) / 1e12
+    log(f"prefill {p_ms * 1e3:.1f} us -> {tflops:.1f} TFLOP/s; write {w_ms * 1e3:.1f} us -> "
+        f"{wbytes / (w_ms * 1e-3) / 1e9:.0f} GB/s")
+    rec = {"metric": "paged causal prefill TFLOP/s, OPT-66B shape (8 x 1024 tokens, 72 heads, d128, bf16)",
+           "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+           "ms_per_step": round(elapsed / K * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "paged prefill step (prompt write + causal prefill)", "prompts": S5,
+                      "prompt_len": L5, "heads": H5, "head_dim": D, "block_size": B,
+                      "seed": "SeedSequence(76005)"},
+           "roofline": {"bound": "mfma", "kernel": "pa_paged_prefill", "achieved": round(tflops, 2),
+                        "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                        "traffic": None, "avg_launch_us": round(p_ms * 1e3, 2), "algorithmic_flops_per_launch": flops},
+           "write": {"kernel": "pa_reshape_and_cache", "avg_launch_us": round(w_ms * 1e3, 2),
+                     "achieved_GBps": round(wbytes / (w_ms * 1e-3) / 1e9, 1), "bytes_per_launch": wbytes}}
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seqs", type=int, default=64, help="sequences in the CPU-oracle sample (0: skip)")
-    ap.add_argument("--workload", choices=["decode", "copy"], default="decode",
+    ap.add_argument("--workload", choices=["decode", "copy", "prefill"], default="decode",
                     help="decode: the OPT-13B decode step (default); copy: pa_copy_blocks over 2048 "
-                         "OPT-13B blocks, a plain copy of known size used to calibrate HBM counters")
+                         "OPT-13B blocks, a plain copy of known size used to calibrate HBM counters; "
+                         "prefill: 8 x 1024-token prompts at the OPT-66B shape (write + causal prefill)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU layout is a design "
@@ -183,6 +242,8 @@ def main() -> int:
     torch.cuda.set_device(0)
     if args.workload == "copy":
         return copy_calibration(args)
+    if args.workload == "prefill":
+        return prefill_bench(args)
     K, W = args.steps, args.warmup
     n_steps = K + W
 

@@ -1,14 +1,333 @@
-// Paged causal prefill (MFMA) — not built yet: every shape reports unsupported.
+// Paged causal prefill: every prompt token attends to the positions up to and
+// including its own, with keys and values read through the block table.
+//
+// What is computed ("vLLM / PagedAttention", awesome.papernotes.org, key
+// design 1): for query i, o_i = sum_{j<=i} a_ij v_j with a_ij = softmax over
+// t <= i of q_i.k_t * scale (eq. 1), the keys/values being gathered block by
+// block through the sequence's block table (eq. 2).  The queries of sequence s
+// are its last q_len_s logical positions; q_len_s = context_len_s is the plain
+// prompt case.
+//
+// gfx950 design (a dense contraction, so MFMA; 128 queries x 64 keys tiles):
+// * Workgroup = 4 wave64s = 128 queries of one (sequence, head); wave w owns
+//   queries 32w..32w+31.  Key/value tiles of 64 tokens are gathered from their
+//   physical blocks (16-byte loads) into LDS: keys as [token][d] rows, values
+//   transposed to [d][token] rows (registers do the 4x8 transpose with
+//   v_perm_b32), both row-padded against bank conflicts.
+// * Scores are formed transposed, S^T = K Q^T, with
+//   v_mfma_f32_32x32x16_{bf16,f16}: the result layout puts one query per lane
+//   column, so the online softmax of a query is in-lane except for one
+//   exchange between the two half-waves.
+// * O^T += V^T P^T with the same MFMA: the B operand P^T for a 16-key step is
+//   exactly 8 of the lane's own score registers (rounded to 16 bits), so P
+//   never leaves the registers; the A operand is two 8-byte LDS reads of V^T.
+// * Tiles entirely above the diagonal are never loaded; the diagonal ones are
+//   masked per element.  Workgroups are issued heaviest-first (last query tile
+//   first).
+#include "pa_device.h"
 #include "pa_internal.h"
 
 namespace pa {
+namespace {
 
-bool prefill_supported(pa_dtype, int, int) { return false; }
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-hipError_t launch_paged_prefill(const Cache&, void*, pa_dtype, const void*, const int32_t*, int32_t,
-                                const int32_t*, const int32_t*, int32_t, int32_t, int32_t, float,
-                                hipStream_t) {
-  return hipErrorNotSupported;
+constexpr int kD = 128;        // head_dim
+constexpr int kBM = 128;       // queries per workgroup
+constexpr int kBN = 64;        // keys per tile
+constexpr int kWaves = 4;
+constexpr int kKRow = kD + 8;  // padded LDS row of a key (elements)
+constexpr int kVRow = kBN + 4; // padded LDS row of a transposed value (elements)
+constexpr float kNegBig = -1e30f;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+__device__ __forceinline__ f32x16 mfma32(BF16, u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(F16, u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                0, 0);
+}
+
+// two fp32 -> one dword of two 16-bit floats (round to nearest even)
+__device__ __forceinline__ uint32_t pack2(BF16, float x, float y) {
+  bf16x2 v = {(__bf16)x, (__bf16)y};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint32_t pack2(F16, float x, float y) {
+  f16x2 v = {(_Float16)x, (_Float16)y};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// sum of the eight 16-bit floats held in a 16-byte operand (exact widening)
+__device__ __forceinline__ float sum_unpacked(BF16, u32x4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc += __uint_as_float(w[i] << 16) + __uint_as_float(w[i] & 0xffff0000u);
+  return acc;
+}
+__device__ __forceinline__ float sum_unpacked(F16, u32x4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f16x2 h = as_f16x2(w[i]);
+    acc += (float)h.x + (float)h.y;
+  }
+  return acc;
+}
+
+struct PrefillArgs {
+  const u32x4* q;  // [sum q][H][D] 16-byte chunks
+  const u32x4* kpool;
+  const u32x4* vpool;
+  const int32_t* tables;
+  const int32_t* cu_q;
+  const int32_t* lens;
+  void* out;
+  int32_t S, H, N, max_blocks, ntiles;  // ntiles = ceil(max_q_len / kBM)
+  float scale_log2;
+  pa_dtype out_dtype;
+};
+
+template <typename E, int BS>
+__global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
+  static_assert(BS >= 4 && (kBN % BS == 0 || BS % kBN == 0), "block size must tile the 64-key step");
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[kBN * kKRow];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_vt[kD * kVRow];
+
+  // heaviest tiles first: the last query tile of every (sequence, head) leads
+  const int per_tile = a.S * a.H;
+  const int tile = a.ntiles - 1 - (int)(blockIdx.x / per_tile);
+  const int rem = blockIdx.x % per_tile;
+  const int s = rem / a.H;
+  const int h = rem % a.H;
+  const int q_begin = a.cu_q[s];
+  const int qlen = a.cu_q[s + 1] - q_begin;
+  const int ctx = a.lens[s];
+  const int q0 = tile * kBM;  // first query row of this workgroup (within the sequence)
+  if (q0 >= qlen || qlen > ctx) return;
+  const int pos0 = ctx - qlen;  // logical position of query row 0
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int g = lane >> 5;     // half-wave
+  const int col = lane & 31;   // this lane's query column
+  const int qrow = q0 + 32 * w + col;
+  const bool qvalid = qrow < qlen;
+  const int qpos = pos0 + qrow;
+
+  // B operand of S^T = K Q^T: Q[query][16ks + 8g .. +8] for k-steps ks = 0..7
+  u32x4 qb[8];
+  {
+    const int64_t qbase = ((int64_t)(q_begin + (qvalid ? qrow : 0)) * a.H + h) * (kD / 8);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qb[ks] = qvalid ? a.q[qbase + 2 * ks + g] : u32x4{0, 0, 0, 0};
+  }
+
+  f32x16 acc_o[4];
+#pragma unroll
+  for (int dm = 0; dm < 4; ++dm)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc_o[dm][i] = 0.f;
+  float m = kNegBig, l = 0.f;
+
+  // keys needed by the workgroup: positions 0 .. pos0 + min(q0 + kBM, qlen) - 1
+  const int last_pos = pos0 + min(q0 + kBM, qlen) - 1;
+  const int nkt = last_pos / kBN + 1;
+  const int wave_min_pos = pos0 + q0 + 32 * w;  // smallest query position of this wave
+
+  // cooperative tile load: thread -> keys 4*kg .. 4*kg+3, dims 8*dc .. 8*dc+7
+  const int kg = tid >> 4;
+  const int dc = tid & 15;
+  const int64_t trow = (int64_t)s * a.max_blocks;
+
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int j0 = kt * kBN;
+    u32x4 kr[4], vr[4];
+    {
+      const int jk = j0 + 4 * kg;  // first of this thread's 4 keys (same block: BS >= 4)
+      const int blk = jk / BS;
+      int phys = (jk < ctx && blk < a.max_blocks) ? a.tables[trow + blk] : -1;
+      const bool ok = phys >= 0 && phys < a.N;
+      const int off = jk % BS;
+      const int64_t base = (((int64_t)(ok ? phys : 0) * a.H + h) * BS + off) * (kD / 8) + dc;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool valid = ok && (jk + u < ctx);
+        kr[u] = valid ? a.kpool[base + u * (kD / 8)] : u32x4{0, 0, 0, 0};
+        vr[u] = valid ? a.vpool[base + u * (kD / 8)] : u32x4{0, 0, 0, 0};
+      }
+    }
+    __syncthreads();  // the previous tile's LDS reads are done
+#pragma unroll
+    for (int u = 0; u < 4; ++u) *(u32x4*)&lds_k[(4 * kg + u) * kKRow + 8 * dc] = kr[u];
+    {
+      // 4 keys x 8 dims -> 8 rows of V^T, 4 keys each
+      const uint32_t w0[4] = {vr[0].x, vr[0].y, vr[0].z, vr[0].w};
+      const uint32_t w1[4] = {vr[1].x, vr[1].y, vr[1].z, vr[1].w};
+      const uint32_t w2[4] = {vr[2].x, vr[2].y, vr[2].z, vr[2].w};
+      const uint32_t w3[4] = {vr[3].x, vr[3].y, vr[3].z, vr[3].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        u32x2 lo, hi;  // dims 8dc+2i (low halves) and 8dc+2i+1 (high halves)
+        lo.x = __builtin_amdgcn_perm(w1[i], w0[i], 0x05040100u);
+        lo.y = __builtin_amdgcn_perm(w3[i], w2[i], 0x05040100u);
+        hi.x = __builtin_amdgcn_perm(w1[i], w0[i], 0x07060302u);
+        hi.y = __builtin_amdgcn_perm(w3[i], w2[i], 0x07060302u);
+        *(u32x2*)&lds_vt[(8 * dc + 2 * i) * kVRow + 4 * kg] = lo;
+        *(u32x2*)&lds_vt[(8 * dc + 2 * i + 1) * kVRow + 4 * kg] = hi;
+      }
+    }
+    __syncthreads();
+
+    // S^T tile: keys 32mb + (result rows), this lane's query = column
+    f32x16 acc_s[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc_s[mb][i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const u32x4 ka = *(const u32x4*)&lds_k[(32 * mb + col) * kKRow + 16 * ks + 8 * g];
+        acc_s[mb] = mfma32(E{}, ka, qb[ks], acc_s[mb]);
+      }
+    }
+
+    // online softmax (log2 domain); key of result element i: 32mb + 8(i/4) + 4g + i%4
+    const bool needs_mask = j0 + kBN - 1 > wave_min_pos;
+    float mt = kNegBig;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float sv = acc_s[mb][i] * a.scale_log2;
+        if (needs_mask) {
+          const int kpos = j0 + 32 * mb + 8 * (i / 4) + 4 * g + (i % 4);
+          sv = kpos <= qpos ? sv : -__builtin_inff();
+        }
+        acc_s[mb][i] = sv;
+        mt = fmaxf(mt, sv);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(m, mt);
+    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+    m = m_new;
+    l *= alpha;
+#pragma unroll
+    for (int dm = 0; dm < 4; ++dm)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc_o[dm][i] *= alpha;
+
+    // P^T operands: k-step (mb, t) takes result elements 8t .. 8t+7 of block mb
+    u32x4 pb[2][2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        float p[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(acc_s[mb][8 * t + j] - m_new);
+        pb[mb][t] = u32x4{pack2(E{}, p[0], p[1]), pack2(E{}, p[2], p[3]), pack2(E{}, p[4], p[5]),
+                          pack2(E{}, p[6], p[7])};
+        // the denominator sums the same rounded weights the MFMA multiplies
+        l += sum_unpacked(E{}, pb[mb][t]);
+      }
+
+    // O^T += V^T P^T; k-slot (g, j) of step (mb, t) is key 32mb + 16t + 8(j/4) + 4g + j%4
+#pragma unroll
+    for (int dm = 0; dm < 4; ++dm)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const uint16_t* vrow = &lds_vt[(32 * dm + col) * kVRow + 32 * mb + 16 * t + 4 * g];
+          const u32x2 v0 = *(const u32x2*)vrow;
+          const u32x2 v1 = *(const u32x2*)(vrow + 8);
+          const u32x4 va = {v0.x, v0.y, v1.x, v1.y};
+          acc_o[dm] = mfma32(E{}, va, pb[mb][t], acc_o[dm]);
+        }
+  }
+
+  // normalise and store: result element i of block dm is dim 32dm + 8(i/4) + 4g + i%4
+  l += __shfl_xor(l, 32);
+  if (!qvalid) return;
+  const float inv_l = 1.f / l;
+  const int64_t obase = ((int64_t)(q_begin + qrow) * a.H + h) * kD;
+#pragma unroll
+  for (int dm = 0; dm < 4; ++dm)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int d = 32 * dm + 8 * r4 + 4 * g;
+      const float o0 = acc_o[dm][4 * r4] * inv_l, o1 = acc_o[dm][4 * r4 + 1] * inv_l;
+      const float o2 = acc_o[dm][4 * r4 + 2] * inv_l, o3 = acc_o[dm][4 * r4 + 3] * inv_l;
+      if (a.out_dtype == PA_F32) {
+        float4 v = {o0, o1, o2, o3};
+        *(float4*)((float*)a.out + obase + d) = v;
+      } else if (a.out_dtype == E::id) {
+        u32x2 v = {pack2(E{}, o0, o1), pack2(E{}, o2, o3)};
+        *(u32x2*)((uint16_t*)a.out + obase + d) = v;
+      }
+    }
+}
+
+struct Variant {
+  pa_dtype dtype;
+  int BS;
+  void (*kernel)(PrefillArgs);
+};
+
+#define PA_PREFILL_VARIANTS(BS) \
+  Variant{PA_BF16, BS, prefill_kernel<BF16, BS>}, Variant { PA_F16, BS, prefill_kernel<F16, BS> }
+
+const Variant kVariants[] = {PA_PREFILL_VARIANTS(16), PA_PREFILL_VARIANTS(32), PA_PREFILL_VARIANTS(64),
+                             PA_PREFILL_VARIANTS(128)};
+
+const Variant* find_variant(pa_dtype dtype, int head_dim, int block_size) {
+  if (head_dim != kD) return nullptr;
+  for (const Variant& v : kVariants)
+    if (v.dtype == dtype && v.BS == block_size) return &v;
+  return nullptr;
+}
+
+}  // namespace
+
+bool prefill_supported(pa_dtype dtype, int head_dim, int block_size) {
+  return find_variant(dtype, head_dim, block_size) != nullptr;
+}
+
+hipError_t launch_paged_prefill(const Cache& c, void* out, pa_dtype out_dtype, const void* query,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* cu_q_lens, const int32_t* context_lens, int32_t S,
+                                int32_t max_q_len, int32_t max_context_len, float scale,
+                                hipStream_t stream) {
+  (void)max_context_len;
+  const Variant* v = find_variant(c.dtype, c.head_dim, c.block_size);
+  if (!v) return hipErrorInvalidValue;
+  PrefillArgs a;
+  a.q = (const u32x4*)query;
+  a.kpool = (const u32x4*)c.k;
+  a.vpool = (const u32x4*)c.v;
+  a.tables = block_tables;
+  a.cu_q = cu_q_lens;
+  a.lens = context_lens;
+  a.out = out;
+  a.S = S;
+  a.H = c.num_heads;
+  a.N = c.num_blocks;
+  a.max_blocks = max_blocks_per_seq;
+  a.ntiles = (max_q_len + kBM - 1) / kBM;
+  a.scale_log2 = scale * kLog2e;
+  a.out_dtype = out_dtype;
+  const int64_t grid = (int64_t)a.ntiles * S * c.num_heads;
+  hipLaunchKernelGGL(v->kernel, dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace pa

@@ -136,3 +136,61 @@ def decode_bytes(lens, num_heads: int, head_dim: int, elem_bytes: int, block_siz
     qo = 2 * S * num_heads * head_dim * elem_bytes
     tbl = 4 * int(sum(-(-int(L) // block_size) for L in lens))
     return kv + qo + tbl + 4 * S
+
+
+@dataclass
+class PrefillBatch:
+    """Prompts whose K/V sit in the paged cache, plus the query rows of the
+    last ``q_lens[s]`` positions of each, resident on the device."""
+
+    cache: KVCache
+    manager: BlockManager
+    q: torch.Tensor            # host [sum q][H][d]
+    k_hist: list
+    v_hist: list
+    q_dev: torch.Tensor
+    tables_dev: torch.Tensor
+    cu_q_dev: torch.Tensor     # int32 [S+1]
+    lens_dev: torch.Tensor
+    lens: np.ndarray
+    q_lens: np.ndarray
+    cu_q: np.ndarray
+    scale: float
+
+
+def build_prefill_batch(config_index: int, lens, q_lens, num_heads: int, head_dim: int, block_size: int,
+                        dtype: str, device: str = "cuda", slack: float = 1.10,
+                        nan_fill: bool = True) -> PrefillBatch:
+    """Histories of ``lens[s]`` tokens written through seeded-shuffled blocks
+    (as :func:`build_decode_batch`), and seeded queries for the last
+    ``q_lens[s]`` positions of every sequence."""
+    lens = np.asarray(lens, dtype=np.int64)
+    q_lens = np.asarray(q_lens, dtype=np.int64)
+    if q_lens.shape != lens.shape or np.any(q_lens < 1) or np.any(q_lens > lens):
+        raise ValueError("need 1 <= q_lens[s] <= lens[s]")
+    h = host_histories(config_index, lens, num_heads, head_dim, block_size, dtype, slack)
+    r_step = inputs.streams(config_index, STREAMS)[5]
+    q = inputs.normal(r_step, (int(q_lens.sum()), num_heads, head_dim), dtype)
+    mgr = h.manager
+    cache = KVCache.empty(mgr.num_blocks + 1, num_heads, block_size, head_dim, TORCH[dtype], device)
+    if nan_fill:
+        cache.k.fill_(float("nan"))
+        cache.v.fill_(float("nan"))
+    pa_reshape_and_cache(cache, h.k_all.to(device), h.v_all.to(device), torch.from_numpy(h.slots).to(device))
+    cu_q = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    return PrefillBatch(
+        cache=cache, manager=mgr, q=q, k_hist=h.k_hist, v_hist=h.v_hist, q_dev=q.to(device),
+        tables_dev=torch.from_numpy(mgr.tables).to(device), cu_q_dev=torch.from_numpy(cu_q).to(device),
+        lens_dev=torch.from_numpy(lens.astype(np.int32)).to(device), lens=lens, q_lens=q_lens, cu_q=cu_q,
+        scale=1.0 / math.sqrt(head_dim))
+
+
+def prefill_flops(lens, q_lens, num_heads: int, head_dim: int) -> int:
+    """Algorithmic flops of causal prefill: 2 matmuls x 2 flops x d for every
+    (query, key <= query) pair."""
+    total = 0
+    for L, n in zip(np.asarray(lens, np.int64), np.asarray(q_lens, np.int64)):
+        first = int(L - n)
+        # query positions first .. L-1 attend to first+1 .. L keys
+        total += (n * (first + 1) + n * (n - 1) // 2)
+    return 4 * head_dim * num_heads * int(total)

@@ -1,0 +1,93 @@
+"""GPU parity of pa_paged_prefill (MFMA) against the float64 oracle's causal
+attention over the logically contiguous prompt."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as oa
+from paged_kv_cache_76_amd import _lib as L
+from paged_kv_cache_76_amd import inputs, workloads
+
+from gpu_util import TOL, check_close
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(b, out_dtype=torch.float32):
+    out = torch.empty((int(b.q_lens.sum()), b.cache.num_heads, b.cache.head_dim), dtype=out_dtype, device="cuda")
+    L.pa_paged_prefill(b.cache, out, b.q_dev, b.tables_dev, b.cu_q_dev, b.lens_dev, int(b.q_lens.max()),
+                       int(b.lens.max()), b.scale)
+    torch.cuda.synchronize()
+    return out
+
+
+def _oracle(b, s, rows=None, heads=None):
+    K = inputs.to_f64(b.k_hist[s])
+    V = inputs.to_f64(b.v_hist[s])
+    Q = inputs.to_f64(b.q[b.cu_q[s]:b.cu_q[s + 1]])
+    if rows is None and heads is None:
+        return oa.prefill(Q, K, V, b.scale)
+    first = int(b.lens[s] - b.q_lens[s])
+    return np.stack([np.stack([oa.attend(Q[i, h], K[: first + i + 1, h], V[: first + i + 1, h], b.scale)
+                               for h in heads]) for i in rows])
+
+
+@pytest.mark.parametrize("dtype,B", [("bf16", 16), ("f16", 16), ("bf16", 32), ("f16", 64), ("bf16", 128)])
+def test_prompt_lengths(dtype, B):
+    print(f"prefill {dtype} B={B}", flush=True)
+    lens = [1, 63, 64, 65, 127, 128, 129, 300]
+    b = workloads.build_prefill_batch(5, lens, lens, num_heads=2, head_dim=128, block_size=B, dtype=dtype)
+    out = _run(b)
+    for s in range(len(lens)):
+        check_close(out[b.cu_q[s]:b.cu_q[s + 1]], _oracle(b, s), TOL[dtype], f"prefill {dtype} B={B} seq {s}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_queries_are_the_last_positions(dtype):
+    # q_len < context_len: the queries are the last q_len logical positions
+    lens, qlens = [300, 257, 40, 129], [77, 257, 1, 128]
+    b = workloads.build_prefill_batch(6, lens, qlens, num_heads=3, head_dim=128, block_size=16, dtype=dtype)
+    out = _run(b)
+    for s in range(len(lens)):
+        check_close(out[b.cu_q[s]:b.cu_q[s + 1]], _oracle(b, s), TOL[dtype], f"partial prefill seq {s}")
+
+
+def test_storage_dtype_output():
+    lens = [200, 90]
+    b = workloads.build_prefill_batch(7, lens, lens, num_heads=2, head_dim=128, block_size=16, dtype="bf16")
+    out = _run(b, out_dtype=torch.bfloat16)
+    for s in range(2):
+        check_close(out[b.cu_q[s]:b.cu_q[s + 1]], _oracle(b, s), TOL["bf16"], f"prefill bf16 out seq {s}")
+
+
+def test_constant_values_and_permutation_invariance():
+    lens = [150, 70]
+    a = workloads.build_prefill_batch(8, lens, lens, num_heads=2, head_dim=128, block_size=16, dtype="bf16")
+    b = workloads.build_prefill_batch(8, lens, lens, num_heads=2, head_dim=128, block_size=16, dtype="bf16",
+                                      slack=1.7)
+    assert not np.array_equal(a.manager.tables[:, :2], b.manager.tables[:, :2])
+    assert torch.equal(_run(a).view(torch.int32), _run(b).view(torch.int32))
+    for s, Ls in enumerate(lens):
+        ones = torch.ones((Ls, 2, 128), dtype=torch.bfloat16)
+        slots = torch.tensor([a.manager.slot(s, p) for p in range(Ls)], dtype=torch.int64)
+        L.pa_reshape_and_cache(a.cache, a.k_hist[s].cuda(), ones.cuda(), slots.cuda())
+    out = _run(a)
+    assert torch.allclose(out, torch.ones_like(out), atol=1e-6, rtol=0)
+
+
+@pytest.mark.slow
+def test_opt66b_prefill_full_size_sampled():
+    # 8 prompts of 1024 tokens, 72 heads, d=128, bf16, B=16 shuffled blocks
+    print("prefill OPT-66B full size (sampled check)", flush=True)
+    lens = [1024] * 8
+    b = workloads.build_prefill_batch(5, lens, lens, num_heads=72, head_dim=128, block_size=16, dtype="bf16")
+    out = _run(b)
+    assert torch.isfinite(out).all()
+    r = np.random.default_rng(1)
+    for s in (0, 3, 7):
+        rows = sorted(set([0, 1, 127, 128, 511, 1023] + r.choice(1024, 6, replace=False).tolist()))
+        heads = [0, 35, 71]
+        ref = _oracle(b, s, rows, heads)
+        got = out[b.cu_q[s]:b.cu_q[s + 1]][rows][:, heads]
+        check_close(got, ref, TOL["bf16"], f"OPT-66B prefill seq {s}")
