@@ -216,16 +216,186 @@ def prefill_bench(args) -> int:
     return 0
 
 
+def _line(metric, value, unit, steps, warmup, ms_per_step, dtype, config, **extra) -> None:
+    rec = {"metric": metric, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": steps,
+           "warmup": warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": dtype, "data": "synthetic", "config": config}
+    rec.update(extra)
+    print(json.dumps(rec), flush=True)
+
+
+def serving_bench(args) -> int:
+    """32 consecutive steps of a 256-sequence serving loop at the OPT-13B
+    shape (fp16), block size 16 and 32.  The host block-manager work of all
+    steps runs first (timed on its own); the device loop then runs from
+    inputs already in HBM.  A second, interleaved pass (host step -> pinned
+    upload -> kernels, every step) gives the wall time per step."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_76_amd import workloads
+    from paged_kv_cache_76_amd.serving import ServingLoop, opt13b_serving_lengths
+
+    prompt, out, start = opt13b_serving_lengths(3, 256)
+    steps = 32
+    for bs in (16, 32):
+        log(f"serving loop: 256 seqs, B={bs}")
+        # device pass: every step's plan made ahead and resident in HBM
+        loop = ServingLoop(3, prompt, out, start, H, D, bs, DTYPE, keep_history=False)
+        counts = loop.active_counts(steps)
+        toks = [loop.tokens(n, "cuda") for n in counts]
+        prepared = []
+        for t in range(steps):
+            rows = loop.active_rows()
+            assert len(rows) == counts[t]
+            host, lens = loop.plan(rows)
+            loop.finish(rows)
+            prepared.append((rows, {k: v.cuda() for k, v in host.items()}, lens))
+        bm_ms = loop.bm_seconds / steps * 1e3
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        from paged_kv_cache_76_amd import _lib as L
+        outs = torch.empty((256, H, D), dtype=torch.float16, device="cuda")
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i, (rows, dev, lens) in enumerate(prepared):
+            k, v, q = toks[i]
+            ev[i][0].record()
+            if dev["pairs"].shape[0]:
+                L.pa_copy_blocks(loop.cache, dev["pairs"])
+            L.pa_reshape_and_cache(loop.cache, k, v, dev["slots"])
+            L.pa_paged_decode(loop.cache, outs[: len(rows)], q, dev["tables"], dev["lens"],
+                              int(lens.max()), loop.scale, loop.ws)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        gpu_s = time.perf_counter() - t0
+        step_ms = [a.elapsed_time(b) for a, b in ev]
+        seq_steps = sum(len(r) for r, _, _ in prepared)
+        nbytes = sum(workloads.decode_bytes(lens, H, D, ELEM, bs) + 4 * len(rows) * H * D * ELEM
+                     for rows, _, lens in prepared)
+        stats = loop.mgr.stats()
+        finished = 256 - len(loop.active_rows())
+        del loop, prepared
+        # interleaved pass: block-manager step -> pinned upload of the plan ->
+        # kernels, every step (activations already on the device, as a
+        # model's projections would be)
+        loop2 = ServingLoop(3, prompt, out, start, H, D, bs, DTYPE, keep_history=False)
+        toks2 = [loop2.tokens(n, "cuda") for n in loop2.active_counts(steps)]
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for t in range(steps):
+            loop2.step(toks=toks2[t])
+        torch.cuda.synchronize()
+        wall_s = time.perf_counter() - t1
+        del loop2, toks2
+        kernel_s = sum(step_ms) * 1e-3
+        _line("paged serving-loop decode seq-steps/s, OPT-13B shape (256 seqs, 32 steps)", seq_steps / kernel_s,
+              "seq-steps/s", steps, 0, sum(step_ms) / steps, "f16",
+              {"workload": "serving loop (append, write, decode per step; finished sequences freed)",
+               "sequences": 256, "heads": H, "head_dim": D, "block_size": bs,
+               "lengths": "prompt lognormal(160,1)<=1024, output lognormal(300,1), total<=2048, "
+                          "uniform progress at step 0", "seed": "SeedSequence(76003)"},
+              achieved_GBps=round(nbytes / kernel_s / 1e9, 1), pct_of_peak=round(100 * nbytes / kernel_s / 1e9 / PEAK_HBM_GBS, 2),
+              seq_steps=seq_steps, finished_in_loop=finished,
+              host_block_manager_ms_per_step=round(bm_ms, 3),
+              wall_ms_per_step_interleaved=round(wall_s / steps * 1e3, 3),
+              gpu_loop_wall_ms_per_step=round(gpu_s / steps * 1e3, 3),
+              tail_waste_slots_end=stats["tail_waste_slots"],
+              slot_utilisation_end=round(stats["slot_utilisation"], 4))
+    return 0
+
+
+def shared_bench(args) -> int:
+    """32 prompt groups of 512 tokens x 4 sequences at the OPT-13B shape in
+    bf16: parallel sampling (prompt blocks shared, reference count 4) and
+    beam search (per-step fork/free remaps, copy-on-write of shared partial
+    blocks through pa_copy_blocks), 64 decode steps each."""
+    import torch
+
+    from paged_kv_cache_76_amd import workloads
+    from paged_kv_cache_76_amd.serving import BeamLoop
+
+    steps = 64
+    for beam in (False, True):
+        log(f"shared blocks: beam={beam}")
+        loop = BeamLoop(4, 32, 4, 512, steps, H, D, B, "bf16", beam=beam, keep_history=False)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        logical = unique = copies = 0
+        saved = []
+        for i in range(steps):
+            rec = loop.step(ev[i])
+            logical += workloads.decode_bytes(rec.context_lens, H, D, 2, B)
+            unique += loop.unique_blocks_read(rec.rows) * B * H * D * 2 * 2
+            copies += rec.n_copies
+            saved.append(loop.mgr.blocks_saved_by_sharing())
+        torch.cuda.synchronize()
+        ms = [a.elapsed_time(b) for a, b in ev]
+        kernel_s = sum(ms) * 1e-3
+        cow_bytes = copies * 2 * 2 * H * B * D * 2
+        name = "beam search (width 4)" if beam else "parallel sampling (4 per prompt)"
+        _line(f"paged decode with shared blocks, unique-HBM GB/s, OPT-13B shape, bf16, {name}",
+              (unique + cow_bytes) / kernel_s / 1e9, "GB/s", steps, 0, sum(ms) / steps, "bf16",
+              {"workload": f"shared-block decode: {name}", "groups": 32, "width": 4, "prompt_len": 512,
+               "heads": H, "head_dim": D, "block_size": B, "seed": "SeedSequence(76004)"},
+              logical_GBps=round(logical / kernel_s / 1e9, 1),
+              pct_of_peak_unique=round(100 * (unique + cow_bytes) / kernel_s / 1e9 / PEAK_HBM_GBS, 2),
+              seq_steps_per_s=round(128 * steps / kernel_s, 1),
+              cow_pairs_per_step=round(copies / steps, 2), blocks_saved_by_sharing_mean=round(sum(saved) / steps, 1),
+              logical_GB_per_step=round(logical / steps / 1e9, 4), unique_GB_per_step=round(unique / steps / 1e9, 4))
+    return 0
+
+
+def longdecode_bench(args) -> int:
+    """16 sequences x 32768 tokens, 72 heads, d=128, bf16, B=16 (19.3 GB of
+    K/V read per step): repeated decode steps over the same cache."""
+    import torch
+
+    from paged_kv_cache_76_amd import _lib as L
+    from paged_kv_cache_76_amd import workloads
+
+    S5, C5, H5 = 16, 32768, 72
+    log("building the 32K long-context cache (device-generated, 19.3 GB)")
+    ld = workloads.build_long_decode(5, S5, C5, H5, D, B, "bf16")
+    ws = L.decode_workspace(ld.cache, S5, C5)
+    out = torch.empty((S5, H5, D), dtype=torch.bfloat16, device="cuda")
+    n = args.steps + args.warmup
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i in range(n):
+        if i == args.warmup:
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+        ev[i][0].record()
+        L.pa_paged_decode(ld.cache, out, ld.q_dev, ld.tables_dev, ld.lens_dev, C5, ld.scale, ws)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = sum(ev[i][0].elapsed_time(ev[i][1]) for i in range(args.warmup, n)) / args.steps
+    nbytes = workloads.decode_bytes(ld.lens, H5, D, 2, B)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    _line("paged long-context decode HBM GB/s (16 x 32768 tokens, 72 heads, d128, bf16)", gbs, "GB/s",
+          args.steps, args.warmup, elapsed / args.steps * 1e3, "bf16",
+          {"workload": "long-context decode", "sequences": S5, "context": C5, "heads": H5, "head_dim": D,
+           "block_size": B, "seed": "torch.Generator(76005) on device"},
+          roofline={"bound": "hbm", "kernel": "pa_paged_decode (partition + merge kernels)", "achieved": round(gbs, 2),
+                    "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                    "avg_launch_us": round(ms * 1e3, 2), "algorithmic_bytes_per_launch": nbytes},
+          seq_steps_per_s=round(S5 / (ms * 1e-3), 1))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seqs", type=int, default=64, help="sequences in the CPU-oracle sample (0: skip)")
-    ap.add_argument("--workload", choices=["decode", "copy", "prefill"], default="decode",
+    ap.add_argument("--workload", choices=["decode", "copy", "prefill", "serving", "shared", "longdecode"],
+                    default="decode",
                     help="decode: the OPT-13B decode step (default); copy: pa_copy_blocks over 2048 "
                          "OPT-13B blocks, a plain copy of known size used to calibrate HBM counters; "
-                         "prefill: 8 x 1024-token prompts at the OPT-66B shape (write + causal prefill)")
+                         "prefill: 8 x 1024-token prompts at the OPT-66B shape (write + causal prefill); "
+                         "serving: 32 steps of a 256-sequence serving loop (B=16 and 32); shared: parallel "
+                         "sampling and beam search over shared prompt blocks (bf16); longdecode: 16 x 32768 "
+                         "tokens at the OPT-66B head count (bf16)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU layout is a design "
@@ -244,6 +414,12 @@ def main() -> int:
         return copy_calibration(args)
     if args.workload == "prefill":
         return prefill_bench(args)
+    if args.workload == "serving":
+        return serving_bench(args)
+    if args.workload == "shared":
+        return shared_bench(args)
+    if args.workload == "longdecode":
+        return longdecode_bench(args)
     K, W = args.steps, args.warmup
     n_steps = K + W
 

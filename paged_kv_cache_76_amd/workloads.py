@@ -194,3 +194,59 @@ def prefill_flops(lens, q_lens, num_heads: int, head_dim: int) -> int:
         # query positions first .. L-1 attend to first+1 .. L keys
         total += (n * (first + 1) + n * (n - 1) // 2)
     return 4 * head_dim * num_heads * int(total)
+
+
+@dataclass
+class LongDecode:
+    """Long-context decode: histories generated on the device by a seeded
+    torch generator (no host copy of the 19 GB), written through the block
+    manager's slots; host copies are kept only for the sampled (sequence,
+    head) pairs a checker asks for."""
+
+    cache: KVCache
+    manager: BlockManager
+    q_dev: torch.Tensor
+    tables_dev: torch.Tensor
+    lens_dev: torch.Tensor
+    lens: np.ndarray
+    scale: float
+    samples: dict              # (seq, head) -> (q [d], K [L][d], V [L][d]) host tensors
+
+
+def build_long_decode(config_index: int, S: int, ctx: int, num_heads: int, head_dim: int, block_size: int,
+                      dtype: str, samples=(), slack: float = 1.02, chunk_tokens: int = 8192) -> LongDecode:
+    """``S`` sequences of ``ctx`` tokens each, N(0,1) keys/values/queries drawn
+    on the device from ``torch.Generator`` seeded with 76000 + config_index."""
+    lens = np.full(S, ctx, dtype=np.int64)
+    r_pool = inputs.streams(config_index, STREAMS)[4]
+    N = pool_blocks(lens, block_size, slack)
+    mgr = BlockManager(N, block_size, max_rows=S, max_blocks_per_seq=-(-ctx // block_size),
+                       free_order=inputs.pool_order(r_pool, N))
+    cache = KVCache.empty(N + 1, num_heads, block_size, head_dim, TORCH[dtype], "cuda")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(76_000 + config_index)
+    want = {}
+    for s, h in samples:
+        want.setdefault(s, []).append(h)
+    kept = {}
+    for s in range(S):
+        slots = torch.from_numpy(mgr.add_prompt(s, ctx)).cuda()
+        ks, vs = [], []
+        for t0 in range(0, ctx, chunk_tokens):
+            n = min(chunk_tokens, ctx - t0)
+            k = torch.randn((n, num_heads, head_dim), generator=gen, device="cuda").to(TORCH[dtype])
+            v = torch.randn((n, num_heads, head_dim), generator=gen, device="cuda").to(TORCH[dtype])
+            pa_reshape_and_cache(cache, k, v, slots[t0:t0 + n])
+            if s in want:
+                ks.append(k[:, want[s]].cpu())
+                vs.append(v[:, want[s]].cpu())
+        if s in want:
+            kept[s] = (torch.cat(ks), torch.cat(vs))
+    q = torch.randn((S, num_heads, head_dim), generator=gen, device="cuda").to(TORCH[dtype])
+    sample_data = {}
+    for s, heads in want.items():
+        K, V = kept[s]
+        for i, h in enumerate(heads):
+            sample_data[(s, h)] = (q[s, h].cpu(), K[:, i], V[:, i])
+    return LongDecode(cache, mgr, q, torch.from_numpy(mgr.tables).cuda(),
+                      torch.from_numpy(lens.astype(np.int32)).cuda(), lens, 1.0 / math.sqrt(head_dim), sample_data)
