@@ -13,7 +13,8 @@
 //   queries 32w..32w+31.  Key/value tiles of 64 tokens are gathered from their
 //   physical blocks (16-byte loads) into LDS: keys as [token][d] rows, values
 //   transposed to [d][token] rows (registers do the 4x8 transpose with
-//   v_perm_b32), both row-padded against bank conflicts.
+//   v_perm_b32), both row-padded so the MFMA operand reads do not conflict
+//   on LDS banks.
 // * Scores are formed transposed, S^T = K Q^T, with
 //   v_mfma_f32_32x32x16_{bf16,f16}: the result layout puts one query per lane
 //   column, so the online softmax of a query is in-lane except for one
@@ -24,8 +25,14 @@
 // * Tiles entirely above the diagonal are never loaded; the diagonal ones are
 //   masked per element.  Workgroups are issued heaviest-first (last query tile
 //   first).
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_internal.h"
+
+#ifndef PA_PREFILL_PIPE
+#define PA_PREFILL_PIPE 1  // 1: the next key tile's global loads overlap this tile's MFMAs
+#endif
 
 namespace pa {
 namespace {
@@ -39,6 +46,7 @@ constexpr int kD = 128;        // head_dim
 constexpr int kBM = 128;       // queries per workgroup
 constexpr int kBN = 64;        // keys per tile
 constexpr int kWaves = 4;
+constexpr int kXcds = 8;       // accelerator complex dies of an MI355X
 constexpr int kKRow = kD + 8;  // padded LDS row of a key (elements)
 constexpr int kVRow = kBN + 4; // padded LDS row of a transposed value (elements)
 constexpr float kNegBig = -1e30f;
@@ -63,23 +71,21 @@ __device__ __forceinline__ uint32_t pack2(F16, float x, float y) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// sum of the eight 16-bit floats held in a 16-byte operand (exact widening)
-__device__ __forceinline__ float sum_unpacked(BF16, u32x4 v) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  float acc = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) acc += __uint_as_float(w[i] << 16) + __uint_as_float(w[i] & 0xffff0000u);
-  return acc;
+// acc + the sum of the eight 16-bit floats of a 16-byte operand: a dot
+// product with (1, 1) pairs (products exact, fp32 accumulation)
+__device__ __forceinline__ float sum_unpacked(BF16, u32x4 v, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.x), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.y), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.z), one, acc, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v.w), one, acc, false);
 }
-__device__ __forceinline__ float sum_unpacked(F16, u32x4 v) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  float acc = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const f16x2 h = as_f16x2(w[i]);
-    acc += (float)h.x + (float)h.y;
-  }
-  return acc;
+__device__ __forceinline__ float sum_unpacked(F16, u32x4 v, float acc) {
+  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+  acc = __builtin_amdgcn_fdot2(as_f16x2(v.x), one, acc, false);
+  acc = __builtin_amdgcn_fdot2(as_f16x2(v.y), one, acc, false);
+  acc = __builtin_amdgcn_fdot2(as_f16x2(v.z), one, acc, false);
+  return __builtin_amdgcn_fdot2(as_f16x2(v.w), one, acc, false);
 }
 
 struct PrefillArgs {
@@ -96,17 +102,23 @@ struct PrefillArgs {
 };
 
 template <typename E, int BS>
-__global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(PrefillArgs a) {
   static_assert(BS >= 4 && (kBN % BS == 0 || BS % kBN == 0), "block size must tile the 64-key step");
   __shared__ __attribute__((aligned(16))) uint16_t lds_k[kBN * kKRow];
   __shared__ __attribute__((aligned(16))) uint16_t lds_vt[kD * kVRow];
 
-  // heaviest tiles first: the last query tile of every (sequence, head) leads
-  const int per_tile = a.S * a.H;
-  const int tile = a.ntiles - 1 - (int)(blockIdx.x / per_tile);
-  const int rem = blockIdx.x % per_tile;
-  const int s = rem / a.H;
-  const int h = rem % a.H;
+  // XCD-aware order: workgroups are handed to the 8 XCDs round-robin, so
+  // XCD x runs blocks x, x+8, ...; give each XCD a contiguous range of
+  // (sequence, head) pairs with all their query tiles (heaviest first), so the
+  // key/value tiles every query tile of a pair re-reads stay in that XCD's L2.
+  const int total = a.ntiles * a.S * a.H;
+  const int xcd = blockIdx.x % kXcds;
+  const int q8 = total / kXcds, r8 = total % kXcds;
+  const int lin = xcd * q8 + min(xcd, r8) + (int)(blockIdx.x / kXcds);
+  const int pair = lin / a.ntiles;
+  const int tile = a.ntiles - 1 - lin % a.ntiles;
+  const int s = pair / a.H;
+  const int h = pair % a.H;
   const int q_begin = a.cu_q[s];
   const int qlen = a.cu_q[s + 1] - q_begin;
   const int ctx = a.lens[s];
@@ -141,90 +153,58 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
   // keys needed by the workgroup: positions 0 .. pos0 + min(q0 + kBM, qlen) - 1
   const int last_pos = pos0 + min(q0 + kBM, qlen) - 1;
   const int nkt = last_pos / kBN + 1;
-  const int wave_min_pos = pos0 + q0 + 32 * w;  // smallest query position of this wave
 
   // cooperative tile load: thread -> keys 4*kg .. 4*kg+3, dims 8*dc .. 8*dc+7
   const int kg = tid >> 4;
   const int dc = tid & 15;
   const int64_t trow = (int64_t)s * a.max_blocks;
 
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int j0 = kt * kBN;
-    u32x4 kr[4], vr[4];
-    {
-      const int jk = j0 + 4 * kg;  // first of this thread's 4 keys (same block: BS >= 4)
-      const int blk = jk / BS;
-      int phys = (jk < ctx && blk < a.max_blocks) ? a.tables[trow + blk] : -1;
-      const bool ok = phys >= 0 && phys < a.N;
-      const int off = jk % BS;
-      const int64_t base = (((int64_t)(ok ? phys : 0) * a.H + h) * BS + off) * (kD / 8) + dc;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const bool valid = ok && (jk + u < ctx);
-        kr[u] = valid ? a.kpool[base + u * (kD / 8)] : u32x4{0, 0, 0, 0};
-        vr[u] = valid ? a.vpool[base + u * (kD / 8)] : u32x4{0, 0, 0, 0};
-      }
-    }
-    __syncthreads();  // the previous tile's LDS reads are done
-#pragma unroll
-    for (int u = 0; u < 4; ++u) *(u32x4*)&lds_k[(4 * kg + u) * kKRow + 8 * dc] = kr[u];
-    {
-      // 4 keys x 8 dims -> 8 rows of V^T, 4 keys each
-      const uint32_t w0[4] = {vr[0].x, vr[0].y, vr[0].z, vr[0].w};
-      const uint32_t w1[4] = {vr[1].x, vr[1].y, vr[1].z, vr[1].w};
-      const uint32_t w2[4] = {vr[2].x, vr[2].y, vr[2].z, vr[2].w};
-      const uint32_t w3[4] = {vr[3].x, vr[3].y, vr[3].z, vr[3].w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        u32x2 lo, hi;  // dims 8dc+2i (low halves) and 8dc+2i+1 (high halves)
-        lo.x = __builtin_amdgcn_perm(w1[i], w0[i], 0x05040100u);
-        lo.y = __builtin_amdgcn_perm(w3[i], w2[i], 0x05040100u);
-        hi.x = __builtin_amdgcn_perm(w1[i], w0[i], 0x07060302u);
-        hi.y = __builtin_amdgcn_perm(w3[i], w2[i], 0x07060302u);
-        *(u32x2*)&lds_vt[(8 * dc + 2 * i) * kVRow + 4 * kg] = lo;
-        *(u32x2*)&lds_vt[(8 * dc + 2 * i + 1) * kVRow + 4 * kg] = hi;
-      }
-    }
-    __syncthreads();
+  // tiles whose keys all precede every query of the workgroup need no mask
+  const int n_full = min(nkt, (pos0 + q0 + 1) / kBN);
+  const int wave_max_pos = pos0 + min(q0 + 32 * w + 31, qlen - 1);  // last query position of this wave
+  const float c = a.scale_log2;
 
-    // S^T tile: keys 32mb + (result rows), this lane's query = column
+  // One key tile: S^T = K Q^T, online softmax, O^T += V^T P^T.  MASKED tiles
+  // straddle the diagonal; scores of keys after the query become -inf.
+  auto compute_tile = [&](const int j0, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     f32x16 acc_s[2];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc_s[mb][i] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
+    for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {  // two independent accumulation chains
         const u32x4 ka = *(const u32x4*)&lds_k[(32 * mb + col) * kKRow + 16 * ks + 8 * g];
         acc_s[mb] = mfma32(E{}, ka, qb[ks], acc_s[mb]);
       }
     }
-
-    // online softmax (log2 domain); key of result element i: 32mb + 8(i/4) + 4g + i%4
-    const bool needs_mask = j0 + kBN - 1 > wave_min_pos;
+    // raw-score max; key of result element i is 32mb + 8(i/4) + 4g + i%4
     float mt = kNegBig;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float sv = acc_s[mb][i] * a.scale_log2;
-        if (needs_mask) {
+        if constexpr (MASKED) {
           const int kpos = j0 + 32 * mb + 8 * (i / 4) + 4 * g + (i % 4);
-          sv = kpos <= qpos ? sv : -__builtin_inff();
+          if (kpos > qpos) acc_s[mb][i] = -__builtin_inff();
         }
-        acc_s[mb][i] = sv;
-        mt = fmaxf(mt, sv);
+        mt = fmaxf(mt, acc_s[mb][i]);
       }
     mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m, mt);
-    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-    m = m_new;
-    l *= alpha;
+    const float m_new = fmaxf(m, mt);  // raw units (scale > 0 keeps the order)
+    if (__any(m_new > m)) {
+      const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c);
+      l *= alpha;
 #pragma unroll
-    for (int dm = 0; dm < 4; ++dm)
+      for (int dm = 0; dm < 4; ++dm)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc_o[dm][i] *= alpha;
-
+        for (int i = 0; i < 16; ++i) acc_o[dm][i] *= alpha;
+      m = m_new;
+    }
+    const float mc = -m * c;
     // P^T operands: k-step (mb, t) takes result elements 8t .. 8t+7 of block mb
     u32x4 pb[2][2];
 #pragma unroll
@@ -233,26 +213,82 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
       for (int t = 0; t < 2; ++t) {
         float p[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(acc_s[mb][8 * t + j] - m_new);
+        for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc_s[mb][8 * t + j], c, mc));
         pb[mb][t] = u32x4{pack2(E{}, p[0], p[1]), pack2(E{}, p[2], p[3]), pack2(E{}, p[4], p[5]),
                           pack2(E{}, p[6], p[7])};
         // the denominator sums the same rounded weights the MFMA multiplies
-        l += sum_unpacked(E{}, pb[mb][t]);
+        l = sum_unpacked(E{}, pb[mb][t], l);
       }
-
     // O^T += V^T P^T; k-slot (g, j) of step (mb, t) is key 32mb + 16t + 8(j/4) + 4g + j%4
 #pragma unroll
-    for (int dm = 0; dm < 4; ++dm)
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int dm = 0; dm < 4; ++dm) {
           const uint16_t* vrow = &lds_vt[(32 * dm + col) * kVRow + 32 * mb + 16 * t + 4 * g];
           const u32x2 v0 = *(const u32x2*)vrow;
           const u32x2 v1 = *(const u32x2*)(vrow + 8);
           const u32x4 va = {v0.x, v0.y, v1.x, v1.y};
           acc_o[dm] = mfma32(E{}, va, pb[mb][t], acc_o[dm]);
         }
+  };
+
+  // Global -> register loads of one key tile (thread: 4 keys x 8 dims of K and V)
+  auto load_tile = [&](const int kt, u32x4* kr, u32x4* vr) {
+    const int jk = kt * kBN + 4 * kg;  // first of this thread's 4 keys (same block: BS >= 4)
+    const int blk = jk / BS;
+    const int phys = (jk < ctx && blk < a.max_blocks) ? a.tables[trow + blk] : -1;
+    const bool ok = phys >= 0 && phys < a.N;
+    const int off = jk % BS;
+    const int64_t base = (((int64_t)(ok ? phys : 0) * a.H + h) * BS + off) * (kD / 8) + dc;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool valid = ok && (jk + u < ctx);
+      kr[u] = valid ? a.kpool[base + u * (kD / 8)] : u32x4{0, 0, 0, 0};
+      vr[u] = valid ? a.vpool[base + u * (kD / 8)] : u32x4{0, 0, 0, 0};
+    }
+  };
+  // Registers -> LDS: K rows as they are, V transposed (4 keys x 8 dims -> 8 rows of V^T)
+  auto store_tile = [&](const u32x4* kr, const u32x4* vr) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) *(u32x4*)&lds_k[(4 * kg + u) * kKRow + 8 * dc] = kr[u];
+    const uint32_t w0[4] = {vr[0].x, vr[0].y, vr[0].z, vr[0].w};
+    const uint32_t w1[4] = {vr[1].x, vr[1].y, vr[1].z, vr[1].w};
+    const uint32_t w2[4] = {vr[2].x, vr[2].y, vr[2].z, vr[2].w};
+    const uint32_t w3[4] = {vr[3].x, vr[3].y, vr[3].z, vr[3].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      u32x2 lo, hi;  // dims 8dc+2i (low halves) and 8dc+2i+1 (high halves)
+      lo.x = __builtin_amdgcn_perm(w1[i], w0[i], 0x05040100u);
+      lo.y = __builtin_amdgcn_perm(w3[i], w2[i], 0x05040100u);
+      hi.x = __builtin_amdgcn_perm(w1[i], w0[i], 0x07060302u);
+      hi.y = __builtin_amdgcn_perm(w3[i], w2[i], 0x07060302u);
+      *(u32x2*)&lds_vt[(8 * dc + 2 * i) * kVRow + 4 * kg] = lo;
+      *(u32x2*)&lds_vt[(8 * dc + 2 * i + 1) * kVRow + 4 * kg] = hi;
+    }
+  };
+
+  u32x4 kr[4], vr[4];
+#if PA_PREFILL_PIPE
+  load_tile(0, kr, vr);
+#endif
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int j0 = kt * kBN;
+#if !PA_PREFILL_PIPE
+    load_tile(kt, kr, vr);
+#endif
+    __syncthreads();  // the previous tile's LDS reads are done
+    store_tile(kr, vr);
+    __syncthreads();
+#if PA_PREFILL_PIPE
+    if (kt + 1 < nkt) load_tile(kt + 1, kr, vr);  // in flight while this tile computes
+#endif
+    if (kt < n_full) {
+      compute_tile(j0, std::false_type{});
+    } else if (j0 <= wave_max_pos) {  // a wave skips tiles wholly after its queries
+      compute_tile(j0, std::true_type{});
+    }
   }
 
   // normalise and store: result element i of block dm is dim 32dm + 8(i/4) + 4g + i%4
