@@ -315,9 +315,9 @@ def shared_bench(args) -> int:
     from paged_kv_cache_76_amd.serving import BeamLoop
 
     steps = 64
-    for beam in (False, True):
-        log(f"shared blocks: beam={beam}")
-        loop = BeamLoop(4, 32, 4, 512, steps, H, D, B, "bf16", beam=beam, keep_history=False)
+    for beam, grouped in ((False, False), (False, True), (True, False), (True, True)):
+        log(f"shared blocks: beam={beam} grouped={grouped}")
+        loop = BeamLoop(4, 32, 4, 512, steps, H, D, B, "bf16", beam=beam, keep_history=False, grouped=grouped)
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         logical = unique = copies = 0
         saved = []
@@ -331,11 +331,13 @@ def shared_bench(args) -> int:
         ms = [a.elapsed_time(b) for a, b in ev]
         kernel_s = sum(ms) * 1e-3
         cow_bytes = copies * 2 * 2 * H * B * D * 2
-        name = "beam search (width 4)" if beam else "parallel sampling (4 per prompt)"
+        name = ("beam search (width 4)" if beam else "parallel sampling (4 per prompt)") + \
+            (", grouped decode" if grouped else "")
         _line(f"paged decode with shared blocks, unique-HBM GB/s, OPT-13B shape, bf16, {name}",
               (unique + cow_bytes) / kernel_s / 1e9, "GB/s", steps, 0, sum(ms) / steps, "bf16",
               {"workload": f"shared-block decode: {name}", "groups": 32, "width": 4, "prompt_len": 512,
-               "heads": H, "head_dim": D, "block_size": B, "seed": "SeedSequence(76004)"},
+               "heads": H, "head_dim": D, "block_size": B, "seed": "SeedSequence(76004)",
+               "decode_entry": "pa_paged_decode_grouped (group 4)" if grouped else "pa_paged_decode"},
               logical_GBps=round(logical / kernel_s / 1e9, 1),
               pct_of_peak_unique=round(100 * (unique + cow_bytes) / kernel_s / 1e9 / PEAK_HBM_GBS, 2),
               seq_steps_per_s=round(128 * steps / kernel_s, 1),

@@ -135,6 +135,30 @@ pa_status pa_paged_decode(const pa_kv_cache* cache, void* out, pa_dtype out_dtyp
                           float scale, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_paged_decode_grouped — pa_paged_decode for batches whose rows share
+ * blocks (parallel samples or beam candidates over a common prefix).
+ * [P1] key design 3 (several logical blocks map to one physical block) and
+ * key design 1 (the attention computed is unchanged).
+ *
+ * Rows are taken group_size at a time (rows 0..g-1, g..2g-1, ...; the last
+ * group may be short).  Wherever all rows of a group map a logical block to
+ * the same physical block, that block is read from HBM once for the whole
+ * group.  The result is the same as pa_paged_decode's for any grouping and
+ * any table contents; only the traffic depends on the actual sharing.
+ *   group_size  1, 2 or 4 (1, or a shape without a grouped build, runs the
+ *               ungrouped kernel).
+ *   workspace   >= pa_decode_grouped_workspace_bytes(...) bytes.
+ * Every other argument is as for pa_paged_decode.
+ */
+size_t pa_decode_grouped_workspace_bytes(const pa_kv_cache* cache, int32_t S, int32_t max_context_len,
+                                         int32_t group_size);
+pa_status pa_paged_decode_grouped(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, const void* query,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, int32_t S, int32_t max_context_len,
+                                  float scale, int32_t group_size, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/*
  * pa_paged_prefill — causal attention for the prompt tokens of S sequences.
  * [P1] key design 1, eq. 1 (query i attends to positions t <= i, itself
  * included) with keys/values read through the block table as in eq. 2;

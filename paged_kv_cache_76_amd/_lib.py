@@ -24,7 +24,8 @@ TORCH_TO_PA = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_
 # every symbol include/pagedattn.h declares
 EXPORTS = (
     "pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_workspace_bytes", "pa_paged_decode",
-    "pa_paged_prefill", "pa_status_string", "pa_last_error", "pa_abi_version",
+    "pa_decode_grouped_workspace_bytes", "pa_paged_decode_grouped", "pa_paged_prefill",
+    "pa_status_string", "pa_last_error", "pa_abi_version",
 )
 
 
@@ -60,9 +61,14 @@ def load_library(path: str) -> ctypes.CDLL:
     L.pa_decode_workspace_bytes.restype = ctypes.c_size_t
     L.pa_paged_decode.argtypes = [C, P, ctypes.c_int, P, I32P, I32, I32P, I32, I32, ctypes.c_float, P,
                                   ctypes.c_size_t, P]
+    L.pa_decode_grouped_workspace_bytes.argtypes = [C, I32, I32, I32]
+    L.pa_decode_grouped_workspace_bytes.restype = ctypes.c_size_t
+    L.pa_paged_decode_grouped.argtypes = [C, P, ctypes.c_int, P, I32P, I32, I32P, I32, I32, ctypes.c_float, I32,
+                                          P, ctypes.c_size_t, P]
     L.pa_paged_prefill.argtypes = [C, P, ctypes.c_int, P, I32P, I32, I32P, I32P, I32, I32, I32,
                                    ctypes.c_float, P]
-    for fn in ("pa_reshape_and_cache", "pa_copy_blocks", "pa_paged_decode", "pa_paged_prefill"):
+    for fn in ("pa_reshape_and_cache", "pa_copy_blocks", "pa_paged_decode", "pa_paged_decode_grouped",
+               "pa_paged_prefill"):
         getattr(L, fn).restype = ctypes.c_int
     L.pa_status_string.argtypes = [ctypes.c_int]
     L.pa_status_string.restype = ctypes.c_char_p
@@ -212,6 +218,46 @@ def pa_paged_decode(cache: KVCache, out: torch.Tensor, query: torch.Tensor,
                                  _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), S,
                                  int(max_context_len), float(scale), _ptr(workspace), ws_bytes,
                                  _stream(stream)))
+    return out
+
+
+def pa_decode_grouped_workspace_bytes(cache: KVCache, S: int, max_context_len: int, group_size: int) -> int:
+    d = cache.desc()
+    n = lib().pa_decode_grouped_workspace_bytes(ctypes.byref(d), S, max_context_len, group_size)
+    if n == ctypes.c_size_t(-1).value:
+        raise PagedAttnError(PA_ERR_INVALID_ARG, lib().pa_last_error().decode())
+    return n
+
+
+def decode_grouped_workspace(cache: KVCache, S: int, max_context_len: int, group_size: int) -> torch.Tensor | None:
+    """Allocate (with torch) the scratch that :func:`pa_paged_decode_grouped` needs."""
+    n = pa_decode_grouped_workspace_bytes(cache, S, max_context_len, group_size)
+    if n == 0:
+        return None
+    return torch.empty(n, dtype=torch.uint8, device=cache.k.device)
+
+
+def pa_paged_decode_grouped(cache: KVCache, out: torch.Tensor, query: torch.Tensor,
+                            block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
+                            scale: float, group_size: int, workspace: torch.Tensor | None = None,
+                            stream=None) -> torch.Tensor:
+    """Decode with rows taken ``group_size`` at a time; blocks shared by a
+    whole group are read once.  Same result as :func:`pa_paged_decode`."""
+    _contig("query", query, cache.dtype)
+    _contig("out", out)
+    _contig("block_tables", block_tables, torch.int32)
+    _contig("context_lens", context_lens, torch.int32)
+    S = query.shape[0]
+    if query.shape != (S, cache.num_heads, cache.head_dim) or out.shape != query.shape:
+        raise ValueError("query/out must be [S][H][d]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_tables must be [S][max_blocks], context_lens [S]")
+    d = cache.desc()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pa_paged_decode_grouped(ctypes.byref(d), _ptr(out), TORCH_TO_PA.get(out.dtype, -1), _ptr(query),
+                                         _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), S,
+                                         int(max_context_len), float(scale), int(group_size), _ptr(workspace),
+                                         ws_bytes, _stream(stream)))
     return out
 
 

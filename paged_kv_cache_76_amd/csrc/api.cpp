@@ -103,16 +103,12 @@ size_t pa_decode_workspace_bytes(const pa_kv_cache* cache, int32_t S, int32_t ma
   return pa::decode_workspace_bytes(c, S, max_context_len);
 }
 
-pa_status pa_paged_decode(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, const void* query,
-                          const int32_t* block_tables, int32_t max_blocks_per_seq,
-                          const int32_t* context_lens, int32_t S, int32_t max_context_len, float scale,
-                          void* workspace, size_t workspace_bytes, void* stream) {
-  const char* fn = "pa_paged_decode";
-  pa::Cache c;
-  pa_status st = check_cache(fn, cache, &c);
-  if (st != PA_OK) return st;
-  if (S < 0) return fail(PA_ERR_INVALID_ARG, "%s: S = %d < 0", fn, S);
-  if (S == 0) return PA_OK;
+namespace {
+
+// Checks shared by the decode entry points (everything but the workspace).
+pa_status check_decode(const char* fn, const pa::Cache& c, const void* out, pa_dtype out_dtype, const void* query,
+                       const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                       int32_t S, int32_t max_context_len, float scale) {
   if (out_dtype != c.dtype && out_dtype != PA_F32)
     return fail(PA_ERR_INVALID_ARG, "%s: out_dtype must be the cache dtype or PA_F32", fn);
   if (!out || !query || !block_tables || !context_lens)
@@ -130,19 +126,84 @@ pa_status pa_paged_decode(const pa_kv_cache* cache, void* out, pa_dtype out_dtyp
   if (P == 0)
     return fail(PA_ERR_UNSUPPORTED, "%s: (dtype %d, head_dim %d, block_size %d) not built", fn, (int)c.dtype,
                 c.head_dim, c.block_size);
-  const int64_t parts = ((int64_t)max_context_len + P - 1) / P;
+  // the smallest partition any decode kernel uses bounds the grid
+  const int64_t parts = ((int64_t)max_context_len + 63) / 64;
   if ((int64_t)S * c.num_heads * parts >= (int64_t)1 << 31)
     return fail(PA_ERR_INVALID_ARG, "%s: grid of S*H*partitions does not fit", fn);
+  return PA_OK;
+}
+
+pa_status check_workspace(const char* fn, size_t need, const void* workspace, size_t workspace_bytes) {
+  if (need == 0) return PA_OK;
+  if (!workspace || workspace_bytes < need)
+    return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn,
+                workspace ? workspace_bytes : (size_t)0, need);
+  if (!aligned(workspace, 16)) return fail(PA_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned", fn);
+  return PA_OK;
+}
+
+}  // namespace
+
+pa_status pa_paged_decode(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, const void* query,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* context_lens, int32_t S, int32_t max_context_len, float scale,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "pa_paged_decode";
+  pa::Cache c;
+  pa_status st = check_cache(fn, cache, &c);
+  if (st != PA_OK) return st;
+  if (S < 0) return fail(PA_ERR_INVALID_ARG, "%s: S = %d < 0", fn, S);
+  if (S == 0) return PA_OK;
+  st = check_decode(fn, c, out, out_dtype, query, block_tables, max_blocks_per_seq, context_lens, S,
+                    max_context_len, scale);
+  if (st != PA_OK) return st;
   const size_t need = pa::decode_workspace_bytes(c, S, max_context_len);
-  if (need > 0) {
-    if (!workspace || workspace_bytes < need)
-      return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn,
-                  workspace ? workspace_bytes : (size_t)0, need);
-    if (!aligned(workspace, 16)) return fail(PA_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned", fn);
-  }
+  st = check_workspace(fn, need, workspace, workspace_bytes);
+  if (st != PA_OK) return st;
   return launched(fn, pa::launch_paged_decode(c, out, out_dtype, query, block_tables, max_blocks_per_seq,
                                               context_lens, S, max_context_len, scale,
                                               need > 0 ? workspace : nullptr, (hipStream_t)stream));
+}
+
+size_t pa_decode_grouped_workspace_bytes(const pa_kv_cache* cache, int32_t S, int32_t max_context_len,
+                                         int32_t group_size) {
+  const char* fn = "pa_decode_grouped_workspace_bytes";
+  pa::Cache c;
+  if (check_cache(fn, cache, &c) != PA_OK) return (size_t)-1;
+  if (S < 0 || max_context_len < 0 || (group_size != 1 && group_size != 2 && group_size != 4)) {
+    fail(PA_ERR_INVALID_ARG, "%s: negative size or group_size not in {1, 2, 4}", fn);
+    return (size_t)-1;
+  }
+  if (pa::decode_partition_tokens(c.dtype, c.head_dim, c.block_size) == 0) {
+    fail(PA_ERR_UNSUPPORTED, "%s: (dtype %d, head_dim %d, block_size %d) not built", fn, (int)c.dtype,
+         c.head_dim, c.block_size);
+    return (size_t)-1;
+  }
+  return pa::decode_grouped_workspace_bytes(c, S, max_context_len, group_size);
+}
+
+pa_status pa_paged_decode_grouped(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, const void* query,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, int32_t S, int32_t max_context_len,
+                                  float scale, int32_t group_size, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  const char* fn = "pa_paged_decode_grouped";
+  pa::Cache c;
+  pa_status st = check_cache(fn, cache, &c);
+  if (st != PA_OK) return st;
+  if (S < 0) return fail(PA_ERR_INVALID_ARG, "%s: S = %d < 0", fn, S);
+  if (group_size != 1 && group_size != 2 && group_size != 4)
+    return fail(PA_ERR_INVALID_ARG, "%s: group_size = %d not in {1, 2, 4}", fn, group_size);
+  if (S == 0) return PA_OK;
+  st = check_decode(fn, c, out, out_dtype, query, block_tables, max_blocks_per_seq, context_lens, S,
+                    max_context_len, scale);
+  if (st != PA_OK) return st;
+  const size_t need = pa::decode_grouped_workspace_bytes(c, S, max_context_len, group_size);
+  st = check_workspace(fn, need, workspace, workspace_bytes);
+  if (st != PA_OK) return st;
+  return launched(fn, pa::launch_paged_decode_grouped(c, out, out_dtype, query, block_tables, max_blocks_per_seq,
+                                                      context_lens, S, max_context_len, scale, group_size,
+                                                      need > 0 ? workspace : nullptr, (hipStream_t)stream));
 }
 
 pa_status pa_paged_prefill(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, const void* query,

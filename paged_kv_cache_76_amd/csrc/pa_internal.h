@@ -38,6 +38,15 @@ hipError_t launch_paged_decode(const Cache& c, void* out, pa_dtype out_dtype, co
                                const int32_t* context_lens, int32_t S, int32_t max_context_len,
                                float scale, void* workspace, hipStream_t stream);
 
+// Grouped decode: rows taken group_size at a time read shared blocks once.
+// Shapes without a grouped build are served by launch_paged_decode.
+bool decode_grouped_built(pa_dtype dtype, int head_dim, int block_size, int group_size);
+size_t decode_grouped_workspace_bytes(const Cache& c, int32_t S, int32_t max_context_len, int32_t group_size);
+hipError_t launch_paged_decode_grouped(const Cache& c, void* out, pa_dtype out_dtype, const void* query,
+                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t* context_lens, int32_t S, int32_t max_context_len,
+                                       float scale, int32_t group_size, void* workspace, hipStream_t stream);
+
 // ---- prefill (paged_prefill.hip) ----------------------------------------------
 bool prefill_supported(pa_dtype dtype, int head_dim, int block_size);
 hipError_t launch_paged_prefill(const Cache& c, void* out, pa_dtype out_dtype, const void* query,

@@ -314,6 +314,195 @@ __global__ __launch_bounds__((DecodeCfg<E, D, BS>::NW * 64)) PA_DECODE_OCC void 
 #endif
 }
 
+// ---- grouped decode: rows that share blocks read them once ----------------------
+// Consecutive batch rows are taken W at a time.  A workgroup serves one
+// (group, head, partition of kGroupTokens tokens); at every block position
+// where all W rows map the same physical block (parallel samples or beams
+// over a common prefix: "vLLM / PagedAttention", key design 3), the
+// (block, head) tile is loaded once and scored against all W queries.
+// Anywhere else each row loads its own block.  Each row keeps its own online
+// softmax, so the result equals pa_paged_decode's for any grouping; only the
+// HBM traffic depends on the sharing.
+#ifndef PA_GROUP_NW
+#define PA_GROUP_NW 4  // waves per workgroup of the grouped kernel
+#endif
+#ifndef PA_GROUP_PT
+#define PA_GROUP_PT 512  // tokens per partition of the grouped kernel
+#endif
+constexpr int kGroupWaves = PA_GROUP_NW;
+constexpr int kGroupTokens = PA_GROUP_PT;
+
+template <typename E, int D, int BS, int W>
+__global__ __launch_bounds__(kGroupWaves * 64) void decode_grouped_kernel(DecodeArgs a, int32_t ngroups) {
+  using C = DecodeCfg<E, D, BS>;
+  constexpr int VEC = C::VEC, LPT = C::LPT, TPL = C::TPL, G = C::G, NCH = C::NCH;
+  constexpr int NW = kGroupWaves, P = kGroupTokens, STEPS = P / G;
+  static_assert(BS >= G && P % BS == 0 && P / BS <= 64, "grouped decode needs whole-block steps");
+  __shared__ float lds_o[NW][W][D];
+  __shared__ float lds_m[NW][W];
+  __shared__ float lds_l[NW][W];
+
+  const int bid = blockIdx.x;
+  const int h = bid % a.H;
+  const int rest = bid / a.H;
+  const int grp = rest % ngroups;
+  const int p = rest / ngroups;
+  const int r0 = grp * W;
+  int ctx[W];
+  int maxctx = 0;
+#pragma unroll
+  for (int r = 0; r < W; ++r) {
+    ctx[r] = (r0 + r < a.S) ? min(a.lens[r0 + r], a.max_parts * P) : 0;
+    maxctx = max(maxctx, ctx[r]);
+  }
+  if (p * P >= maxctx) return;  // uniform for the whole workgroup
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tr = lane / LPT;  // token row within a wave-wide load
+  const int c = lane % LPT;   // 16-byte column within the row
+  const int jb = p * (P / BS);
+
+  int tbl[W];
+  u32x4 qc[W];
+  float m[W], l[W], o[W][VEC];
+#pragma unroll
+  for (int r = 0; r < W; ++r) {
+    const int nblk = (ctx[r] + BS - 1) / BS;
+    const int j = jb + lane;
+    tbl[r] = (lane < P / BS && j < nblk && j < a.max_blocks) ? a.tables[(int64_t)(r0 + r) * a.max_blocks + j] : -1;
+    qc[r] = ctx[r] > 0 ? a.q[((int64_t)(r0 + r) * a.H + h) * LPT + c] : u32x4{0, 0, 0, 0};
+    m[r] = kNegBig;
+    l[r] = 0.f;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) o[r][e] = 0.f;
+  }
+
+  // online-softmax update of row r with one step's chunks
+  auto update = [&](const int r, const u32x4* kc, const u32x4* vc, const bool* valid) {
+    float sc[NCH];
+    float mblk = kNegBig;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const float d = group_sum<LPT>(dot_chunk(E{}, qc[r], kc[i])) * a.scale_log2;
+      sc[i] = valid[i] ? d : -__builtin_inff();
+      mblk = fmaxf(mblk, sc[i]);
+    }
+    const float m_new = fmaxf(m[r], mblk);
+    const float alpha = fast_exp2(m[r] - m_new);
+    l[r] *= alpha;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) o[r][e] *= alpha;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const float pi = fast_exp2(sc[i] - m_new);
+      l[r] += pi;
+      float vf[VEC];
+      widen(E{}, vc[i], vf);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) o[r][e] = __builtin_fmaf(pi, vf[e], o[r][e]);
+    }
+    m[r] = m_new;
+  };
+
+  const int nsteps = min(STEPS, (maxctx - p * P + G - 1) / G);
+  for (int step = w; step < nsteps; step += NW) {
+    const int tb = p * P + step * G;
+    const int jl = (step * G) / BS;
+    const int off0 = (step * G) % BS;
+    int phys[W];
+    bool shared = true;
+#pragma unroll
+    for (int r = 0; r < W; ++r) {
+      phys[r] = __builtin_amdgcn_readlane(tbl[r], jl);
+      shared = shared && (tb + G <= ctx[r]) && (phys[r] == phys[0]);
+    }
+    shared = shared && phys[0] >= 0 && phys[0] < a.N;
+    u32x4 kc[NCH], vc[NCH];
+    bool valid[NCH];
+    if (shared) {
+      const int64_t base = (((int64_t)phys[0] * a.H + h) * BS + off0 + tr) * LPT + c;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        kc[i] = load_kv(&a.kpool[base + i * TPL * LPT]);
+        vc[i] = load_kv(&a.vpool[base + i * TPL * LPT]);
+        valid[i] = true;
+      }
+#pragma unroll
+      for (int r = 0; r < W; ++r) update(r, kc, vc, valid);
+    } else {
+#pragma unroll
+      for (int r = 0; r < W; ++r) {
+        if (tb >= ctx[r]) continue;  // uniform
+        const bool in_pool = phys[r] >= 0 && phys[r] < a.N;
+        const int64_t base = (((int64_t)(in_pool ? phys[r] : 0) * a.H + h) * BS + off0 + tr) * LPT + c;
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+          valid[i] = in_pool && (tb + i * TPL + tr < ctx[r]);
+          kc[i] = valid[i] ? load_kv(&a.kpool[base + i * TPL * LPT]) : u32x4{0, 0, 0, 0};
+          vc[i] = valid[i] ? load_kv(&a.vpool[base + i * TPL * LPT]) : u32x4{0, 0, 0, 0};
+        }
+        update(r, kc, vc, valid);
+      }
+    }
+  }
+
+  // per row: merge the token rows of the wave, then the waves
+#pragma unroll
+  for (int r = 0; r < W; ++r) {
+#pragma unroll
+    for (int off = LPT; off < 64; off <<= 1) {
+      const float m2 = __shfl_xor(m[r], off);
+      const float l2 = __shfl_xor(l[r], off);
+      const float M = fmaxf(m[r], m2);
+      const float f1 = fast_exp2(m[r] - M), f2 = fast_exp2(m2 - M);
+      l[r] = l[r] * f1 + l2 * f2;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) o[r][e] = o[r][e] * f1 + __shfl_xor(o[r][e], off) * f2;
+      m[r] = M;
+    }
+    if (lane < LPT) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) lds_o[w][r][c * VEC + e] = o[r][e];
+    }
+    if (lane == 0) {
+      lds_m[w][r] = m[r];
+      lds_l[w][r] = l[r];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < W; ++r) {
+    if (p * P >= ctx[r]) continue;  // this row has no token in the partition
+    const int nparts = (ctx[r] + P - 1) / P;
+    float M = kNegBig;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) M = fmaxf(M, lds_m[k][r]);
+    float L = 0.f;
+    float fw[NW];
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+      fw[k] = fast_exp2(lds_m[k][r] - M);
+      L += lds_l[k][r] * fw[k];
+    }
+    const int64_t sh = (int64_t)(r0 + r) * a.H + h;
+    for (int d = threadIdx.x; d < D; d += NW * 64) {
+      float O = 0.f;
+#pragma unroll
+      for (int k = 0; k < NW; ++k) O += lds_o[k][r][d] * fw[k];
+      if (nparts == 1) {
+        store_out(a.out, sh * D + d, O / L, a.out_dtype);
+      } else {
+        a.ws_o[(sh * a.max_parts + p) * D + d] = O;
+      }
+    }
+    if (nparts > 1 && threadIdx.x == 0) {
+      a.ws_ml[(sh * a.max_parts + p) * 2] = M;
+      a.ws_ml[(sh * a.max_parts + p) * 2 + 1] = L;
+    }
+  }
+}
+
 // Merge of the partitions of each (sequence, head) split into several:
 // o = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p with M = max_p m_p.
 // One wave per (sequence, head): the (m_p, l_p) pairs are read in parallel,
@@ -394,6 +583,25 @@ size_t counter_bytes(int32_t S, int32_t H) {
   return ((size_t)S * H * sizeof(int32_t) + 255) / 256 * 256;
 }
 
+struct GroupedVariant {
+  pa_dtype dtype;
+  int D, BS, W;
+  void (*kernel)(DecodeArgs, int32_t);
+};
+
+#define PA_GROUPED_VARIANT(E, D, BS, W) GroupedVariant{E::id, D, BS, W, decode_grouped_kernel<E, D, BS, W>}
+#define PA_GROUPED_ALL(BS, W) \
+  PA_GROUPED_VARIANT(F32, 128, BS, W), PA_GROUPED_VARIANT(F16, 128, BS, W), PA_GROUPED_VARIANT(BF16, 128, BS, W)
+
+const GroupedVariant kGroupedVariants[] = {PA_GROUPED_ALL(16, 2), PA_GROUPED_ALL(16, 4), PA_GROUPED_ALL(32, 2),
+                                           PA_GROUPED_ALL(32, 4)};
+
+const GroupedVariant* find_grouped(pa_dtype dtype, int D, int BS, int W) {
+  for (const GroupedVariant& v : kGroupedVariants)
+    if (v.dtype == dtype && v.D == D && v.BS == BS && v.W == W) return &v;
+  return nullptr;
+}
+
 int64_t max_parts_for(const Variant& v, int32_t max_context_len) {
   return ((int64_t)max_context_len + v.P - 1) / v.P;
 }
@@ -413,13 +621,11 @@ size_t decode_workspace_bytes(const Cache& c, int32_t S, int32_t max_context_len
   return counter_bytes(S, c.num_heads) + (size_t)S * c.num_heads * mp * (c.head_dim + 2) * sizeof(float);
 }
 
-hipError_t launch_paged_decode(const Cache& c, void* out, pa_dtype out_dtype, const void* query,
-                               const int32_t* block_tables, int32_t max_blocks_per_seq,
-                               const int32_t* context_lens, int32_t S, int32_t max_context_len,
-                               float scale, void* workspace, hipStream_t stream) {
-  const Variant* v = find_variant(c.dtype, c.head_dim, c.block_size);
-  if (!v) return hipErrorInvalidValue;
-  const int64_t mp = max_parts_for(*v, max_context_len);
+namespace {
+
+DecodeArgs make_args(const Cache& c, void* out, pa_dtype out_dtype, const void* query,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                     int32_t S, int64_t mp, float scale, void* workspace) {
   DecodeArgs a;
   a.q = (const u32x4*)query;
   a.kpool = (const u32x4*)c.k;
@@ -439,12 +645,59 @@ hipError_t launch_paged_decode(const Cache& c, void* out, pa_dtype out_dtype, co
   a.max_parts = (int32_t)mp;
   a.scale_log2 = scale * kLog2e;
   a.out_dtype = out_dtype;
+  return a;
+}
+
+}  // namespace
+
+hipError_t launch_paged_decode(const Cache& c, void* out, pa_dtype out_dtype, const void* query,
+                               const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, int32_t S, int32_t max_context_len,
+                               float scale, void* workspace, hipStream_t stream) {
+  const Variant* v = find_variant(c.dtype, c.head_dim, c.block_size);
+  if (!v) return hipErrorInvalidValue;
+  const int64_t mp = max_parts_for(*v, max_context_len);
+  DecodeArgs a = make_args(c, out, out_dtype, query, block_tables, max_blocks_per_seq, context_lens, S, mp, scale,
+                           workspace);
   const int64_t grid = (int64_t)S * c.num_heads * mp;
   hipLaunchKernelGGL(v->kernel, dim3((unsigned)grid), dim3(v->NW * 64), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || mp <= 1 || PA_DECODE_FUSED) return err;
   hipLaunchKernelGGL(decode_reduce_kernel, dim3((unsigned)(S * c.num_heads)), dim3(64), 0, stream, a,
                      (int32_t)c.head_dim, (int32_t)v->P);
+  return hipGetLastError();
+}
+
+bool decode_grouped_built(pa_dtype dtype, int head_dim, int block_size, int group_size) {
+  return find_grouped(dtype, head_dim, block_size, group_size) != nullptr;
+}
+
+size_t decode_grouped_workspace_bytes(const Cache& c, int32_t S, int32_t max_context_len, int32_t group_size) {
+  if (!find_grouped(c.dtype, c.head_dim, c.block_size, group_size))
+    return decode_workspace_bytes(c, S, max_context_len);  // served by the ungrouped kernel
+  const int64_t mp = ((int64_t)max_context_len + kGroupTokens - 1) / kGroupTokens;
+  if (mp <= 1) return 0;
+  return counter_bytes(S, c.num_heads) + (size_t)S * c.num_heads * mp * (c.head_dim + 2) * sizeof(float);
+}
+
+hipError_t launch_paged_decode_grouped(const Cache& c, void* out, pa_dtype out_dtype, const void* query,
+                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t* context_lens, int32_t S, int32_t max_context_len,
+                                       float scale, int32_t group_size, void* workspace, hipStream_t stream) {
+  const GroupedVariant* v = find_grouped(c.dtype, c.head_dim, c.block_size, group_size);
+  if (!v)  // no grouped build for this shape: the ungrouped kernel gives the same result
+    return launch_paged_decode(c, out, out_dtype, query, block_tables, max_blocks_per_seq, context_lens, S,
+                               max_context_len, scale, workspace, stream);
+  const int64_t mp = ((int64_t)max_context_len + kGroupTokens - 1) / kGroupTokens;
+  const int32_t ngroups = (S + group_size - 1) / group_size;
+  DecodeArgs a = make_args(c, out, out_dtype, query, block_tables, max_blocks_per_seq, context_lens, S, mp, scale,
+                           workspace);
+  const int64_t grid = (int64_t)ngroups * c.num_heads * mp;
+  hipLaunchKernelGGL(v->kernel, dim3((unsigned)grid), dim3(kGroupWaves * 64), 0, stream, a, ngroups);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || mp <= 1) return err;
+  hipLaunchKernelGGL(decode_reduce_kernel, dim3((unsigned)(S * c.num_heads)), dim3(64), 0, stream, a,
+                     (int32_t)c.head_dim, (int32_t)kGroupTokens);
   return hipGetLastError();
 }
 

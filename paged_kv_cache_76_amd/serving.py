@@ -32,7 +32,8 @@ import numpy as np
 import torch
 
 from . import inputs
-from ._lib import KVCache, decode_workspace, pa_copy_blocks, pa_paged_decode, pa_reshape_and_cache
+from ._lib import (KVCache, decode_grouped_workspace, decode_workspace, pa_copy_blocks, pa_paged_decode,
+                   pa_paged_decode_grouped, pa_reshape_and_cache)
 from .block_manager import BlockManager
 from .workloads import STREAMS, TORCH
 
@@ -212,7 +213,7 @@ class BeamLoop:
 
     def __init__(self, config_index: int, groups: int, width: int, prompt_len: int, steps: int,
                  num_heads: int, head_dim: int, block_size: int, dtype: str, beam: bool,
-                 device: str = "cuda", keep_history: bool = True, slack: float = 1.25):
+                 device: str = "cuda", keep_history: bool = True, slack: float = 1.25, grouped: bool = False):
         self.G, self.W, self.beam = groups, width, beam
         self.H, self.d, self.B = num_heads, head_dim, block_size
         self.dtype, self.device = dtype, device
@@ -249,7 +250,13 @@ class BeamLoop:
                              torch.from_numpy(np.concatenate(slots)).to(device))
         self.cur = np.arange(n)
         self.nxt = np.arange(n, 2 * n)
-        self.ws = decode_workspace(self.cache, n, prompt_len + steps + 1)
+        # grouped: the decode batch's rows come group by group, so the width
+        # sequences sharing a prompt form one group of pa_paged_decode_grouped
+        self.grouped = grouped
+        if grouped:
+            self.ws = decode_grouped_workspace(self.cache, n, prompt_len + steps + 1, width)
+        else:
+            self.ws = decode_workspace(self.cache, n, prompt_len + steps + 1)
 
     def remap(self) -> None:
         """Beam search: the children of each group fork from parents drawn
@@ -290,8 +297,12 @@ class BeamLoop:
         if len(pairs):
             pa_copy_blocks(self.cache, dev["pairs"])
         pa_reshape_and_cache(self.cache, dev["k"], dev["v"], dev["slots"])
-        pa_paged_decode(self.cache, out, dev["q"], dev["tables"], dev["lens"], int(lens.max()), self.scale,
-                        self.ws)
+        if self.grouped:
+            pa_paged_decode_grouped(self.cache, out, dev["q"], dev["tables"], dev["lens"], int(lens.max()),
+                                    self.scale, self.W, self.ws)
+        else:
+            pa_paged_decode(self.cache, out, dev["q"], dev["tables"], dev["lens"], int(lens.max()), self.scale,
+                            self.ws)
         if events is not None:
             events[1].record()
         if self.keep_history:

@@ -50,11 +50,11 @@ def test_serving_loop_opt13b(B, H):
     assert finished > 0
 
 
-@pytest.mark.parametrize("beam", [False, True])
-def test_shared_prompt_groups_bf16(beam):
-    print(f"shared blocks beam={beam}", flush=True)
+@pytest.mark.parametrize("beam,grouped", [(False, False), (True, False), (False, True), (True, True)])
+def test_shared_prompt_groups_bf16(beam, grouped):
+    print(f"shared blocks beam={beam} grouped={grouped}", flush=True)
     loop = BeamLoop(4, groups=32, width=4, prompt_len=512, steps=64, num_heads=8, head_dim=128,
-                    block_size=16, dtype="bf16", beam=beam)
+                    block_size=16, dtype="bf16", beam=beam, grouped=grouped)
     r = np.random.default_rng(int(beam))
     copies = 0
     for step in range(64):
