@@ -384,20 +384,173 @@ def longdecode_bench(args) -> int:
     return 0
 
 
+def accounting_bench(args) -> int:
+    """Share of held KV slots that store tokens, contiguous reservation vs
+    paged blocks, on the serving-loop length mix (no GPU involved)."""
+    from paged_kv_cache_76_amd import accounting
+    from paged_kv_cache_76_amd.serving import opt13b_serving_lengths
+
+    prompt, out, start = opt13b_serving_lengths(3, 256)
+    for bs in (16, 32):
+        u = accounting.utilisation(prompt, out, prompt + start, 2048, bs)
+        _line("KV memory holding token states (fraction of held slots)", 100 * u["paged"], "%", 1, 0, 0.0, "int64",
+              {"workload": "reservation accounting, 256-request serving snapshot", "block_size": bs,
+               "max_len": 2048, "seed": "SeedSequence(76003)"},
+              contiguous_max_pct=round(100 * u["max"], 2), contiguous_pow2_pct=round(100 * u["pow2"], 2),
+              contiguous_oracle_pct=round(100 * u["oracle"], 2), paged_pct=round(100 * u["paged"], 2))
+    return 0
+
+
+def blocksize_bench(args) -> int:
+    """The OPT-13B decode workload (64 x 40 heads, d=128, fp16, contexts
+    U[1,2048]) for block sizes 8..128: decode GB/s against tail waste."""
+    import torch
+
+    from paged_kv_cache_76_amd import _lib as L
+    from paged_kv_cache_76_amd import workloads
+
+    lens = workloads.opt13b_decode_lengths(2, S)
+    nbytes = None
+    for bs in (8, 16, 32, 64, 128):
+        b = workloads.build_decode_batch(2, lens, H, D, bs, DTYPE, nan_fill=False)
+        ws = L.decode_workspace(b.cache, S, b.max_context_len)
+        out = torch.empty((S, H, D), dtype=torch.float16, device="cuda")
+        fn = lambda: L.pa_paged_decode(b.cache, out, b.q_dev, b.tables_dev, b.lens_dev, b.max_context_len,
+                                       b.scale, ws)
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for e0, e1 in ev:
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)[args.steps // 2]
+        nbytes = workloads.decode_bytes(lens, H, D, ELEM, bs)
+        waste = int(b.manager.tail_waste().sum())
+        _line("paged decode HBM GB/s vs block size, OPT-13B shape", nbytes / (ms * 1e-3) / 1e9, "GB/s",
+              args.steps, args.warmup, ms, "f16",
+              {"workload": "block-size sweep of the OPT-13B decode", "block_size": bs, "sequences": S, "heads": H,
+               "head_dim": D, "seed": "SeedSequence(76002)"},
+              pct_of_peak=round(100 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2), median_us=round(ms * 1e3, 2),
+              tail_waste_slots=waste, tail_waste_pct=round(100 * waste / (waste + int(lens.sum())), 3))
+        del b, ws, out
+    return 0
+
+
+def copy_ablation_bench(args) -> int:
+    """Copy-on-write copies issued as one batched pa_copy_blocks launch versus
+    one device-to-device memcpy per block and pool (the alternative the pages
+    reject), for bursts of 8..512 OPT-13B blocks."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_76_amd import _lib as L
+
+    N = 2048
+    cache = L.KVCache.empty(N, H, B, D, torch.float16)
+    cache.k.fill_(1.0)
+    cache.v.fill_(2.0)
+    ids = np.random.default_rng(0).permutation(N)
+    for n in (8, 38, 96, 512):
+        pairs_np = np.stack([ids[:n], ids[n:2 * n]], axis=1).astype(np.int64)
+        pairs = torch.from_numpy(pairs_np).cuda()
+
+        def fused():
+            L.pa_copy_blocks(cache, pairs)
+
+        def per_block():
+            for s_, d_ in pairs_np:
+                cache.k[d_].copy_(cache.k[s_], non_blocking=True)
+                cache.v[d_].copy_(cache.v[s_], non_blocking=True)
+
+        res = {}
+        for name, fn in (("fused", fused), ("memcpy_per_block", per_block)):
+            for _ in range(args.warmup):
+                fn()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record()
+            for _ in range(args.steps):
+                fn()
+            ev1.record()
+            torch.cuda.synchronize()
+            res[name] = (ev0.elapsed_time(ev1) / args.steps, (time.perf_counter() - t0) / args.steps * 1e3)
+        moved = 2 * 2 * n * H * B * D * ELEM
+        _line("copy-on-write block copies GB/s (read + write), batched kernel", moved / (res["fused"][0] * 1e-3) / 1e9,
+              "GB/s", args.steps, args.warmup, res["fused"][0], "f16",
+              {"workload": "CoW copy burst", "pairs": n, "heads": H, "block_size": B, "head_dim": D},
+              fused_us=round(res["fused"][0] * 1e3, 2), per_block_memcpy_us=round(res["memcpy_per_block"][0] * 1e3, 2),
+              per_block_memcpy_host_ms=round(res["memcpy_per_block"][1], 3),
+              speedup=round(res["memcpy_per_block"][0] / res["fused"][0], 2))
+    return 0
+
+
+def prefix_bench(args) -> int:
+    """A provider prefix of 1024 tokens (a few-shot prompt) shared by 32
+    requests whose task inputs are lognormal (median 100, sigma 1, <= 1024),
+    OPT-13B heads, bf16: prefill over the task inputs only (the prefix's K/V
+    are cached) against prefilling every full prompt."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_76_amd import _lib as L
+    from paged_kv_cache_76_amd import inputs, workloads
+
+    r_len = inputs.streams(6, workloads.STREAMS)[0]
+    tasks = inputs.lognormal_lengths(r_len, 32, 100, 1.0, 1, 1024)
+    prefix = 1024
+    b = workloads.build_shared_prefix(6, prefix, tasks, H, D, B, "bf16")
+    full = workloads.build_prefill_batch(6, prefix + tasks, prefix + tasks, H, D, B, "bf16", nan_fill=False)
+    res = {}
+    for name, bb, qmax in (("task_only", b, int(tasks.max())), ("full_prompt", full, int((prefix + tasks).max()))):
+        rows = int(bb.cu_q[-1])
+        out = torch.empty((rows, H, D), dtype=torch.bfloat16, device="cuda")
+        fn = lambda: L.pa_paged_prefill(bb.cache, out, bb.q_dev, bb.tables_dev, bb.cu_q_dev, bb.lens_dev, qmax,
+                                        int(bb.lens.max()), bb.scale)
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for e0, e1 in ev:
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        res[name] = sorted(e0.elapsed_time(e1) for e0, e1 in ev)[args.steps // 2]
+    f_task = workloads.prefill_flops(prefix + tasks, tasks, H, D)
+    f_full = workloads.prefill_flops(prefix + tasks, prefix + tasks, H, D)
+    _line("prefill time saved by a cached shared prefix (speedup vs full-prompt prefill)",
+          res["full_prompt"] / res["task_only"], "x", args.steps, args.warmup, res["task_only"], "bf16",
+          {"workload": "shared prefix: 32 requests, 1024-token cached prefix, lognormal(100,1) task inputs",
+           "heads": H, "head_dim": D, "block_size": B, "seed": "SeedSequence(76006)"},
+          task_only_us=round(res["task_only"] * 1e3, 1), full_prompt_us=round(res["full_prompt"] * 1e3, 1),
+          task_only_TFLOPs=round(f_task / (res["task_only"] * 1e-3) / 1e12, 1),
+          full_prompt_TFLOPs=round(f_full / (res["full_prompt"] * 1e-3) / 1e12, 1),
+          flop_ratio=round(f_full / f_task, 2), cow_copies=b.copies)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seqs", type=int, default=64, help="sequences in the CPU-oracle sample (0: skip)")
-    ap.add_argument("--workload", choices=["decode", "copy", "prefill", "serving", "shared", "longdecode"],
+    ap.add_argument("--workload", choices=["decode", "copy", "prefill", "serving", "shared", "longdecode",
+                                           "blocksize", "copyablation", "accounting", "prefix"],
                     default="decode",
                     help="decode: the OPT-13B decode step (default); copy: pa_copy_blocks over 2048 "
                          "OPT-13B blocks, a plain copy of known size used to calibrate HBM counters; "
                          "prefill: 8 x 1024-token prompts at the OPT-66B shape (write + causal prefill); "
                          "serving: 32 steps of a 256-sequence serving loop (B=16 and 32); shared: parallel "
                          "sampling and beam search over shared prompt blocks (bf16); longdecode: 16 x 32768 "
-                         "tokens at the OPT-66B head count (bf16)")
+                         "tokens at the OPT-66B head count (bf16); blocksize: OPT-13B decode for block "
+                         "sizes 8..128; copyablation: one batched pa_copy_blocks vs one memcpy per block; "
+                         "accounting: KV utilisation of contiguous reservation vs paged blocks (host only); "
+                         "prefix: prefill over task inputs only, with a cached 1024-token shared prefix")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU layout is a design "
@@ -410,8 +563,16 @@ def main() -> int:
     from paged_kv_cache_76_amd import _lib as L
     from paged_kv_cache_76_amd import inputs, workloads
 
+    if args.workload == "accounting":
+        return accounting_bench(args)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.workload == "blocksize":
+        return blocksize_bench(args)
+    if args.workload == "copyablation":
+        return copy_ablation_bench(args)
+    if args.workload == "prefix":
+        return prefix_bench(args)
     if args.workload == "copy":
         return copy_calibration(args)
     if args.workload == "prefill":

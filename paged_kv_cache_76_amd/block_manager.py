@@ -172,6 +172,44 @@ class BlockManager:
         pairs = np.stack([src, new_ids[cow]], axis=1) if len(src) else np.zeros((0, 2), np.int64)
         return slots.astype(np.int64), pairs.astype(np.int64)
 
+    def extend(self, row: int, n: int) -> tuple[np.ndarray, np.ndarray]:
+        """Append ``n`` tokens to one row at once (the same outcome as ``n``
+        single appends): returns the tokens' slots and the copy pairs.
+
+        Used for a request that maps a cached prefix and then writes its own
+        task input ("vLLM / PagedAttention (SOSP 2023)" guide, section 04:
+        the last prefix block is copy-on-write)."""
+        self._check_row(row, live=True)
+        if n <= 0:
+            return np.zeros(0, np.int64), np.zeros((0, 2), np.int64)
+        L = int(self.lens[row])
+        nb = int(self.nblocks[row])
+        off = L % self.B
+        room = (self.B - off) % self.B          # free slots in the last block
+        new_blocks = -(-(n - room) // self.B) if n > room else 0
+        last = int(self.tables[row, nb - 1])
+        cow = room > 0 and self.ref[last] > 1    # the first token lands in a shared partial block
+        if nb + new_blocks > self.max_blocks:
+            raise ValueError("a sequence outgrew max_blocks_per_seq")
+        ids = self._pop(new_blocks + int(cow))   # raises before any change
+        pairs = np.zeros((0, 2), np.int64)
+        if cow:
+            copy = int(ids[0])
+            pairs = np.array([[last, copy]], np.int64)
+            self.ref[last] -= 1
+            self.ref[copy] = 1
+            self.tables[row, nb - 1] = copy
+            self.cow_copies += 1
+            last = copy
+            ids = ids[1:]
+        self.tables[row, nb:nb + new_blocks] = ids
+        self.ref[ids] = 1
+        self.nblocks[row] = nb + new_blocks
+        self.lens[row] = L + n
+        pos = np.arange(L, L + n, dtype=np.int64)
+        table = self.tables[row, : nb + new_blocks].astype(np.int64)
+        return table[pos // self.B] * self.B + pos % self.B, pairs
+
     def fork(self, src_row: int, dst_row: int) -> None:
         """``dst_row`` shares every block of ``src_row`` (counts + 1)."""
         self._check_row(src_row, live=True)

@@ -16,7 +16,7 @@ import numpy as np
 import torch
 
 from . import inputs
-from ._lib import KVCache, pa_reshape_and_cache
+from ._lib import KVCache, pa_copy_blocks, pa_reshape_and_cache
 from .block_manager import BlockManager
 
 TORCH = inputs.DTYPES
@@ -250,3 +250,69 @@ def build_long_decode(config_index: int, S: int, ctx: int, num_heads: int, head_
             sample_data[(s, h)] = (q[s, h].cpu(), K[:, i], V[:, i])
     return LongDecode(cache, mgr, q, torch.from_numpy(mgr.tables).cuda(),
                       torch.from_numpy(lens.astype(np.int32)).cuda(), lens, 1.0 / math.sqrt(head_dim), sample_data)
+
+
+@dataclass
+class PrefixBatch:
+    """Requests that map a provider's cached prefix and prefill only their
+    own task input ("vLLM / PagedAttention (SOSP 2023)" guide, section 04)."""
+
+    cache: KVCache
+    manager: BlockManager
+    prefix_k: torch.Tensor     # host [P][H][d]
+    prefix_v: torch.Tensor
+    task_k: list               # host per request [T_i][H][d]
+    task_v: list
+    q: torch.Tensor            # host [sum T_i][H][d], queries of the task tokens
+    q_dev: torch.Tensor
+    tables_dev: torch.Tensor   # int32 [R][max_blocks] (rows 1..R of the manager)
+    cu_q_dev: torch.Tensor
+    lens_dev: torch.Tensor
+    lens: np.ndarray           # prefix + task
+    task_lens: np.ndarray
+    cu_q: np.ndarray
+    copies: int
+    scale: float
+
+
+def build_shared_prefix(config_index: int, prefix_len: int, task_lens, num_heads: int, head_dim: int,
+                        block_size: int, dtype: str, device: str = "cuda") -> PrefixBatch:
+    """Row 0 of the block manager holds a provider prefix of ``prefix_len``
+    tokens (written once); request i forks it, extends by ``task_lens[i]``
+    tokens (copying the partial last prefix block first) and writes its own
+    keys/values.  Queries cover the task tokens only."""
+    task_lens = np.asarray(task_lens, np.int64)
+    R = len(task_lens)
+    _, r_q, r_k, r_v, r_pool, _, _ = inputs.streams(config_index, STREAMS)
+    max_len = prefix_len + int(task_lens.max())
+    need = -(-prefix_len // block_size) + int(sum(-(-(int(t) + block_size) // block_size) for t in task_lens))
+    N = int(math.ceil(need * 1.1)) + 1
+    mgr = BlockManager(N, block_size, max_rows=R + 1, max_blocks_per_seq=-(-max_len // block_size),
+                       free_order=inputs.pool_order(r_pool, N))
+    cache = KVCache.empty(N + 1, num_heads, block_size, head_dim, TORCH[dtype], device)
+    cache.k.fill_(float("nan"))
+    cache.v.fill_(float("nan"))
+    pk = inputs.normal(r_k, (prefix_len, num_heads, head_dim), dtype)
+    pv = inputs.normal(r_v, (prefix_len, num_heads, head_dim), dtype)
+    pslots = mgr.add_prompt(0, prefix_len)
+    pa_reshape_and_cache(cache, pk.to(device), pv.to(device), torch.from_numpy(pslots).to(device))
+    tk, tv, all_slots, all_pairs = [], [], [], []
+    for i, t in enumerate(task_lens, start=1):
+        mgr.fork(0, i)
+        slots, pairs = mgr.extend(i, int(t))
+        all_slots.append(slots)
+        all_pairs.append(pairs)
+        tk.append(inputs.normal(r_k, (int(t), num_heads, head_dim), dtype))
+        tv.append(inputs.normal(r_v, (int(t), num_heads, head_dim), dtype))
+    pairs = np.concatenate(all_pairs) if all_pairs else np.zeros((0, 2), np.int64)
+    if len(pairs):  # copy-on-write of the shared partial block, before any task write
+        pa_copy_blocks(cache, torch.from_numpy(pairs).to(device))
+    pa_reshape_and_cache(cache, torch.cat(tk).to(device), torch.cat(tv).to(device),
+                         torch.from_numpy(np.concatenate(all_slots)).to(device))
+    q = inputs.normal(r_q, (int(task_lens.sum()), num_heads, head_dim), dtype)
+    lens = (prefix_len + task_lens).astype(np.int64)
+    cu_q = np.concatenate([[0], np.cumsum(task_lens)]).astype(np.int32)
+    return PrefixBatch(cache, mgr, pk, pv, tk, tv, q, q.to(device),
+                       torch.from_numpy(np.ascontiguousarray(mgr.tables[1:R + 1])).to(device),
+                       torch.from_numpy(cu_q).to(device), torch.from_numpy(lens.astype(np.int32)).to(device),
+                       lens, task_lens, cu_q, len(pairs), 1.0 / math.sqrt(head_dim))

@@ -161,3 +161,33 @@ def test_beam_remaps_keep_invariants_and_release_pruned_blocks():
         assert pairs.tolist() == [list(e[1]) for e in exp if e[1]]
         model.check_invariants()
         _same(prod, model)
+
+
+@pytest.mark.parametrize("B,prefix,tasks", [(4, 7, [1, 5, 9]), (16, 200, [13, 1, 40]), (16, 32, [3, 17]),
+                                            (8, 8, [8, 1])])
+def test_extend_matches_single_appends(B, prefix, tasks):
+    # a provider prefix held by row 0; each request forks it and extends by its
+    # task input (CoW of the partial last prefix block), as in the shared-prefix
+    # description of the pages
+    r = np.random.default_rng(B + prefix)
+    N = 256
+    order = r.permutation(N)
+    prod = BlockManager(N, B, max_rows=len(tasks) + 1, max_blocks_per_seq=64, free_order=order)
+    model = bm.BlockModel(N, B, order)
+    assert prod.add_prompt(0, prefix).tolist() == model.add_prompt(0, prefix)
+    for i, n in enumerate(tasks, start=1):
+        prod.fork(0, i)
+        model.fork(0, i)
+        slots, pairs = prod.extend(i, n)
+        exp_slots, exp_pairs = [], []
+        for _ in range(n):
+            slot, pair = model.append(i)
+            exp_slots.append(slot)
+            if pair:
+                exp_pairs.append(list(pair))
+        assert slots.tolist() == exp_slots
+        assert pairs.tolist() == exp_pairs
+        model.check_invariants()
+        _same(prod, model)
+    # the prefix row still maps the original prefix blocks
+    assert prod.table(0) == model.table(0)

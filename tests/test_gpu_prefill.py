@@ -91,3 +91,28 @@ def test_opt66b_prefill_full_size_sampled():
         ref = _oracle(b, s, rows, heads)
         got = out[b.cu_q[s]:b.cu_q[s + 1]][rows][:, heads]
         check_close(got, ref, TOL["bf16"], f"OPT-66B prefill seq {s}")
+
+
+@pytest.mark.parametrize("dtype,B,prefix,tasks", [("bf16", 16, 200, [13, 1, 129, 40]),
+                                                  ("f16", 16, 256, [64, 3]),
+                                                  ("bf16", 32, 77, [200, 5, 31])])
+def test_shared_prefix_prefill_over_task_input_only(dtype, B, prefix, tasks):
+    # requests fork a cached provider prefix, extend by their task input (CoW of
+    # a partial last prefix block) and prefill only the task tokens
+    print(f"shared prefix {dtype} B={B} prefix={prefix}", flush=True)
+    from oracle import cache as oc
+    b = workloads.build_shared_prefix(11, prefix, tasks, num_heads=3, head_dim=128, block_size=B, dtype=dtype)
+    assert b.copies == (len(tasks) if prefix % B else 0)
+    out = torch.empty((int(b.task_lens.sum()), 3, 128), dtype=torch.float32, device="cuda")
+    L.pa_paged_prefill(b.cache, out, b.q_dev, b.tables_dev, b.cu_q_dev, b.lens_dev, int(b.task_lens.max()),
+                       int(b.lens.max()), b.scale)
+    torch.cuda.synchronize()
+    for i in range(len(tasks)):
+        K = inputs.to_f64(torch.cat([b.prefix_k, b.task_k[i]]))
+        V = inputs.to_f64(torch.cat([b.prefix_v, b.task_v[i]]))
+        Q = inputs.to_f64(b.q[b.cu_q[i]:b.cu_q[i + 1]])
+        check_close(out[b.cu_q[i]:b.cu_q[i + 1]], oa.prefill(Q, K, V, b.scale), TOL[dtype], f"prefix request {i}")
+    # the provider's prefix blocks still hold the prefix, bit for bit
+    kp = b.cache.k.cpu().view(torch.int16).numpy()
+    got = oc.gather_history(kp, b.manager.table(0), prefix)
+    assert np.array_equal(got, b.prefix_k.view(torch.int16).numpy())
