@@ -533,6 +533,66 @@ def prefix_bench(args) -> int:
     return 0
 
 
+def swap_bench(args) -> int:
+    """Preemption by swapping: 16 sequences x 1024 tokens at the OPT-13B
+    shape (fp16) leave the device for a pinned host pool in one batched call
+    and come back in another (1024 blocks, 320 MiB each way)."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_76_amd import _lib as L
+    from paged_kv_cache_76_amd.block_manager import BlockManager
+
+    S16, L16 = 16, 1024
+    nblk = S16 * L16 // B
+    N = nblk + 64
+    cache = L.KVCache.empty(N, H, B, D, torch.float16)
+    cache.k.fill_(1.0)
+    cache.v.fill_(2.0)
+    m = BlockManager(N, B, max_rows=S16, max_blocks_per_seq=L16 // B, host_blocks=nblk,
+                     free_order=np.random.default_rng(0).permutation(N))
+    for s_ in range(S16):
+        m.add_prompt(s_, L16)
+    host_k = torch.empty((nblk, H, B, D), dtype=torch.float16, pin_memory=True)
+    host_v = torch.empty((nblk, H, B, D), dtype=torch.float16, pin_memory=True)
+    t_host = time.perf_counter()
+    out_pairs = torch.from_numpy(m.swap_out(range(S16))).cuda()
+    in_pairs = torch.from_numpy(m.swap_in(range(S16))).cuda()
+    bm_ms = (time.perf_counter() - t_host) * 1e3 / 2
+    moved = 2 * nblk * H * B * D * 2                 # keys and values, one direction
+    res = {}
+    for name, pairs, direction in (("out", out_pairs, L.PA_SWAP_OUT), ("in", in_pairs, L.PA_SWAP_IN)):
+        for _ in range(args.warmup):
+            L.pa_swap_blocks(cache, host_k, host_v, pairs, direction)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for e0, e1 in ev:
+            e0.record()
+            L.pa_swap_blocks(cache, host_k, host_v, pairs, direction)
+            e1.record()
+        torch.cuda.synchronize()
+        res[name] = sorted(e0.elapsed_time(e1) for e0, e1 in ev)[args.steps // 2]
+    # reference: one plain host<->device copy of the same number of bytes
+    flat_dev = cache.k.view(-1)[: nblk * H * B * D]
+    flat_host = host_k.view(-1)
+    flat_host.copy_(flat_dev, non_blocking=True)     # untimed first copy
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(2):
+        flat_host.copy_(flat_dev, non_blocking=True)
+    e1.record()
+    torch.cuda.synchronize()
+    memcpy_gbs = 2 * flat_dev.numel() * 2 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    _line("preemption swap GB/s (device -> pinned host), 16 x 1024 OPT-13B tokens", moved / (res["out"] * 1e-3) / 1e9,
+          "GB/s", args.steps, args.warmup, res["out"], "f16",
+          {"workload": "swap out / swap in of a 16-sequence group", "blocks": nblk, "heads": H, "block_size": B,
+           "head_dim": D, "bytes_each_way": moved},
+          swap_in_GBps=round(moved / (res["in"] * 1e-3) / 1e9, 1), swap_out_us=round(res["out"] * 1e3, 1),
+          swap_in_us=round(res["in"] * 1e3, 1), contiguous_memcpy_d2h_GBps=round(memcpy_gbs, 1),
+          host_block_manager_ms=round(bm_ms, 3))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -540,7 +600,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seqs", type=int, default=64, help="sequences in the CPU-oracle sample (0: skip)")
     ap.add_argument("--workload", choices=["decode", "copy", "prefill", "serving", "shared", "longdecode",
-                                           "blocksize", "copyablation", "accounting", "prefix"],
+                                           "blocksize", "copyablation", "accounting", "prefix", "swap"],
                     default="decode",
                     help="decode: the OPT-13B decode step (default); copy: pa_copy_blocks over 2048 "
                          "OPT-13B blocks, a plain copy of known size used to calibrate HBM counters; "
@@ -550,7 +610,8 @@ def main() -> int:
                          "tokens at the OPT-66B head count (bf16); blocksize: OPT-13B decode for block "
                          "sizes 8..128; copyablation: one batched pa_copy_blocks vs one memcpy per block; "
                          "accounting: KV utilisation of contiguous reservation vs paged blocks (host only); "
-                         "prefix: prefill over task inputs only, with a cached 1024-token shared prefix")
+                         "prefix: prefill over task inputs only, with a cached 1024-token shared prefix; "
+                         "swap: a preempted group's blocks to pinned host memory and back")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU layout is a design "
@@ -573,6 +634,8 @@ def main() -> int:
         return copy_ablation_bench(args)
     if args.workload == "prefix":
         return prefix_bench(args)
+    if args.workload == "swap":
+        return swap_bench(args)
     if args.workload == "copy":
         return copy_calibration(args)
     if args.workload == "prefill":

@@ -103,6 +103,28 @@ pa_status pa_reshape_and_cache(const pa_kv_cache* cache, const void* key, const 
 pa_status pa_copy_blocks(const pa_kv_cache* cache, const int64_t* pairs, int32_t n, void* stream);
 
 /*
+ * pa_swap_blocks — move whole blocks between the device pools and a pinned
+ * host pool, in one batched call.
+ * [P2] 调度和抢占 (a preempted request's KV blocks, all of them, are swapped
+ * to CPU memory and brought back when memory frees up); [P3] section 05
+ * (all-or-nothing eviction of a sequence's blocks; the swap space lives in
+ * CPU RAM); [P1] key design 4.
+ *
+ *   host_k, host_v   pinned host memory the device can address (hipHostMalloc,
+ *                    or a torch tensor with pin_memory=True), each
+ *                    [host_num_blocks][num_heads][block_size][head_dim] of the
+ *                    cache dtype.  Anything else is rejected (PA_ERR_INVALID_ARG)
+ *                    before any launch.
+ *   pairs            int64 [n][2] on the device: (src, dst).  PA_SWAP_OUT:
+ *                    src = device block, dst = host block; PA_SWAP_IN: src =
+ *                    host block, dst = device block.  Destinations distinct.
+ * Effect: dst block = src block for keys and values, bit-exact.
+ */
+typedef enum { PA_SWAP_OUT = 0, PA_SWAP_IN = 1 } pa_swap_dir;
+pa_status pa_swap_blocks(const pa_kv_cache* cache, void* host_k, void* host_v, int32_t host_num_blocks,
+                         const int64_t* pairs, int32_t n, pa_swap_dir dir, void* stream);
+
+/*
  * Workspace of pa_paged_decode, in bytes, for S sequences whose longest
  * context is max_context_len tokens.  0 means "no workspace needed".
  * Returns (size_t)-1 for an unsupported cache description.

@@ -75,6 +75,19 @@ def copy_blocks(k_pool: np.ndarray, v_pool: np.ndarray,
     return k_out, v_out
 
 
+def swap_blocks(src_k: np.ndarray, src_v: np.ndarray, dst_k: np.ndarray, dst_v: np.ndarray,
+                pairs) -> tuple[np.ndarray, np.ndarray]:
+    """Expected destination pools after copying whole blocks from one pool to
+    another (device <-> host swapping, "vLLM" notes, 调度和抢占): for each
+    ``(src, dst)``, ``dst_pool[dst] = src_pool[src]`` for keys and values."""
+    k_out = dst_k.copy()
+    v_out = dst_v.copy()
+    for src, dst in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):
+        k_out[dst] = src_k[src]
+        v_out[dst] = src_v[src]
+    return k_out, v_out
+
+
 def gather_history(pool: np.ndarray, block_table, context_len: int) -> np.ndarray:
     """The logically contiguous ``[L][H][d]`` history of one sequence, read
     through its block table: logical position ``p`` is slot ``p % B`` of

@@ -19,11 +19,12 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedatt
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_LAUNCH = range(5)
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+PA_SWAP_OUT, PA_SWAP_IN = 0, 1
 TORCH_TO_PA = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
 
 # every symbol include/pagedattn.h declares
 EXPORTS = (
-    "pa_reshape_and_cache", "pa_copy_blocks", "pa_decode_workspace_bytes", "pa_paged_decode",
+    "pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_decode_workspace_bytes", "pa_paged_decode",
     "pa_decode_grouped_workspace_bytes", "pa_paged_decode_grouped", "pa_paged_prefill",
     "pa_status_string", "pa_last_error", "pa_abi_version",
 )
@@ -57,6 +58,7 @@ def load_library(path: str) -> ctypes.CDLL:
     C = ctypes.POINTER(PaKVCache)
     L.pa_reshape_and_cache.argtypes = [C, P, P, I64P, I32, P]
     L.pa_copy_blocks.argtypes = [C, I64P, I32, P]
+    L.pa_swap_blocks.argtypes = [C, P, P, I32, I64P, I32, ctypes.c_int, P]
     L.pa_decode_workspace_bytes.argtypes = [C, I32, I32]
     L.pa_decode_workspace_bytes.restype = ctypes.c_size_t
     L.pa_paged_decode.argtypes = [C, P, ctypes.c_int, P, I32P, I32, I32P, I32, I32, ctypes.c_float, P,
@@ -67,7 +69,7 @@ def load_library(path: str) -> ctypes.CDLL:
                                           P, ctypes.c_size_t, P]
     L.pa_paged_prefill.argtypes = [C, P, ctypes.c_int, P, I32P, I32, I32P, I32P, I32, I32, I32,
                                    ctypes.c_float, P]
-    for fn in ("pa_reshape_and_cache", "pa_copy_blocks", "pa_paged_decode", "pa_paged_decode_grouped",
+    for fn in ("pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_paged_decode", "pa_paged_decode_grouped",
                "pa_paged_prefill"):
         getattr(L, fn).restype = ctypes.c_int
     L.pa_status_string.argtypes = [ctypes.c_int]
@@ -181,6 +183,22 @@ def pa_copy_blocks(cache: KVCache, pairs: torch.Tensor, stream=None) -> None:
         raise ValueError("pairs must be [n][2]")
     d = cache.desc()
     _check(lib().pa_copy_blocks(ctypes.byref(d), _ptr(pairs) if n else None, n, _stream(stream)))
+
+
+def pa_swap_blocks(cache: KVCache, host_k: torch.Tensor, host_v: torch.Tensor, pairs: torch.Tensor,
+                   direction: int, stream=None) -> None:
+    """Copy whole blocks between the device pools and pinned host pools
+    ``[host_blocks][H][B][d]``; ``pairs int64 [n][2]`` on the device are
+    (device, host) for PA_SWAP_OUT and (host, device) for PA_SWAP_IN."""
+    _contig("pairs", pairs, torch.int64)
+    for name, t in (("host_k", host_k), ("host_v", host_v)):
+        _contig(name, t, cache.dtype)
+        if t.shape[1:] != cache.k.shape[1:] or t.device.type != "cpu":
+            raise ValueError(f"{name} must be a host tensor [blocks][H][B][d]")
+    n = pairs.shape[0] if pairs.numel() else 0
+    d = cache.desc()
+    _check(lib().pa_swap_blocks(ctypes.byref(d), _ptr(host_k), _ptr(host_v), host_k.shape[0],
+                                _ptr(pairs) if n else None, n, int(direction), _stream(stream)))
 
 
 def pa_decode_workspace_bytes(cache: KVCache, S: int, max_context_len: int) -> int:

@@ -46,7 +46,7 @@ class OutOfBlocks(RuntimeError):
 
 class BlockManager:
     def __init__(self, num_blocks: int, block_size: int, max_rows: int, max_blocks_per_seq: int,
-                 free_order=None, poison: int | None = None):
+                 free_order=None, poison: int | None = None, host_blocks: int = 0):
         if block_size < 1 or num_blocks < 1:
             raise ValueError("num_blocks and block_size must be >= 1")
         self.num_blocks = int(num_blocks)
@@ -66,6 +66,11 @@ class BlockManager:
         self.nblocks = np.zeros(max_rows, dtype=np.int32)
         self.lens = np.zeros(max_rows, dtype=np.int64)
         self.cow_copies = 0
+        # host (swap) pool: FIFO free list, reference counts, swapped rows
+        self.host_blocks = int(host_blocks)
+        self._host_free = list(range(self.host_blocks))
+        self.host_ref = np.zeros(self.host_blocks, dtype=np.int32)
+        self.swapped: dict[int, tuple[np.ndarray, int]] = {}   # row -> (host ids, length)
 
     # ---- free list ----------------------------------------------------------
     @property
@@ -97,6 +102,8 @@ class BlockManager:
     def _check_row(self, row: int, live: bool) -> None:
         if not 0 <= row < self.max_rows:
             raise IndexError(f"row {row} outside [0, {self.max_rows})")
+        if row in self.swapped:
+            raise KeyError(f"row {row} is swapped out")
         if live and self.lens[row] == 0:
             raise KeyError(f"row {row} holds no sequence")
         if not live and self.lens[row] != 0:
@@ -231,6 +238,68 @@ class BlockManager:
         self.tables[row, :] = self.poison
         self.nblocks[row] = 0
         self.lens[row] = 0
+
+    # ---- swapping (preemption) ----------------------------------------------
+    def swap_out(self, rows) -> np.ndarray:
+        """Evict a group of rows all-or-nothing: every distinct block they map
+        moves to the host pool ("vLLM" notes, 调度和抢占; the SOSP guide,
+        section 05).  Returns (device, host) pairs for ``pa_swap_blocks``;
+        the copies must run before the freed device blocks are reused.  A
+        block shared inside the group stays shared on the host."""
+        rows = sorted(set(int(r) for r in rows))
+        for r in rows:
+            self._check_row(r, live=True)
+        dev = []
+        seen = set()
+        for r in rows:
+            for b in self.tables[r, : self.nblocks[r]].tolist():
+                if b not in seen:
+                    seen.add(b)
+                    dev.append(b)
+        if len(dev) > len(self._host_free):
+            raise OutOfBlocks(f"{len(dev)} host blocks needed, {len(self._host_free)} free")
+        host = [self._host_free.pop(0) for _ in dev]
+        to_host = dict(zip(dev, host))
+        for r in rows:
+            ids = self.tables[r, : self.nblocks[r]].astype(np.int64)
+            hids = np.array([to_host[int(b)] for b in ids], dtype=np.int64)
+            self.host_ref[hids] += 1
+            self.swapped[r] = (hids, int(self.lens[r]))
+            self.ref[ids] -= 1
+            self._push(ids[self.ref[ids] == 0])
+            self.tables[r, :] = self.poison
+            self.nblocks[r] = 0
+            self.lens[r] = 0
+        return np.array([[d, h] for d, h in zip(dev, host)], dtype=np.int64).reshape(-1, 2)
+
+    def swap_in(self, rows) -> np.ndarray:
+        """Bring swapped rows back: one fresh device block per distinct host
+        block.  Returns (host, device) pairs for ``pa_swap_blocks``."""
+        rows = sorted(set(int(r) for r in rows))
+        for r in rows:
+            if r not in self.swapped:
+                raise KeyError(f"row {r} is not swapped out")
+        hosts = []
+        seen = set()
+        for r in rows:
+            for h in self.swapped[r][0].tolist():
+                if h not in seen:
+                    seen.add(h)
+                    hosts.append(h)
+        ids = self._pop(len(hosts))              # raises before any change
+        to_dev = dict(zip(hosts, ids.tolist()))
+        for r in rows:
+            hids, length = self.swapped.pop(r)
+            dev = np.array([to_dev[int(h)] for h in hids], dtype=np.int64)
+            self.tables[r, : len(dev)] = dev
+            self.nblocks[r] = len(dev)
+            self.lens[r] = length
+            np.add.at(self.ref, dev, 1)
+            self.host_ref[hids] -= 1
+        for h in hosts:
+            if self.host_ref[h] == 0:
+                self._host_free.append(h)
+        return np.array([[h, to_dev[h]] for h in hosts], dtype=np.int64).reshape(-1, 2)
 
     # ---- views and accounting -------------------------------------------------
     def table(self, row: int) -> list[int]:

@@ -88,6 +88,36 @@ pa_status pa_copy_blocks(const pa_kv_cache* cache, const int64_t* pairs, int32_t
   return launched(fn, pa::launch_copy_blocks(c, pairs, n, (hipStream_t)stream));
 }
 
+pa_status pa_swap_blocks(const pa_kv_cache* cache, void* host_k, void* host_v, int32_t host_num_blocks,
+                         const int64_t* pairs, int32_t n, pa_swap_dir dir, void* stream) {
+  const char* fn = "pa_swap_blocks";
+  pa::Cache c;
+  pa_status st = check_cache(fn, cache, &c);
+  if (st != PA_OK) return st;
+  if (dir != PA_SWAP_OUT && dir != PA_SWAP_IN) return fail(PA_ERR_INVALID_ARG, "%s: bad direction %d", fn, (int)dir);
+  if (n < 0 || host_num_blocks < 0) return fail(PA_ERR_INVALID_ARG, "%s: negative size", fn);
+  if (n == 0) return PA_OK;
+  if (!pairs || !host_k || !host_v) return fail(PA_ERR_INVALID_ARG, "%s: NULL pairs/host pool", fn);
+  if (!aligned(pairs, 8) || !aligned(host_k, 16) || !aligned(host_v, 16))
+    return fail(PA_ERR_INVALID_ARG, "%s: misaligned pairs/host pool", fn);
+  if (n > (1 << 30)) return fail(PA_ERR_INVALID_ARG, "%s: n = %d is too large", fn, n);
+  // the kernel dereferences the host pools: they must be pinned host memory
+  // the device can address (a pageable pointer would fault the GPU)
+  void* dev_ptr[2] = {nullptr, nullptr};
+  void* host_ptr[2] = {host_k, host_v};
+  for (int i = 0; i < 2; ++i) {
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, host_ptr[i]) != hipSuccess || attr.type != hipMemoryTypeHost ||
+        attr.devicePointer == nullptr) {
+      (void)hipGetLastError();  // clear the query's error state
+      return fail(PA_ERR_INVALID_ARG, "%s: host pool %d is not pinned, device-accessible host memory", fn, i);
+    }
+    dev_ptr[i] = attr.devicePointer;
+  }
+  return launched(fn, pa::launch_swap_blocks(c, dev_ptr[0], dev_ptr[1], host_num_blocks, pairs, n,
+                                             dir == PA_SWAP_OUT, (hipStream_t)stream));
+}
+
 size_t pa_decode_workspace_bytes(const pa_kv_cache* cache, int32_t S, int32_t max_context_len) {
   pa::Cache c;
   if (check_cache("pa_decode_workspace_bytes", cache, &c) != PA_OK) return (size_t)-1;

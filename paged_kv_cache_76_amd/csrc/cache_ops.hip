@@ -70,7 +70,51 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
   }
 }
 
+// Whole-block copies between two pools of the same block shape (device and
+// pinned host memory for swapping).  grid.x = pair * 2 + pool, grid.y = chunk.
+__global__ __launch_bounds__(kCopyThreads) void swap_blocks_kernel(
+    const u32x4* __restrict__ src_k, const u32x4* __restrict__ src_v, u32x4* __restrict__ dst_k,
+    u32x4* __restrict__ dst_v, const int64_t* __restrict__ pairs, int64_t vec_per_block, int64_t src_blocks,
+    int64_t dst_blocks) {
+  const int64_t pair = blockIdx.x >> 1;
+  const u32x4* __restrict__ src = (blockIdx.x & 1) ? src_v : src_k;
+  u32x4* __restrict__ dst = (blockIdx.x & 1) ? dst_v : dst_k;
+  const int64_t s = pairs[2 * pair];
+  const int64_t d = pairs[2 * pair + 1];
+  if (s < 0 || s >= src_blocks || d < 0 || d >= dst_blocks) return;
+  const int64_t base = (int64_t)blockIdx.y * (kCopyThreads * kCopyUnroll) + threadIdx.x;
+  u32x4 buf[kCopyUnroll];
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const int64_t e = base + u * kCopyThreads;
+    if (e < vec_per_block) buf[u] = __builtin_nontemporal_load(&src[s * vec_per_block + e]);
+  }
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const int64_t e = base + u * kCopyThreads;
+    if (e < vec_per_block) dst[d * vec_per_block + e] = buf[u];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_swap_blocks(const Cache& c, void* host_k, void* host_v, int32_t host_blocks,
+                              const int64_t* pairs, int32_t n, bool to_host, hipStream_t stream) {
+  const int64_t block_bytes =
+      (int64_t)c.num_heads * c.block_size * c.head_dim * dtype_bytes(c.dtype);
+  const int64_t vec_per_block = block_bytes / 16;
+  const int64_t per_wg = kCopyThreads * kCopyUnroll;
+  dim3 grid((unsigned)(2 * n), (unsigned)((vec_per_block + per_wg - 1) / per_wg));
+  const u32x4* src_k = (const u32x4*)(to_host ? c.k : host_k);
+  const u32x4* src_v = (const u32x4*)(to_host ? c.v : host_v);
+  u32x4* dst_k = (u32x4*)(to_host ? host_k : c.k);
+  u32x4* dst_v = (u32x4*)(to_host ? host_v : c.v);
+  const int64_t src_blocks = to_host ? c.num_blocks : host_blocks;
+  const int64_t dst_blocks = to_host ? host_blocks : c.num_blocks;
+  hipLaunchKernelGGL(swap_blocks_kernel, grid, dim3(kCopyThreads), 0, stream, src_k, src_v, dst_k, dst_v, pairs,
+                     vec_per_block, src_blocks, dst_blocks);
+  return hipGetLastError();
+}
 
 hipError_t launch_reshape_and_cache(const Cache& c, const void* key, const void* value,
                                     const int64_t* slot_mapping, int32_t T, hipStream_t stream) {

@@ -27,6 +27,10 @@ inline int dtype_bytes(pa_dtype t) { return t == PA_F32 ? 4 : 2; }
 hipError_t launch_reshape_and_cache(const Cache& c, const void* key, const void* value,
                                     const int64_t* slot_mapping, int32_t T, hipStream_t stream);
 hipError_t launch_copy_blocks(const Cache& c, const int64_t* pairs, int32_t n, hipStream_t stream);
+// host_k / host_v are device-accessible addresses of pinned host pools of
+// host_blocks blocks; to_host: device -> host (pairs = (device, host)).
+hipError_t launch_swap_blocks(const Cache& c, void* host_k, void* host_v, int32_t host_blocks,
+                              const int64_t* pairs, int32_t n, bool to_host, hipStream_t stream);
 
 // ---- decode (paged_decode.hip) ------------------------------------------------
 // Tokens per context partition for this cache shape, or 0 if the shape is

@@ -191,3 +191,79 @@ def test_extend_matches_single_appends(B, prefix, tasks):
         _same(prod, model)
     # the prefix row still maps the original prefix blocks
     assert prod.table(0) == model.table(0)
+
+
+def _consistent(m: BlockManager):
+    # device reference counts equal table references; free and used partition the pool
+    counts = np.zeros(m.num_blocks, np.int64)
+    for r in m.live_rows():
+        np.add.at(counts, m.tables[r, : m.nblocks[r]].astype(np.int64), 1)
+    assert np.array_equal(counts, m.ref)
+    assert sorted(m.free_list() + np.nonzero(m.ref)[0].tolist()) == list(range(m.num_blocks))
+    hc = np.zeros(m.host_blocks, np.int64)
+    for hids, _ in m.swapped.values():
+        np.add.at(hc, hids, 1)
+    assert np.array_equal(hc, m.host_ref)
+    assert sorted(m._host_free + np.nonzero(m.host_ref)[0].tolist()) == list(range(m.host_blocks))
+
+
+def test_swap_out_and_in_preserves_histories_and_sharing():
+    # histories tracked slot by slot through device and host pools
+    from oracle import cache as oc
+    r = np.random.default_rng(3)
+    B, N, NH = 4, 64, 32
+    m = BlockManager(N, B, max_rows=8, max_blocks_per_seq=N, free_order=r.permutation(N), host_blocks=NH)
+    dev = np.zeros((N, 1, B, 1), np.float64)
+    host = np.zeros((NH, 1, B, 1), np.float64)
+    hist = {}
+    counter = iter(range(1, 10_000))
+
+    def write(slots):
+        vals = [float(next(counter)) for _ in slots]
+        for s_, v_ in zip(slots, vals):
+            dev[s_ // B, 0, s_ % B, 0] = v_
+        return vals
+
+    def read(row):
+        return [dev[m.slot(row, p) // B, 0, m.slot(row, p) % B, 0] for p in range(int(m.lens[row]))]
+
+    hist[0] = write(m.add_prompt(0, 10))
+    m.fork(0, 1)
+    hist[1] = list(hist[0])
+    hist[2] = write(m.add_prompt(2, 5))
+    for _ in range(3):
+        slots, pairs = m.append_step([0, 1, 2])
+        for src, dst in pairs:
+            dev[dst] = dev[src]
+        vals = write(slots)
+        for row, v_ in zip([0, 1, 2], vals):
+            hist[row].append(v_)
+    used_before = m.used()
+    shared_before = m.blocks_saved_by_sharing()
+    pairs = m.swap_out([0, 1])
+    _consistent(m)
+    host, _ = oc.swap_blocks(dev, dev, host, host, pairs)
+    assert len(pairs) == len(set(m.swapped[0][0].tolist()) | set(m.swapped[1][0].tolist()))
+    assert m.used() < used_before
+    # the freed device blocks are reused (and overwritten) by a new sequence
+    write(m.add_prompt(3, 4 * (N - m.used() - 8)))
+    m.free(3)
+    pairs = m.swap_in([1, 0])
+    _consistent(m)
+    dev, _ = oc.swap_blocks(host, host, dev, dev, pairs)
+    for row in (0, 1, 2):
+        assert read(row) == hist[row]
+    assert m.blocks_saved_by_sharing() == shared_before
+    assert not m.swapped and m.host_ref.sum() == 0
+
+
+def test_swap_is_all_or_nothing():
+    m = BlockManager(16, 4, max_rows=4, max_blocks_per_seq=8, host_blocks=2)
+    m.add_prompt(0, 12)                       # 3 blocks, host pool holds 2
+    state = (m.tables.copy(), m.ref.copy(), list(m._host_free))
+    with pytest.raises(OutOfBlocks):
+        m.swap_out([0])
+    assert np.array_equal(m.tables, state[0]) and np.array_equal(m.ref, state[1])
+    assert m._host_free == state[2]
+    with pytest.raises(KeyError):
+        m.swap_in([0])

@@ -115,3 +115,16 @@ def test_copy_on_write_keeps_both_histories():
     for sid in (0, 1):
         expect = np.concatenate([prompt, new[sid]])
         assert np.array_equal(oc.gather_history(kp, model.table(sid), 8), expect)
+
+
+def test_swap_blocks_copies_across_pools():
+    r = np.random.default_rng(5)
+    dk, dv = _pools(r, 6, 2, 4, 8)
+    hk, hv = _pools(r, 4, 2, 4, 8)
+    pairs = [(5, 0), (1, 3)]
+    k2, v2 = oc.swap_blocks(dk, dv, hk, hv, pairs)
+    assert np.array_equal(k2[0], dk[5]) and np.array_equal(v2[3], dv[1])
+    assert np.array_equal(k2[1], hk[1]) and np.array_equal(k2[2], hk[2])
+    # and back: a round trip restores the device pool bit for bit
+    dk2, dv2 = oc.swap_blocks(k2, v2, np.zeros_like(dk), np.zeros_like(dv), [(0, 5), (3, 1)])
+    assert np.array_equal(dk2[5], dk[5]) and np.array_equal(dv2[1], dv[1])
