@@ -25,14 +25,15 @@
 // * Tiles entirely above the diagonal are never loaded; the diagonal ones are
 //   masked per element.  Workgroups are issued heaviest-first (last query tile
 //   first).
+// * Pipeline: LDS holds two key/value tiles.  After tile j is computed from
+//   one buffer, tile j+1 (loaded into registers during tile j-1) is written to
+//   the other and the global loads of tile j+2 are issued; the block-table
+//   entry of tile j+2 is read before tile j's compute, so no load waits on a
+//   table read.  One barrier per tile, ordering LDS only.
 #include <type_traits>
 
 #include "pa_device.h"
 #include "pa_internal.h"
-
-#ifndef PA_PREFILL_PIPE
-#define PA_PREFILL_PIPE 1  // 1: the next key tile's global loads overlap this tile's MFMAs
-#endif
 
 namespace pa {
 namespace {
@@ -41,6 +42,33 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// x combined with the same register of lane (l ^ 32) by a commutative op:
+// v_permlane32_swap exchanges the upper half-wave of one register with the
+// lower half-wave of another, so with both operands = x the two results hold
+// x of lanes l % 32 and 32 + l % 32.  (The result is taken by value as a
+// 2-vector: this clang mis-reads element 1 of an `auto` result.)
+__device__ __forceinline__ float halves_max(float x) {
+  const u32x2 r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                   false, false);
+  const uint32_t lo = r.x, hi = r.y;
+  return fmaxf(__builtin_bit_cast(float, lo), __builtin_bit_cast(float, hi));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const u32x2 r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                   false, false);
+  const uint32_t lo = r.x, hi = r.y;
+  return __builtin_bit_cast(float, lo) + __builtin_bit_cast(float, hi);
+}
+
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also
+// releases global memory, which makes every wave wait for its in-flight global
+// loads (the next tiles) at each barrier; the tiles need only LDS ordering.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 constexpr int kD = 128;        // head_dim
 constexpr int kBM = 128;       // queries per workgroup
@@ -104,8 +132,8 @@ struct PrefillArgs {
 template <typename E, int BS>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(PrefillArgs a) {
   static_assert(BS >= 4 && (kBN % BS == 0 || BS % kBN == 0), "block size must tile the 64-key step");
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[kBN * kKRow];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_vt[kD * kVRow];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][kBN * kKRow];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_vt[2][kD * kVRow];
 
   // XCD-aware order: workgroups are handed to the 8 XCDs round-robin, so
   // XCD x runs blocks x, x+8, ...; give each XCD a contiguous range of
@@ -166,7 +194,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
 
   // One key tile: S^T = K Q^T, online softmax, O^T += V^T P^T.  MASKED tiles
   // straddle the diagonal; scores of keys after the query become -inf.
-  auto compute_tile = [&](const int j0, auto masked_tag) {
+  auto compute_tile = [&](const int j0, const uint16_t* __restrict__ tk, const uint16_t* __restrict__ tvt,
+                          auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     f32x16 acc_s[2];
 #pragma unroll
@@ -177,7 +206,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
     for (int ks = 0; ks < 8; ++ks) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {  // two independent accumulation chains
-        const u32x4 ka = *(const u32x4*)&lds_k[(32 * mb + col) * kKRow + 16 * ks + 8 * g];
+        const u32x4 ka = *(const u32x4*)&tk[(32 * mb + col) * kKRow + 16 * ks + 8 * g];
         acc_s[mb] = mfma32(E{}, ka, qb[ks], acc_s[mb]);
       }
     }
@@ -193,7 +222,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
         }
         mt = fmaxf(mt, acc_s[mb][i]);
       }
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    mt = halves_max(mt);
     const float m_new = fmaxf(m, mt);  // raw units (scale > 0 keeps the order)
     if (__any(m_new > m)) {
       const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c);
@@ -226,7 +255,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int dm = 0; dm < 4; ++dm) {
-          const uint16_t* vrow = &lds_vt[(32 * dm + col) * kVRow + 32 * mb + 16 * t + 4 * g];
+          const uint16_t* vrow = &tvt[(32 * dm + col) * kVRow + 32 * mb + 16 * t + 4 * g];
           const u32x2 v0 = *(const u32x2*)vrow;
           const u32x2 v1 = *(const u32x2*)(vrow + 8);
           const u32x4 va = {v0.x, v0.y, v1.x, v1.y};
@@ -234,11 +263,17 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
         }
   };
 
+  // Physical block of this thread's four keys in key tile kt.  The read is
+  // unconditional (index clamped into the table row) so the compiler keeps
+  // no predicated definition of it alive across the loop; load_tile ignores
+  // the entry for keys at or past the context length.
+  auto table_entry = [&](const int kt) -> int {
+    const int blk = min((kt * kBN + 4 * kg) / BS, a.max_blocks - 1);
+    return a.tables[trow + blk];
+  };
   // Global -> register loads of one key tile (thread: 4 keys x 8 dims of K and V)
-  auto load_tile = [&](const int kt, u32x4* kr, u32x4* vr) {
+  auto load_tile = [&](const int kt, const int phys, u32x4* kr, u32x4* vr) {
     const int jk = kt * kBN + 4 * kg;  // first of this thread's 4 keys (same block: BS >= 4)
-    const int blk = jk / BS;
-    const int phys = (jk < ctx && blk < a.max_blocks) ? a.tables[trow + blk] : -1;
     const bool ok = phys >= 0 && phys < a.N;
     const int off = jk % BS;
     const int64_t base = (((int64_t)(ok ? phys : 0) * a.H + h) * BS + off) * (kD / 8) + dc;
@@ -249,10 +284,11 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
       vr[u] = valid ? a.vpool[base + u * (kD / 8)] : u32x4{0, 0, 0, 0};
     }
   };
-  // Registers -> LDS: K rows as they are, V transposed (4 keys x 8 dims -> 8 rows of V^T)
-  auto store_tile = [&](const u32x4* kr, const u32x4* vr) {
+  // Registers -> one LDS buffer: K rows as they are, V transposed (4 keys x 8
+  // dims -> 8 rows of V^T)
+  auto store_tile = [&](const int buf, const u32x4* kr, const u32x4* vr) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) *(u32x4*)&lds_k[(4 * kg + u) * kKRow + 8 * dc] = kr[u];
+    for (int u = 0; u < 4; ++u) *(u32x4*)&lds_k[buf][(4 * kg + u) * kKRow + 8 * dc] = kr[u];
     const uint32_t w0[4] = {vr[0].x, vr[0].y, vr[0].z, vr[0].w};
     const uint32_t w1[4] = {vr[1].x, vr[1].y, vr[1].z, vr[1].w};
     const uint32_t w2[4] = {vr[2].x, vr[2].y, vr[2].z, vr[2].w};
@@ -264,35 +300,45 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
       lo.y = __builtin_amdgcn_perm(w3[i], w2[i], 0x05040100u);
       hi.x = __builtin_amdgcn_perm(w1[i], w0[i], 0x07060302u);
       hi.y = __builtin_amdgcn_perm(w3[i], w2[i], 0x07060302u);
-      *(u32x2*)&lds_vt[(8 * dc + 2 * i) * kVRow + 4 * kg] = lo;
-      *(u32x2*)&lds_vt[(8 * dc + 2 * i + 1) * kVRow + 4 * kg] = hi;
+      *(u32x2*)&lds_vt[buf][(8 * dc + 2 * i) * kVRow + 4 * kg] = lo;
+      *(u32x2*)&lds_vt[buf][(8 * dc + 2 * i + 1) * kVRow + 4 * kg] = hi;
     }
   };
 
+  // prologue: tile 0 in LDS buffer 0, tile 1 in flight
   u32x4 kr[4], vr[4];
-#if PA_PREFILL_PIPE
-  load_tile(0, kr, vr);
-#endif
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int j0 = kt * kBN;
-#if !PA_PREFILL_PIPE
-    load_tile(kt, kr, vr);
-#endif
-    __syncthreads();  // the previous tile's LDS reads are done
-    store_tile(kr, vr);
-    __syncthreads();
-#if PA_PREFILL_PIPE
-    if (kt + 1 < nkt) load_tile(kt + 1, kr, vr);  // in flight while this tile computes
-#endif
-    if (kt < n_full) {
-      compute_tile(j0, std::false_type{});
-    } else if (j0 <= wave_max_pos) {  // a wave skips tiles wholly after its queries
-      compute_tile(j0, std::true_type{});
+  load_tile(0, table_entry(0), kr, vr);
+  const int phys1 = table_entry(1);
+  store_tile(0, kr, vr);
+  if (nkt > 1) load_tile(1, phys1, kr, vr);
+  lds_barrier();
+  // After tile kt: write tile kt + 1 into the other buffer (last read during
+  // tile kt - 1, before the previous barrier), start the loads of tile kt + 2.
+  auto advance = [&](const int kt, const int phys2) {
+    if (kt + 1 < nkt) {
+      store_tile((kt & 1) ^ 1, kr, vr);
+      if (kt + 2 < nkt) load_tile(kt + 2, phys2, kr, vr);
     }
+    lds_barrier();
+  };
+  // Two loops, so each has one compute path and the accumulators stay in
+  // place (a join of two inlined paths makes the compiler copy them).
+  int kt = 0;
+  for (; kt < n_full; ++kt) {
+    const int phys2 = table_entry(kt + 2);  // issued before the compute, used after it
+    compute_tile(kt * kBN, lds_k[kt & 1], lds_vt[kt & 1], std::false_type{});
+    advance(kt, phys2);
+  }
+  for (; kt < nkt; ++kt) {
+    const int phys2 = table_entry(kt + 2);
+    const int j0 = kt * kBN;
+    if (j0 <= wave_max_pos)  // a wave skips tiles wholly after its queries
+      compute_tile(j0, lds_k[kt & 1], lds_vt[kt & 1], std::true_type{});
+    advance(kt, phys2);
   }
 
   // normalise and store: result element i of block dm is dim 32dm + 8(i/4) + 4g + i%4
-  l += __shfl_xor(l, 32);
+  l = halves_sum(l);
   if (!qvalid) return;
   const float inv_l = 1.f / l;
   const int64_t obase = ((int64_t)(q_begin + qrow) * a.H + h) * kD;
