@@ -193,6 +193,7 @@ pa_status pa_paged_decode_grouped(const pa_kv_cache* cache, void* out, pa_dtype 
  *   context_lens   int32 [S]; q_len_s <= context_lens[s]; the queries are the
  *                  last q_len_s logical positions of the sequence.
  *   max_q_len, max_context_len  host-side upper bounds.
+ *   scale          score scale, finite and > 0 (PA_ERR_INVALID_ARG otherwise).
  */
 pa_status pa_paged_prefill(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, const void* query,
                            const int32_t* block_tables, int32_t max_blocks_per_seq,

@@ -260,7 +260,8 @@ pa_status pa_paged_prefill(const pa_kv_cache* cache, void* out, pa_dtype out_dty
   if (max_blocks_per_seq < 1 || (int64_t)max_blocks_per_seq * c.block_size < max_context_len)
     return fail(PA_ERR_INVALID_ARG, "%s: max_blocks_per_seq = %d cannot hold %d tokens of block %d", fn,
                 max_blocks_per_seq, max_context_len, c.block_size);
-  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "%s: scale is not finite", fn);
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(PA_ERR_INVALID_ARG, "%s: scale must be finite and > 0", fn);
   if (!pa::prefill_supported(c.dtype, c.head_dim, c.block_size))
     return fail(PA_ERR_UNSUPPORTED, "%s: (dtype %d, head_dim %d, block_size %d) not built", fn, (int)c.dtype,
                 c.head_dim, c.block_size);

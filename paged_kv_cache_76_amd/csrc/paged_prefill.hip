@@ -13,8 +13,9 @@
 //   queries 32w..32w+31.  Key/value tiles of 64 tokens are gathered from their
 //   physical blocks (16-byte loads) into LDS: keys as [token][d] rows, values
 //   transposed to [d][token] rows (registers do the 4x8 transpose with
-//   v_perm_b32), both row-padded so the MFMA operand reads do not conflict
-//   on LDS banks.
+//   v_perm_b32), both row-padded, and the value rows' key units XOR-swizzled,
+//   so neither the tile writes nor the MFMA operand reads conflict on LDS
+//   banks.
 // * Scores are formed transposed, S^T = K Q^T, with
 //   v_mfma_f32_32x32x16_{bf16,f16}: the result layout puts one query per lane
 //   column, so the online softmax of a query is in-lane except for one
@@ -71,13 +72,19 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 constexpr int kD = 128;        // head_dim
-constexpr int kBM = 128;       // queries per workgroup
 constexpr int kBN = 64;        // keys per tile
-constexpr int kWaves = 4;
 constexpr int kXcds = 8;       // accelerator complex dies of an MI355X
 constexpr int kKRow = kD + 8;  // padded LDS row of a key (elements)
 constexpr int kVRow = kBN + 4; // padded LDS row of a transposed value (elements)
 constexpr float kNegBig = -1e30f;
+constexpr float kRescaleLog2 = 8.0f;
+
+// V^T rows hold 64 keys as 16 units of four; dimension block dm (rows
+// 32dm .. 32dm+31) stores key unit u at position u ^ 4dm.  The transposing
+// tile writes (rows 8 apart across lanes) then spread over all 64 banks
+// (two lanes per bank, the minimum for 8-byte writes) instead of a quarter of
+// them, and an operand read's two halves stay 16 bytes apart.
+__device__ __forceinline__ int vt_unit(const int u, const int dm) { return u ^ (4 * dm); }
 constexpr float kLog2e = 1.44269504088896340736f;
 
 __device__ __forceinline__ f32x16 mfma32(BF16, u32x4 a, u32x4 b, f32x16 c) {
@@ -129,9 +136,16 @@ struct PrefillArgs {
   pa_dtype out_dtype;
 };
 
-template <typename E, int BS>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(PrefillArgs a) {
-  static_assert(BS >= 4 && (kBN % BS == 0 || BS % kBN == 0), "block size must tile the 64-key step");
+// One workgroup = NW waves; a wave owns QB blocks of 32 queries.  With QB = 2
+// every key/value operand read from LDS feeds two MFMAs, and the exponentials
+// of one query block overlap the MFMAs of the other.
+template <typename E, int BS, int NW, int QB>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(QB == 2 || NW == 8 ? 1 : 2))) void prefill_kernel(
+    PrefillArgs a) {
+  constexpr int kBM = NW * QB * 32;  // queries per workgroup
+  constexpr int KPT = 16 / NW;       // keys per thread in a tile load (16-byte chunk dc of each)
+  static_assert(KPT == 2 || KPT % 4 == 0, "tile loads take 2 or a multiple of 4 keys per thread");
+  static_assert(BS >= KPT && (kBN % BS == 0 || BS % kBN == 0), "block size must tile the 64-key step");
   __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][kBN * kKRow];
   __shared__ __attribute__((aligned(16))) uint16_t lds_vt[2][kD * kVRow];
 
@@ -158,59 +172,60 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int g = lane >> 5;     // half-wave
-  const int col = lane & 31;   // this lane's query column
-  const int qrow = q0 + 32 * w + col;
-  const bool qvalid = qrow < qlen;
-  const int qpos = pos0 + qrow;
-
-  // B operand of S^T = K Q^T: Q[query][16ks + 8g .. +8] for k-steps ks = 0..7
-  u32x4 qb[8];
-  {
-    const int64_t qbase = ((int64_t)(q_begin + (qvalid ? qrow : 0)) * a.H + h) * (kD / 8);
+  const int col = lane & 31;   // this lane's query column within a block
+  int qrow[QB];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qb[ks] = qvalid ? a.q[qbase + 2 * ks + g] : u32x4{0, 0, 0, 0};
+  for (int qb = 0; qb < QB; ++qb) qrow[qb] = q0 + 32 * (QB * w + qb) + col;
+
+  // B operands of S^T = K Q^T: Q[query][16ks + 8g .. +8] for k-steps ks = 0..7
+  u32x4 qop[QB][8];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const bool valid = qrow[qb] < qlen;
+    const int64_t qbase = ((int64_t)(q_begin + (valid ? qrow[qb] : 0)) * a.H + h) * (kD / 8);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qop[qb][ks] = valid ? a.q[qbase + 2 * ks + g] : u32x4{0, 0, 0, 0};
   }
 
-  f32x16 acc_o[4];
+  f32x16 acc_o[QB][4];
 #pragma unroll
-  for (int dm = 0; dm < 4; ++dm)
+  for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc_o[dm][i] = 0.f;
-  float m = kNegBig, l = 0.f;
+    for (int dm = 0; dm < 4; ++dm)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc_o[qb][dm][i] = 0.f;
+  float m[QB], l[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m[qb] = kNegBig;
+    l[qb] = 0.f;
+  }
 
   // keys needed by the workgroup: positions 0 .. pos0 + min(q0 + kBM, qlen) - 1
   const int last_pos = pos0 + min(q0 + kBM, qlen) - 1;
   const int nkt = last_pos / kBN + 1;
 
-  // cooperative tile load: thread -> keys 4*kg .. 4*kg+3, dims 8*dc .. 8*dc+7
+  // cooperative tile load: thread -> keys KPT*kg .. +KPT-1, dims 8*dc .. 8*dc+7
   const int kg = tid >> 4;
   const int dc = tid & 15;
   const int64_t trow = (int64_t)s * a.max_blocks;
 
   // tiles whose keys all precede every query of the workgroup need no mask
   const int n_full = min(nkt, (pos0 + q0 + 1) / kBN);
-  const int wave_max_pos = pos0 + min(q0 + 32 * w + 31, qlen - 1);  // last query position of this wave
+  const int wave_max_pos = pos0 + min(q0 + 32 * QB * w + 32 * QB - 1, qlen - 1);  // last query of this wave
   const float c = a.scale_log2;
+  // Lazy rescale: the running max used for the weights is only raised (and
+  // the accumulators rescaled) when some query's max grows by more than
+  // kRescaleLog2 in log2 units.  Weights are then at most 2^kRescaleLog2,
+  // and numerator and denominator share the same reference, so the result is
+  // unchanged up to rounding; after the first tiles the rescale is rare.
+  const float slack = kRescaleLog2 / c;  // in raw score units (c > 0)
 
-  // One key tile: S^T = K Q^T, online softmax, O^T += V^T P^T.  MASKED tiles
-  // straddle the diagonal; scores of keys after the query become -inf.
-  auto compute_tile = [&](const int j0, const uint16_t* __restrict__ tk, const uint16_t* __restrict__ tvt,
-                          auto masked_tag) {
+  // Softmax of one query block's scores: mask, new running max, rescale.
+  // Returns the per-lane max (raw units) in m_new.
+  auto block_max = [&](f32x16* acc_s, const int j0, const int qb, auto masked_tag) -> float {
     constexpr bool MASKED = decltype(masked_tag)::value;
-    f32x16 acc_s[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc_s[mb][i] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {  // two independent accumulation chains
-        const u32x4 ka = *(const u32x4*)&tk[(32 * mb + col) * kKRow + 16 * ks + 8 * g];
-        acc_s[mb] = mfma32(E{}, ka, qb[ks], acc_s[mb]);
-      }
-    }
-    // raw-score max; key of result element i is 32mb + 8(i/4) + 4g + i%4
+    const int qpos = pos0 + qrow[qb];
     float mt = kNegBig;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -222,20 +237,21 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
         }
         mt = fmaxf(mt, acc_s[mb][i]);
       }
-    mt = halves_max(mt);
-    const float m_new = fmaxf(m, mt);  // raw units (scale > 0 keeps the order)
-    if (__any(m_new > m)) {
-      const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c);
-      l *= alpha;
+    return fmaxf(m[qb], halves_max(mt));  // raw units (scale > 0 keeps the order)
+  };
+  auto rescale = [&](const int qb, const float m_new) {
+    const float alpha = __builtin_amdgcn_exp2f((m[qb] - m_new) * c);
+    l[qb] *= alpha;
 #pragma unroll
-      for (int dm = 0; dm < 4; ++dm)
+    for (int dm = 0; dm < 4; ++dm)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc_o[dm][i] *= alpha;
-      m = m_new;
-    }
-    const float mc = -m * c;
-    // P^T operands: k-step (mb, t) takes result elements 8t .. 8t+7 of block mb
-    u32x4 pb[2][2];
+      for (int i = 0; i < 16; ++i) acc_o[qb][dm][i] *= alpha;
+    m[qb] = m_new;
+  };
+  // P^T operands: k-step (mb, t) takes result elements 8t .. 8t+7 of block mb;
+  // the denominator sums the same rounded weights the MFMA multiplies
+  auto weights = [&](const f32x16* acc_s, const int qb, u32x4 (*pb)[2]) {
+    const float mc = -m[qb] * c;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -245,9 +261,39 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
         for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc_s[mb][8 * t + j], c, mc));
         pb[mb][t] = u32x4{pack2(E{}, p[0], p[1]), pack2(E{}, p[2], p[3]), pack2(E{}, p[4], p[5]),
                           pack2(E{}, p[6], p[7])};
-        // the denominator sums the same rounded weights the MFMA multiplies
-        l = sum_unpacked(E{}, pb[mb][t], l);
+        l[qb] = sum_unpacked(E{}, pb[mb][t], l[qb]);
       }
+  };
+
+  // One key tile: S^T = K Q^T, online softmax, O^T += V^T P^T.  MASKED tiles
+  // straddle the diagonal; scores of keys after the query become -inf.
+  auto compute_tile = [&](const int j0, const uint16_t* __restrict__ tk, const uint16_t* __restrict__ tvt,
+                          auto masked_tag) {
+    f32x16 acc_s[QB][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc_s[qb][mb][i] = 0.f;
+    u32x4 pb[QB][2][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      // key operands are re-read per query block (holding all sixteen would
+      // not fit beside two blocks' accumulators)
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          const u32x4 ka = *(const u32x4*)&tk[(32 * mb + col) * kKRow + 16 * ks + 8 * g];
+          acc_s[qb][mb] = mfma32(E{}, ka, qop[qb][ks], acc_s[qb][mb]);
+        }
+      // the previous block's weights overlap this block's MFMAs
+      if (qb > 0) weights(acc_s[qb - 1], qb - 1, pb[qb - 1]);
+      const float m_new = block_max(acc_s[qb], j0, qb, masked_tag);
+      if (__any(m_new > m[qb] + slack)) rescale(qb, m_new);
+    }
+    weights(acc_s[QB - 1], QB - 1, pb[QB - 1]);
     // O^T += V^T P^T; k-slot (g, j) of step (mb, t) is key 32mb + 16t + 8(j/4) + 4g + j%4
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
@@ -255,58 +301,74 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int dm = 0; dm < 4; ++dm) {
-          const uint16_t* vrow = &tvt[(32 * dm + col) * kVRow + 32 * mb + 16 * t + 4 * g];
+          const uint16_t* vrow = &tvt[(32 * dm + col) * kVRow + 4 * vt_unit(8 * mb + 4 * t + g, dm)];
           const u32x2 v0 = *(const u32x2*)vrow;
           const u32x2 v1 = *(const u32x2*)(vrow + 8);
           const u32x4 va = {v0.x, v0.y, v1.x, v1.y};
-          acc_o[dm] = mfma32(E{}, va, pb[mb][t], acc_o[dm]);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) acc_o[qb][dm] = mfma32(E{}, va, pb[qb][mb][t], acc_o[qb][dm]);
         }
   };
 
-  // Physical block of this thread's four keys in key tile kt.  The read is
+  // Physical block of this thread's keys in key tile kt.  The read is
   // unconditional (index clamped into the table row) so the compiler keeps
   // no predicated definition of it alive across the loop; load_tile ignores
   // the entry for keys at or past the context length.
   auto table_entry = [&](const int kt) -> int {
-    const int blk = min((kt * kBN + 4 * kg) / BS, a.max_blocks - 1);
+    const int blk = min((kt * kBN + KPT * kg) / BS, a.max_blocks - 1);
     return a.tables[trow + blk];
   };
-  // Global -> register loads of one key tile (thread: 4 keys x 8 dims of K and V)
+  // Global -> register loads of one key tile (thread: KPT keys x 8 dims of K and V)
   auto load_tile = [&](const int kt, const int phys, u32x4* kr, u32x4* vr) {
-    const int jk = kt * kBN + 4 * kg;  // first of this thread's 4 keys (same block: BS >= 4)
+    const int jk = kt * kBN + KPT * kg;  // first of this thread's keys (one block: BS >= KPT)
     const bool ok = phys >= 0 && phys < a.N;
     const int off = jk % BS;
     const int64_t base = (((int64_t)(ok ? phys : 0) * a.H + h) * BS + off) * (kD / 8) + dc;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < KPT; ++u) {
       const bool valid = ok && (jk + u < ctx);
       kr[u] = valid ? a.kpool[base + u * (kD / 8)] : u32x4{0, 0, 0, 0};
       vr[u] = valid ? a.vpool[base + u * (kD / 8)] : u32x4{0, 0, 0, 0};
     }
   };
   // Registers -> one LDS buffer: K rows as they are, V transposed (4 keys x 8
-  // dims -> 8 rows of V^T)
+  // dims -> 8 rows of V^T, per group of four keys)
   auto store_tile = [&](const int buf, const u32x4* kr, const u32x4* vr) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) *(u32x4*)&lds_k[buf][(4 * kg + u) * kKRow + 8 * dc] = kr[u];
-    const uint32_t w0[4] = {vr[0].x, vr[0].y, vr[0].z, vr[0].w};
-    const uint32_t w1[4] = {vr[1].x, vr[1].y, vr[1].z, vr[1].w};
-    const uint32_t w2[4] = {vr[2].x, vr[2].y, vr[2].z, vr[2].w};
-    const uint32_t w3[4] = {vr[3].x, vr[3].y, vr[3].z, vr[3].w};
+    for (int u = 0; u < KPT; ++u) *(u32x4*)&lds_k[buf][(KPT * kg + u) * kKRow + 8 * dc] = kr[u];
+    if constexpr (KPT == 2) {  // two keys x 8 dims -> 8 rows of V^T, 4 bytes each
+      const uint32_t w0[4] = {vr[0].x, vr[0].y, vr[0].z, vr[0].w};
+      const uint32_t w1[4] = {vr[1].x, vr[1].y, vr[1].z, vr[1].w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      u32x2 lo, hi;  // dims 8dc+2i (low halves) and 8dc+2i+1 (high halves)
-      lo.x = __builtin_amdgcn_perm(w1[i], w0[i], 0x05040100u);
-      lo.y = __builtin_amdgcn_perm(w3[i], w2[i], 0x05040100u);
-      hi.x = __builtin_amdgcn_perm(w1[i], w0[i], 0x07060302u);
-      hi.y = __builtin_amdgcn_perm(w3[i], w2[i], 0x07060302u);
-      *(u32x2*)&lds_vt[buf][(8 * dc + 2 * i) * kVRow + 4 * kg] = lo;
-      *(u32x2*)&lds_vt[buf][(8 * dc + 2 * i + 1) * kVRow + 4 * kg] = hi;
+      for (int i = 0; i < 4; ++i) {
+        const int e = 4 * vt_unit(kg >> 1, dc >> 2) + 2 * (kg & 1);  // rows 8dc.. lie in dim block dc / 4
+        *(uint32_t*)&lds_vt[buf][(8 * dc + 2 * i) * kVRow + e] = __builtin_amdgcn_perm(w1[i], w0[i], 0x05040100u);
+        *(uint32_t*)&lds_vt[buf][(8 * dc + 2 * i + 1) * kVRow + e] = __builtin_amdgcn_perm(w1[i], w0[i], 0x07060302u);
+      }
+    }
+#pragma unroll
+    for (int q4 = 0; q4 < KPT / 4; ++q4) {
+      const u32x4* v4 = vr + 4 * q4;
+      const uint32_t w0[4] = {v4[0].x, v4[0].y, v4[0].z, v4[0].w};
+      const uint32_t w1[4] = {v4[1].x, v4[1].y, v4[1].z, v4[1].w};
+      const uint32_t w2[4] = {v4[2].x, v4[2].y, v4[2].z, v4[2].w};
+      const uint32_t w3[4] = {v4[3].x, v4[3].y, v4[3].z, v4[3].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        u32x2 lo, hi;  // dims 8dc+2i (low halves) and 8dc+2i+1 (high halves)
+        lo.x = __builtin_amdgcn_perm(w1[i], w0[i], 0x05040100u);
+        lo.y = __builtin_amdgcn_perm(w3[i], w2[i], 0x05040100u);
+        hi.x = __builtin_amdgcn_perm(w1[i], w0[i], 0x07060302u);
+        hi.y = __builtin_amdgcn_perm(w3[i], w2[i], 0x07060302u);
+        const int e = 4 * vt_unit(KPT / 4 * kg + q4, dc >> 2);
+        *(u32x2*)&lds_vt[buf][(8 * dc + 2 * i) * kVRow + e] = lo;
+        *(u32x2*)&lds_vt[buf][(8 * dc + 2 * i + 1) * kVRow + e] = hi;
+      }
     }
   };
 
   // prologue: tile 0 in LDS buffer 0, tile 1 in flight
-  u32x4 kr[4], vr[4];
+  u32x4 kr[KPT], vr[KPT];
   load_tile(0, table_entry(0), kr, vr);
   const int phys1 = table_entry(1);
   store_tile(0, kr, vr);
@@ -338,26 +400,39 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2))
   }
 
   // normalise and store: result element i of block dm is dim 32dm + 8(i/4) + 4g + i%4
-  l = halves_sum(l);
-  if (!qvalid) return;
-  const float inv_l = 1.f / l;
-  const int64_t obase = ((int64_t)(q_begin + qrow) * a.H + h) * kD;
 #pragma unroll
-  for (int dm = 0; dm < 4; ++dm)
+  for (int qb = 0; qb < QB; ++qb) {
+    const float lsum = halves_sum(l[qb]);
+    if (qrow[qb] >= qlen) continue;
+    const float inv_l = 1.f / lsum;
+    const int64_t obase = ((int64_t)(q_begin + qrow[qb]) * a.H + h) * kD;
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int d = 32 * dm + 8 * r4 + 4 * g;
-      const float o0 = acc_o[dm][4 * r4] * inv_l, o1 = acc_o[dm][4 * r4 + 1] * inv_l;
-      const float o2 = acc_o[dm][4 * r4 + 2] * inv_l, o3 = acc_o[dm][4 * r4 + 3] * inv_l;
-      if (a.out_dtype == PA_F32) {
-        float4 v = {o0, o1, o2, o3};
-        *(float4*)((float*)a.out + obase + d) = v;
-      } else if (a.out_dtype == E::id) {
-        u32x2 v = {pack2(E{}, o0, o1), pack2(E{}, o2, o3)};
-        *(u32x2*)((uint16_t*)a.out + obase + d) = v;
+    for (int dm = 0; dm < 4; ++dm)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d = 32 * dm + 8 * r4 + 4 * g;
+        const float o0 = acc_o[qb][dm][4 * r4] * inv_l, o1 = acc_o[qb][dm][4 * r4 + 1] * inv_l;
+        const float o2 = acc_o[qb][dm][4 * r4 + 2] * inv_l, o3 = acc_o[qb][dm][4 * r4 + 3] * inv_l;
+        if (a.out_dtype == PA_F32) {
+          float4 v = {o0, o1, o2, o3};
+          *(float4*)((float*)a.out + obase + d) = v;
+        } else if (a.out_dtype == E::id) {
+          u32x2 v = {pack2(E{}, o0, o1), pack2(E{}, o2, o3)};
+          *(u32x2*)((uint16_t*)a.out + obase + d) = v;
+        }
       }
-    }
+  }
 }
+
+#ifndef PA_PREFILL_NW
+#define PA_PREFILL_NW 4  // waves per workgroup
+#endif
+#ifndef PA_PREFILL_QB
+#define PA_PREFILL_QB 1  // 32-query blocks per wave
+#endif
+constexpr int kNW = PA_PREFILL_NW;
+constexpr int kQB = PA_PREFILL_QB;
+constexpr int kTileQ = kNW * kQB * 32;  // queries per workgroup
 
 struct Variant {
   pa_dtype dtype;
@@ -365,8 +440,10 @@ struct Variant {
   void (*kernel)(PrefillArgs);
 };
 
-#define PA_PREFILL_VARIANTS(BS) \
-  Variant{PA_BF16, BS, prefill_kernel<BF16, BS>}, Variant { PA_F16, BS, prefill_kernel<F16, BS> }
+#define PA_PREFILL_VARIANTS(BS)                                    \
+  Variant{PA_BF16, BS, prefill_kernel<BF16, BS, kNW, kQB>}, Variant { \
+    PA_F16, BS, prefill_kernel<F16, BS, kNW, kQB>                     \
+  }
 
 const Variant kVariants[] = {PA_PREFILL_VARIANTS(16), PA_PREFILL_VARIANTS(32), PA_PREFILL_VARIANTS(64),
                              PA_PREFILL_VARIANTS(128)};
@@ -404,11 +481,11 @@ hipError_t launch_paged_prefill(const Cache& c, void* out, pa_dtype out_dtype, c
   a.H = c.num_heads;
   a.N = c.num_blocks;
   a.max_blocks = max_blocks_per_seq;
-  a.ntiles = (max_q_len + kBM - 1) / kBM;
+  a.ntiles = (max_q_len + kTileQ - 1) / kTileQ;
   a.scale_log2 = scale * kLog2e;
   a.out_dtype = out_dtype;
   const int64_t grid = (int64_t)a.ntiles * S * c.num_heads;
-  hipLaunchKernelGGL(v->kernel, dim3((unsigned)grid), dim3(kWaves * 64), 0, stream, a);
+  hipLaunchKernelGGL(v->kernel, dim3((unsigned)grid), dim3(kNW * 64), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -134,3 +134,25 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(RuntimeError, match="no non-HIP fallback"):
         L.lib()
+
+
+def test_prefill_argument_checks():
+    lib = L.lib()
+    d = _desc(dtype=L.PA_BF16)
+
+    def call(out_dtype=L.PA_BF16, maxb=8, S=2, maxq=64, maxctx=100, scale=0.1):
+        return lib.pa_paged_prefill(ctypes.byref(d), FAKE, out_dtype, FAKE, FAKE, maxb, FAKE, FAKE, S, maxq, maxctx,
+                                    scale, None)
+
+    _err(call(S=-1), "< 0")
+    _err(call(out_dtype=L.PA_F16), "out_dtype")
+    _err(call(maxq=0), "max_q_len")
+    _err(call(maxq=101), "max_q_len")
+    _err(call(maxb=2), "cannot hold")
+    # the causal kernel orders raw scores by value, which needs a positive scale
+    _err(call(scale=float("nan")), "scale")
+    _err(call(scale=0.0), "> 0")
+    _err(call(scale=-0.1), "> 0")
+    d2 = _desc(dtype=L.PA_BF16, head_dim=64)
+    assert lib.pa_paged_prefill(ctypes.byref(d2), FAKE, L.PA_BF16, FAKE, FAKE, 8, FAKE, FAKE, 2, 64, 100, 0.1,
+                                None) == L.PA_ERR_UNSUPPORTED
