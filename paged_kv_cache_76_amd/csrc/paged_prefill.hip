@@ -10,27 +10,27 @@
 //
 // gfx950 design (a dense contraction, so MFMA; 128 queries x 64 keys tiles):
 // * Workgroup = 4 wave64s = 128 queries of one (sequence, head); wave w owns
-//   queries 32w..32w+31.  Key/value tiles of 64 tokens are gathered from their
-//   physical blocks (16-byte loads) into LDS: keys as [token][d] rows, values
-//   transposed to [d][token] rows (registers do the 4x8 transpose with
-//   v_perm_b32), both row-padded, and the value rows' key units XOR-swizzled,
-//   so neither the tile writes nor the MFMA operand reads conflict on LDS
-//   banks.
+//   queries 32w..32w+31.  Key and value tiles of 64 tokens go from their
+//   physical blocks straight into LDS (global_load_lds_dwordx4: no registers,
+//   no LDS write instructions), both as [token][d] rows of 256 bytes whose
+//   16-byte chunks are XOR-swizzled by token so the operand reads below do
+//   not conflict on LDS banks.
 // * Scores are formed transposed, S^T = K Q^T, with
 //   v_mfma_f32_32x32x16_{bf16,f16}: the result layout puts one query per lane
 //   column, so the online softmax of a query is in-lane except for one
 //   exchange between the two half-waves.
 // * O^T += V^T P^T with the same MFMA: the B operand P^T for a 16-key step is
 //   exactly 8 of the lane's own score registers (rounded to 16 bits), so P
-//   never leaves the registers; the A operand is two 8-byte LDS reads of V^T.
+//   never leaves the registers; the A operand V^T is read from the [token][d]
+//   tile with two transposing LDS reads (ds_read_b64_tr_b16).
 // * Tiles entirely above the diagonal are never loaded; the diagonal ones are
 //   masked per element.  Workgroups are issued heaviest-first (last query tile
-//   first).
-// * Pipeline: LDS holds two key/value tiles.  After tile j is computed from
-//   one buffer, tile j+1 (loaded into registers during tile j-1) is written to
-//   the other and the global loads of tile j+2 are issued; the block-table
-//   entry of tile j+2 is read before tile j's compute, so no load waits on a
-//   table read.  One barrier per tile, ordering LDS only.
+//   first), XCD-aware.
+// * Pipeline: LDS holds two key/value tiles.  While tile j is computed from
+//   one buffer, the loads of tile j+1 (issued after tile j-1) fill the other;
+//   each wave then waits for its own loads, one barrier per tile publishes
+//   them, and the loads of tile j+2 go into the buffer just released.  The
+//   block-table entries of tile j+2 are read before tile j's compute.
 #include <type_traits>
 
 #include "pa_device.h"
@@ -43,6 +43,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
 // x combined with the same register of lane (l ^ 32) by a commutative op:
 // v_permlane32_swap exchanges the upper half-wave of one register with the
@@ -63,29 +66,46 @@ __device__ __forceinline__ float halves_sum(float x) {
 }
 
 // Workgroup barrier that orders LDS accesses only.  __syncthreads() also
-// releases global memory, which makes every wave wait for its in-flight global
-// loads (the next tiles) at each barrier; the tiles need only LDS ordering.
+// releases global memory, which makes every wave wait for all its in-flight
+// global loads at each barrier; the waits this kernel needs are explicit.
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
+// s_waitcnt vmcnt(0) only: this wave's global loads (including those that
+// write LDS directly) have completed
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x3f70); }
+// 16 bytes per lane from global memory straight into LDS at lds_base + 16 *
+// lane (global_load_lds_dwordx4; lds_base is wave-uniform and goes to M0,
+// which nothing else in this kernel uses; one wait state after the M0 write).
+// Issued as inline assembly so the compiler does not hold every later LDS
+// read back until these loads complete: the kernel orders them itself
+// (wait_vmem, then a barrier, before any wave reads the buffer).
+__device__ __forceinline__ void load_to_lds(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base)
+               : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_void_t*)p;
+}
 
-constexpr int kD = 128;        // head_dim
-constexpr int kBN = 64;        // keys per tile
-constexpr int kXcds = 8;       // accelerator complex dies of an MI355X
-constexpr int kKRow = kD + 8;  // padded LDS row of a key (elements)
-constexpr int kVRow = kBN + 4; // padded LDS row of a transposed value (elements)
+constexpr int kD = 128;         // head_dim
+constexpr int kBN = 64;         // keys per tile
+constexpr int kRowBytes = kD * 2;
+constexpr int kTileBytes = kBN * kRowBytes;  // 16 KiB per K or V tile
+constexpr int kXcds = 8;        // accelerator complex dies of an MI355X
 constexpr float kNegBig = -1e30f;
 constexpr float kRescaleLog2 = 8.0f;
-
-// V^T rows hold 64 keys as 16 units of four; dimension block dm (rows
-// 32dm .. 32dm+31) stores key unit u at position u ^ 4dm.  The transposing
-// tile writes (rows 8 apart across lanes) then spread over all 64 banks
-// (two lanes per bank, the minimum for 8-byte writes) instead of a quarter of
-// them, and an operand read's two halves stay 16 bytes apart.
-__device__ __forceinline__ int vt_unit(const int u, const int dm) { return u ^ (4 * dm); }
 constexpr float kLog2e = 1.44269504088896340736f;
+
+// 16-byte chunk c of token row t is stored at chunk position c ^ swz(t).
+// Keys: the QK operand read takes one chunk of 16 consecutive tokens per
+// group of lanes, so 16 distinct positions cover all banks.  Values: a
+// transposing read takes two adjacent chunks of four consecutive tokens per
+// 16 lanes; positions 4(t % 4) apart keep 32 lanes conflict-free.
+__device__ __forceinline__ int k_swz(const int t) { return t & 15; }
+__device__ __forceinline__ int v_swz(const int t) { return 4 * (t & 3); }
 
 __device__ __forceinline__ f32x16 mfma32(BF16, u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
@@ -131,23 +151,20 @@ struct PrefillArgs {
   const int32_t* cu_q;
   const int32_t* lens;
   void* out;
-  int32_t S, H, N, max_blocks, ntiles;  // ntiles = ceil(max_q_len / kBM)
+  int32_t S, H, N, max_blocks, ntiles;  // ntiles = ceil(max_q_len / queries per workgroup)
   float scale_log2;
   pa_dtype out_dtype;
 };
 
-// One workgroup = NW waves; a wave owns QB blocks of 32 queries.  With QB = 2
-// every key/value operand read from LDS feeds two MFMAs, and the exponentials
-// of one query block overlap the MFMAs of the other.
+// One workgroup = NW waves; a wave owns QB blocks of 32 queries.
 template <typename E, int BS, int NW, int QB>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(QB == 2 || NW == 8 ? 1 : 2))) void prefill_kernel(
     PrefillArgs a) {
   constexpr int kBM = NW * QB * 32;  // queries per workgroup
-  constexpr int KPT = 16 / NW;       // keys per thread in a tile load (16-byte chunk dc of each)
-  static_assert(KPT == 2 || KPT % 4 == 0, "tile loads take 2 or a multiple of 4 keys per thread");
-  static_assert(BS >= KPT && (kBN % BS == 0 || BS % kBN == 0), "block size must tile the 64-key step");
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][kBN * kKRow];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_vt[2][kD * kVRow];
+  constexpr int KPW = kBN / NW;      // tile keys each wave loads, four per load instruction
+  static_assert(KPW % 4 == 0 && BS >= 4 && (kBN % BS == 0 || BS % kBN == 0), "block size must tile the 64-key step");
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v[2][kTileBytes];
 
   // XCD-aware order: workgroups are handed to the 8 XCDs round-robin, so
   // XCD x runs blocks x, x+8, ...; give each XCD a contiguous range of
@@ -170,7 +187,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(QB == 2
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5;     // half-wave
   const int col = lane & 31;   // this lane's query column within a block
   int qrow[QB];
@@ -204,10 +221,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(QB == 2
   // keys needed by the workgroup: positions 0 .. pos0 + min(q0 + kBM, qlen) - 1
   const int last_pos = pos0 + min(q0 + kBM, qlen) - 1;
   const int nkt = last_pos / kBN + 1;
-
-  // cooperative tile load: thread -> keys KPT*kg .. +KPT-1, dims 8*dc .. 8*dc+7
-  const int kg = tid >> 4;
-  const int dc = tid & 15;
   const int64_t trow = (int64_t)s * a.max_blocks;
 
   // tiles whose keys all precede every query of the workgroup need no mask
@@ -221,8 +234,44 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(QB == 2
   // unchanged up to rounding; after the first tiles the rescale is rare.
   const float slack = kRescaleLog2 / c;  // in raw score units (c > 0)
 
-  // Softmax of one query block's scores: mask, new running max, rescale.
-  // Returns the per-lane max (raw units) in m_new.
+  // ---- tile loads: wave w brings keys KPW*w .. KPW*w + KPW-1 of a tile, four
+  // tokens (1 KiB) per instruction per pool; lane -> token 4i + lane/16,
+  // chunk position lane % 16.  Tokens at or past the context length load the
+  // last token instead: finite data, whose scores the causal mask removes
+  // and whose weights are then exactly zero.
+  constexpr int NI = KPW / 4;                // load instructions per pool per wave
+  constexpr int NE = BS >= KPW ? 1 : NI;     // distinct blocks among them
+  auto clamp_phys = [&](const int e) { return (e >= 0 && e < a.N) ? e : 0; };
+  // Block-table entries of the wave's tokens in tile kt (read unconditionally
+  // at a clamped index, so the read can be issued a tile ahead).
+  auto entries = [&](const int kt, int* ent) {
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+      const int blk = min((kt * kBN + KPW * w + 4 * i) / BS, a.max_blocks - 1);
+      ent[i] = a.tables[trow + blk];
+    }
+  };
+  const int last_row_phys = clamp_phys(a.tables[trow + min((ctx - 1) / BS, a.max_blocks - 1)]);
+  const int64_t last_row = ((int64_t)last_row_phys * a.H + h) * BS + (ctx - 1) % BS;
+  const int tok_in_inst = lane >> 4;
+  const int chunk_pos = lane & 15;
+  auto issue_tile = [&](const int kt, const int buf, const int* ent) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int t0 = KPW * w + 4 * i;  // first tile token of this instruction (wave-uniform)
+      const int phys = clamp_phys(__builtin_amdgcn_readfirstlane(ent[NE == 1 ? 0 : i]));
+      const int t = t0 + tok_in_inst;
+      const int jk = kt * kBN + t;
+      const int64_t own = ((int64_t)phys * a.H + h) * BS + jk % BS;
+      const int64_t row = jk < ctx ? own : last_row;
+      const u32x4* kg = a.kpool + row * (kD / 8) + (chunk_pos ^ k_swz(t));
+      const u32x4* vg = a.vpool + row * (kD / 8) + (chunk_pos ^ v_swz(t));
+      load_to_lds(kg, lds_addr(&lds_k[buf][t0 * kRowBytes]));
+      load_to_lds(vg, lds_addr(&lds_v[buf][t0 * kRowBytes]));
+    }
+  };
+
+  // Softmax of one query block's scores: mask, new running max.
   auto block_max = [&](f32x16* acc_s, const int j0, const int qb, auto masked_tag) -> float {
     constexpr bool MASKED = decltype(masked_tag)::value;
     const int qpos = pos0 + qrow[qb];
@@ -267,7 +316,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(QB == 2
 
   // One key tile: S^T = K Q^T, online softmax, O^T += V^T P^T.  MASKED tiles
   // straddle the diagonal; scores of keys after the query become -inf.
-  auto compute_tile = [&](const int j0, const uint16_t* __restrict__ tk, const uint16_t* __restrict__ tvt,
+  auto compute_tile = [&](const int j0, const uint8_t* __restrict__ tk, const uint8_t* __restrict__ tv,
                           auto masked_tag) {
     f32x16 acc_s[QB][2];
 #pragma unroll
@@ -279,13 +328,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(QB == 2
     u32x4 pb[QB][2][2];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      // key operands are re-read per query block (holding all sixteen would
-      // not fit beside two blocks' accumulators)
+      // key operand: token 32mb + col, dims 16ks + 8g .. +8 (chunk 2ks + g)
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
-          const u32x4 ka = *(const u32x4*)&tk[(32 * mb + col) * kKRow + 16 * ks + 8 * g];
+          const int t = 32 * mb + col;
+          const u32x4 ka = *(const u32x4*)&tk[t * kRowBytes + 16 * ((2 * ks + g) ^ k_swz(t))];
           acc_s[qb][mb] = mfma32(E{}, ka, qop[qb][ks], acc_s[qb][mb]);
         }
       // the previous block's weights overlap this block's MFMAs
@@ -294,109 +343,67 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(QB == 2
       if (__any(m_new > m[qb] + slack)) rescale(qb, m_new);
     }
     weights(acc_s[QB - 1], QB - 1, pb[QB - 1]);
-    // O^T += V^T P^T; k-slot (g, j) of step (mb, t) is key 32mb + 16t + 8(j/4) + 4g + j%4
+    // O^T += V^T P^T; k-slot (g, j) of step (mb, t) is key 32mb + 16t + 8(j/4) + 4g + j%4.
+    // Transposing read: in each 16-lane group, lane r points at 4 dims of
+    // token k0 + r/4 and receives the 4 tokens k0 .. k0+3 of one dim.
+    const int grp = lane >> 4, r = lane & 15;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int dm = 0; dm < 4; ++dm) {
-          const uint16_t* vrow = &tvt[(32 * dm + col) * kVRow + 4 * vt_unit(8 * mb + 4 * t + g, dm)];
-          const u32x2 v0 = *(const u32x2*)vrow;
-          const u32x2 v1 = *(const u32x2*)(vrow + 8);
-          const u32x4 va = {v0.x, v0.y, v1.x, v1.y};
+          const int d = 32 * dm + 16 * (grp & 1) + 4 * (r & 3);
+          uint32_t va[4];
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) acc_o[qb][dm] = mfma32(E{}, va, pb[qb][mb][t], acc_o[qb][dm]);
+          for (int half = 0; half < 2; ++half) {
+            const int tok = 32 * mb + 16 * t + 8 * half + 4 * (grp >> 1) + (r >> 2);
+            const uint8_t* pv = &tv[tok * kRowBytes + 16 * ((d >> 3) ^ v_swz(tok)) + 2 * (d & 7)];
+            const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)pv);
+            const u32x2 xw = __builtin_bit_cast(u32x2, x);
+            va[2 * half] = xw.x;
+            va[2 * half + 1] = xw.y;
+          }
+          const u32x4 vop = {va[0], va[1], va[2], va[3]};
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) acc_o[qb][dm] = mfma32(E{}, vop, pb[qb][mb][t], acc_o[qb][dm]);
         }
   };
 
-  // Physical block of this thread's keys in key tile kt.  The read is
-  // unconditional (index clamped into the table row) so the compiler keeps
-  // no predicated definition of it alive across the loop; load_tile ignores
-  // the entry for keys at or past the context length.
-  auto table_entry = [&](const int kt) -> int {
-    const int blk = min((kt * kBN + KPT * kg) / BS, a.max_blocks - 1);
-    return a.tables[trow + blk];
-  };
-  // Global -> register loads of one key tile (thread: KPT keys x 8 dims of K and V)
-  auto load_tile = [&](const int kt, const int phys, u32x4* kr, u32x4* vr) {
-    const int jk = kt * kBN + KPT * kg;  // first of this thread's keys (one block: BS >= KPT)
-    const bool ok = phys >= 0 && phys < a.N;
-    const int off = jk % BS;
-    const int64_t base = (((int64_t)(ok ? phys : 0) * a.H + h) * BS + off) * (kD / 8) + dc;
-#pragma unroll
-    for (int u = 0; u < KPT; ++u) {
-      const bool valid = ok && (jk + u < ctx);
-      kr[u] = valid ? a.kpool[base + u * (kD / 8)] : u32x4{0, 0, 0, 0};
-      vr[u] = valid ? a.vpool[base + u * (kD / 8)] : u32x4{0, 0, 0, 0};
+  // prologue: tiles 0 and 1 in buffers 0 and 1
+  {
+    int ent[NE];
+    entries(0, ent);
+    issue_tile(0, 0, ent);
+    if (nkt > 1) {
+      entries(1, ent);
+      issue_tile(1, 1, ent);
     }
-  };
-  // Registers -> one LDS buffer: K rows as they are, V transposed (4 keys x 8
-  // dims -> 8 rows of V^T, per group of four keys)
-  auto store_tile = [&](const int buf, const u32x4* kr, const u32x4* vr) {
-#pragma unroll
-    for (int u = 0; u < KPT; ++u) *(u32x4*)&lds_k[buf][(KPT * kg + u) * kKRow + 8 * dc] = kr[u];
-    if constexpr (KPT == 2) {  // two keys x 8 dims -> 8 rows of V^T, 4 bytes each
-      const uint32_t w0[4] = {vr[0].x, vr[0].y, vr[0].z, vr[0].w};
-      const uint32_t w1[4] = {vr[1].x, vr[1].y, vr[1].z, vr[1].w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = 4 * vt_unit(kg >> 1, dc >> 2) + 2 * (kg & 1);  // rows 8dc.. lie in dim block dc / 4
-        *(uint32_t*)&lds_vt[buf][(8 * dc + 2 * i) * kVRow + e] = __builtin_amdgcn_perm(w1[i], w0[i], 0x05040100u);
-        *(uint32_t*)&lds_vt[buf][(8 * dc + 2 * i + 1) * kVRow + e] = __builtin_amdgcn_perm(w1[i], w0[i], 0x07060302u);
-      }
-    }
-#pragma unroll
-    for (int q4 = 0; q4 < KPT / 4; ++q4) {
-      const u32x4* v4 = vr + 4 * q4;
-      const uint32_t w0[4] = {v4[0].x, v4[0].y, v4[0].z, v4[0].w};
-      const uint32_t w1[4] = {v4[1].x, v4[1].y, v4[1].z, v4[1].w};
-      const uint32_t w2[4] = {v4[2].x, v4[2].y, v4[2].z, v4[2].w};
-      const uint32_t w3[4] = {v4[3].x, v4[3].y, v4[3].z, v4[3].w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        u32x2 lo, hi;  // dims 8dc+2i (low halves) and 8dc+2i+1 (high halves)
-        lo.x = __builtin_amdgcn_perm(w1[i], w0[i], 0x05040100u);
-        lo.y = __builtin_amdgcn_perm(w3[i], w2[i], 0x05040100u);
-        hi.x = __builtin_amdgcn_perm(w1[i], w0[i], 0x07060302u);
-        hi.y = __builtin_amdgcn_perm(w3[i], w2[i], 0x07060302u);
-        const int e = 4 * vt_unit(KPT / 4 * kg + q4, dc >> 2);
-        *(u32x2*)&lds_vt[buf][(8 * dc + 2 * i) * kVRow + e] = lo;
-        *(u32x2*)&lds_vt[buf][(8 * dc + 2 * i + 1) * kVRow + e] = hi;
-      }
-    }
-  };
-
-  // prologue: tile 0 in LDS buffer 0, tile 1 in flight
-  u32x4 kr[KPT], vr[KPT];
-  load_tile(0, table_entry(0), kr, vr);
-  const int phys1 = table_entry(1);
-  store_tile(0, kr, vr);
-  if (nkt > 1) load_tile(1, phys1, kr, vr);
-  lds_barrier();
-  // After tile kt: write tile kt + 1 into the other buffer (last read during
-  // tile kt - 1, before the previous barrier), start the loads of tile kt + 2.
-  auto advance = [&](const int kt, const int phys2) {
-    if (kt + 1 < nkt) {
-      store_tile((kt & 1) ^ 1, kr, vr);
-      if (kt + 2 < nkt) load_tile(kt + 2, phys2, kr, vr);
-    }
+    wait_vmem();
     lds_barrier();
-  };
-  // Two loops, so each has one compute path and the accumulators stay in
-  // place (a join of two inlined paths makes the compiler copy them).
+  }
+  // Tile kt: read the table entries of tile kt + 2, compute tile kt, wait for
+  // this wave's loads of tile kt + 1, barrier, then load tile kt + 2 into the
+  // buffer every wave has just finished with.  Two loops, so each has one
+  // compute path and the accumulators stay in place.
   int kt = 0;
   for (; kt < n_full; ++kt) {
-    const int phys2 = table_entry(kt + 2);  // issued before the compute, used after it
-    compute_tile(kt * kBN, lds_k[kt & 1], lds_vt[kt & 1], std::false_type{});
-    advance(kt, phys2);
+    int ent[NE];
+    entries(kt + 2, ent);
+    compute_tile(kt * kBN, lds_k[kt & 1], lds_v[kt & 1], std::false_type{});
+    wait_vmem();
+    lds_barrier();
+    if (kt + 2 < nkt) issue_tile(kt + 2, kt & 1, ent);
   }
   for (; kt < nkt; ++kt) {
-    const int phys2 = table_entry(kt + 2);
+    int ent[NE];
+    entries(kt + 2, ent);
     const int j0 = kt * kBN;
     if (j0 <= wave_max_pos)  // a wave skips tiles wholly after its queries
-      compute_tile(j0, lds_k[kt & 1], lds_vt[kt & 1], std::true_type{});
-    advance(kt, phys2);
+      compute_tile(j0, lds_k[kt & 1], lds_v[kt & 1], std::true_type{});
+    wait_vmem();
+    lds_barrier();
+    if (kt + 2 < nkt) issue_tile(kt + 2, kt & 1, ent);
   }
 
   // normalise and store: result element i of block dm is dim 32dm + 8(i/4) + 4g + i%4
