@@ -26,11 +26,13 @@
 // * Tiles entirely above the diagonal are never loaded; the diagonal ones are
 //   masked per element.  Workgroups are issued heaviest-first (last query tile
 //   first), XCD-aware.
-// * Pipeline: LDS holds two key/value tiles.  While tile j is computed from
-//   one buffer, the loads of tile j+1 (issued after tile j-1) fill the other;
-//   each wave then waits for its own loads, one barrier per tile publishes
-//   them, and the loads of tile j+2 go into the buffer just released.  The
-//   block-table entries of tile j+2 are read before tile j's compute.
+// * Software pipeline: keys run one tile ahead of values, so the MFMAs of
+//   S(j+1) = K(j+1) Q^T are in flight while the exponentials of S(j) are
+//   computed, and P(j) V(j) follows.  LDS holds two key and two value tiles;
+//   the loads of K(j+2) and V(j+1) are issued at the start of step j into the
+//   buffers the previous barrier released, each wave waits for its own loads
+//   at the end of the step, and one barrier per step publishes them.  The
+//   block-table entries the workgroup needs are copied to LDS once.
 #include <type_traits>
 
 #include "pa_device.h"
@@ -156,15 +158,18 @@ struct PrefillArgs {
   pa_dtype out_dtype;
 };
 
-// One workgroup = NW waves; a wave owns QB blocks of 32 queries.
-template <typename E, int BS, int NW, int QB>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(QB == 2 || NW == 8 ? 1 : 2))) void prefill_kernel(
+constexpr int kTabCache = 2048;  // block-table entries a workgroup keeps in LDS
+
+// One workgroup = NW waves of 32 queries each.
+template <typename E, int BS, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(
     PrefillArgs a) {
-  constexpr int kBM = NW * QB * 32;  // queries per workgroup
-  constexpr int KPW = kBN / NW;      // tile keys each wave loads, four per load instruction
+  constexpr int kBM = NW * 32;   // queries per workgroup
+  constexpr int KPW = kBN / NW;  // tile keys each wave loads, four per load instruction
   static_assert(KPW % 4 == 0 && BS >= 4 && (kBN % BS == 0 || BS % kBN == 0), "block size must tile the 64-key step");
   __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t lds_v[2][kTileBytes];
+  __shared__ int32_t lds_tab[kTabCache];
 
   // XCD-aware order: workgroups are handed to the 8 XCDs round-robin, so
   // XCD x runs blocks x, x+8, ...; give each XCD a contiguous range of
@@ -189,34 +194,28 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(QB == 2
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5;     // half-wave
-  const int col = lane & 31;   // this lane's query column within a block
-  int qrow[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) qrow[qb] = q0 + 32 * (QB * w + qb) + col;
+  const int col = lane & 31;   // this lane's query column
+  const int qrow = q0 + 32 * w + col;
+  const int qpos = pos0 + qrow;
 
   // B operands of S^T = K Q^T: Q[query][16ks + 8g .. +8] for k-steps ks = 0..7
-  u32x4 qop[QB][8];
+  u32x4 qop[8];
+  {
+    const bool valid = qrow < qlen;
+    const int64_t qbase = ((int64_t)(q_begin + (valid ? qrow : 0)) * a.H + h) * (kD / 8);
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const bool valid = qrow[qb] < qlen;
-    const int64_t qbase = ((int64_t)(q_begin + (valid ? qrow[qb] : 0)) * a.H + h) * (kD / 8);
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qop[qb][ks] = valid ? a.q[qbase + 2 * ks + g] : u32x4{0, 0, 0, 0};
+    for (int ks = 0; ks < 8; ++ks) qop[ks] = valid ? a.q[qbase + 2 * ks + g] : u32x4{0, 0, 0, 0};
   }
 
-  f32x16 acc_o[QB][4];
+  f32x16 acc_o[4];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
+  for (int dm = 0; dm < 4; ++dm)
 #pragma unroll
-    for (int dm = 0; dm < 4; ++dm)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc_o[qb][dm][i] = 0.f;
-  float m[QB], l[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m[qb] = kNegBig;
-    l[qb] = 0.f;
-  }
+    for (int i = 0; i < 16; ++i) acc_o[dm][i] = 0.f;
+  // running max (raw units) and the denominator as four partial sums, so the
+  // per-tile additions form four short dependency chains instead of one
+  float m = kNegBig;
+  float lp[4] = {0.f, 0.f, 0.f, 0.f};
 
   // keys needed by the workgroup: positions 0 .. pos0 + min(q0 + kBM, qlen) - 1
   const int last_pos = pos0 + min(q0 + kBM, qlen) - 1;
@@ -225,7 +224,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(QB == 2
 
   // tiles whose keys all precede every query of the workgroup need no mask
   const int n_full = min(nkt, (pos0 + q0 + 1) / kBN);
-  const int wave_max_pos = pos0 + min(q0 + 32 * QB * w + 32 * QB - 1, qlen - 1);  // last query of this wave
+  const int wave_max_pos = pos0 + min(q0 + 32 * w + 31, qlen - 1);  // last query of this wave
+  const int wave_tiles = min(nkt, wave_max_pos / kBN + 1);         // tiles with keys this wave needs
   const float c = a.scale_log2;
   // Lazy rescale: the running max used for the weights is only raised (and
   // the accumulators rescaled) when some query's max grows by more than
@@ -234,48 +234,69 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(QB == 2
   // unchanged up to rounding; after the first tiles the rescale is rare.
   const float slack = kRescaleLog2 / c;  // in raw score units (c > 0)
 
-  // ---- tile loads: wave w brings keys KPW*w .. KPW*w + KPW-1 of a tile, four
-  // tokens (1 KiB) per instruction per pool; lane -> token 4i + lane/16,
-  // chunk position lane % 16.  Tokens at or past the context length load the
-  // last token instead: finite data, whose scores the causal mask removes
-  // and whose weights are then exactly zero.
-  constexpr int NI = KPW / 4;                // load instructions per pool per wave
-  constexpr int NE = BS >= KPW ? 1 : NI;     // distinct blocks among them
+  // ---- block table: the entries of the tokens the tiles cover (up to
+  // kTabCache of them) are copied to LDS once; entries are clamped into the
+  // pool.  Entries past those are never used for a load (tokens at or past
+  // the context length are redirected below).
   auto clamp_phys = [&](const int e) { return (e >= 0 && e < a.N) ? e : 0; };
-  // Block-table entries of the wave's tokens in tile kt (read unconditionally
-  // at a clamped index, so the read can be issued a tile ahead).
-  auto entries = [&](const int kt, int* ent) {
-#pragma unroll
-    for (int i = 0; i < NE; ++i) {
-      const int blk = min((kt * kBN + KPW * w + 4 * i) / BS, a.max_blocks - 1);
-      ent[i] = a.tables[trow + blk];
-    }
+  const int n_tab = min(min(nkt * kBN, ctx) - 1, (a.max_blocks - 1) * BS) / BS + 1;
+  for (int i = tid; i < min(n_tab, kTabCache); i += NW * 64) lds_tab[i] = clamp_phys(a.tables[trow + i]);
+  lds_barrier();
+  auto entry = [&](const int blk) -> int {
+    const int b = min(blk, a.max_blocks - 1);
+    return b < kTabCache ? lds_tab[b] : clamp_phys(a.tables[trow + b]);
   };
-  const int last_row_phys = clamp_phys(a.tables[trow + min((ctx - 1) / BS, a.max_blocks - 1)]);
-  const int64_t last_row = ((int64_t)last_row_phys * a.H + h) * BS + (ctx - 1) % BS;
+  const int64_t last_row = ((int64_t)clamp_phys(a.tables[trow + min((ctx - 1) / BS, a.max_blocks - 1)]) * a.H + h) *
+                               BS + (ctx - 1) % BS;
+
+  // ---- tile loads: wave w brings tokens KPW*w .. KPW*w + KPW-1 of a tile,
+  // four (1 KiB) per instruction; lane -> token 4i + lane/16, chunk position
+  // lane % 16.  Tokens at or past the context length load the last token
+  // instead: finite data, whose scores the causal mask removes and whose
+  // weights are then exactly zero.
   const int tok_in_inst = lane >> 4;
   const int chunk_pos = lane & 15;
-  auto issue_tile = [&](const int kt, const int buf, const int* ent) {
+  // physical blocks of this wave's tokens in tile kt (one per four tokens;
+  // a single one when a block holds all of them)
+  constexpr int NI = KPW / 4;
+  constexpr int NE = BS >= KPW ? 1 : NI;
+  auto entries = [&](const int kt, int* ent) {
+#pragma unroll
+    for (int i = 0; i < NE; ++i) ent[i] = __builtin_amdgcn_readfirstlane(entry((kt * kBN + KPW * w + 4 * i) / BS));
+  };
+  auto issue = [&](const u32x4* pool, uint8_t* dst, const int kt, const int* ent, const bool is_v) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int t0 = KPW * w + 4 * i;  // first tile token of this instruction (wave-uniform)
-      const int phys = clamp_phys(__builtin_amdgcn_readfirstlane(ent[NE == 1 ? 0 : i]));
+      const int phys = ent[NE == 1 ? 0 : i];
       const int t = t0 + tok_in_inst;
       const int jk = kt * kBN + t;
-      const int64_t own = ((int64_t)phys * a.H + h) * BS + jk % BS;
-      const int64_t row = jk < ctx ? own : last_row;
-      const u32x4* kg = a.kpool + row * (kD / 8) + (chunk_pos ^ k_swz(t));
-      const u32x4* vg = a.vpool + row * (kD / 8) + (chunk_pos ^ v_swz(t));
-      load_to_lds(kg, lds_addr(&lds_k[buf][t0 * kRowBytes]));
-      load_to_lds(vg, lds_addr(&lds_v[buf][t0 * kRowBytes]));
+      const int64_t row = jk < ctx ? ((int64_t)phys * a.H + h) * BS + jk % BS : last_row;
+      const int cpos = chunk_pos ^ (is_v ? v_swz(t) : k_swz(t));
+      load_to_lds(pool + row * (kD / 8) + cpos, lds_addr(dst + t0 * kRowBytes));
     }
   };
 
-  // Softmax of one query block's scores: mask, new running max.
-  auto block_max = [&](f32x16* acc_s, const int j0, const int qb, auto masked_tag) -> float {
+  // ---- the three stages of a tile
+  // S^T = K Q^T for one key tile (key operand: token 32mb + col, chunk 2ks + g)
+  auto qk = [&](const uint8_t* __restrict__ tk, f32x16* acc_s) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc_s[mb][i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const int t = 32 * mb + col;
+        const u32x4 ka = *(const u32x4*)&tk[t * kRowBytes + 16 * ((2 * ks + g) ^ k_swz(t))];
+        acc_s[mb] = mfma32(E{}, ka, qop[ks], acc_s[mb]);
+      }
+  };
+  // mask (diagonal tiles), running max, lazy rescale
+  auto softmax_max = [&](f32x16* acc_s, const int j0, auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
-    const int qpos = pos0 + qrow[qb];
-    float mt = kNegBig;
+    float mt[4] = {kNegBig, kNegBig, kNegBig, kNegBig};  // four independent max chains
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -284,23 +305,25 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(QB == 2
           const int kpos = j0 + 32 * mb + 8 * (i / 4) + 4 * g + (i % 4);
           if (kpos > qpos) acc_s[mb][i] = -__builtin_inff();
         }
-        mt = fmaxf(mt, acc_s[mb][i]);
+        mt[i & 3] = fmaxf(mt[i & 3], acc_s[mb][i]);
       }
-    return fmaxf(m[qb], halves_max(mt));  // raw units (scale > 0 keeps the order)
-  };
-  auto rescale = [&](const int qb, const float m_new) {
-    const float alpha = __builtin_amdgcn_exp2f((m[qb] - m_new) * c);
-    l[qb] *= alpha;
+    const float mtile = fmaxf(fmaxf(mt[0], mt[1]), fmaxf(mt[2], mt[3]));
+    const float m_new = fmaxf(m, halves_max(mtile));  // raw units (scale > 0 keeps the order)
+    if (__any(m_new > m + slack)) {
+      const float alpha = __builtin_amdgcn_exp2f((m - m_new) * c);
 #pragma unroll
-    for (int dm = 0; dm < 4; ++dm)
+      for (int k = 0; k < 4; ++k) lp[k] *= alpha;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc_o[qb][dm][i] *= alpha;
-    m[qb] = m_new;
+      for (int dm = 0; dm < 4; ++dm)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc_o[dm][i] *= alpha;
+      m = m_new;
+    }
   };
   // P^T operands: k-step (mb, t) takes result elements 8t .. 8t+7 of block mb;
   // the denominator sums the same rounded weights the MFMA multiplies
-  auto weights = [&](const f32x16* acc_s, const int qb, u32x4 (*pb)[2]) {
-    const float mc = -m[qb] * c;
+  auto weights = [&](const f32x16* acc_s, u32x4 (*pb)[2]) {
+    const float mc = -m * c;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
@@ -310,136 +333,115 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(QB == 2
         for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc_s[mb][8 * t + j], c, mc));
         pb[mb][t] = u32x4{pack2(E{}, p[0], p[1]), pack2(E{}, p[2], p[3]), pack2(E{}, p[4], p[5]),
                           pack2(E{}, p[6], p[7])};
-        l[qb] = sum_unpacked(E{}, pb[mb][t], l[qb]);
+        lp[2 * mb + t] = sum_unpacked(E{}, pb[mb][t], lp[2 * mb + t]);
       }
   };
-
-  // One key tile: S^T = K Q^T, online softmax, O^T += V^T P^T.  MASKED tiles
-  // straddle the diagonal; scores of keys after the query become -inf.
-  auto compute_tile = [&](const int j0, const uint8_t* __restrict__ tk, const uint8_t* __restrict__ tv,
-                          auto masked_tag) {
-    f32x16 acc_s[QB][2];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc_s[qb][mb][i] = 0.f;
-    u32x4 pb[QB][2][2];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      // key operand: token 32mb + col, dims 16ks + 8g .. +8 (chunk 2ks + g)
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          const int t = 32 * mb + col;
-          const u32x4 ka = *(const u32x4*)&tk[t * kRowBytes + 16 * ((2 * ks + g) ^ k_swz(t))];
-          acc_s[qb][mb] = mfma32(E{}, ka, qop[qb][ks], acc_s[qb][mb]);
-        }
-      // the previous block's weights overlap this block's MFMAs
-      if (qb > 0) weights(acc_s[qb - 1], qb - 1, pb[qb - 1]);
-      const float m_new = block_max(acc_s[qb], j0, qb, masked_tag);
-      if (__any(m_new > m[qb] + slack)) rescale(qb, m_new);
-    }
-    weights(acc_s[QB - 1], QB - 1, pb[QB - 1]);
-    // O^T += V^T P^T; k-slot (g, j) of step (mb, t) is key 32mb + 16t + 8(j/4) + 4g + j%4.
-    // Transposing read: in each 16-lane group, lane r points at 4 dims of
-    // token k0 + r/4 and receives the 4 tokens k0 .. k0+3 of one dim.
-    const int grp = lane >> 4, r = lane & 15;
+  // O^T += V^T P^T; k-slot (g, j) of step (mb, t) is key 32mb + 16t + 8(j/4) + 4g + j%4.
+  // Transposing read: in each 16-lane group, lane r points at 4 dims of
+  // token k0 + r/4 and receives the 4 tokens k0 .. k0+3 of one dim.
+  const int grp = lane >> 4, r16 = lane & 15;
+  auto pv = [&](const uint8_t* __restrict__ tv, u32x4 (*pb)[2]) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int dm = 0; dm < 4; ++dm) {
-          const int d = 32 * dm + 16 * (grp & 1) + 4 * (r & 3);
+          const int d = 32 * dm + 16 * (grp & 1) + 4 * (r16 & 3);
           uint32_t va[4];
 #pragma unroll
           for (int half = 0; half < 2; ++half) {
-            const int tok = 32 * mb + 16 * t + 8 * half + 4 * (grp >> 1) + (r >> 2);
-            const uint8_t* pv = &tv[tok * kRowBytes + 16 * ((d >> 3) ^ v_swz(tok)) + 2 * (d & 7)];
-            const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)pv);
+            const int tok = 32 * mb + 16 * t + 8 * half + 4 * (grp >> 1) + (r16 >> 2);
+            const uint8_t* p = &tv[tok * kRowBytes + 16 * ((d >> 3) ^ v_swz(tok)) + 2 * (d & 7)];
+            const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
             const u32x2 xw = __builtin_bit_cast(u32x2, x);
             va[2 * half] = xw.x;
             va[2 * half + 1] = xw.y;
           }
-          const u32x4 vop = {va[0], va[1], va[2], va[3]};
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) acc_o[qb][dm] = mfma32(E{}, vop, pb[qb][mb][t], acc_o[qb][dm]);
+          acc_o[dm] = mfma32(E{}, u32x4{va[0], va[1], va[2], va[3]}, pb[mb][t], acc_o[dm]);
         }
   };
 
-  // prologue: tiles 0 and 1 in buffers 0 and 1
+  // ---- software pipeline: keys run one tile ahead of values.  Step j
+  // holds S(j) (scores of key tile j) on entry, and K(j+1), V(j) in LDS.
+  // It starts the loads of K(j+2) and V(j+1) (into the buffers released by
+  // the barrier that ended step j-1), finishes the softmax of S(j), forms
+  // S(j+1) on the MFMAs while the exponentials of S(j) run, accumulates
+  // P(j) V(j), then waits for its loads and ends with a barrier.
   {
-    int ent[NE];
-    entries(0, ent);
-    issue_tile(0, 0, ent);
-    if (nkt > 1) {
-      entries(1, ent);
-      issue_tile(1, 1, ent);
+    int e0[NE], e1[NE];
+    entries(0, e0);
+    entries(1, e1);
+    issue(a.kpool, lds_k[0], 0, e0, false);
+    issue(a.vpool, lds_v[0], 0, e0, true);
+    if (nkt > 1) issue(a.kpool, lds_k[1], 1, e1, false);
+  }
+  wait_vmem();
+  lds_barrier();  // K(0), V(0), K(1) are visible
+  f32x16 s_cur[2];
+  qk(lds_k[0], s_cur);
+  lds_barrier();  // every wave has read K(0): its buffer can take K(2)
+
+  auto step = [&](const int j, auto masked_tag, auto has_next_tag) {
+    constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
+    {
+      int ek[NE], ev[NE];
+      entries(j + 2, ek);
+      entries(j + 1, ev);
+      if (j + 2 < nkt) issue(a.kpool, lds_k[j & 1], j + 2, ek, false);
+      if (j + 1 < nkt) issue(a.vpool, lds_v[(j + 1) & 1], j + 1, ev, true);
+    }
+    if (j < wave_tiles) {
+      softmax_max(s_cur, j * kBN, masked_tag);
+      f32x16 s_next[2];
+      if constexpr (HAS_NEXT) qk(lds_k[(j + 1) & 1], s_next);
+      u32x4 pb[2][2];
+      weights(s_cur, pb);
+      pv(lds_v[j & 1], pb);
+      if constexpr (HAS_NEXT) {
+        s_cur[0] = s_next[0];
+        s_cur[1] = s_next[1];
+      }
     }
     wait_vmem();
     lds_barrier();
-  }
-  // Tile kt: read the table entries of tile kt + 2, compute tile kt, wait for
-  // this wave's loads of tile kt + 1, barrier, then load tile kt + 2 into the
-  // buffer every wave has just finished with.  Two loops, so each has one
-  // compute path and the accumulators stay in place.
-  int kt = 0;
-  for (; kt < n_full; ++kt) {
-    int ent[NE];
-    entries(kt + 2, ent);
-    compute_tile(kt * kBN, lds_k[kt & 1], lds_v[kt & 1], std::false_type{});
-    wait_vmem();
-    lds_barrier();
-    if (kt + 2 < nkt) issue_tile(kt + 2, kt & 1, ent);
-  }
-  for (; kt < nkt; ++kt) {
-    int ent[NE];
-    entries(kt + 2, ent);
-    const int j0 = kt * kBN;
-    if (j0 <= wave_max_pos)  // a wave skips tiles wholly after its queries
-      compute_tile(j0, lds_k[kt & 1], lds_v[kt & 1], std::true_type{});
-    wait_vmem();
-    lds_barrier();
-    if (kt + 2 < nkt) issue_tile(kt + 2, kt & 1, ent);
-  }
+  };
+  // unmasked steps whose next tile exists, then masked ones, then the last
+  int j = 0;
+  const int last = nkt - 1;
+  for (; j < min(n_full, last); ++j) step(j, std::false_type{}, std::true_type{});
+  for (; j < min(last, wave_tiles - 1); ++j) step(j, std::true_type{}, std::true_type{});
+  for (; j < last; ++j) step(j, std::true_type{}, std::false_type{});  // this wave's last tile, then none
+  if (last < n_full) step(last, std::false_type{}, std::false_type{});
+  else step(last, std::true_type{}, std::false_type{});
 
   // normalise and store: result element i of block dm is dim 32dm + 8(i/4) + 4g + i%4
+  const float l = halves_sum((lp[0] + lp[1]) + (lp[2] + lp[3]));
+  if (qrow >= qlen) return;
+  const float inv_l = 1.f / l;
+  const int64_t obase = ((int64_t)(q_begin + qrow) * a.H + h) * kD;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float lsum = halves_sum(l[qb]);
-    if (qrow[qb] >= qlen) continue;
-    const float inv_l = 1.f / lsum;
-    const int64_t obase = ((int64_t)(q_begin + qrow[qb]) * a.H + h) * kD;
+  for (int dm = 0; dm < 4; ++dm)
 #pragma unroll
-    for (int dm = 0; dm < 4; ++dm)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int d = 32 * dm + 8 * r4 + 4 * g;
-        const float o0 = acc_o[qb][dm][4 * r4] * inv_l, o1 = acc_o[qb][dm][4 * r4 + 1] * inv_l;
-        const float o2 = acc_o[qb][dm][4 * r4 + 2] * inv_l, o3 = acc_o[qb][dm][4 * r4 + 3] * inv_l;
-        if (a.out_dtype == PA_F32) {
-          float4 v = {o0, o1, o2, o3};
-          *(float4*)((float*)a.out + obase + d) = v;
-        } else if (a.out_dtype == E::id) {
-          u32x2 v = {pack2(E{}, o0, o1), pack2(E{}, o2, o3)};
-          *(u32x2*)((uint16_t*)a.out + obase + d) = v;
-        }
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int d = 32 * dm + 8 * r4 + 4 * g;
+      const float o0 = acc_o[dm][4 * r4] * inv_l, o1 = acc_o[dm][4 * r4 + 1] * inv_l;
+      const float o2 = acc_o[dm][4 * r4 + 2] * inv_l, o3 = acc_o[dm][4 * r4 + 3] * inv_l;
+      if (a.out_dtype == PA_F32) {
+        float4 v = {o0, o1, o2, o3};
+        *(float4*)((float*)a.out + obase + d) = v;
+      } else if (a.out_dtype == E::id) {
+        u32x2 v = {pack2(E{}, o0, o1), pack2(E{}, o2, o3)};
+        *(u32x2*)((uint16_t*)a.out + obase + d) = v;
       }
-  }
+    }
 }
 
 #ifndef PA_PREFILL_NW
 #define PA_PREFILL_NW 4  // waves per workgroup
 #endif
-#ifndef PA_PREFILL_QB
-#define PA_PREFILL_QB 1  // 32-query blocks per wave
-#endif
 constexpr int kNW = PA_PREFILL_NW;
-constexpr int kQB = PA_PREFILL_QB;
-constexpr int kTileQ = kNW * kQB * 32;  // queries per workgroup
+constexpr int kTileQ = kNW * 32;  // queries per workgroup
 
 struct Variant {
   pa_dtype dtype;
@@ -448,8 +450,8 @@ struct Variant {
 };
 
 #define PA_PREFILL_VARIANTS(BS)                                    \
-  Variant{PA_BF16, BS, prefill_kernel<BF16, BS, kNW, kQB>}, Variant { \
-    PA_F16, BS, prefill_kernel<F16, BS, kNW, kQB>                     \
+  Variant{PA_BF16, BS, prefill_kernel<BF16, BS, kNW>}, Variant { \
+    PA_F16, BS, prefill_kernel<F16, BS, kNW>                     \
   }
 
 const Variant kVariants[] = {PA_PREFILL_VARIANTS(16), PA_PREFILL_VARIANTS(32), PA_PREFILL_VARIANTS(64),
