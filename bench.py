@@ -64,28 +64,30 @@ def blas_threads() -> int:
 
 COUNTERS = os.path.join(ROOT, "profiles", "decode_opt13b_fp16_b16_counters.txt")
 DECODE_SOURCES = ("paged_kv_cache_76_amd/csrc/paged_decode.hip", "paged_kv_cache_76_amd/csrc/pa_device.h")
+PREFILL_COUNTERS = os.path.join(ROOT, "profiles", "prefill_opt66b_bf16_8x1024_counters.txt")
+PREFILL_SOURCES = ("paged_kv_cache_76_amd/csrc/paged_prefill.hip",)
 
 
-def measured_traffic() -> float | None:
-    """HBM bytes per pa_paged_decode launch from the committed rocprofv3
-    FETCH_SIZE / WRITE_SIZE runs (scaled by the copy-kernel calibration), or
-    None if the decode sources changed since those counters were taken."""
+def measured_traffic(path=COUNTERS, sources=DECODE_SOURCES, kernels=("decode_partition_kernel",
+                                                                        "decode_reduce_kernel")) -> float | None:
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    runs (scaled by the copy-kernel calibration), summed over ``kernels``, or
+    None if the kernel sources changed since those counters were taken."""
     import hashlib
 
     try:
         kv = {}
-        for line in open(COUNTERS):
+        for line in open(path):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
         h = hashlib.sha256()
-        for f in DECODE_SOURCES:
+        for f in sources:
             h.update(open(os.path.join(ROOT, f), "rb").read())
         if h.hexdigest() != kv["kernel_source_sha256"]:
             return None
         fs, ws = float(kv["fetch_scale"]), float(kv["write_scale"])
-        kib = (float(kv["decode_partition_kernel_fetch_kib"]) + float(kv["decode_reduce_kernel_fetch_kib"])) * fs \
-            + (float(kv["decode_partition_kernel_write_kib"]) + float(kv["decode_reduce_kernel_write_kib"])) * ws
+        kib = sum(float(kv[f"{k}_fetch_kib"]) * fs + float(kv[f"{k}_write_kib"]) * ws for k in kernels)
         return kib * 1024.0
     except (OSError, KeyError, ValueError):
         return None
@@ -200,6 +202,25 @@ def prefill_bench(args) -> int:
     tflops = flops / (p_ms * 1e-3) / 1e12
     log(f"prefill {p_ms * 1e3:.1f} us -> {tflops:.1f} TFLOP/s; write {w_ms * 1e3:.1f} us -> "
         f"{wbytes / (w_ms * 1e-3) / 1e9:.0f} GB/s")
+    cpu = None
+    if args.cpu_seqs > 0:
+        # the float64 oracle on a bounded sample: sequence 0, all heads, every query
+        from oracle import attention as oa
+
+        qh = b.q[:L5].to(torch.float64).numpy()
+        kh = b.k_hist[0].to(torch.float64).numpy()
+        vh = b.v_hist[0].to(torch.float64).numpy()
+        times = []
+        for _ in range(3):
+            t1 = time.perf_counter()
+            oa.prefill(qh, kh, vh, b.scale)
+            times.append(time.perf_counter() - t1)
+        dt = sorted(times)[1]
+        sample_flops = workloads.prefill_flops([L5], [L5], H5, D)
+        cpu = {"value": sample_flops / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+               "sample": f"sequence 0 of {S5} (all {H5} heads, {L5} causal queries), median of 3, float64 NumPy on "
+                         f"{os.cpu_count()} host cores ({cpu_model()})", "seconds": dt}
+        log(f"cpu oracle sample: {dt:.2f} s -> {cpu['value'] * 1e3:.3f} GFLOP/s")
     rec = {"metric": "paged causal prefill TFLOP/s, OPT-66B shape (8 x 1024 tokens, 72 heads, d128, bf16)",
            "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
            "ms_per_step": round(elapsed / K * 1e3, 4), "higher_is_better": True, "scaling": "weak",
@@ -209,9 +230,11 @@ def prefill_bench(args) -> int:
                       "seed": "SeedSequence(76005)"},
            "roofline": {"bound": "mfma", "kernel": "pa_paged_prefill", "achieved": round(tflops, 2),
                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                        "traffic": None, "avg_launch_us": round(p_ms * 1e3, 2), "algorithmic_flops_per_launch": flops},
+                        "traffic": measured_traffic(PREFILL_COUNTERS, PREFILL_SOURCES, ("prefill_kernel",)),
+                        "avg_launch_us": round(p_ms * 1e3, 2), "algorithmic_flops_per_launch": flops},
            "write": {"kernel": "pa_reshape_and_cache", "avg_launch_us": round(w_ms * 1e3, 2),
-                     "achieved_GBps": round(wbytes / (w_ms * 1e-3) / 1e9, 1), "bytes_per_launch": wbytes}}
+                     "achieved_GBps": round(wbytes / (w_ms * 1e-3) / 1e9, 1), "bytes_per_launch": wbytes},
+           "cpu_baseline": cpu}
     print(json.dumps(rec), flush=True)
     return 0
 
