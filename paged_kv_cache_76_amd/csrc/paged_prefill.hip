@@ -93,9 +93,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 
 constexpr int kD = 128;         // head_dim
-constexpr int kBN = 64;         // keys per tile
 constexpr int kRowBytes = kD * 2;
-constexpr int kTileBytes = kBN * kRowBytes;  // 16 KiB per K or V tile
 constexpr int kXcds = 8;        // accelerator complex dies of an MI355X
 constexpr float kNegBig = -1e30f;
 constexpr float kRescaleLog2 = 8.0f;
@@ -158,15 +156,19 @@ struct PrefillArgs {
   pa_dtype out_dtype;
 };
 
-constexpr int kTabCache = 2048;  // block-table entries a workgroup keeps in LDS
-
-// One workgroup = NW waves of 32 queries each.
-template <typename E, int BS, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(
+// One workgroup = NW waves of 32 queries each; key tiles of BN tokens (MB
+// blocks of 32).  BN = 32 halves the LDS of a workgroup so that more of them
+// share a CU.
+template <typename E, int BS, int NW, int BN>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BN == 32 ? 3 : 2))) void prefill_kernel(
     PrefillArgs a) {
   constexpr int kBM = NW * 32;   // queries per workgroup
-  constexpr int KPW = kBN / NW;  // tile keys each wave loads, four per load instruction
-  static_assert(KPW % 4 == 0 && BS >= 4 && (kBN % BS == 0 || BS % kBN == 0), "block size must tile the 64-key step");
+  constexpr int MB = BN / 32;    // 32-key blocks per tile
+  constexpr int KPW = BN / NW;   // tile keys each wave loads, four per load instruction
+  constexpr int kTileBytes = BN * kRowBytes;
+  constexpr int kTabCache = BN == 32 ? 1024 : 2048;  // block-table entries a workgroup keeps in LDS
+  static_assert((BN == 32 || BN == 64) && KPW % 4 == 0 && BS >= 4 && (BN % BS == 0 || BS % BN == 0),
+                "block size must tile the key step");
   __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t lds_v[2][kTileBytes];
   __shared__ int32_t lds_tab[kTabCache];
@@ -219,13 +221,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 
   // keys needed by the workgroup: positions 0 .. pos0 + min(q0 + kBM, qlen) - 1
   const int last_pos = pos0 + min(q0 + kBM, qlen) - 1;
-  const int nkt = last_pos / kBN + 1;
+  const int nkt = last_pos / BN + 1;
   const int64_t trow = (int64_t)s * a.max_blocks;
 
   // tiles whose keys all precede every query of the workgroup need no mask
-  const int n_full = min(nkt, (pos0 + q0 + 1) / kBN);
+  const int n_full = min(nkt, (pos0 + q0 + 1) / BN);
   const int wave_max_pos = pos0 + min(q0 + 32 * w + 31, qlen - 1);  // last query of this wave
-  const int wave_tiles = min(nkt, wave_max_pos / kBN + 1);         // tiles with keys this wave needs
+  const int wave_tiles = min(nkt, wave_max_pos / BN + 1);         // tiles with keys this wave needs
   const float c = a.scale_log2;
   // Lazy rescale: the running max used for the weights is only raised (and
   // the accumulators rescaled) when some query's max grows by more than
@@ -239,7 +241,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   // pool.  Entries past those are never used for a load (tokens at or past
   // the context length are redirected below).
   auto clamp_phys = [&](const int e) { return (e >= 0 && e < a.N) ? e : 0; };
-  const int n_tab = min(min(nkt * kBN, ctx) - 1, (a.max_blocks - 1) * BS) / BS + 1;
+  const int n_tab = min(min(nkt * BN, ctx) - 1, (a.max_blocks - 1) * BS) / BS + 1;
   for (int i = tid; i < min(n_tab, kTabCache); i += NW * 64) lds_tab[i] = clamp_phys(a.tables[trow + i]);
   lds_barrier();
   auto entry = [&](const int blk) -> int {
@@ -262,7 +264,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   constexpr int NE = BS >= KPW ? 1 : NI;
   auto entries = [&](const int kt, int* ent) {
 #pragma unroll
-    for (int i = 0; i < NE; ++i) ent[i] = __builtin_amdgcn_readfirstlane(entry((kt * kBN + KPW * w + 4 * i) / BS));
+    for (int i = 0; i < NE; ++i) ent[i] = __builtin_amdgcn_readfirstlane(entry((kt * BN + KPW * w + 4 * i) / BS));
   };
   auto issue = [&](const u32x4* pool, uint8_t* dst, const int kt, const int* ent, const bool is_v) {
 #pragma unroll
@@ -270,7 +272,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       const int t0 = KPW * w + 4 * i;  // first tile token of this instruction (wave-uniform)
       const int phys = ent[NE == 1 ? 0 : i];
       const int t = t0 + tok_in_inst;
-      const int jk = kt * kBN + t;
+      const int jk = kt * BN + t;
       const int64_t row = jk < ctx ? ((int64_t)phys * a.H + h) * BS + jk % BS : last_row;
       const int cpos = chunk_pos ^ (is_v ? v_swz(t) : k_swz(t));
       load_to_lds(pool + row * (kD / 8) + cpos, lds_addr(dst + t0 * kRowBytes));
@@ -281,13 +283,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   // S^T = K Q^T for one key tile (key operand: token 32mb + col, chunk 2ks + g)
   auto qk = [&](const uint8_t* __restrict__ tk, f32x16* acc_s) {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc_s[mb][i] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
+      for (int mb = 0; mb < MB; ++mb) {
         const int t = 32 * mb + col;
         const u32x4 ka = *(const u32x4*)&tk[t * kRowBytes + 16 * ((2 * ks + g) ^ k_swz(t))];
         acc_s[mb] = mfma32(E{}, ka, qop[ks], acc_s[mb]);
@@ -298,7 +300,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     constexpr bool MASKED = decltype(masked_tag)::value;
     float mt[4] = {kNegBig, kNegBig, kNegBig, kNegBig};  // four independent max chains
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         if constexpr (MASKED) {
@@ -325,7 +327,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   auto weights = [&](const f32x16* acc_s, u32x4 (*pb)[2]) {
     const float mc = -m * c;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         float p[8];
@@ -342,7 +344,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int grp = lane >> 4, r16 = lane & 15;
   auto pv = [&](const uint8_t* __restrict__ tv, u32x4 (*pb)[2]) {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -378,7 +380,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   }
   wait_vmem();
   lds_barrier();  // K(0), V(0), K(1) are visible
-  f32x16 s_cur[2];
+  f32x16 s_cur[MB];
   qk(lds_k[0], s_cur);
   lds_barrier();  // every wave has read K(0): its buffer can take K(2)
 
@@ -392,15 +394,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
       if (j + 1 < nkt) issue(a.vpool, lds_v[(j + 1) & 1], j + 1, ev, true);
     }
     if (j < wave_tiles) {
-      softmax_max(s_cur, j * kBN, masked_tag);
-      f32x16 s_next[2];
+      softmax_max(s_cur, j * BN, masked_tag);
+      f32x16 s_next[MB];
       if constexpr (HAS_NEXT) qk(lds_k[(j + 1) & 1], s_next);
-      u32x4 pb[2][2];
+      u32x4 pb[MB][2];
       weights(s_cur, pb);
       pv(lds_v[j & 1], pb);
       if constexpr (HAS_NEXT) {
-        s_cur[0] = s_next[0];
-        s_cur[1] = s_next[1];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) s_cur[mb] = s_next[mb];
       }
     }
     wait_vmem();
@@ -437,6 +439,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     }
 }
 
+#ifndef PA_PREFILL_BN
+#define PA_PREFILL_BN 64  // keys per tile
+#endif
 #ifndef PA_PREFILL_NW
 #define PA_PREFILL_NW 4  // waves per workgroup
 #endif
@@ -450,8 +455,8 @@ struct Variant {
 };
 
 #define PA_PREFILL_VARIANTS(BS)                                    \
-  Variant{PA_BF16, BS, prefill_kernel<BF16, BS, kNW>}, Variant { \
-    PA_F16, BS, prefill_kernel<F16, BS, kNW>                     \
+  Variant{PA_BF16, BS, prefill_kernel<BF16, BS, kNW, PA_PREFILL_BN>}, Variant { \
+    PA_F16, BS, prefill_kernel<F16, BS, kNW, PA_PREFILL_BN>                     \
   }
 
 const Variant kVariants[] = {PA_PREFILL_VARIANTS(16), PA_PREFILL_VARIANTS(32), PA_PREFILL_VARIANTS(64),
