@@ -93,6 +93,25 @@ def test_opt66b_prefill_full_size_sampled():
         check_close(got, ref, TOL["bf16"], f"OPT-66B prefill seq {s}")
 
 
+@pytest.mark.parametrize("B,qlen", [(16, 33000), (16, 300), (32, 1200)])
+def test_long_prompt_past_the_table_cache(B, qlen):
+    # a 33000-token history needs 2063 blocks of 16, more than the workgroup's
+    # LDS copy of the block table holds (2048 entries): later tiles read their
+    # entries from global memory; a 1200-query tail and a short tail as well
+    print(f"prefill long prompt B={B} q_len={qlen}", flush=True)
+    lens = [33000, 700]
+    b = workloads.build_prefill_batch(8, lens, [qlen, min(qlen, 700)], num_heads=2, head_dim=128, block_size=B,
+                                      dtype="bf16")
+    out = _run(b)
+    assert torch.isfinite(out).all()
+    for s in range(2):
+        n = int(b.q_lens[s])
+        rows = sorted(set([0, n // 2, n - 1] + ([n - 300, 127, 128] if n > 300 else [])))
+        ref = _oracle(b, s, rows, [0, 1])
+        got = out[b.cu_q[s]:b.cu_q[s + 1]][rows]
+        check_close(got, ref, TOL["bf16"], f"long prompt seq {s}")
+
+
 @pytest.mark.parametrize("dtype,B,prefix,tasks", [("bf16", 16, 200, [13, 1, 129, 40]),
                                                   ("f16", 16, 256, [64, 3]),
                                                   ("bf16", 32, 77, [200, 5, 31])])
