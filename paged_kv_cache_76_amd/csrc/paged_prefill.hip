@@ -95,6 +95,10 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 constexpr int kD = 128;         // head_dim
 constexpr int kRowBytes = kD * 2;
 constexpr int kXcds = 8;        // accelerator complex dies of an MI355X
+#ifndef PA_PREFILL_PAIR_GROUP
+#define PA_PREFILL_PAIR_GROUP 4
+#endif
+constexpr int kPairGroup = PA_PREFILL_PAIR_GROUP;  // (sequence, head) pairs ordered together
 constexpr float kNegBig = -1e30f;
 constexpr float kRescaleLog2 = 8.0f;
 constexpr float kLog2e = 1.44269504088896340736f;
@@ -174,15 +178,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BN == 3
   __shared__ int32_t lds_tab[kTabCache];
 
   // XCD-aware order: workgroups are handed to the 8 XCDs round-robin, so
-  // XCD x runs blocks x, x+8, ...; give each XCD a contiguous range of
-  // (sequence, head) pairs with all their query tiles (heaviest first), so the
-  // key/value tiles every query tile of a pair re-reads stay in that XCD's L2.
+  // XCD x runs blocks x, x+8, ...; give each XCD a contiguous range of the
+  // work list, so the key/value tiles every query tile of a (sequence, head)
+  // pair re-reads stay in that XCD's L2.  The list takes pairs in groups of
+  // kPairGroup (their keys/values fit an XCD's L2 together) and, within a
+  // group, query tiles heaviest first across the group's pairs, so the last
+  // workgroups dispatched are the short ones.
   const int total = a.ntiles * a.S * a.H;
   const int xcd = blockIdx.x % kXcds;
   const int q8 = total / kXcds, r8 = total % kXcds;
   const int lin = xcd * q8 + min(xcd, r8) + (int)(blockIdx.x / kXcds);
-  const int pair = lin / a.ntiles;
-  const int tile = a.ntiles - 1 - lin % a.ntiles;
+  const int grp0 = lin / (kPairGroup * a.ntiles) * kPairGroup;       // first pair of this group
+  const int gn = min(kPairGroup, a.S * a.H - grp0);                 // pairs in this group
+  const int gr = lin - grp0 * a.ntiles;
+  const int pair = grp0 + gr % gn;
+  const int tile = a.ntiles - 1 - gr / gn;
   const int s = pair / a.H;
   const int h = pair % a.H;
   const int q_begin = a.cu_q[s];
@@ -243,11 +253,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BN == 3
   auto clamp_phys = [&](const int e) { return (e >= 0 && e < a.N) ? e : 0; };
   const int n_tab = min(min(nkt * BN, ctx) - 1, (a.max_blocks - 1) * BS) / BS + 1;
   for (int i = tid; i < min(n_tab, kTabCache); i += NW * 64) lds_tab[i] = clamp_phys(a.tables[trow + i]);
-  lds_barrier();
+  // (published by the barrier that follows the first tile loads)
   auto entry = [&](const int blk) -> int {
     const int b = min(blk, a.max_blocks - 1);
     return b < kTabCache ? lds_tab[b] : clamp_phys(a.tables[trow + b]);
   };
+  auto entry_global = [&](const int blk) -> int { return clamp_phys(a.tables[trow + min(blk, a.max_blocks - 1)]); };
   const int64_t last_row = ((int64_t)clamp_phys(a.tables[trow + min((ctx - 1) / BS, a.max_blocks - 1)]) * a.H + h) *
                                BS + (ctx - 1) % BS;
 
@@ -265,6 +276,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BN == 3
   auto entries = [&](const int kt, int* ent) {
 #pragma unroll
     for (int i = 0; i < NE; ++i) ent[i] = __builtin_amdgcn_readfirstlane(entry((kt * BN + KPW * w + 4 * i) / BS));
+  };
+  // the same, read from global memory (before the LDS copy is published)
+  auto entries_global = [&](const int kt, int* ent) {
+#pragma unroll
+    for (int i = 0; i < NE; ++i)
+      ent[i] = __builtin_amdgcn_readfirstlane(entry_global((kt * BN + KPW * w + 4 * i) / BS));
   };
   auto issue = [&](const u32x4* pool, uint8_t* dst, const int kt, const int* ent, const bool is_v) {
 #pragma unroll
@@ -372,14 +389,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BN == 3
   // P(j) V(j), then waits for its loads and ends with a barrier.
   {
     int e0[NE], e1[NE];
-    entries(0, e0);
-    entries(1, e1);
+    entries_global(0, e0);
+    entries_global(1, e1);
     issue(a.kpool, lds_k[0], 0, e0, false);
     issue(a.vpool, lds_v[0], 0, e0, true);
     if (nkt > 1) issue(a.kpool, lds_k[1], 1, e1, false);
   }
   wait_vmem();
-  lds_barrier();  // K(0), V(0), K(1) are visible
+  lds_barrier();  // K(0), V(0), K(1) and the block-table copy are visible
   f32x16 s_cur[MB];
   qk(lds_k[0], s_cur);
   lds_barrier();  // every wave has read K(0): its buffer can take K(2)
