@@ -91,6 +91,18 @@ __device__ __forceinline__ void load_to_lds(const void* src, uint32_t lds_base) 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(lds_void_t*)p;
 }
+// Four such loads of consecutive 1 KiB global pieces from one address
+// register: the immediate offset k * 1024 advances both the global address
+// and the LDS address; M0 takes m[k] (so the LDS pieces may have gaps).
+__device__ __forceinline__ void load4_to_lds(const void* src, uint32_t m0, uint32_t m1, uint32_t m2, uint32_t m3) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off\n\t"
+      "s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:1024\n\t"
+      "s_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:2048\n\t"
+      "s_mov_b32 m0, %4\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:3072" ::"v"(src),
+      "s"(m0), "s"(m1), "s"(m2), "s"(m3)
+      : "memory");
+}
 
 constexpr int kD = 128;         // head_dim
 constexpr int kRowBytes = kD * 2;
@@ -103,13 +115,22 @@ constexpr float kNegBig = -1e30f;
 constexpr float kRescaleLog2 = 8.0f;
 constexpr float kLog2e = 1.44269504088896340736f;
 
-// 16-byte chunk c of token row t is stored at chunk position c ^ swz(t).
-// Keys: the QK operand read takes one chunk of 16 consecutive tokens per
-// group of lanes, so 16 distinct positions cover all banks.  Values: a
-// transposing read takes two adjacent chunks of four consecutive tokens per
-// 16 lanes; positions 4(t % 4) apart keep 32 lanes conflict-free.
-__device__ __forceinline__ int k_swz(const int t) { return t & 15; }
-__device__ __forceinline__ int v_swz(const int t) { return 4 * (t & 3); }
+// LDS tile layouts.  A token row is 256 bytes; its 16-byte chunk c sits at
+// chunk position c ^ swz(t), and the swizzles depend only on t % 4 (a
+// token's place within the four a load instruction brings), so all the
+// loads of a wave can share one address register.  Keys: rows in groups of
+// four, groups 1024 + 64 bytes apart; with chunk ^ (t % 4) the QK operand
+// read (one chunk of 16 consecutive tokens per group of lanes) hits all 64
+// banks once.  Values: rows 256 bytes apart, chunk ^ 4(t % 4): a transposing
+// read takes two adjacent chunks of four consecutive tokens per 16 lanes,
+// conflict-free for 32 lanes.
+constexpr int kKGroupBytes = 4 * kRowBytes + 64;
+__device__ __forceinline__ int k_off(const int t, const int chunk) {
+  return (t >> 2) * kKGroupBytes + (t & 3) * kRowBytes + 16 * (chunk ^ (t & 3));
+}
+__device__ __forceinline__ int v_off(const int t, const int chunk) {
+  return t * kRowBytes + 16 * (chunk ^ (4 * (t & 3)));
+}
 
 __device__ __forceinline__ f32x16 mfma32(BF16, u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
@@ -169,12 +190,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BN == 3
   constexpr int kBM = NW * 32;   // queries per workgroup
   constexpr int MB = BN / 32;    // 32-key blocks per tile
   constexpr int KPW = BN / NW;   // tile keys each wave loads, four per load instruction
-  constexpr int kTileBytes = BN * kRowBytes;
+  constexpr int kKTileBytes = BN / 4 * kKGroupBytes;
+  constexpr int kVTileBytes = BN * kRowBytes;
   constexpr int kTabCache = BN == 32 ? 1024 : 2048;  // block-table entries a workgroup keeps in LDS
   static_assert((BN == 32 || BN == 64) && KPW % 4 == 0 && BS >= 4 && (BN % BS == 0 || BS % BN == 0),
                 "block size must tile the key step");
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_v[2][kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][kKTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v[2][kVTileBytes];
   __shared__ int32_t lds_tab[kTabCache];
 
   // XCD-aware order: workgroups are handed to the 8 XCDs round-robin, so
@@ -283,16 +305,26 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BN == 3
     for (int i = 0; i < NE; ++i)
       ent[i] = __builtin_amdgcn_readfirstlane(entry_global((kt * BN + KPW * w + 4 * i) / BS));
   };
+  // LDS byte offset of the first row of tile token t0 (a multiple of 4)
+  auto row_base = [&](const int t0, const bool is_v) { return is_v ? t0 * kRowBytes : t0 / 4 * kKGroupBytes; };
   auto issue = [&](const u32x4* pool, uint8_t* dst, const int kt, const int* ent, const bool is_v) {
+    const int cpos = is_v ? chunk_pos ^ (4 * tok_in_inst) : chunk_pos ^ tok_in_inst;  // t % 4 == tok_in_inst
+    if (NE == 1 && NI == 4 && kt * BN + KPW * (w + 1) <= ctx) {
+      // the wave's 16 tokens are consecutive rows of one block, all in the
+      // context: one address, four loads with immediate offsets
+      const int64_t row = ((int64_t)ent[0] * a.H + h) * BS + (kt * BN + KPW * w) % BS + tok_in_inst;
+      const uint32_t m = lds_addr(dst + row_base(KPW * w, is_v));
+      const uint32_t gap = is_v ? 0 : kKGroupBytes - 4 * kRowBytes;  // LDS bytes between pieces beyond 1 KiB
+      load4_to_lds(pool + row * (kD / 8) + cpos, m, m + gap, m + 2 * gap, m + 3 * gap);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int t0 = KPW * w + 4 * i;  // first tile token of this instruction (wave-uniform)
       const int phys = ent[NE == 1 ? 0 : i];
-      const int t = t0 + tok_in_inst;
-      const int jk = kt * BN + t;
+      const int jk = kt * BN + t0 + tok_in_inst;
       const int64_t row = jk < ctx ? ((int64_t)phys * a.H + h) * BS + jk % BS : last_row;
-      const int cpos = chunk_pos ^ (is_v ? v_swz(t) : k_swz(t));
-      load_to_lds(pool + row * (kD / 8) + cpos, lds_addr(dst + t0 * kRowBytes));
+      load_to_lds(pool + row * (kD / 8) + cpos, lds_addr(dst + row_base(t0, is_v)));
     }
   };
 
@@ -308,7 +340,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BN == 3
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         const int t = 32 * mb + col;
-        const u32x4 ka = *(const u32x4*)&tk[t * kRowBytes + 16 * ((2 * ks + g) ^ k_swz(t))];
+        const u32x4 ka = *(const u32x4*)&tk[k_off(t, 2 * ks + g)];
         acc_s[mb] = mfma32(E{}, ka, qop[ks], acc_s[mb]);
       }
   };
@@ -371,7 +403,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BN == 3
 #pragma unroll
           for (int half = 0; half < 2; ++half) {
             const int tok = 32 * mb + 16 * t + 8 * half + 4 * (grp >> 1) + (r16 >> 2);
-            const uint8_t* p = &tv[tok * kRowBytes + 16 * ((d >> 3) ^ v_swz(tok)) + 2 * (d & 7)];
+            const uint8_t* p = &tv[v_off(tok, d >> 3) + 2 * (d & 7)];
             const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
             const u32x2 xw = __builtin_bit_cast(u32x2, x);
             va[2 * half] = xw.x;
