@@ -232,6 +232,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BN == 3
   const int qrow = q0 + 32 * w + col;
   const int qpos = pos0 + qrow;
 
+  // The block-table entries the first tile loads need (and the last
+  // token's, which keys past the context length load instead) are read
+  // first, together, so the first tiles can be requested before the queries
+  // and the LDS copy of the table have arrived.
+  constexpr int KPW0 = BN / NW;
+  constexpr int NE0 = BS >= KPW0 ? 1 : KPW0 / 4;
+  const int64_t trow = (int64_t)s * a.max_blocks;
+  const int raw_last = a.tables[trow + min((ctx - 1) / BS, a.max_blocks - 1)];
+  int raw_e0[NE0], raw_e1[NE0];
+#pragma unroll
+  for (int i = 0; i < NE0; ++i) {
+    raw_e0[i] = a.tables[trow + min((KPW0 * w + 4 * i) / BS, a.max_blocks - 1)];
+    raw_e1[i] = a.tables[trow + min((BN + KPW0 * w + 4 * i) / BS, a.max_blocks - 1)];
+  }
+
   // B operands of S^T = K Q^T: Q[query][16ks + 8g .. +8] for k-steps ks = 0..7
   u32x4 qop[8];
   {
@@ -254,7 +269,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BN == 3
   // keys needed by the workgroup: positions 0 .. pos0 + min(q0 + kBM, qlen) - 1
   const int last_pos = pos0 + min(q0 + kBM, qlen) - 1;
   const int nkt = last_pos / BN + 1;
-  const int64_t trow = (int64_t)s * a.max_blocks;
 
   // tiles whose keys all precede every query of the workgroup need no mask
   const int n_full = min(nkt, (pos0 + q0 + 1) / BN);
@@ -274,15 +288,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BN == 3
   // the context length are redirected below).
   auto clamp_phys = [&](const int e) { return (e >= 0 && e < a.N) ? e : 0; };
   const int n_tab = min(min(nkt * BN, ctx) - 1, (a.max_blocks - 1) * BS) / BS + 1;
-  for (int i = tid; i < min(n_tab, kTabCache); i += NW * 64) lds_tab[i] = clamp_phys(a.tables[trow + i]);
-  // (published by the barrier that follows the first tile loads)
   auto entry = [&](const int blk) -> int {
     const int b = min(blk, a.max_blocks - 1);
     return b < kTabCache ? lds_tab[b] : clamp_phys(a.tables[trow + b]);
   };
-  auto entry_global = [&](const int blk) -> int { return clamp_phys(a.tables[trow + min(blk, a.max_blocks - 1)]); };
-  const int64_t last_row = ((int64_t)clamp_phys(a.tables[trow + min((ctx - 1) / BS, a.max_blocks - 1)]) * a.H + h) *
-                               BS + (ctx - 1) % BS;
+  const int64_t last_row = ((int64_t)clamp_phys(raw_last) * a.H + h) * BS + (ctx - 1) % BS;
 
   // ---- tile loads: wave w brings tokens KPW*w .. KPW*w + KPW-1 of a tile,
   // four (1 KiB) per instruction; lane -> token 4i + lane/16, chunk position
@@ -299,12 +309,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BN == 3
 #pragma unroll
     for (int i = 0; i < NE; ++i) ent[i] = __builtin_amdgcn_readfirstlane(entry((kt * BN + KPW * w + 4 * i) / BS));
   };
-  // the same, read from global memory (before the LDS copy is published)
-  auto entries_global = [&](const int kt, int* ent) {
-#pragma unroll
-    for (int i = 0; i < NE; ++i)
-      ent[i] = __builtin_amdgcn_readfirstlane(entry_global((kt * BN + KPW * w + 4 * i) / BS));
-  };
+  static_assert(NE == NE0 && KPW == KPW0, "early table reads cover the first tiles");
   // LDS byte offset of the first row of tile token t0 (a multiple of 4)
   auto row_base = [&](const int t0, const bool is_v) { return is_v ? t0 * kRowBytes : t0 / 4 * kKGroupBytes; };
   auto issue = [&](const u32x4* pool, uint8_t* dst, const int kt, const int* ent, const bool is_v) {
@@ -421,12 +426,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BN == 3
   // P(j) V(j), then waits for its loads and ends with a barrier.
   {
     int e0[NE], e1[NE];
-    entries_global(0, e0);
-    entries_global(1, e1);
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+      e0[i] = __builtin_amdgcn_readfirstlane(clamp_phys(raw_e0[i]));
+      e1[i] = __builtin_amdgcn_readfirstlane(clamp_phys(raw_e1[i]));
+    }
     issue(a.kpool, lds_k[0], 0, e0, false);
     issue(a.vpool, lds_v[0], 0, e0, true);
     if (nkt > 1) issue(a.kpool, lds_k[1], 1, e1, false);
   }
+  // the LDS copy of the block table, published by the barrier below
+  for (int i = tid; i < min(n_tab, kTabCache); i += NW * 64) lds_tab[i] = clamp_phys(a.tables[trow + i]);
   wait_vmem();
   lds_barrier();  // K(0), V(0), K(1) and the block-table copy are visible
   f32x16 s_cur[MB];
