@@ -14,13 +14,14 @@
  *   [P2] "vLLM" notes (formulaic.cloudchewie.com), "PagedAttention 原理" and
  *        "在不同解码策略下的效果".
  *   [P3] "vLLM / PagedAttention (SOSP 2023)" guide (upskillscore),
- *        sections 03-04.
+ *        sections 03-05.
  *
  * Conventions shared by every call
  * --------------------------------
- * - All data pointers are DEVICE pointers owned by the caller; the library
- *   never allocates or frees device memory, never synchronises, and keeps no
- *   global mutable state except a thread-local "last error" string.
+ * - All data pointers are DEVICE pointers owned by the caller (the one
+ *   exception: the pinned host pools of pa_swap_blocks); the library never
+ *   allocates or frees memory, never synchronises, and keeps no global
+ *   mutable state except a thread-local "last error" string.
  * - Every compute call is asynchronous on `stream` (a hipStream_t passed as
  *   void*; NULL is the default stream).  Buffers must stay alive until the
  *   stream has executed the call.
@@ -194,6 +195,10 @@ pa_status pa_paged_decode_grouped(const pa_kv_cache* cache, void* out, pa_dtype 
  *                  last q_len_s logical positions of the sequence.
  *   max_q_len, max_context_len  host-side upper bounds.
  *   scale          score scale, finite and > 0 (PA_ERR_INVALID_ARG otherwise).
+ *   out_dtype      the cache dtype or PA_F32.
+ * Built for head_dim 128, bf16 and fp16 caches, block_size 16, 32, 64 and
+ * 128 (MFMA tiles of 128 queries x 64 keys); other descriptions return
+ * PA_ERR_UNSUPPORTED.  Queries whose q_len is 0 produce no rows.
  */
 pa_status pa_paged_prefill(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, const void* query,
                            const int32_t* block_tables, int32_t max_blocks_per_seq,
