@@ -330,6 +330,7 @@ __global__ __launch_bounds__((DecodeCfg<E, D, BS>::NW * 64)) PA_DECODE_OCC void 
 #define PA_GROUP_PT 512  // tokens per partition of the grouped kernel
 #endif
 constexpr int kGroupWaves = PA_GROUP_NW;
+constexpr float kGroupSlack = 8.0f;  // lazy-rescale slack of the grouped kernel, log2 units
 constexpr int kGroupTokens = PA_GROUP_PT;
 
 template <typename E, int D, int BS, int W>
@@ -378,8 +379,12 @@ __global__ __launch_bounds__(kGroupWaves * 64) void decode_grouped_kernel(Decode
     for (int e = 0; e < VEC; ++e) o[r][e] = 0.f;
   }
 
-  // online-softmax update of row r with one step's chunks
-  auto update = [&](const int r, const u32x4* kc, const u32x4* vc, const bool* valid) {
+  // online-softmax update of row r with one step's chunks (values already
+  // widened, once for all the rows that share them).  Lazy rescale: a lane's
+  // reference max only moves when its max grows by more than kGroupSlack
+  // (log2 units), so weights stay below 2^kGroupSlack and most steps skip
+  // the rescale; numerator and denominator share the reference.
+  auto update = [&](const int r, const u32x4* kc, const float (*vf)[VEC], const bool* valid) {
     float sc[NCH];
     float mblk = kNegBig;
 #pragma unroll
@@ -388,21 +393,22 @@ __global__ __launch_bounds__(kGroupWaves * 64) void decode_grouped_kernel(Decode
       sc[i] = valid[i] ? d : -__builtin_inff();
       mblk = fmaxf(mblk, sc[i]);
     }
-    const float m_new = fmaxf(m[r], mblk);
-    const float alpha = fast_exp2(m[r] - m_new);
-    l[r] *= alpha;
+    const bool raise = mblk > m[r] + kGroupSlack;
+    if (__any(raise)) {
+      const float m_new = raise ? mblk : m[r];
+      const float alpha = fast_exp2(m[r] - m_new);
+      l[r] *= alpha;
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) o[r][e] *= alpha;
+      for (int e = 0; e < VEC; ++e) o[r][e] *= alpha;
+      m[r] = m_new;
+    }
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const float pi = fast_exp2(sc[i] - m_new);
+      const float pi = fast_exp2(sc[i] - m[r]);
       l[r] += pi;
-      float vf[VEC];
-      widen(E{}, vc[i], vf);
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) o[r][e] = __builtin_fmaf(pi, vf[e], o[r][e]);
+      for (int e = 0; e < VEC; ++e) o[r][e] = __builtin_fmaf(pi, vf[i][e], o[r][e]);
     }
-    m[r] = m_new;
   };
 
   const int nsteps = min(STEPS, (maxctx - p * P + G - 1) / G);
@@ -428,8 +434,11 @@ __global__ __launch_bounds__(kGroupWaves * 64) void decode_grouped_kernel(Decode
         vc[i] = load_kv(&a.vpool[base + i * TPL * LPT]);
         valid[i] = true;
       }
+      float vf[NCH][VEC];
 #pragma unroll
-      for (int r = 0; r < W; ++r) update(r, kc, vc, valid);
+      for (int i = 0; i < NCH; ++i) widen(E{}, vc[i], vf[i]);
+#pragma unroll
+      for (int r = 0; r < W; ++r) update(r, kc, vf, valid);
     } else {
 #pragma unroll
       for (int r = 0; r < W; ++r) {
@@ -442,7 +451,10 @@ __global__ __launch_bounds__(kGroupWaves * 64) void decode_grouped_kernel(Decode
           kc[i] = valid[i] ? load_kv(&a.kpool[base + i * TPL * LPT]) : u32x4{0, 0, 0, 0};
           vc[i] = valid[i] ? load_kv(&a.vpool[base + i * TPL * LPT]) : u32x4{0, 0, 0, 0};
         }
-        update(r, kc, vc, valid);
+        float vf[NCH][VEC];
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) widen(E{}, vc[i], vf[i]);
+        update(r, kc, vf, valid);
       }
     }
   }
