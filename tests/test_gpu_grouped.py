@@ -121,3 +121,28 @@ def test_shape_without_grouped_build_falls_back():
     ref = np.stack([oa.decode(inputs.to_f64(b.q[s]), inputs.to_f64(b.k_hist[s]), inputs.to_f64(b.v_hist[s]))
                     for s in range(b.S)])
     check_close(out, ref, TOL["bf16"], "fallback")
+
+
+@pytest.mark.parametrize("W", [2, 4])
+def test_rising_scores_force_rescales(W):
+    gen = torch.Generator().manual_seed(7601)  # seeded inputs
+    # keys aligned with the query and growing along the sequence: the running
+    # max keeps moving by many powers of two, so the lazy rescale path runs
+    # over and over (random inputs almost never take it after the first tiles)
+    H, d, B = 2, 128, 16
+    lens = [700] * W
+    b = workloads.build_decode_batch(11, lens, num_heads=H, head_dim=d, block_size=B, dtype="f32", nan_fill=True)
+    u = torch.randn(generator=gen, size=(H, d), dtype=torch.float32)
+    u = u / u.norm(dim=-1, keepdim=True)
+    ramp = torch.linspace(-60.0, 60.0, 700).view(700, 1, 1)          # score range ~ 120 / sqrt(128) * log2e
+    k = (ramp * u.view(1, H, d) + 0.1 * torch.randn(generator=gen, size=(700, H, d))).to(torch.float32)
+    v = torch.randn(generator=gen, size=(700, H, d), dtype=torch.float32)
+    slots = np.concatenate([[b.manager.slot(s, p) for p in range(700)] for s in range(W)]).astype(np.int64)
+    L.pa_reshape_and_cache(b.cache, torch.cat([k] * W).cuda(), torch.cat([v] * W).cuda(), torch.from_numpy(slots).cuda())
+    q = (u.view(1, H, d) * 8.0).repeat(W, 1, 1)
+    ws = L.decode_grouped_workspace(b.cache, W, 700, W)
+    out = torch.empty((W, H, d), dtype=torch.float32, device="cuda")
+    L.pa_paged_decode_grouped(b.cache, out, q.cuda(), b.tables_dev, b.lens_dev, 700, b.scale, W, ws)
+    torch.cuda.synchronize()
+    ref = np.stack([oa.decode(inputs.to_f64(q[s]), inputs.to_f64(k), inputs.to_f64(v)) for s in range(W)])
+    check_close(out, ref, TOL["f32"] * 10, f"rising scores W={W}")

@@ -93,6 +93,30 @@ def test_opt66b_prefill_full_size_sampled():
         check_close(got, ref, TOL["bf16"], f"OPT-66B prefill seq {s}")
 
 
+@pytest.mark.parametrize("direction", [1.0, -1.0])
+def test_rising_and_falling_scores(direction):
+    gen = torch.Generator().manual_seed(7602)  # seeded inputs
+    # queries and keys aligned, key magnitude ramping along the prompt: with
+    # rising scores the running max moves by many powers of two from tile to
+    # tile (the lazy rescale runs repeatedly); with falling ones the first
+    # keys dominate and later weights underflow
+    H, d, n = 2, 128, 600
+    b = workloads.build_prefill_batch(12, [n], [n], num_heads=H, head_dim=d, block_size=16, dtype="bf16")
+    u = torch.randn(generator=gen, size=(H, d), dtype=torch.float32)
+    u = u / u.norm(dim=-1, keepdim=True)
+    ramp = direction * torch.linspace(-40.0, 40.0, n).view(n, 1, 1)
+    k = (ramp * u.view(1, H, d) + 0.1 * torch.randn(generator=gen, size=(n, H, d))).to(torch.bfloat16)
+    v = torch.randn(generator=gen, size=(n, H, d)).to(torch.bfloat16)
+    q = (4.0 * u.view(1, H, d) + 0.1 * torch.randn(generator=gen, size=(n, H, d))).to(torch.bfloat16)
+    slots = np.array([b.manager.slot(0, p) for p in range(n)], dtype=np.int64)
+    L.pa_reshape_and_cache(b.cache, k.cuda(), v.cuda(), torch.from_numpy(slots).cuda())
+    out = torch.empty((n, H, d), dtype=torch.float32, device="cuda")
+    L.pa_paged_prefill(b.cache, out, q.cuda(), b.tables_dev, b.cu_q_dev, b.lens_dev, n, n, b.scale)
+    torch.cuda.synchronize()
+    ref = oa.prefill(inputs.to_f64(q), inputs.to_f64(k), inputs.to_f64(v), b.scale)
+    check_close(out, ref, TOL["bf16"], f"ramped scores {direction:+.0f}")
+
+
 @pytest.mark.parametrize("B,qlen", [(16, 33000), (16, 300), (32, 1200)])
 def test_long_prompt_past_the_table_cache(B, qlen):
     # a 33000-token history needs 2063 blocks of 16, more than the workgroup's

@@ -84,7 +84,8 @@ def test_preemption_round_trip_then_decode():
     L.pa_swap_blocks(cache, host_k, host_v, torch.from_numpy(m.swap_out([0, 3])).cuda(), L.PA_SWAP_OUT)
     assert m.used() == before - len(set(m.swapped[0][0].tolist()) | set(m.swapped[3][0].tolist()))
     n_free = m.num_free
-    junk = torch.randn((n_free * B, H, d), device="cuda").to(torch.float16)
+    gen = torch.Generator(device="cuda").manual_seed(7603)
+    junk = torch.randn((n_free * B, H, d), device="cuda", generator=gen).to(torch.float16)
     L.pa_reshape_and_cache(cache, junk, junk, torch.from_numpy(m.add_prompt(4, n_free * B)).cuda())
     m.free(4)
     L.pa_swap_blocks(cache, host_k, host_v, torch.from_numpy(m.swap_in([3, 0])).cuda(), L.PA_SWAP_IN)
