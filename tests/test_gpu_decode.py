@@ -27,7 +27,9 @@ DT = inputs.DTYPES
 
 def _run(batch, out_dtype=torch.float32, tables=None):
     ws = L.decode_workspace(batch.cache, batch.S, batch.max_context_len)
-    out = torch.empty((batch.S, batch.cache.num_heads, batch.cache.head_dim), dtype=out_dtype, device="cuda")
+    # NaN-filled: a (sequence, head) row that no workgroup writes fails the check
+    out = torch.full((batch.S, batch.cache.num_heads, batch.cache.head_dim), float("nan"), dtype=out_dtype,
+                     device="cuda")
     L.pa_paged_decode(batch.cache, out, batch.q_dev, batch.tables_dev if tables is None else tables,
                       batch.lens_dev, batch.max_context_len, batch.scale, ws)
     torch.cuda.synchronize()
@@ -68,6 +70,23 @@ def test_shapes(dtype, d, B):
     lens = [1, B - 1 if B > 1 else 1, B, B + 1, 63, 64, 65, 300, 777]
     b = workloads.build_decode_batch(3, lens, num_heads=3, head_dim=d, block_size=B, dtype=dtype)
     check_close(_run(b), _oracle(b), TOL[dtype], f"decode {dtype} d={d} B={B}")
+
+
+@pytest.mark.parametrize("case", ["mixed", "long_32k", "many_sequences"])
+def test_every_row_written_once(case):
+    # The grid covers (sequence, partition, head) items, most of them empty or
+    # short in these mixes; every (sequence, head) row must come out right.
+    rng = np.random.default_rng(7604)
+    if case == "mixed":  # ties, every step count of a partition, empty second partitions
+        lens = np.concatenate([rng.integers(1, 2049, 40), [1, 16, 17, 1024, 1025, 2048, 2048, 1040],
+                               np.full(16, 700)])
+    elif case == "long_32k":  # 32 partitions for the longest sequence
+        lens = np.concatenate([[32768], rng.integers(1, 32769, 15)])
+    else:  # 260 sequences
+        lens = rng.integers(1, 2049, 260)
+    print(f"decode rows {case}: S={len(lens)} max ctx {int(lens.max())}", flush=True)
+    b = workloads.build_decode_batch(5, lens.tolist(), num_heads=2, head_dim=128, block_size=16, dtype="f16")
+    check_close(_run(b), _oracle(b), TOL["f16"], f"decode rows {case}")
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
