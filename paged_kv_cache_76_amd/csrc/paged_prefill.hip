@@ -217,35 +217,43 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BN == 3
   const int tile = a.ntiles - 1 - gr / gn;
   const int s = pair / a.H;
   const int h = pair % a.H;
-  const int q_begin = a.cu_q[s];
-  const int qlen = a.cu_q[s + 1] - q_begin;
-  const int ctx = a.lens[s];
-  const int q0 = tile * kBM;  // first query row of this workgroup (within the sequence)
-  if (q0 >= qlen || qlen > ctx) return;
-  const int pos0 = ctx - qlen;  // logical position of query row 0
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 5;     // half-wave
-  const int col = lane & 31;   // this lane's query column
-  const int qrow = q0 + 32 * w + col;
-  const int qpos = pos0 + qrow;
 
-  // The block-table entries the first tile loads need (and the last
-  // token's, which keys past the context length load instead) are read
-  // first, together, so the first tiles can be requested before the queries
-  // and the LDS copy of the table have arrived.
+  // Everything the first tile loads depend on -- the query range, the
+  // context length and the block-table entries of the first two tiles and of
+  // token 0 -- is read in one batch with a single wait: these reads do not
+  // depend on each other, and a chain of dependent reads at the start of
+  // every workgroup would leave it idle for several memory round trips.
   constexpr int KPW0 = BN / NW;
   constexpr int NE0 = BS >= KPW0 ? 1 : KPW0 / 4;
   const int64_t trow = (int64_t)s * a.max_blocks;
-  const int raw_last = a.tables[trow + min((ctx - 1) / BS, a.max_blocks - 1)];
+  const int q_begin = a.cu_q[s];
+  const int q_end = a.cu_q[s + 1];
+  const int ctx = a.lens[s];
+  const int raw_first = a.tables[trow];
   int raw_e0[NE0], raw_e1[NE0];
 #pragma unroll
   for (int i = 0; i < NE0; ++i) {
     raw_e0[i] = a.tables[trow + min((KPW0 * w + 4 * i) / BS, a.max_blocks - 1)];
     raw_e1[i] = a.tables[trow + min((BN + KPW0 * w + 4 * i) / BS, a.max_blocks - 1)];
   }
+  // keeps the compiler from sinking the reads above past the early exit
+  // below (which would serialise them again)
+  asm volatile("" ::"s"(q_begin), "s"(q_end), "s"(ctx), "s"(raw_first));
+#pragma unroll
+  for (int i = 0; i < NE0; ++i) asm volatile("" ::"s"(raw_e0[i]), "s"(raw_e1[i]));
+
+  const int qlen = q_end - q_begin;
+  const int q0 = tile * kBM;  // first query row of this workgroup (within the sequence)
+  if (q0 >= qlen || qlen > ctx) return;
+  const int pos0 = ctx - qlen;  // logical position of query row 0
+
+  const int g = lane >> 5;     // half-wave
+  const int col = lane & 31;   // this lane's query column
+  const int qrow = q0 + 32 * w + col;
+  const int qpos = pos0 + qrow;
 
   // B operands of S^T = K Q^T: Q[query][16ks + 8g .. +8] for k-steps ks = 0..7
   u32x4 qop[8];
@@ -292,13 +300,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BN == 3
     const int b = min(blk, a.max_blocks - 1);
     return b < kTabCache ? lds_tab[b] : clamp_phys(a.tables[trow + b]);
   };
-  const int64_t last_row = ((int64_t)clamp_phys(raw_last) * a.H + h) * BS + (ctx - 1) % BS;
+  const int64_t first_row = ((int64_t)clamp_phys(raw_first) * a.H + h) * BS;  // token 0 (ctx >= 1)
 
   // ---- tile loads: wave w brings tokens KPW*w .. KPW*w + KPW-1 of a tile,
   // four (1 KiB) per instruction; lane -> token 4i + lane/16, chunk position
-  // lane % 16.  Tokens at or past the context length load the last token
-  // instead: finite data, whose scores the causal mask removes and whose
-  // weights are then exactly zero.
+  // lane % 16.  Tokens at or past the context length load the sequence's
+  // token 0 instead: finite data, whose scores the causal mask removes and
+  // whose weights are then exactly zero.
   const int tok_in_inst = lane >> 4;
   const int chunk_pos = lane & 15;
   // physical blocks of this wave's tokens in tile kt (one per four tokens;
@@ -328,7 +336,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BN == 3
       const int t0 = KPW * w + 4 * i;  // first tile token of this instruction (wave-uniform)
       const int phys = ent[NE == 1 ? 0 : i];
       const int jk = kt * BN + t0 + tok_in_inst;
-      const int64_t row = jk < ctx ? ((int64_t)phys * a.H + h) * BS + jk % BS : last_row;
+      const int64_t row = jk < ctx ? ((int64_t)phys * a.H + h) * BS + jk % BS : first_row;
       load_to_lds(pool + row * (kD / 8) + cpos, lds_addr(dst + row_base(t0, is_v)));
     }
   };
