@@ -112,12 +112,27 @@ def cpu_baseline(batch, n_seq: int, repeats: int = 10) -> dict:
         times.append(time.perf_counter() - t0)
     dt = sorted(times)[len(times) // 2]
     nbytes = workloads.decode_bytes(batch.lens[:n_seq], H, D, ELEM, B)
+    # the same sample with the BLAS pool held to one thread (median of 3)
+    from threadpoolctl import threadpool_limits
+
+    times1 = []
+    with threadpool_limits(limits=1):
+        for _ in range(3):
+            t0 = time.perf_counter()
+            for s in range(n_seq):
+                oa.decode(qs[s], ks[s], vs[s], batch.scale)
+            times1.append(time.perf_counter() - t0)
+    dt1 = sorted(times1)[1]
+    # the reported value is the faster of the two runs, with the threads it used
+    best, threads = (dt, blas_threads()) if dt < dt1 else (dt1, 1)
     return {
-        "value": nbytes / dt / 1e9, "unit": "GB/s", "cores": blas_threads(),
+        "value": nbytes / best / 1e9, "unit": "GB/s", "cores": threads,
         "kind": "oracle",
         "sample": f"{n_seq} of {S} sequences (all {H} heads, contexts {int(batch.lens[:n_seq].sum())} tokens), "
-                  f"one decode step, median of {repeats}, float64 NumPy on {os.cpu_count()} host cores ({cpu_model()})",
-        "seq_steps_per_s": n_seq / dt, "seconds": dt,
+                  f"one decode step, float64 NumPy on a {os.cpu_count()}-core host ({cpu_model()}); "
+                  f"median of {repeats} with {blas_threads()} BLAS threads, of 3 with 1",
+        "seq_steps_per_s": n_seq / best, "seconds": best,
+        "GBps_by_threads": {str(blas_threads()): nbytes / dt / 1e9, "1": nbytes / dt1 / 1e9},
     }
 
 
@@ -163,6 +178,29 @@ def copy_calibration(args) -> int:
 PEAK_BF16_TFLOPS = 2500.0
 
 
+def gemm_ceiling(n: int = 8192, reps: int = 10) -> dict:
+    """A measured dense bf16 ceiling: torch.matmul (hipBLASLt) of two
+    contiguous n x n bf16 matrices, median of ``reps`` after warm-up."""
+    import torch
+
+    gen = torch.Generator(device="cuda").manual_seed(76005)
+    a = torch.randn((n, n), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    b = torch.randn((n, n), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    c = torch.empty((n, n), device="cuda", dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record()
+        torch.matmul(a, b, out=c)
+        e1.record()
+    torch.cuda.synchronize()
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)[reps // 2]
+    del a, b, c
+    return {"kernel": f"torch.matmul bf16 {n}x{n}x{n}", "tflops": round(2 * n ** 3 / (ms * 1e-3) / 1e12, 1)}
+
+
 def prefill_bench(args) -> int:
     """8 prompts x 1024 tokens, 72 heads, d=128, bf16, block 16 (OPT-66B
     layer shape): one step writes the prompts' K/V through their slots and runs
@@ -202,6 +240,8 @@ def prefill_bench(args) -> int:
     tflops = flops / (p_ms * 1e-3) / 1e12
     log(f"prefill {p_ms * 1e3:.1f} us -> {tflops:.1f} TFLOP/s; write {w_ms * 1e3:.1f} us -> "
         f"{wbytes / (w_ms * 1e-3) / 1e9:.0f} GB/s")
+    gemm = gemm_ceiling()
+    log(f"dense bf16 GEMM ceiling on this GPU: {gemm['tflops']:.0f} TFLOP/s")
     cpu = None
     if args.cpu_seqs > 0:
         # the float64 oracle on a bounded sample: sequence 0, all heads, every query
@@ -232,6 +272,7 @@ def prefill_bench(args) -> int:
                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                         "traffic": measured_traffic(PREFILL_COUNTERS, PREFILL_SOURCES, ("prefill_kernel",)),
                         "avg_launch_us": round(p_ms * 1e3, 2), "algorithmic_flops_per_launch": flops},
+           "gemm_ceiling": dict(gemm, pct_achieved=round(100 * tflops / gemm["tflops"], 2)),
            "write": {"kernel": "pa_reshape_and_cache", "avg_launch_us": round(w_ms * 1e3, 2),
                      "achieved_GBps": round(wbytes / (w_ms * 1e-3) / 1e9, 1), "bytes_per_launch": wbytes},
            "cpu_baseline": cpu}
@@ -732,6 +773,8 @@ def main() -> int:
     value = step_bytes / elapsed / 1e9
     ms_per_step = elapsed / K * 1e3
     dec_avg_ms = sum(dec_ms) / K
+    dec_sorted = sorted(dec_ms)
+    pct = lambda q: dec_sorted[min(K - 1, int(q * K))] * 1e3
     dec_gbs = (sum(dec_bytes) / K) / (dec_avg_ms * 1e-3) / 1e9
     log(f"step {ms_per_step:.3f} ms, decode {dec_avg_ms * 1e3:.1f} us -> {dec_gbs:.0f} GB/s")
 
@@ -764,6 +807,7 @@ def main() -> int:
         "roofline": {"bound": "hbm", "kernel": "pa_paged_decode (partition + merge kernels)", "achieved": round(dec_gbs, 2),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
                      "traffic": traffic, "avg_launch_us": round(dec_avg_ms * 1e3, 2),
+                     "launch_us_p10_p50_p90": [round(pct(0.1), 2), round(pct(0.5), 2), round(pct(0.9), 2)],
                      "algorithmic_bytes_per_launch": int(sum(dec_bytes) / K)},
         "cpu_baseline": cpu,
     }
