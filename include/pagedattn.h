@@ -198,7 +198,9 @@ pa_status pa_paged_decode_grouped(const pa_kv_cache* cache, void* out, pa_dtype 
  *   out_dtype      the cache dtype or PA_F32.
  * Built for head_dim 128, bf16 and fp16 caches, block_size 16, 32, 64 and
  * 128 (MFMA tiles of 128 queries x 64 keys); other descriptions return
- * PA_ERR_UNSUPPORTED.  Queries whose q_len is 0 produce no rows.
+ * PA_ERR_UNSUPPORTED.  Queries whose q_len is 0 produce no rows.  The launch
+ * has S * num_heads * ceil(max_q_len / 128) workgroups of 256 threads, whose
+ * work-items must fit 32 bits (PA_ERR_INVALID_ARG otherwise).
  */
 pa_status pa_paged_prefill(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, const void* query,
                            const int32_t* block_tables, int32_t max_blocks_per_seq,

@@ -156,3 +156,5 @@ def test_prefill_argument_checks():
     d2 = _desc(dtype=L.PA_BF16, head_dim=64)
     assert lib.pa_paged_prefill(ctypes.byref(d2), FAKE, L.PA_BF16, FAKE, FAKE, 8, FAKE, FAKE, 2, 64, 100, 0.1,
                                 None) == L.PA_ERR_UNSUPPORTED
+    # a grid beyond the 32-bit launch limits is refused, not truncated
+    _err(call(S=1 << 20, maxq=1 << 14, maxctx=1 << 14, maxb=1 << 14), "launch limit")
