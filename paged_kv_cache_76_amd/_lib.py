@@ -153,6 +153,20 @@ class KVCache:
                        torch.empty(shape, dtype=dtype, device=device))
 
 
+def _device(cache: "KVCache", **tensors) -> None:
+    """The pools are GPU tensors on the current device, and every device
+    argument lives with them (a host or foreign pointer handed to a kernel
+    would fault the GPU rather than raise)."""
+    dev = cache.k.device
+    if dev.type != "cuda" or cache.v.device != dev:
+        raise ValueError(f"the k and v pools must be on one GPU, got {dev} and {cache.v.device}")
+    if dev.index is not None and dev.index != torch.cuda.current_device():
+        raise ValueError(f"the pools are on {dev} but the current device is cuda:{torch.cuda.current_device()}")
+    for name, t in tensors.items():
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} must be on {dev}, got {t.device}")
+
+
 def _contig(name: str, t: torch.Tensor, dtype=None) -> torch.Tensor:
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
@@ -170,6 +184,7 @@ def pa_reshape_and_cache(cache: KVCache, key: torch.Tensor, value: torch.Tensor,
     T = slot_mapping.numel()
     if key.shape != (T, cache.num_heads, cache.head_dim) or value.shape != key.shape:
         raise ValueError(f"key/value must be [{T}][{cache.num_heads}][{cache.head_dim}]")
+    _device(cache, key=key, value=value, slot_mapping=slot_mapping)
     d = cache.desc()
     _check(lib().pa_reshape_and_cache(ctypes.byref(d), _ptr(key), _ptr(value), _ptr(slot_mapping),
                                       T, _stream(stream)))
@@ -181,6 +196,7 @@ def pa_copy_blocks(cache: KVCache, pairs: torch.Tensor, stream=None) -> None:
     n = pairs.shape[0] if pairs.numel() else 0
     if pairs.numel() and (pairs.dim() != 2 or pairs.shape[1] != 2):
         raise ValueError("pairs must be [n][2]")
+    _device(cache, pairs=pairs)
     d = cache.desc()
     _check(lib().pa_copy_blocks(ctypes.byref(d), _ptr(pairs) if n else None, n, _stream(stream)))
 
@@ -195,7 +211,10 @@ def pa_swap_blocks(cache: KVCache, host_k: torch.Tensor, host_v: torch.Tensor, p
         _contig(name, t, cache.dtype)
         if t.shape[1:] != cache.k.shape[1:] or t.device.type != "cpu":
             raise ValueError(f"{name} must be a host tensor [blocks][H][B][d]")
+    if pairs.numel() and (pairs.dim() != 2 or pairs.shape[1] != 2):
+        raise ValueError("pairs must be [n][2]")
     n = pairs.shape[0] if pairs.numel() else 0
+    _device(cache, pairs=pairs)
     d = cache.desc()
     _check(lib().pa_swap_blocks(ctypes.byref(d), _ptr(host_k), _ptr(host_v), host_k.shape[0],
                                 _ptr(pairs) if n else None, n, int(direction), _stream(stream)))
@@ -230,6 +249,7 @@ def pa_paged_decode(cache: KVCache, out: torch.Tensor, query: torch.Tensor,
         raise ValueError("query/out must be [S][H][d]")
     if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
         raise ValueError("block_tables must be [S][max_blocks], context_lens [S]")
+    _device(cache, out=out, query=query, block_tables=block_tables, context_lens=context_lens, workspace=workspace)
     d = cache.desc()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().pa_paged_decode(ctypes.byref(d), _ptr(out), TORCH_TO_PA.get(out.dtype, -1), _ptr(query),
@@ -270,6 +290,7 @@ def pa_paged_decode_grouped(cache: KVCache, out: torch.Tensor, query: torch.Tens
         raise ValueError("query/out must be [S][H][d]")
     if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
         raise ValueError("block_tables must be [S][max_blocks], context_lens [S]")
+    _device(cache, out=out, query=query, block_tables=block_tables, context_lens=context_lens, workspace=workspace)
     d = cache.desc()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().pa_paged_decode_grouped(ctypes.byref(d), _ptr(out), TORCH_TO_PA.get(out.dtype, -1), _ptr(query),
@@ -289,8 +310,12 @@ def pa_paged_prefill(cache: KVCache, out: torch.Tensor, query: torch.Tensor,
     _contig("cu_q_lens", cu_q_lens, torch.int32)
     _contig("context_lens", context_lens, torch.int32)
     S = context_lens.shape[0]
-    if cu_q_lens.shape != (S + 1,) or out.shape != query.shape or block_tables.shape[0] != S:
+    if query.dim() != 3 or query.shape[1:] != (cache.num_heads, cache.head_dim):
+        raise ValueError(f"query must be [rows][{cache.num_heads}][{cache.head_dim}]")
+    if (cu_q_lens.shape != (S + 1,) or out.shape != query.shape or block_tables.dim() != 2
+            or block_tables.shape[0] != S):
         raise ValueError("cu_q_lens must be [S+1], block_tables [S][max_blocks], out like query")
+    _device(cache, out=out, query=query, block_tables=block_tables, cu_q_lens=cu_q_lens, context_lens=context_lens)
     d = cache.desc()
     _check(lib().pa_paged_prefill(ctypes.byref(d), _ptr(out), TORCH_TO_PA.get(out.dtype, -1), _ptr(query),
                                   _ptr(block_tables), block_tables.shape[1], _ptr(cu_q_lens),

@@ -171,3 +171,14 @@ def test_opt13b_decode_full_size_sampled():
     ref = _oracle(b, rows, heads)
     got = out[rows][:, heads]
     check_close(got, ref, TOL["f16"], "OPT-13B sampled")
+
+
+def test_host_arguments_are_refused():
+    # a host tensor beside device pools is refused before any launch
+    b = workloads.build_decode_batch(2, [5, 9], num_heads=2, head_dim=128, block_size=16, dtype="f16")
+    ws = L.decode_workspace(b.cache, b.S, b.max_context_len)
+    out = torch.empty((b.S, 2, 128), dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError, match="query must be on"):
+        L.pa_paged_decode(b.cache, out, b.q_dev.cpu(), b.tables_dev, b.lens_dev, b.max_context_len, b.scale, ws)
+    with pytest.raises(ValueError, match="block_tables must be on"):
+        L.pa_paged_decode(b.cache, out, b.q_dev, b.tables_dev.cpu(), b.lens_dev, b.max_context_len, b.scale, ws)
