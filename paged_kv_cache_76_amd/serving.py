@@ -275,7 +275,12 @@ class BeamLoop:
                 del self.hist[int(s)]
         self.cur, self.nxt = self.nxt, self.cur
 
-    def step(self, events=None) -> StepRecord:
+    def plan(self) -> dict:
+        """Host half of a step: the beam-search remap, the block manager's
+        append (slots and copy-on-write pairs), the new tokens' activations,
+        the history bookkeeping, and the upload of everything the kernels read.
+        Plans can be made ahead of their launches: the kernels' effect on the
+        pools depends only on the order in which the plans are launched."""
         if self.beam:
             self.remap()
         rows = self.cur
@@ -291,25 +296,36 @@ class BeamLoop:
                "q": q, "tables": torch.from_numpy(np.ascontiguousarray(self.mgr.tables[rows_sorted])),
                "lens": torch.from_numpy(lens)}
         dev = {k: t.to(self.device) for k, t in dev.items()}
-        out = torch.empty((n, self.H, self.d), dtype=TORCH[self.dtype], device=self.device)
-        if events is not None:
-            events[0].record()
-        if len(pairs):
-            pa_copy_blocks(self.cache, dev["pairs"])
-        pa_reshape_and_cache(self.cache, dev["k"], dev["v"], dev["slots"])
-        if self.grouped:
-            pa_paged_decode_grouped(self.cache, out, dev["q"], dev["tables"], dev["lens"], int(lens.max()),
-                                    self.scale, self.W, self.ws)
-        else:
-            pa_paged_decode(self.cache, out, dev["q"], dev["tables"], dev["lens"], int(lens.max()), self.scale,
-                            self.ws)
-        if events is not None:
-            events[1].record()
         if self.keep_history:
             for i, s in enumerate(rows_sorted):
                 self.hist[int(s)].k.append(k_new[i:i + 1])
                 self.hist[int(s)].v.append(v_new[i:i + 1])
-        return StepRecord(rows_sorted, lens, len(pairs), out, q)
+        return {"rows": rows_sorted, "lens": lens, "n_pairs": len(pairs), "dev": dev, "q": q,
+                "max_ctx": int(lens.max())}
+
+    def launch(self, plan: dict, events=None) -> StepRecord:
+        """Device half of a step: copy-on-write copies, the new tokens' cache
+        write and the decode, bracketed by ``events`` if given."""
+        dev = plan["dev"]
+        n = len(plan["rows"])
+        out = torch.empty((n, self.H, self.d), dtype=TORCH[self.dtype], device=self.device)
+        if events is not None:
+            events[0].record()
+        if plan["n_pairs"]:
+            pa_copy_blocks(self.cache, dev["pairs"])
+        pa_reshape_and_cache(self.cache, dev["k"], dev["v"], dev["slots"])
+        if self.grouped:
+            pa_paged_decode_grouped(self.cache, out, dev["q"], dev["tables"], dev["lens"], plan["max_ctx"],
+                                    self.scale, self.W, self.ws)
+        else:
+            pa_paged_decode(self.cache, out, dev["q"], dev["tables"], dev["lens"], plan["max_ctx"], self.scale,
+                            self.ws)
+        if events is not None:
+            events[1].record()
+        return StepRecord(plan["rows"], plan["lens"], plan["n_pairs"], out, plan["q"])
+
+    def step(self, events=None) -> StepRecord:
+        return self.launch(self.plan(), events)
 
     def unique_blocks_read(self, rows) -> int:
         """Distinct physical blocks the decode of ``rows`` reads."""
