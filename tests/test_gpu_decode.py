@@ -123,7 +123,7 @@ def test_tiny_worked_example_replica():
         L.pa_reshape_and_cache(cache, k_new.cuda(), v_new.cuda(), torch.from_numpy(slot).cuda())
         K, V = torch.cat([K, k_new]), torch.cat([V, v_new])
         ctx = 8 + step
-        out = torch.empty((1, H, d), dtype=torch.float32, device="cuda")
+        out = torch.full((1, H, d), float("nan"), dtype=torch.float32, device="cuda")
         L.pa_paged_decode(cache, out, q.cuda(), torch.from_numpy(mgr.tables).cuda(),
                           torch.tensor([ctx], dtype=torch.int32, device="cuda"), ctx, 1 / math.sqrt(d))
         torch.cuda.synchronize()
@@ -177,7 +177,7 @@ def test_host_arguments_are_refused():
     # a host tensor beside device pools is refused before any launch
     b = workloads.build_decode_batch(2, [5, 9], num_heads=2, head_dim=128, block_size=16, dtype="f16")
     ws = L.decode_workspace(b.cache, b.S, b.max_context_len)
-    out = torch.empty((b.S, 2, 128), dtype=torch.float32, device="cuda")
+    out = torch.full((b.S, 2, 128), float("nan"), dtype=torch.float32, device="cuda")
     with pytest.raises(ValueError, match="query must be on"):
         L.pa_paged_decode(b.cache, out, b.q_dev.cpu(), b.tables_dev, b.lens_dev, b.max_context_len, b.scale, ws)
     with pytest.raises(ValueError, match="block_tables must be on"):

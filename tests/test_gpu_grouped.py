@@ -90,7 +90,7 @@ def test_grouped_matches_oracle(share, W, dtype, B, prompt, tails):
     S = q.shape[0]
     scale = 1 / math.sqrt(d)
     ws = L.decode_grouped_workspace(cache, S, int(lens.max()), W)
-    out = torch.empty((S, H, d), dtype=torch.float32, device="cuda")
+    out = torch.full((S, H, d), float("nan"), dtype=torch.float32, device="cuda")
     L.pa_paged_decode_grouped(cache, out, q.cuda(), torch.from_numpy(mgr.tables).cuda(),
                               torch.from_numpy(lens).cuda(), int(lens.max()), scale, W, ws)
     torch.cuda.synchronize()
@@ -103,7 +103,7 @@ def test_any_grouping_of_unrelated_rows(W):
     lens = [1, 16, 17, 255, 256, 1000, 2049]
     b = workloads.build_decode_batch(9, lens, num_heads=3, head_dim=128, block_size=16, dtype="f16")
     ws = L.decode_grouped_workspace(b.cache, b.S, b.max_context_len, W)
-    out = torch.empty((b.S, 3, 128), dtype=torch.float32, device="cuda")
+    out = torch.full((b.S, 3, 128), float("nan"), dtype=torch.float32, device="cuda")
     L.pa_paged_decode_grouped(b.cache, out, b.q_dev, b.tables_dev, b.lens_dev, b.max_context_len, b.scale, W, ws)
     torch.cuda.synchronize()
     ref = np.stack([oa.decode(inputs.to_f64(b.q[s]), inputs.to_f64(b.k_hist[s]), inputs.to_f64(b.v_hist[s]))
@@ -115,7 +115,7 @@ def test_shape_without_grouped_build_falls_back():
     # head_dim 64 has no grouped build: the ungrouped kernel serves the call
     b = workloads.build_decode_batch(10, [5, 300, 40], num_heads=2, head_dim=64, block_size=16, dtype="bf16")
     ws = L.decode_grouped_workspace(b.cache, b.S, b.max_context_len, 4)
-    out = torch.empty((b.S, 2, 64), dtype=torch.float32, device="cuda")
+    out = torch.full((b.S, 2, 64), float("nan"), dtype=torch.float32, device="cuda")
     L.pa_paged_decode_grouped(b.cache, out, b.q_dev, b.tables_dev, b.lens_dev, b.max_context_len, b.scale, 4, ws)
     torch.cuda.synchronize()
     ref = np.stack([oa.decode(inputs.to_f64(b.q[s]), inputs.to_f64(b.k_hist[s]), inputs.to_f64(b.v_hist[s]))
@@ -141,7 +141,7 @@ def test_rising_scores_force_rescales(W):
     L.pa_reshape_and_cache(b.cache, torch.cat([k] * W).cuda(), torch.cat([v] * W).cuda(), torch.from_numpy(slots).cuda())
     q = (u.view(1, H, d) * 8.0).repeat(W, 1, 1)
     ws = L.decode_grouped_workspace(b.cache, W, 700, W)
-    out = torch.empty((W, H, d), dtype=torch.float32, device="cuda")
+    out = torch.full((W, H, d), float("nan"), dtype=torch.float32, device="cuda")
     L.pa_paged_decode_grouped(b.cache, out, q.cuda(), b.tables_dev, b.lens_dev, 700, b.scale, W, ws)
     torch.cuda.synchronize()
     ref = np.stack([oa.decode(inputs.to_f64(q[s]), inputs.to_f64(k), inputs.to_f64(v)) for s in range(W)])

@@ -15,7 +15,9 @@ pytestmark = pytest.mark.gpu
 
 
 def _run(b, out_dtype=torch.float32):
-    out = torch.empty((int(b.q_lens.sum()), b.cache.num_heads, b.cache.head_dim), dtype=out_dtype, device="cuda")
+    # NaN-filled: a row no workgroup writes fails the comparison
+    out = torch.full((int(b.q_lens.sum()), b.cache.num_heads, b.cache.head_dim), float("nan"), dtype=out_dtype,
+                     device="cuda")
     L.pa_paged_prefill(b.cache, out, b.q_dev, b.tables_dev, b.cu_q_dev, b.lens_dev, int(b.q_lens.max()),
                        int(b.lens.max()), b.scale)
     torch.cuda.synchronize()
@@ -110,7 +112,7 @@ def test_rising_and_falling_scores(direction):
     q = (4.0 * u.view(1, H, d) + 0.1 * torch.randn(generator=gen, size=(n, H, d))).to(torch.bfloat16)
     slots = np.array([b.manager.slot(0, p) for p in range(n)], dtype=np.int64)
     L.pa_reshape_and_cache(b.cache, k.cuda(), v.cuda(), torch.from_numpy(slots).cuda())
-    out = torch.empty((n, H, d), dtype=torch.float32, device="cuda")
+    out = torch.full((n, H, d), float("nan"), dtype=torch.float32, device="cuda")
     L.pa_paged_prefill(b.cache, out, q.cuda(), b.tables_dev, b.cu_q_dev, b.lens_dev, n, n, b.scale)
     torch.cuda.synchronize()
     ref = oa.prefill(inputs.to_f64(q), inputs.to_f64(k), inputs.to_f64(v), b.scale)
@@ -146,7 +148,7 @@ def test_shared_prefix_prefill_over_task_input_only(dtype, B, prefix, tasks):
     from oracle import cache as oc
     b = workloads.build_shared_prefix(11, prefix, tasks, num_heads=3, head_dim=128, block_size=B, dtype=dtype)
     assert b.copies == (len(tasks) if prefix % B else 0)
-    out = torch.empty((int(b.task_lens.sum()), 3, 128), dtype=torch.float32, device="cuda")
+    out = torch.full((int(b.task_lens.sum()), 3, 128), float("nan"), dtype=torch.float32, device="cuda")
     L.pa_paged_prefill(b.cache, out, b.q_dev, b.tables_dev, b.cu_q_dev, b.lens_dev, int(b.task_lens.max()),
                        int(b.lens.max()), b.scale)
     torch.cuda.synchronize()

@@ -79,7 +79,7 @@ def test_long_context_decode_32k_sampled():
     ld = workloads.build_long_decode(5, 16, 32768, 72, 128, 16, "bf16", samples=samples)
     from paged_kv_cache_76_amd import _lib as L
     ws = L.decode_workspace(ld.cache, 16, 32768)
-    out = torch.empty((16, 72, 128), dtype=torch.float32, device="cuda")
+    out = torch.full((16, 72, 128), float("nan"), dtype=torch.float32, device="cuda")
     L.pa_paged_decode(ld.cache, out, ld.q_dev, ld.tables_dev, ld.lens_dev, 32768, ld.scale, ws)
     torch.cuda.synchronize()
     assert torch.isfinite(out).all()

@@ -93,7 +93,7 @@ def test_preemption_round_trip_then_decode():
     ctx = m.lens[rows].astype(np.int32)
     tables = torch.from_numpy(np.ascontiguousarray(m.tables[rows])).cuda()
     q = inputs.normal(r_q, (4, H, d), "f16")
-    out = torch.empty((4, H, d), dtype=torch.float32, device="cuda")
+    out = torch.full((4, H, d), float("nan"), dtype=torch.float32, device="cuda")
     ws = L.decode_workspace(cache, 4, int(ctx.max()))
     L.pa_paged_decode(cache, out, q.cuda(), tables, torch.from_numpy(ctx).cuda(), int(ctx.max()),
                       d ** -0.5, ws)
