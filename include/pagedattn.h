@@ -190,6 +190,11 @@ pa_status pa_paged_decode_grouped(const pa_kv_cache* cache, void* out, pa_dtype 
  *
  *   query, out     [sum_s q_len_s][num_heads][head_dim]; rows of sequence s
  *                  are cu_q_lens[s] .. cu_q_lens[s+1]-1.
+ *   block_tables   int32 [S][max_blocks_per_seq] as for pa_paged_decode, except
+ *                  that entries at or beyond ceil(context_lens[s]/B) may be
+ *                  read (the first tiles' entries are fetched before the
+ *                  length is known) but are never used: the whole array must
+ *                  be readable.
  *   cu_q_lens      int32 [S+1], cu_q_lens[0] = 0, non-decreasing.
  *   context_lens   int32 [S]; q_len_s <= context_lens[s]; the queries are the
  *                  last q_len_s logical positions of the sequence.
