@@ -201,11 +201,14 @@ pa_status pa_paged_decode_grouped(const pa_kv_cache* cache, void* out, pa_dtype 
  *   max_q_len, max_context_len  host-side upper bounds.
  *   scale          score scale, finite and > 0 (PA_ERR_INVALID_ARG otherwise).
  *   out_dtype      the cache dtype or PA_F32.
- * Built for head_dim 128, bf16 and fp16 caches, block_size 16, 32, 64 and
- * 128 (MFMA tiles of 128 queries x 64 keys); other descriptions return
- * PA_ERR_UNSUPPORTED.  Queries whose q_len is 0 produce no rows.  The launch
- * has S * num_heads * ceil(max_q_len / 128) workgroups of 256 threads, whose
- * work-items must fit 32 bits (PA_ERR_INVALID_ARG otherwise).
+ * head_dim 128 with bf16 or fp16 caches and block_size 16, 32, 64 or 128
+ * runs on MFMA (tiles of 128 queries x 64 keys; S * num_heads *
+ * ceil(max_q_len / 128) workgroups of 256 threads).  Every other description
+ * with head_dim <= 512 (fp32 included, any block size) runs a generic kernel
+ * made for correctness rather than speed (one wave per query row and head:
+ * S * num_heads * max_q_len workgroups of 64 threads); head_dim > 512 returns
+ * PA_ERR_UNSUPPORTED.  The launch's work-items must fit 32 bits
+ * (PA_ERR_INVALID_ARG otherwise).  Queries whose q_len is 0 produce no rows.
  */
 pa_status pa_paged_prefill(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, const void* query,
                            const int32_t* block_tables, int32_t max_blocks_per_seq,

@@ -266,12 +266,11 @@ pa_status pa_paged_prefill(const pa_kv_cache* cache, void* out, pa_dtype out_dty
   if (!pa::prefill_supported(c.dtype, c.head_dim, c.block_size))
     return fail(PA_ERR_UNSUPPORTED, "%s: (dtype %d, head_dim %d, block_size %d) not built", fn, (int)c.dtype,
                 c.head_dim, c.block_size);
-  // one workgroup of 256 threads per (sequence, head, 128-query tile): the
-  // grid and its work-items must fit the launch's 32-bit limits
-  const int64_t prefill_wgs = ((int64_t)max_q_len + 127) / 128 * S * c.num_heads;
-  if (prefill_wgs * 256 > (int64_t)UINT32_MAX)
-    return fail(PA_ERR_INVALID_ARG, "%s: %lld workgroups (S x heads x query tiles) exceed the launch limit", fn,
-                (long long)prefill_wgs);
+  // the launch's work-items (S x heads x query tiles or rows) must fit 32 bits
+  const int64_t items = pa::prefill_work_items(c, S, max_q_len);
+  if (items > (int64_t)UINT32_MAX)
+    return fail(PA_ERR_INVALID_ARG, "%s: %lld work-items (S x heads x queries) exceed the launch limit", fn,
+                (long long)items);
   return launched(fn, pa::launch_paged_prefill(c, out, out_dtype, query, block_tables, max_blocks_per_seq,
                                                cu_q_lens, context_lens, S, max_q_len, max_context_len, scale,
                                                (hipStream_t)stream));

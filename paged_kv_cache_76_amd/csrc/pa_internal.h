@@ -53,6 +53,8 @@ hipError_t launch_paged_decode_grouped(const Cache& c, void* out, pa_dtype out_d
 
 // ---- prefill (paged_prefill.hip) ----------------------------------------------
 bool prefill_supported(pa_dtype dtype, int head_dim, int block_size);
+// work-items of the prefill launch for this cache description (32-bit limit)
+int64_t prefill_work_items(const Cache& c, int32_t S, int32_t max_q_len);
 hipError_t launch_paged_prefill(const Cache& c, void* out, pa_dtype out_dtype, const void* query,
                                 const int32_t* block_tables, int32_t max_blocks_per_seq,
                                 const int32_t* cu_q_lens, const int32_t* context_lens, int32_t S,

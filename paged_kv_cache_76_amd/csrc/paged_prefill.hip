@@ -506,6 +506,107 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BN == 3
     }
 }
 
+
+// ---- generic path --------------------------------------------------------------
+// Every cache description the MFMA kernel is not built for (fp32, other head
+// dims, small blocks) takes this kernel: one wave per (query row, head).  A
+// query row is the decode of its own position over the keys t <= position
+// (the same sum as above, [P1] key design 1 eq. 1, read through the table as
+// in eq. 2).  Lanes take 64 keys at a time for the scores (fp32 dot products
+// against the query held in LDS), the running max and sum are wave-wide, and
+// for P V the lanes take head dims.  Made for correctness on small shapes,
+// not for speed; a block id outside the pool contributes nothing.
+constexpr int kGenericMaxD = 512;
+
+__device__ __forceinline__ float load_elem(F32, const void* p, int64_t i) { return ((const float*)p)[i]; }
+__device__ __forceinline__ float load_elem(F16, const void* p, int64_t i) {
+  return (float)((const _Float16*)p)[i];
+}
+__device__ __forceinline__ float load_elem(BF16, const void* p, int64_t i) {
+  return __uint_as_float((uint32_t)((const uint16_t*)p)[i] << 16);
+}
+__device__ __forceinline__ float wave_max64(float x) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) x = fmaxf(x, __shfl_xor(x, off));
+  return x;
+}
+__device__ __forceinline__ float wave_sum64(float x) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+template <typename E>
+__global__ __launch_bounds__(64) void prefill_generic_kernel(PrefillArgs a, int32_t D, int32_t BS,
+                                                              int32_t max_q_len) {
+  constexpr int kSlots = kGenericMaxD / 64;  // head dims per lane
+  __shared__ float q_lds[kGenericMaxD];
+  __shared__ float p_lds[64];
+  __shared__ int64_t row_lds[64];
+  const int lane = threadIdx.x;
+  const int64_t bid = blockIdx.x;
+  const int h = (int)(bid % a.H);
+  const int64_t rest = bid / a.H;
+  const int i = (int)(rest % max_q_len);
+  const int s = (int)(rest / max_q_len);
+  const int q_begin = a.cu_q[s];
+  const int qlen = a.cu_q[s + 1] - q_begin;
+  const int ctx = a.lens[s];
+  if (i >= qlen || qlen > ctx) return;  // uniform for the wave
+  const int nkeys = ctx - qlen + i + 1;  // causal: positions 0 .. the query's own
+  const int64_t qrow = (int64_t)(q_begin + i) * a.H + h;
+  for (int d = lane; d < D; d += 64) q_lds[d] = load_elem(E{}, a.q, qrow * D + d);
+  __syncthreads();
+
+  float o[kSlots];
+#pragma unroll
+  for (int k = 0; k < kSlots; ++k) o[k] = 0.f;
+  float m = kNegBig, l = 0.f;  // running max (log2 units) and sum
+  const int64_t trow = (int64_t)s * a.max_blocks;
+  for (int t0 = 0; t0 < nkeys; t0 += 64) {
+    const int t = t0 + lane;
+    float sc = -__builtin_inff();
+    int64_t row = -1;
+    if (t < nkeys) {
+      const int phys = a.tables[trow + t / BS];
+      if (phys >= 0 && phys < a.N) {
+        row = ((int64_t)phys * a.H + h) * BS + t % BS;
+        float acc = 0.f;
+        for (int d = 0; d < D; ++d) acc = __builtin_fmaf(q_lds[d], load_elem(E{}, a.kpool, row * D + d), acc);
+        sc = acc * a.scale_log2;
+      }
+    }
+    const float m_new = fmaxf(m, wave_max64(sc));
+    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+    const float p = row >= 0 ? __builtin_amdgcn_exp2f(sc - m_new) : 0.f;
+    l = l * alpha + wave_sum64(p);
+    p_lds[lane] = p;
+    row_lds[lane] = row;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kSlots; ++k) o[k] *= alpha;
+    const int nj = min(64, nkeys - t0);
+    for (int j = 0; j < nj; ++j) {
+      const int64_t rj = row_lds[j];
+      if (rj < 0) continue;  // uniform: every lane reads the same entry
+      const float pj = p_lds[j];
+#pragma unroll
+      for (int k = 0; k < kSlots; ++k) {
+        const int d = lane + 64 * k;
+        if (d < D) o[k] = __builtin_fmaf(pj, load_elem(E{}, a.vpool, rj * D + d), o[k]);
+      }
+    }
+    m = m_new;
+    __syncthreads();
+  }
+  const float inv_l = 1.f / l;
+#pragma unroll
+  for (int k = 0; k < kSlots; ++k) {
+    const int d = lane + 64 * k;
+    if (d < D) store_out(a.out, qrow * D + d, o[k] * inv_l, a.out_dtype);
+  }
+}
+
 #ifndef PA_PREFILL_BN
 #define PA_PREFILL_BN 64  // keys per tile
 #endif
@@ -539,7 +640,14 @@ const Variant* find_variant(pa_dtype dtype, int head_dim, int block_size) {
 }  // namespace
 
 bool prefill_supported(pa_dtype dtype, int head_dim, int block_size) {
-  return find_variant(dtype, head_dim, block_size) != nullptr;
+  return find_variant(dtype, head_dim, block_size) != nullptr || (head_dim >= 1 && head_dim <= kGenericMaxD &&
+                                                                  block_size >= 1);
+}
+
+int64_t prefill_work_items(const Cache& c, int32_t S, int32_t max_q_len) {
+  if (find_variant(c.dtype, c.head_dim, c.block_size))
+    return ((int64_t)max_q_len + kTileQ - 1) / kTileQ * S * c.num_heads * (kNW * 64);
+  return (int64_t)max_q_len * S * c.num_heads * 64;
 }
 
 hipError_t launch_paged_prefill(const Cache& c, void* out, pa_dtype out_dtype, const void* query,
@@ -549,7 +657,7 @@ hipError_t launch_paged_prefill(const Cache& c, void* out, pa_dtype out_dtype, c
                                 hipStream_t stream) {
   (void)max_context_len;
   const Variant* v = find_variant(c.dtype, c.head_dim, c.block_size);
-  if (!v) return hipErrorInvalidValue;
+  if (!v && !prefill_supported(c.dtype, c.head_dim, c.block_size)) return hipErrorInvalidValue;
   PrefillArgs a;
   a.q = (const u32x4*)query;
   a.kpool = (const u32x4*)c.k;
@@ -565,6 +673,15 @@ hipError_t launch_paged_prefill(const Cache& c, void* out, pa_dtype out_dtype, c
   a.ntiles = (max_q_len + kTileQ - 1) / kTileQ;
   a.scale_log2 = scale * kLog2e;
   a.out_dtype = out_dtype;
+  if (!v) {
+    const int64_t grid = (int64_t)max_q_len * S * c.num_heads;
+    void (*k)(PrefillArgs, int32_t, int32_t, int32_t) =
+        c.dtype == PA_F32 ? prefill_generic_kernel<F32>
+                          : (c.dtype == PA_F16 ? prefill_generic_kernel<F16> : prefill_generic_kernel<BF16>);
+    hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(64), 0, stream, a, (int32_t)c.head_dim,
+                       (int32_t)c.block_size, max_q_len);
+    return hipGetLastError();
+  }
   const int64_t grid = (int64_t)a.ntiles * S * c.num_heads;
   hipLaunchKernelGGL(v->kernel, dim3((unsigned)grid), dim3(kNW * 64), 0, stream, a);
   return hipGetLastError();

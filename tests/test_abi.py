@@ -154,7 +154,8 @@ def test_prefill_argument_checks():
     _err(call(scale=float("nan")), "scale")
     _err(call(scale=0.0), "> 0")
     _err(call(scale=-0.1), "> 0")
-    d2 = _desc(dtype=L.PA_BF16, head_dim=64)
+    # head dims beyond the generic kernel's 512 are not built
+    d2 = _desc(dtype=L.PA_BF16, head_dim=1024)
     assert lib.pa_paged_prefill(ctypes.byref(d2), FAKE, L.PA_BF16, FAKE, FAKE, 8, FAKE, FAKE, 2, 64, 100, 0.1,
                                 None) == L.PA_ERR_UNSUPPORTED
     # a grid beyond the 32-bit launch limits is refused, not truncated

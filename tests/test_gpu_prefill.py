@@ -1,4 +1,4 @@
-"""GPU parity of pa_paged_prefill (MFMA) against the float64 oracle's causal
+"""GPU parity of pa_paged_prefill (the MFMA kernel and the generic one) against the float64 oracle's causal
 attention over the logically contiguous prompt."""
 
 import numpy as np
@@ -43,6 +43,28 @@ def test_prompt_lengths(dtype, B):
     out = _run(b)
     for s in range(len(lens)):
         check_close(out[b.cu_q[s]:b.cu_q[s + 1]], _oracle(b, s), TOL[dtype], f"prefill {dtype} B={B} seq {s}")
+
+
+@pytest.mark.parametrize("dtype,d,B", [("f32", 8, 4), ("f16", 64, 8), ("bf16", 256, 32), ("f32", 128, 16),
+                                       ("f16", 128, 4), ("bf16", 8, 8)])
+def test_generic_shapes(dtype, d, B):
+    # shapes the MFMA kernel is not built for take the generic kernel; full
+    # and partial prompts (q_len < context_len), lengths around block and
+    # 64-key boundaries
+    print(f"prefill generic {dtype} d={d} B={B}", flush=True)
+    lens = [1, 7, B - 1 if B > 1 else 1, B + 1, 64, 65, 130, 200]
+    qlens = [1, 7, 1, B + 1, 3, 65, 64, 200]
+    b = workloads.build_prefill_batch(8, lens, qlens, num_heads=2, head_dim=d, block_size=B, dtype=dtype)
+    out = _run(b)
+    for s in range(len(lens)):
+        check_close(out[b.cu_q[s]:b.cu_q[s + 1]], _oracle(b, s), TOL[dtype], f"prefill {dtype} d={d} B={B} seq {s}")
+
+
+def test_tiny_worked_example_prompt():
+    # the pages' 7-token prompt at B = 4 (fp32, one head, d = 8): causal
+    # attention over the prompt the walk-through writes into two blocks
+    b = workloads.build_prefill_batch(1, [7], [7], num_heads=1, head_dim=8, block_size=4, dtype="f32")
+    check_close(_run(b), _oracle(b, 0), TOL["f32"], "tiny prompt")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
