@@ -46,6 +46,9 @@
 #ifndef PA_DECODE_FUSED
 #define PA_DECODE_FUSED 0  // 1: the last partition of a (sequence, head) merges all of them
 #endif
+#ifndef PA_DECODE_FAST_MERGE
+#define PA_DECODE_FAST_MERGE 1  // 1: one-round-trip merge for up to kFastParts partitions
+#endif
 #ifndef PA_DECODE_MINW
 #define PA_DECODE_MINW 0  // >0: ask for at least this many waves per SIMD (caps VGPRs)
 #endif
@@ -521,6 +524,7 @@ __global__ __launch_bounds__(kGroupWaves * 64) void decode_grouped_kernel(Decode
 // one per lane, and the weights go through LDS to the lanes owning the dims.
 constexpr int kReduceChunk = 256;  // partitions whose weights sit in LDS at once
 
+constexpr int kFastParts = 4;
 __global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeArgs a, int32_t D, int32_t P) {
   __shared__ float lds_w[kReduceChunk];
   const int bid = blockIdx.x;
@@ -533,13 +537,55 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeArgs a, int32_t
   const int64_t sh = (int64_t)s * a.H + h;
   const float* ml = a.ws_ml + sh * a.max_parts * 2;
   const float* po = a.ws_o + sh * a.max_parts * D;
+  constexpr int kMaxDimsPerLane = 4;  // head_dim <= 256
+#if PA_DECODE_FAST_MERGE
+  if (nparts <= kFastParts) {
+    // few partitions: every lane reads all the (max, sum) pairs and its own
+    // dims of every partial output at once (they do not depend on each
+    // other), so the merge is one round trip instead of a chain
+    float mq[kFastParts], lq[kFastParts], pq[kFastParts][kMaxDimsPerLane];
+#pragma unroll
+    for (int q = 0; q < kFastParts; ++q) {
+      mq[q] = kNegBig;
+      lq[q] = 0.f;
+      if (q < nparts) {
+        mq[q] = ml[2 * q];
+        lq[q] = ml[2 * q + 1];
+      }
+#pragma unroll
+      for (int k = 0; k < kMaxDimsPerLane; ++k) {
+        const int d = lane + 64 * k;
+        pq[q][k] = (q < nparts && d < D) ? po[(int64_t)q * D + d] : 0.f;
+      }
+    }
+    float M = mq[0];
+#pragma unroll
+    for (int q = 1; q < kFastParts; ++q) M = fmaxf(M, mq[q]);
+    float L = 0.f, wq[kFastParts];
+#pragma unroll
+    for (int q = 0; q < kFastParts; ++q) {
+      wq[q] = q < nparts ? fast_exp2(mq[q] - M) : 0.f;
+      L += lq[q] * wq[q];
+    }
+    const float inv_L = 1.f / L;
+#pragma unroll
+    for (int k = 0; k < kMaxDimsPerLane; ++k) {
+      const int d = lane + 64 * k;
+      if (d >= D) break;
+      float O = 0.f;
+#pragma unroll
+      for (int q = 0; q < kFastParts; ++q) O += pq[q][k] * wq[q];
+      store_out(a.out, sh * D + d, O * inv_L, a.out_dtype);
+    }
+    return;
+  }
+#endif
   float mloc = kNegBig;
   for (int q = lane; q < nparts; q += 64) mloc = fmaxf(mloc, ml[2 * q]);
   const float M = wave_max(mloc);
   float lloc = 0.f;
   for (int q = lane; q < nparts; q += 64) lloc += ml[2 * q + 1] * fast_exp2(ml[2 * q] - M);
   const float inv_L = 1.f / wave_sum(lloc);
-  constexpr int kMaxDimsPerLane = 4;  // head_dim <= 256
   float O[kMaxDimsPerLane] = {0.f, 0.f, 0.f, 0.f};
   for (int q0 = 0; q0 < nparts; q0 += kReduceChunk) {
     const int nq = min(kReduceChunk, nparts - q0);
