@@ -195,6 +195,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BN == 3
   constexpr int kTabCache = BN == 32 ? 1024 : 2048;  // block-table entries a workgroup keeps in LDS
   static_assert((BN == 32 || BN == 64) && KPW % 4 == 0 && BS >= 4 && (BN % BS == 0 || BS % BN == 0),
                 "block size must tile the key step");
+  static_assert(NW % 2 == 0 && NW / 2 * 32 * kRowBytes <= (int)sizeof(uint8_t[2][kVTileBytes]) &&
+                    NW / 2 * 32 * kRowBytes <= (int)sizeof(uint8_t[2][kKTileBytes]),
+                "the output staging of half the waves fits each tile buffer pair");
   __shared__ __attribute__((aligned(16))) uint8_t lds_k[2][kKTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t lds_v[2][kVTileBytes];
   __shared__ int32_t lds_tab[kTabCache];
@@ -240,7 +243,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BN == 3
     raw_e1[i] = a.tables[trow + min((BN + KPW0 * w + 4 * i) / BS, a.max_blocks - 1)];
   }
   // keeps the compiler from sinking the reads above past the early exit
-  // below (which would serialise them again)
+  // below (which would serialise them again), and from placing a use of one
+  // of them between the reads (which would wait for the first before issuing
+  // the rest)
+  __builtin_amdgcn_sched_barrier(0);
   asm volatile("" ::"s"(q_begin), "s"(q_end), "s"(ctx), "s"(raw_first));
 #pragma unroll
   for (int i = 0; i < NE0; ++i) asm volatile("" ::"s"(raw_e0[i]), "s"(raw_e1[i]));
@@ -443,8 +449,24 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BN == 3
     issue(a.vpool, lds_v[0], 0, e0, true);
     if (nkt > 1) issue(a.kpool, lds_k[1], 1, e1, false);
   }
-  // the LDS copy of the block table, published by the barrier below
-  for (int i = tid; i < min(n_tab, kTabCache); i += NW * 64) lds_tab[i] = clamp_phys(a.tables[trow + i]);
+  // the LDS copy of the block table, published by the barrier below: all of
+  // a thread's entries are requested before the first is stored, so the copy
+  // costs one memory round trip whatever its length
+  {
+    constexpr int kTabRounds = kTabCache / (NW * 64);
+    const int nt = min(n_tab, kTabCache);
+    int tv[kTabRounds];
+#pragma unroll
+    for (int r = 0; r < kTabRounds; ++r) {
+      const int i = tid + r * NW * 64;
+      tv[r] = i < nt ? a.tables[trow + i] : 0;
+    }
+#pragma unroll
+    for (int r = 0; r < kTabRounds; ++r) {
+      const int i = tid + r * NW * 64;
+      if (i < nt) lds_tab[i] = clamp_phys(tv[r]);
+    }
+  }
   wait_vmem();
   lds_barrier();  // K(0), V(0), K(1) and the block-table copy are visible
   f32x16 s_cur[MB];
@@ -486,23 +508,49 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BN == 3
 
   // normalise and store: result element i of block dm is dim 32dm + 8(i/4) + 4g + i%4
   const float l = halves_sum((lp[0] + lp[1]) + (lp[2] + lp[3]));
-  if (qrow >= qlen) return;
   const float inv_l = 1.f / l;
+  if (a.out_dtype == E::id) {
+    // In the cache dtype the rows go out whole: a lane holds 4 dims of one
+    // query per result block, so storing from registers would touch 32 rows
+    // (18 KiB apart) per instruction, 16 bytes each.  Each wave instead puts
+    // its 32 x 128 tile into LDS (free after the last barrier; wave-private
+    // regions, so no further barrier), rows 256 bytes apart with 16-byte
+    // chunk c at position c ^ (row % 16), and reads it back as 4 whole rows
+    // per instruction.
+    uint8_t* const stage = (w < NW / 2 ? &lds_k[0][0] : &lds_v[0][0]) + (w % (NW / 2)) * (32 * kRowBytes);
+#pragma unroll
+    for (int dm = 0; dm < 4; ++dm)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const float o0 = acc_o[dm][4 * r4] * inv_l, o1 = acc_o[dm][4 * r4 + 1] * inv_l;
+        const float o2 = acc_o[dm][4 * r4 + 2] * inv_l, o3 = acc_o[dm][4 * r4 + 3] * inv_l;
+        const u32x2 v = {pack2(E{}, o0, o1), pack2(E{}, o2, o3)};
+        *(u32x2*)&stage[col * kRowBytes + 16 * ((4 * dm + r4) ^ (col & 15)) + 8 * g] = v;
+      }
+    const int c = lane & 15;
+    u32x4 rows[8];  // all eight reads in flight before the first store
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = 4 * j + (lane >> 4);
+      rows[j] = *(const u32x4*)&stage[r * kRowBytes + 16 * (c ^ (r & 15))];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = q0 + 32 * w + 4 * j + (lane >> 4);
+      if (row < qlen) *(u32x4*)((uint16_t*)a.out + ((int64_t)(q_begin + row) * a.H + h) * kD + 8 * c) = rows[j];
+    }
+    return;
+  }
+  if (qrow >= qlen || a.out_dtype != PA_F32) return;
   const int64_t obase = ((int64_t)(q_begin + qrow) * a.H + h) * kD;
 #pragma unroll
   for (int dm = 0; dm < 4; ++dm)
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const int d = 32 * dm + 8 * r4 + 4 * g;
-      const float o0 = acc_o[dm][4 * r4] * inv_l, o1 = acc_o[dm][4 * r4 + 1] * inv_l;
-      const float o2 = acc_o[dm][4 * r4 + 2] * inv_l, o3 = acc_o[dm][4 * r4 + 3] * inv_l;
-      if (a.out_dtype == PA_F32) {
-        float4 v = {o0, o1, o2, o3};
-        *(float4*)((float*)a.out + obase + d) = v;
-      } else if (a.out_dtype == E::id) {
-        u32x2 v = {pack2(E{}, o0, o1), pack2(E{}, o2, o3)};
-        *(u32x2*)((uint16_t*)a.out + obase + d) = v;
-      }
+      float4 v = {acc_o[dm][4 * r4] * inv_l, acc_o[dm][4 * r4 + 1] * inv_l, acc_o[dm][4 * r4 + 2] * inv_l,
+                  acc_o[dm][4 * r4 + 3] * inv_l};
+      *(float4*)((float*)a.out + obase + d) = v;
     }
 }
 

@@ -196,6 +196,19 @@ def prefill_flops(lens, q_lens, num_heads: int, head_dim: int) -> int:
     return 4 * head_dim * num_heads * int(total)
 
 
+def prefill_bytes(lens, q_lens, num_heads: int, head_dim: int, elem_bytes: int, block_size: int) -> int:
+    """Algorithmic HBM bytes of one prefill launch: every query row read and
+    every output row written once, every key and value row of the contexts
+    read once, the table entries in use, the query offsets and the lengths."""
+    lens = np.asarray(lens, dtype=np.int64)
+    q_lens = np.asarray(q_lens, dtype=np.int64)
+    row = num_heads * head_dim * elem_bytes
+    qo = 2 * int(q_lens.sum()) * row
+    kv = 2 * int(lens.sum()) * row
+    tbl = 4 * int(sum(-(-int(L) // block_size) for L in lens))
+    return qo + kv + tbl + 4 * (2 * len(lens) + 1)
+
+
 @dataclass
 class LongDecode:
     """Long-context decode: histories generated on the device by a seeded

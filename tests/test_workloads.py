@@ -35,6 +35,20 @@ def test_opt13b_lengths_and_bytes():
     assert kv < nbytes < kv * 1.01
 
 
+def test_prefill_flops_and_bytes_by_counting():
+    # a context of 5 with the last 3 positions as queries: the queries attend
+    # to 3, 4 and 5 keys; count the pairs and the rows one by one
+    pairs = sum(1 for i in range(2, 5) for j in range(5) if j <= i)
+    assert pairs == 12
+    assert workloads.prefill_flops([5], [3], 2, 8) == 4 * 8 * 2 * pairs
+    row = 2 * 8 * 2
+    blocks = 2  # ceil(5 / 4)
+    assert workloads.prefill_bytes([5], [3], 2, 8, 2, 4) == 2 * 3 * row + 2 * 5 * row + 4 * blocks + 4 * 3
+    # the OPT-66B prompt step: q, k, v and out once each dominate
+    full = workloads.prefill_bytes([1024] * 8, [1024] * 8, 72, 128, 2, 16)
+    assert 4 * 8 * 1024 * 72 * 128 * 2 < full < 4 * 8 * 1024 * 72 * 128 * 2 * 1.001
+
+
 def test_streams_are_independent_of_the_count():
     a = inputs.streams(2, 5)[3].standard_normal(4)
     b = inputs.streams(2, 7)[3].standard_normal(4)
