@@ -262,8 +262,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BN == 3
   const int qpos = pos0 + qrow;
 
   // B operands of S^T = K Q^T: Q[query][16ks + 8g .. +8] for k-steps ks = 0..7
+  // Queries go through LDS when the two value buffers hold the workgroup's
+  // query tile: loaded into a lane's operand layout directly, each
+  // instruction would fetch 16 bytes from each of 32 rows (rows of [H][d]
+  // are 18 KiB apart at 72 heads), which measured ~4 % slower than moving
+  // whole rows and redistributing them through LDS.
+  constexpr bool kStageQ = NW * 32 * kRowBytes <= 2 * kVTileBytes;
   u32x4 qop[8];
-  {
+  if constexpr (!kStageQ) {
     const bool valid = qrow < qlen;
     const int64_t qbase = ((int64_t)(q_begin + (valid ? qrow : 0)) * a.H + h) * (kD / 8);
 #pragma unroll
@@ -438,15 +444,34 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BN == 3
   // the barrier that ended step j-1), finishes the softmax of S(j), forms
   // S(j+1) on the MFMAs while the exponentials of S(j) run, accumulates
   // P(j) V(j), then waits for its loads and ends with a barrier.
-  {
-    int e0[NE], e1[NE];
+  // Query staging (kStageQ): wave w's 32 rows sit where its own share of the
+  // value tiles goes -- rows 0-15 in bytes [4 KiB w, 4 KiB (w+1)) of value
+  // buffer 0, rows 16-31 at the same place in buffer 1 -- so a wave's value
+  // loads overwrite only its own staged queries, after it has read them.
+  // Row r is 256 bytes with chunk c at position c ^ (r % 16).  Rows past the
+  // query count load the sequence's first query row (finite; their outputs
+  // are never stored).
+  auto q_stage = [&](const int r) { return &lds_v[r >> 4][KPW * w * kRowBytes + (r & 15) * kRowBytes]; };
+  int e0[NE];
 #pragma unroll
-    for (int i = 0; i < NE; ++i) {
-      e0[i] = __builtin_amdgcn_readfirstlane(clamp_phys(raw_e0[i]));
-      e1[i] = __builtin_amdgcn_readfirstlane(clamp_phys(raw_e1[i]));
+  for (int i = 0; i < NE; ++i) e0[i] = __builtin_amdgcn_readfirstlane(clamp_phys(raw_e0[i]));
+  {
+    int e1[NE];
+#pragma unroll
+    for (int i = 0; i < NE; ++i) e1[i] = __builtin_amdgcn_readfirstlane(clamp_phys(raw_e1[i]));
+    if constexpr (kStageQ) {
+      static_assert(KPW == 16, "a wave's share of a value tile holds 16 staged query rows");
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 4 * i + tok_in_inst;  // this lane's row; four rows per instruction
+        const int row = q0 + 32 * w + r;
+        const int64_t src = ((int64_t)(q_begin + (row < qlen ? row : 0)) * a.H + h) * (kD / 8);
+        load_to_lds(a.q + src + (chunk_pos ^ (r & 15)), lds_addr(q_stage(4 * i)));
+      }
+    } else {
+      issue(a.vpool, lds_v[0], 0, e0, true);
     }
     issue(a.kpool, lds_k[0], 0, e0, false);
-    issue(a.vpool, lds_v[0], 0, e0, true);
     if (nkt > 1) issue(a.kpool, lds_k[1], 1, e1, false);
   }
   // the LDS copy of the block table, published by the barrier below: all of
@@ -468,12 +493,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BN == 3
     }
   }
   wait_vmem();
-  lds_barrier();  // K(0), V(0), K(1) and the block-table copy are visible
+  lds_barrier();  // K(0), K(1), the block-table copy (and V(0) or the staged queries) are visible
+  if constexpr (kStageQ) {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qop[ks] = *(const u32x4*)(q_stage(col) + 16 * ((2 * ks + g) ^ (col & 15)));
+    // the value loads below overwrite this wave's staged rows: its reads
+    // must have returned first
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    issue(a.vpool, lds_v[0], 0, e0, true);
+  }
   f32x16 s_cur[MB];
   qk(lds_k[0], s_cur);
   lds_barrier();  // every wave has read K(0): its buffer can take K(2)
 
-  auto step = [&](const int j, auto masked_tag, auto has_next_tag) {
+  auto step = [&](const int j, auto masked_tag, auto has_next_tag, auto first_tag) {
     constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
     {
       int ek[NE], ev[NE];
@@ -482,7 +515,26 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BN == 3
       if (j + 2 < nkt) issue(a.kpool, lds_k[j & 1], j + 2, ek, false);
       if (j + 1 < nkt) issue(a.vpool, lds_v[(j + 1) & 1], j + 1, ev, true);
     }
-    if (j < wave_tiles) {
+    if constexpr (decltype(first_tag)::value) {
+      // Step 0 with staged queries: V(0) was requested after the query
+      // reads, so P(0) V(0) waits for it.  Every wave takes part (tile 0
+      // precedes every query); the step is built masked and with S(1), which
+      // is correct for any tile (an unmasked tile masks nothing; S(1) from a
+      // buffer never loaded when there is no tile 1 is never used).
+      softmax_max(s_cur, 0, masked_tag);
+      f32x16 s_next[MB];
+      qk(lds_k[1], s_next);
+      u32x4 pb[MB][2];
+      weights(s_cur, pb);
+      // the loads this wave issued after V(0): K(2) and V(1), NI each
+      if (nkt > 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * NI));
+      else if (nkt > 1) __builtin_amdgcn_s_waitcnt(0x0F70 | NI);
+      else wait_vmem();
+      lds_barrier();  // V(0) from every wave is visible
+      pv(lds_v[0], pb);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) s_cur[mb] = s_next[mb];
+    } else if (j < wave_tiles) {
       softmax_max(s_cur, j * BN, masked_tag);
       f32x16 s_next[MB];
       if constexpr (HAS_NEXT) qk(lds_k[(j + 1) & 1], s_next);
@@ -498,13 +550,22 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BN == 3
     lds_barrier();
   };
   // unmasked steps whose next tile exists, then masked ones, then the last
+  // (with staged queries, step 0 is its own form)
   int j = 0;
   const int last = nkt - 1;
-  for (; j < min(n_full, last); ++j) step(j, std::false_type{}, std::true_type{});
-  for (; j < min(last, wave_tiles - 1); ++j) step(j, std::true_type{}, std::true_type{});
-  for (; j < last; ++j) step(j, std::true_type{}, std::false_type{});  // this wave's last tile, then none
-  if (last < n_full) step(last, std::false_type{}, std::false_type{});
-  else step(last, std::true_type{}, std::false_type{});
+  constexpr std::false_type no;
+  constexpr std::true_type yes;
+  if constexpr (kStageQ) {
+    step(0, yes, yes, yes);
+    j = 1;
+  }
+  for (; j < min(n_full, last); ++j) step(j, no, yes, no);
+  for (; j < min(last, wave_tiles - 1); ++j) step(j, yes, yes, no);
+  for (; j < last; ++j) step(j, yes, no, no);  // this wave's last tile, then none
+  if (j == last) {
+    if (last < n_full) step(last, no, no, no);
+    else step(last, yes, no, no);
+  }
 
   // normalise and store: result element i of block dm is dim 32dm + 8(i/4) + 4g + i%4
   const float l = halves_sum((lp[0] + lp[1]) + (lp[2] + lp[3]));
