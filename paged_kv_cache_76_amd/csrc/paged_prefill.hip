@@ -327,7 +327,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BN == 3
   constexpr int NE = BS >= KPW ? 1 : NI;
   auto entries = [&](const int kt, int* ent) {
 #pragma unroll
-    for (int i = 0; i < NE; ++i) ent[i] = __builtin_amdgcn_readfirstlane(entry((kt * BN + KPW * w + 4 * i) / BS));
+    for (int i = 0; i < NE; ++i) ent[i] = entry((kt * BN + KPW * w + 4 * i) / BS);
   };
   static_assert(NE == NE0 && KPW == KPW0, "early table reads cover the first tiles");
   // LDS byte offset of the first row of tile token t0 (a multiple of 4)
@@ -506,14 +506,25 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(BN == 3
   qk(lds_k[0], s_cur);
   lds_barrier();  // every wave has read K(0): its buffer can take K(2)
 
+  // Block-table entries run one step ahead: step j reads (from the LDS
+  // copy) the entries of the tiles step j + 1 loads, so the read's latency
+  // is spent under step j's arithmetic rather than in front of its loads.
+  int ek_next[NE], ev_next[NE];
+  entries(2, ek_next);
+  entries(1, ev_next);
   auto step = [&](const int j, auto masked_tag, auto has_next_tag, auto first_tag) {
     constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
     {
       int ek[NE], ev[NE];
-      entries(j + 2, ek);
-      entries(j + 1, ev);
+#pragma unroll
+      for (int i = 0; i < NE; ++i) {
+        ek[i] = __builtin_amdgcn_readfirstlane(ek_next[i]);
+        ev[i] = __builtin_amdgcn_readfirstlane(ev_next[i]);
+      }
       if (j + 2 < nkt) issue(a.kpool, lds_k[j & 1], j + 2, ek, false);
       if (j + 1 < nkt) issue(a.vpool, lds_v[(j + 1) & 1], j + 1, ev, true);
+      entries(j + 3, ek_next);
+      entries(j + 2, ev_next);
     }
     if constexpr (decltype(first_tag)::value) {
       // Step 0 with staged queries: V(0) was requested after the query
