@@ -93,6 +93,51 @@ def measured_traffic(path=COUNTERS, sources=DECODE_SOURCES, kernels=("decode_par
         return None
 
 
+def achievable_reads(cache, tables, lens, reps: int = 10) -> dict:
+    """The achievable HBM read rates a decode step is measured against: a
+    front-to-back stream over 2 GiB, and the (block, head) key and value tiles
+    one decode step reads (the same tiles, in [sequence][head][block] order),
+    read with no arithmetic.  Medians of `reps` timed launches."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_76_amd import _lib as L
+
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    H, B = cache.num_heads, cache.block_size
+    tile_bytes = B * cache.head_dim * cache.k.element_size()
+    ids = []
+    for s, n in enumerate(lens):
+        nb = -(-int(n) // B)
+        ids.append((tables[s, :nb][None, :].astype(np.int64) * H + np.arange(H)[:, None]).reshape(-1))
+    tiles = torch.from_numpy(np.concatenate(ids).astype(np.int32)).cuda()
+    stream_bytes = 2 << 30
+    buf = torch.empty(stream_bytes, dtype=torch.uint8, device="cuda")
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return sorted(ts)[len(ts) // 2]
+
+    t_stream = timed(lambda: L.pa_read_stream(buf, sink))
+    t_tiles = timed(lambda: (L.pa_read_tiles(cache.k, tile_bytes, tiles, sink),
+                             L.pa_read_tiles(cache.v, tile_bytes, tiles, sink)))
+    tile_total = 2 * tiles.numel() * tile_bytes
+    del buf
+    return {"stream_read_GBps": round(stream_bytes / t_stream / 1e9, 1),
+            "kv_tile_read_GBps": round(tile_total / t_tiles / 1e9, 1),
+            "kv_tile_bytes": tile_total, "tile_bytes": tile_bytes,
+            "kernels": "pa_read_stream / pa_read_tiles (plain 16-byte non-temporal reads, no arithmetic)"}
+
+
 def cpu_baseline(batch, n_seq: int, repeats: int = 10) -> dict:
     """The float64 oracle on the first ``n_seq`` sequences of the step (all
     heads), timed on this host's cores."""
@@ -805,6 +850,12 @@ def main() -> int:
         cpu = cpu_baseline(batch, args.cpu_seqs)
 
     traffic = measured_traffic()
+    last = steps[-1]
+    ach = achievable_reads(batch.cache, last["tables"].cpu().numpy(), last["lens_host"])
+    ach["decode_frac_of_kv_tile_read"] = round(dec_gbs / ach["kv_tile_read_GBps"], 4)
+    ach["decode_frac_of_stream_read"] = round(dec_gbs / ach["stream_read_GBps"], 4)
+    log(f"achievable reads: stream {ach['stream_read_GBps']:.0f} GB/s, decode's K/V tiles "
+        f"{ach['kv_tile_read_GBps']:.0f} GB/s; decode at {100 * ach['decode_frac_of_kv_tile_read']:.1f} % of the latter")
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -831,6 +882,7 @@ def main() -> int:
                      "launch_us_p10_p50_p90": [round(pct(0.1), 2), round(pct(0.5), 2), round(pct(0.9), 2)],
                      "algorithmic_bytes_per_launch": int(sum(dec_bytes) / K)},
         "cpu_baseline": cpu,
+        "achievable": ach,
     }
     print(json.dumps(rec), flush=True)
     return 0

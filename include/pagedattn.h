@@ -215,6 +215,32 @@ pa_status pa_paged_prefill(const pa_kv_cache* cache, void* out, pa_dtype out_dty
                            const int32_t* cu_q_lens, const int32_t* context_lens, int32_t S,
                            int32_t max_q_len, int32_t max_context_len, float scale, void* stream);
 
+/*
+ * Measurement helpers (not part of the method; the pages define no such
+ * operation).  Plain reads with no arithmetic, whose rates are the
+ * achievable HBM bandwidth the kernels above are measured against.  Both
+ * fold what they read into 16 bytes and write `sink` only if the fold equals
+ * a fixed value, so the reads cannot be optimised away; the contents of
+ * `sink` afterwards are unspecified.
+ *
+ * pa_read_stream — read bytes of device memory at buf once, front to back,
+ * with 16-byte non-temporal loads.
+ *   buf    device, 16-byte aligned; bytes a multiple of 16, >= 0 (0: no-op).
+ *   sink   device, 16 bytes, 16-byte aligned.
+ *
+ * pa_read_tiles — the paged access pattern without its arithmetic: read the
+ * n tiles buf + tiles[i] * tile_bytes (i = 0 .. n-1), each tile_bytes long,
+ * with 16-byte non-temporal loads.
+ *   buf         device, 16-byte aligned, num_tiles * tile_bytes bytes.
+ *   tile_bytes  > 0, a multiple of 16.
+ *   tiles       device int32 [n], 4-byte aligned; an id outside
+ *               [0, num_tiles) is skipped.
+ *   n           >= 0 (0: no-op).
+ */
+pa_status pa_read_stream(const void* buf, int64_t bytes, void* sink, void* stream);
+pa_status pa_read_tiles(const void* buf, int64_t tile_bytes, int32_t num_tiles, const int32_t* tiles, int32_t n,
+                        void* sink, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* pa_status_string(pa_status status);
 /* Detail of the last non-OK status returned on this thread ("" if none). */

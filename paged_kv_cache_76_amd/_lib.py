@@ -26,7 +26,7 @@ TORCH_TO_PA = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_
 EXPORTS = (
     "pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_decode_workspace_bytes", "pa_paged_decode",
     "pa_decode_grouped_workspace_bytes", "pa_paged_decode_grouped", "pa_paged_prefill",
-    "pa_status_string", "pa_last_error", "pa_abi_version",
+    "pa_read_stream", "pa_read_tiles", "pa_status_string", "pa_last_error", "pa_abi_version",
 )
 
 
@@ -69,8 +69,10 @@ def load_library(path: str) -> ctypes.CDLL:
                                           P, ctypes.c_size_t, P]
     L.pa_paged_prefill.argtypes = [C, P, ctypes.c_int, P, I32P, I32, I32P, I32P, I32, I32, I32,
                                    ctypes.c_float, P]
+    L.pa_read_stream.argtypes = [P, ctypes.c_int64, P, P]
+    L.pa_read_tiles.argtypes = [P, ctypes.c_int64, I32, I32P, I32, P, P]
     for fn in ("pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_paged_decode", "pa_paged_decode_grouped",
-               "pa_paged_prefill"):
+               "pa_paged_prefill", "pa_read_stream", "pa_read_tiles"):
         getattr(L, fn).restype = ctypes.c_int
     L.pa_status_string.argtypes = [ctypes.c_int]
     L.pa_status_string.restype = ctypes.c_char_p
@@ -322,3 +324,28 @@ def pa_paged_prefill(cache: KVCache, out: torch.Tensor, query: torch.Tensor,
                                   _ptr(context_lens), S, int(max_q_len), int(max_context_len),
                                   float(scale), _stream(stream)))
     return out
+
+
+# ---- measurement reads (not part of the method) ----------------------------------
+
+def _on_gpu(**tensors) -> None:
+    for name, t in tensors.items():
+        if t.device.type != "cuda" or (t.device.index is not None and t.device.index != torch.cuda.current_device()):
+            raise ValueError(f"{name} must be on the current GPU, got {t.device}")
+
+
+def pa_read_stream(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Read all of ``buf`` once (the achievable streaming-read rate)."""
+    _on_gpu(buf=buf, sink=sink)
+    _contig("buf", buf)
+    _check(lib().pa_read_stream(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)))
+
+
+def pa_read_tiles(buf: torch.Tensor, tile_bytes: int, tiles: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Read the tiles ``buf`` + ``tiles[i]`` * ``tile_bytes`` (the block-table access pattern, no arithmetic)."""
+    _on_gpu(buf=buf, tiles=tiles, sink=sink)
+    _contig("buf", buf)
+    tiles = _contig("tiles", tiles, torch.int32)
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib().pa_read_tiles(_ptr(buf), int(tile_bytes), nbytes // int(tile_bytes), _ptr(tiles), tiles.numel(),
+                               _ptr(sink), _stream(stream)))

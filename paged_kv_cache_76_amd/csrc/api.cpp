@@ -276,6 +276,29 @@ pa_status pa_paged_prefill(const pa_kv_cache* cache, void* out, pa_dtype out_dty
                                                (hipStream_t)stream));
 }
 
+pa_status pa_read_stream(const void* buf, int64_t bytes, void* sink, void* stream) {
+  const char* fn = "pa_read_stream";
+  if (bytes < 0 || bytes % 16) return fail(PA_ERR_INVALID_ARG, "%s: bytes = %lld must be >= 0 and a multiple of 16", fn,
+                                           (long long)bytes);
+  if (bytes == 0) return PA_OK;
+  if (!buf || !sink) return fail(PA_ERR_INVALID_ARG, "%s: NULL buffer or sink", fn);
+  if (!aligned(buf, 16) || !aligned(sink, 16)) return fail(PA_ERR_INVALID_ARG, "%s: pointers must be 16-byte aligned", fn);
+  return launched(fn, pa::launch_read_stream(buf, bytes, sink, (hipStream_t)stream));
+}
+
+pa_status pa_read_tiles(const void* buf, int64_t tile_bytes, int32_t num_tiles, const int32_t* tiles, int32_t n,
+                        void* sink, void* stream) {
+  const char* fn = "pa_read_tiles";
+  if (tile_bytes <= 0 || tile_bytes % 16)
+    return fail(PA_ERR_INVALID_ARG, "%s: tile_bytes = %lld must be > 0 and a multiple of 16", fn, (long long)tile_bytes);
+  if (n < 0 || num_tiles < 0) return fail(PA_ERR_INVALID_ARG, "%s: negative size", fn);
+  if (n == 0) return PA_OK;
+  if (!buf || !tiles || !sink) return fail(PA_ERR_INVALID_ARG, "%s: NULL buffer, tiles or sink", fn);
+  if (!aligned(buf, 16) || !aligned(sink, 16) || !aligned(tiles, 4))
+    return fail(PA_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+  return launched(fn, pa::launch_read_tiles(buf, tile_bytes, num_tiles, tiles, n, sink, (hipStream_t)stream));
+}
+
 const char* pa_status_string(pa_status status) {
   switch (status) {
     case PA_OK: return "PA_OK";

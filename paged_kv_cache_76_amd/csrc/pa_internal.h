@@ -61,4 +61,9 @@ hipError_t launch_paged_prefill(const Cache& c, void* out, pa_dtype out_dtype, c
                                 int32_t max_q_len, int32_t max_context_len, float scale,
                                 hipStream_t stream);
 
+// ---- measurement reads (read_bench.hip) -----------------------------------------
+hipError_t launch_read_stream(const void* buf, int64_t bytes, void* sink, hipStream_t stream);
+hipError_t launch_read_tiles(const void* buf, int64_t tile_bytes, int32_t num_tiles, const int32_t* tiles,
+                             int32_t n, void* sink, hipStream_t stream);
+
 }  // namespace pa

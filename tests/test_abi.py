@@ -181,3 +181,21 @@ def test_binding_refuses_host_tensors():
     # a query whose head count differs from the pools' is refused by shape
     with pytest.raises(ValueError, match="query must be"):
         L.pa_paged_prefill(cache, q[:, :1].clone(), q[:, :1].clone(), tables, cu, lens, 1, 1, 0.1)
+
+
+def test_read_helper_argument_checks():
+    lib = L.lib()
+    sink = ctypes.c_void_p(16)
+    # sizes that are not multiples of 16, negative sizes, NULL and misaligned pointers
+    assert lib.pa_read_stream(ctypes.c_void_p(4096), 24, sink, None) == L.PA_ERR_INVALID_ARG
+    assert lib.pa_read_stream(ctypes.c_void_p(4096), -16, sink, None) == L.PA_ERR_INVALID_ARG
+    assert lib.pa_read_stream(None, 32, sink, None) == L.PA_ERR_INVALID_ARG
+    assert lib.pa_read_stream(ctypes.c_void_p(4104), 32, sink, None) == L.PA_ERR_INVALID_ARG
+    assert lib.pa_read_stream(None, 0, None, None) == L.PA_OK  # no-op
+    tiles = ctypes.c_void_p(64)
+    assert lib.pa_read_tiles(ctypes.c_void_p(4096), 0, 4, tiles, 2, sink, None) == L.PA_ERR_INVALID_ARG
+    assert lib.pa_read_tiles(ctypes.c_void_p(4096), 40, 4, tiles, 2, sink, None) == L.PA_ERR_INVALID_ARG
+    assert lib.pa_read_tiles(ctypes.c_void_p(4096), 64, -1, tiles, 2, sink, None) == L.PA_ERR_INVALID_ARG
+    assert lib.pa_read_tiles(ctypes.c_void_p(4096), 64, 4, None, 2, sink, None) == L.PA_ERR_INVALID_ARG
+    assert lib.pa_read_tiles(ctypes.c_void_p(4096), 64, 4, ctypes.c_void_p(66), 2, sink, None) == L.PA_ERR_INVALID_ARG
+    assert lib.pa_read_tiles(None, 64, 4, None, 0, None, None) == L.PA_OK  # no-op
