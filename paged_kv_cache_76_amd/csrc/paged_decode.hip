@@ -337,7 +337,10 @@ constexpr float kGroupSlack = 8.0f;  // lazy-rescale slack of the grouped kernel
 constexpr int kGroupTokens = PA_GROUP_PT;
 
 template <typename E, int D, int BS, int W>
-__global__ __launch_bounds__(kGroupWaves * 64) void decode_grouped_kernel(DecodeArgs a, int32_t ngroups) {
+// (at B = 16 the W = 4 build fits 4 waves per SIMD without spills; at B = 32 it
+// would spill, so it keeps 3)
+__global__ __launch_bounds__(kGroupWaves * 64) __attribute__((amdgpu_waves_per_eu(BS <= 16 ? 4 : 3)))
+void decode_grouped_kernel(DecodeArgs a, int32_t ngroups) {
   using C = DecodeCfg<E, D, BS>;
   constexpr int VEC = C::VEC, LPT = C::LPT, TPL = C::TPL, G = C::G, NCH = C::NCH;
   constexpr int NW = kGroupWaves, P = kGroupTokens, STEPS = P / G;
@@ -382,12 +385,14 @@ __global__ __launch_bounds__(kGroupWaves * 64) void decode_grouped_kernel(Decode
     for (int e = 0; e < VEC; ++e) o[r][e] = 0.f;
   }
 
-  // online-softmax update of row r with one step's chunks (values already
-  // widened, once for all the rows that share them).  Lazy rescale: a lane's
-  // reference max only moves when its max grows by more than kGroupSlack
-  // (log2 units), so weights stay below 2^kGroupSlack and most steps skip
-  // the rescale; numerator and denominator share the reference.
-  auto update = [&](const int r, const u32x4* kc, const float (*vf)[VEC], const bool* valid) {
+  // Online-softmax update of row r with one step's chunks; the value
+  // chunks are widened one at a time (a shared tile's chunk once for all its
+  // rows, below), which keeps the W = 4 kernel at 4 waves per SIMD without
+  // spills at B = 16.  Lazy rescale: a lane's reference max only moves when
+  // its max grows by more than kGroupSlack (log2 units), so weights stay
+  // below 2^kGroupSlack and most steps skip the rescale; numerator and
+  // denominator share the reference.
+  auto update = [&](const int r, const u32x4* kc, const u32x4* vc, const bool* valid) {
     float sc[NCH];
     float mblk = kNegBig;
 #pragma unroll
@@ -409,8 +414,10 @@ __global__ __launch_bounds__(kGroupWaves * 64) void decode_grouped_kernel(Decode
     for (int i = 0; i < NCH; ++i) {
       const float pi = fast_exp2(sc[i] - m[r]);
       l[r] += pi;
+      float vf[VEC];
+      widen(E{}, vc[i], vf);
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) o[r][e] = __builtin_fmaf(pi, vf[i][e], o[r][e]);
+      for (int e = 0; e < VEC; ++e) o[r][e] = __builtin_fmaf(pi, vf[e], o[r][e]);
     }
   };
 
@@ -437,11 +444,39 @@ __global__ __launch_bounds__(kGroupWaves * 64) void decode_grouped_kernel(Decode
         vc[i] = load_kv(&a.vpool[base + i * TPL * LPT]);
         valid[i] = true;
       }
-      float vf[NCH][VEC];
+      // scores of every row first (the key chunks die here), then one value
+      // chunk widened at a time for all rows
+      float sc[W][NCH];
 #pragma unroll
-      for (int i = 0; i < NCH; ++i) widen(E{}, vc[i], vf[i]);
+      for (int r = 0; r < W; ++r) {
+        float mblk = kNegBig;
 #pragma unroll
-      for (int r = 0; r < W; ++r) update(r, kc, vf, valid);
+        for (int i = 0; i < NCH; ++i) {
+          sc[r][i] = group_sum<LPT>(dot_chunk(E{}, qc[r], kc[i])) * a.scale_log2;
+          mblk = fmaxf(mblk, sc[r][i]);
+        }
+        const bool raise = mblk > m[r] + kGroupSlack;
+        if (__any(raise)) {
+          const float m_new = raise ? mblk : m[r];
+          const float alpha = fast_exp2(m[r] - m_new);
+          l[r] *= alpha;
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) o[r][e] *= alpha;
+          m[r] = m_new;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        float vf[VEC];
+        widen(E{}, vc[i], vf);
+#pragma unroll
+        for (int r = 0; r < W; ++r) {
+          const float pi = fast_exp2(sc[r][i] - m[r]);
+          l[r] += pi;
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) o[r][e] = __builtin_fmaf(pi, vf[e], o[r][e]);
+        }
+      }
     } else {
 #pragma unroll
       for (int r = 0; r < W; ++r) {
@@ -454,10 +489,7 @@ __global__ __launch_bounds__(kGroupWaves * 64) void decode_grouped_kernel(Decode
           kc[i] = valid[i] ? load_kv(&a.kpool[base + i * TPL * LPT]) : u32x4{0, 0, 0, 0};
           vc[i] = valid[i] ? load_kv(&a.vpool[base + i * TPL * LPT]) : u32x4{0, 0, 0, 0};
         }
-        float vf[NCH][VEC];
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) widen(E{}, vc[i], vf[i]);
-        update(r, kc, vf, valid);
+        update(r, kc, vc, valid);
       }
     }
   }
