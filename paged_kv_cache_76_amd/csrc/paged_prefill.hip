@@ -32,7 +32,11 @@
 //   the loads of K(j+2) and V(j+1) are issued at the start of step j into the
 //   buffers the previous barrier released, each wave waits for its own loads
 //   at the end of the step, and one barrier per step publishes them.  The
-//   block-table entries the workgroup needs are copied to LDS once.
+//   block-table entries the workgroup needs are copied to LDS once, and a
+//   step reads the entries of the next step's loads.
+// * Queries come in and outputs go out as whole 256-byte rows through LDS:
+//   the operand layout would otherwise make every load or store instruction
+//   touch 16 bytes in each of 32 rows that lie H * 256 bytes apart.
 #include <type_traits>
 
 #include "pa_device.h"
