@@ -713,13 +713,63 @@ def swap_bench(args) -> int:
     e1.record()
     torch.cuda.synchronize()
     memcpy_gbs = 2 * flat_dev.numel() * 2 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+    # Overlap: the OPT-13B decode step of the sequences that stay runs on the
+    # current stream while the group swaps out on a second stream (default
+    # priority); each stream is timed with its own events.
+    from paged_kv_cache_76_amd import workloads
+    lens0 = workloads.opt13b_decode_lengths(2, S)
+    db = workloads.build_decode_batch(2, lens0, H, D, B, DTYPE, nan_fill=False)
+    dws = L.decode_workspace(db.cache, S, db.max_context_len)
+    dout = torch.empty((S, H, D), dtype=torch.float16, device="cuda")
+    n_dec = 30
+
+    def decode():
+        L.pa_paged_decode(db.cache, dout, db.q_dev, db.tables_dev, db.lens_dev, db.max_context_len, db.scale, dws)
+
+    side = torch.cuda.Stream()
+
+    def run(with_swap: bool, with_decode: bool):
+        es = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        ed = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        torch.cuda.synchronize()
+        if with_swap:
+            es[0].record(side)
+            L.pa_swap_blocks(cache, host_k, host_v, out_pairs, L.PA_SWAP_OUT, stream=side)
+            es[1].record(side)
+        if with_decode:
+            ed[0].record()
+            for _ in range(n_dec):
+                decode()
+            ed[1].record()
+        torch.cuda.synchronize()
+        return (ed[0].elapsed_time(ed[1]) * 1e3 / n_dec if with_decode else None,
+                es[0].elapsed_time(es[1]) * 1e-3 if with_swap else None)
+
+    for _ in range(2):
+        run(True, True)
+    alone = [run(False, True)[0] for _ in range(5)]
+    swap_alone = [run(True, False)[1] for _ in range(5)]
+    both = [run(True, True) for _ in range(5)]
+    med = lambda v: sorted(v)[len(v) // 2]
+    dec_bytes = workloads.decode_bytes(lens0, H, D, 2, B)
+    overlap = {"decode_alone_us": round(med(alone), 1),
+               "decode_during_swap_us": round(med([b[0] for b in both]), 1),
+               "decode_alone_GBps": round(dec_bytes / (med(alone) * 1e-6) / 1e9, 1),
+               "decode_during_swap_GBps": round(dec_bytes / (med([b[0] for b in both]) * 1e-6) / 1e9, 1),
+               "swap_out_alone_GBps": round(moved / med(swap_alone) / 1e9, 1),
+               "swap_out_during_decode_GBps": round(moved / med([b[1] for b in both]) / 1e9, 1),
+               "decodes_per_swap": n_dec}
+    log(f"overlap: decode {overlap['decode_alone_us']} us alone, {overlap['decode_during_swap_us']} us during the "
+        f"swap; swap-out {overlap['swap_out_alone_GBps']} GB/s alone, {overlap['swap_out_during_decode_GBps']} "
+        "GB/s during the decodes")
     _line("preemption swap GB/s (device -> pinned host), 16 x 1024 OPT-13B tokens", moved / (res["out"] * 1e-3) / 1e9,
           "GB/s", args.steps, args.warmup, res["out"], "f16",
           {"workload": "swap out / swap in of a 16-sequence group", "blocks": nblk, "heads": H, "block_size": B,
            "head_dim": D, "bytes_each_way": moved},
           swap_in_GBps=round(moved / (res["in"] * 1e-3) / 1e9, 1), swap_out_us=round(res["out"] * 1e3, 1),
           swap_in_us=round(res["in"] * 1e3, 1), contiguous_memcpy_d2h_GBps=round(memcpy_gbs, 1),
-          host_block_manager_ms=round(bm_ms, 3))
+          host_block_manager_ms=round(bm_ms, 3), overlap_with_decode=overlap)
     return 0
 
 
