@@ -926,7 +926,8 @@ def main() -> int:
         "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "seq_steps_per_s": round(S * K / elapsed, 1),
         "host_block_manager_ms_per_step": round(sum(host_ms) / len(host_ms), 4),
-        "roofline": {"bound": "hbm", "kernel": "pa_paged_decode (partition + merge kernels)", "achieved": round(dec_gbs, 2),
+        "roofline": {"bound": "hbm", "kernel": "pa_paged_decode (partition kernel; its merge kernel runs only for "
+                                               "contexts longer than one 4096-token partition)", "achieved": round(dec_gbs, 2),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
                      "traffic": traffic, "avg_launch_us": round(dec_avg_ms * 1e3, 2),
                      "launch_us_p10_p50_p90": [round(pct(0.1), 2), round(pct(0.5), 2), round(pct(0.9), 2)],

@@ -28,17 +28,19 @@
 #include "pa_device.h"
 #include "pa_internal.h"
 
-// Tuning knobs.  Defaults are the measured best at the OPT-13B shape (64 x 40
-// heads, d=128, fp16, B=16, contexts U[1,2048]) on MI355X: non-temporal K/V
-// loads are worth ~14% (the K/V stream is read once and must not evict the
-// table, q and partials from L2); 8 waves x 1024-token partitions beat 4 x 256
-// by ~4%.  FUSED (the last partition merges the others after a device-scope
-// fence) is kept as a knob only: the fence costs milliseconds on this part.
+// Tuning knobs.  Defaults are the measured best on MI355X at head_dim 128,
+// B=16: non-temporal K/V loads are worth ~14% (the K/V stream is read once
+// and must not evict the table, q and partials from L2); 16 waves x
+// 4096-token partitions beat 8 x 1024 by 1-3% on the OPT-13B step (contexts
+// U[1,2048]), a serving mix (lognormal around 400) and 32K contexts, and
+// leave no merge at all for contexts up to 4096.  FUSED (the last partition
+// merges the others after a device-scope fence) is kept as a knob only: the
+// fence costs milliseconds on this part.
 #ifndef PA_DECODE_NW
-#define PA_DECODE_NW 8  // waves per workgroup (head_dim >= 64)
+#define PA_DECODE_NW 16  // waves per workgroup (head_dim >= 64)
 #endif
 #ifndef PA_DECODE_PT
-#define PA_DECODE_PT 1024  // tokens per context partition (head_dim >= 64)
+#define PA_DECODE_PT 4096  // tokens per context partition (head_dim >= 64)
 #endif
 #ifndef PA_DECODE_NT
 #define PA_DECODE_NT 1  // 1: non-temporal K/V loads

@@ -78,9 +78,10 @@ def test_every_row_written_once(case):
     # short in these mixes; every (sequence, head) row must come out right.
     rng = np.random.default_rng(7604)
     if case == "mixed":  # ties, every step count of a partition, empty second partitions
-        # (3 to 5 partitions of 1024: both merge paths)
-        lens = np.concatenate([rng.integers(1, 2049, 40), [1, 16, 17, 1024, 1025, 2048, 2048, 1040, 3000, 4096, 4097],
-                               np.full(16, 700)])
+        # (lengths on both sides of multiples of 1024 and 4096: one to five
+        # partitions at either size, so both merge paths)
+        lens = np.concatenate([rng.integers(1, 2049, 40), [1, 16, 17, 1024, 1025, 2048, 2048, 1040, 3000, 4096, 4097,
+                                                           8192, 12289, 16385], np.full(16, 700)])
     elif case == "long_32k":  # 32 partitions for the longest sequence
         lens = np.concatenate([[32768], rng.integers(1, 32769, 15)])
     else:  # 260 sequences
