@@ -327,6 +327,22 @@ class BeamLoop:
     def step(self, events=None) -> StepRecord:
         return self.launch(self.plan(), events)
 
+    def warm(self, plan: dict) -> None:
+        """Launch this loop's kernels once without changing the cache: a copy
+        of block 0 onto itself and the decode of ``plan``'s inputs (read-only;
+        the cache write already ran when the prompts were written).  The
+        first launch of each kernel in a process loads its code, which must
+        not fall inside timed steps."""
+        dev = plan["dev"]
+        out = torch.empty((len(plan["rows"]), self.H, self.d), dtype=TORCH[self.dtype], device=self.device)
+        pa_copy_blocks(self.cache, torch.zeros((1, 2), dtype=torch.int64, device=self.device))
+        if self.grouped:
+            pa_paged_decode_grouped(self.cache, out, dev["q"], dev["tables"], dev["lens"], plan["max_ctx"],
+                                    self.scale, self.W, self.ws)
+        else:
+            pa_paged_decode(self.cache, out, dev["q"], dev["tables"], dev["lens"], plan["max_ctx"], self.scale,
+                            self.ws)
+
     def unique_blocks_read(self, rows) -> int:
         """Distinct physical blocks the decode of ``rows`` reads."""
         ids = set()
