@@ -30,17 +30,30 @@
 
 // Tuning knobs.  Defaults are the measured best on MI355X at head_dim 128,
 // B=16: non-temporal K/V loads are worth ~14% (the K/V stream is read once
-// and must not evict the table, q and partials from L2); 16 waves x
-// 4096-token partitions beat 8 x 1024 by 1-3% on the OPT-13B step (contexts
+// and must not evict the table, q and partials from L2).  Two partitionings
+// are built and picked per launch: the wide one (16 waves x 4096-token
+// partitions) beats 8 x 1024 by 1-3% on the OPT-13B step (contexts
 // U[1,2048]), a serving mix (lognormal around 400) and 32K contexts, and
-// leave no merge at all for contexts up to 4096.  FUSED (the last partition
-// merges the others after a device-scope fence) is kept as a knob only: the
-// fence costs milliseconds on this part.
+// leaves no merge at all for contexts up to 4096; when it would give the
+// GPU fewer than kWideMinWorkgroups workgroups (a few long sequences: one
+// 32K sequence at 40 heads is 320 of them) the narrow one (8 x 1024) runs,
+// 17% faster there.  FUSED (the last partition merges the others after a
+// device-scope fence) is kept as a knob only: the fence costs milliseconds
+// on this part.
 #ifndef PA_DECODE_NW
-#define PA_DECODE_NW 16  // waves per workgroup (head_dim >= 64)
+#define PA_DECODE_NW 16  // waves per workgroup, wide partitioning (head_dim >= 64)
 #endif
 #ifndef PA_DECODE_PT
-#define PA_DECODE_PT 4096  // tokens per context partition (head_dim >= 64)
+#define PA_DECODE_PT 4096  // tokens per context partition, wide partitioning (head_dim >= 64)
+#endif
+#ifndef PA_DECODE_NW_NARROW
+#define PA_DECODE_NW_NARROW 8
+#endif
+#ifndef PA_DECODE_PT_NARROW
+#define PA_DECODE_PT_NARROW 1024
+#endif
+#ifndef PA_DECODE_WIDE_MIN_WG
+#define PA_DECODE_WIDE_MIN_WG 1024  // four per CU of an MI355X
 #endif
 #ifndef PA_DECODE_NT
 #define PA_DECODE_NT 1  // 1: non-temporal K/V loads
@@ -94,7 +107,7 @@ struct DecodeArgs {
 constexpr int cmin(int a, int b) { return a < b ? a : b; }
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
-template <typename E, int D, int BS>
+template <typename E, int D, int BS, bool WIDE = true>
 struct DecodeCfg {
   static constexpr int VEC = 16 / E::bytes;               // elements per 16-byte chunk
   static constexpr int LPT = D / VEC;                     // lanes per token row
@@ -102,8 +115,8 @@ struct DecodeCfg {
   static constexpr int G = cmax(TPL, cmin(BS, 4 * TPL));  // tokens per step
   static constexpr int NCH = G / TPL;                     // loads per lane per step, per pool
   static constexpr bool SMALL = D < 64;
-  static constexpr int NW = SMALL ? 1 : PA_DECODE_NW;     // waves per workgroup
-  static constexpr int PT = SMALL ? 64 : PA_DECODE_PT;    // target tokens per partition
+  static constexpr int NW = SMALL ? 1 : (WIDE ? PA_DECODE_NW : PA_DECODE_NW_NARROW);  // waves per workgroup
+  static constexpr int PT = SMALL ? 64 : (WIDE ? PA_DECODE_PT : PA_DECODE_PT_NARROW);  // target tokens per partition
   static constexpr int STEPS = cmax(1, PT / G);           // steps per partition
   static constexpr int P = STEPS * G;                     // tokens per partition
   static_assert(D % VEC == 0 && LPT >= 1 && LPT <= 64, "unsupported head_dim");
@@ -144,9 +157,10 @@ __device__ __forceinline__ void merge_partitions(const DecodeArgs& a, int64_t sh
   }
 }
 
-template <typename E, int D, int BS>
-__global__ __launch_bounds__((DecodeCfg<E, D, BS>::NW * 64)) PA_DECODE_OCC void decode_partition_kernel(DecodeArgs a) {
-  using C = DecodeCfg<E, D, BS>;
+template <typename E, int D, int BS, bool WIDE>
+__global__ __launch_bounds__((DecodeCfg<E, D, BS, WIDE>::NW * 64)) PA_DECODE_OCC void decode_partition_kernel(
+    DecodeArgs a) {
+  using C = DecodeCfg<E, D, BS, WIDE>;
   constexpr int VEC = C::VEC, LPT = C::LPT, TPL = C::TPL, G = C::G, NCH = C::NCH;
   constexpr int NW = C::NW, STEPS = C::STEPS, P = C::P;
   __shared__ float lds_o[NW][D];
@@ -645,14 +659,20 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeArgs a, int32_t
 }
 
 // ---- instantiation table -------------------------------------------------------
-struct Variant {
-  pa_dtype dtype;
-  int D, BS, P, NW;
+struct Partitioning {
+  int P, NW;
   void (*kernel)(DecodeArgs);
 };
+struct Variant {
+  pa_dtype dtype;
+  int D, BS;
+  Partitioning wide, narrow;
+};
 
+#define PA_DECODE_PARTITIONING(E, D, BS, WIDE) \
+  Partitioning { DecodeCfg<E, D, BS, WIDE>::P, DecodeCfg<E, D, BS, WIDE>::NW, decode_partition_kernel<E, D, BS, WIDE> }
 #define PA_DECODE_VARIANT(E, D, BS) \
-  Variant { E::id, D, BS, DecodeCfg<E, D, BS>::P, DecodeCfg<E, D, BS>::NW, decode_partition_kernel<E, D, BS> }
+  Variant { E::id, D, BS, PA_DECODE_PARTITIONING(E, D, BS, true), PA_DECODE_PARTITIONING(E, D, BS, false) }
 
 #define PA_DECODE_ALL_TYPES(D, BS) \
   PA_DECODE_VARIANT(F32, D, BS), PA_DECODE_VARIANT(F16, D, BS), PA_DECODE_VARIANT(BF16, D, BS)
@@ -694,21 +714,27 @@ const GroupedVariant* find_grouped(pa_dtype dtype, int D, int BS, int W) {
   return nullptr;
 }
 
-int64_t max_parts_for(const Variant& v, int32_t max_context_len) {
-  return ((int64_t)max_context_len + v.P - 1) / v.P;
+int64_t max_parts_for(const Partitioning& p, int32_t max_context_len) {
+  return ((int64_t)max_context_len + p.P - 1) / p.P;
+}
+
+// the wide partitioning unless its grid would leave most of the GPU idle
+constexpr int64_t kWideMinWorkgroups = PA_DECODE_WIDE_MIN_WG;
+const Partitioning& pick_partitioning(const Variant& v, int32_t S, int32_t H, int32_t max_context_len) {
+  return (int64_t)S * H * max_parts_for(v.wide, max_context_len) >= kWideMinWorkgroups ? v.wide : v.narrow;
 }
 
 }  // namespace
 
 int decode_partition_tokens(pa_dtype dtype, int head_dim, int block_size) {
   const Variant* v = find_variant(dtype, head_dim, block_size);
-  return v ? v->P : 0;
+  return v ? v->wide.P : 0;
 }
 
 size_t decode_workspace_bytes(const Cache& c, int32_t S, int32_t max_context_len) {
   const Variant* v = find_variant(c.dtype, c.head_dim, c.block_size);
   if (!v) return (size_t)-1;
-  const int64_t mp = max_parts_for(*v, max_context_len);
+  const int64_t mp = max_parts_for(pick_partitioning(*v, S, c.num_heads, max_context_len), max_context_len);
   if (mp <= 1) return 0;
   return counter_bytes(S, c.num_heads) + (size_t)S * c.num_heads * mp * (c.head_dim + 2) * sizeof(float);
 }
@@ -748,15 +774,16 @@ hipError_t launch_paged_decode(const Cache& c, void* out, pa_dtype out_dtype, co
                                float scale, void* workspace, hipStream_t stream) {
   const Variant* v = find_variant(c.dtype, c.head_dim, c.block_size);
   if (!v) return hipErrorInvalidValue;
-  const int64_t mp = max_parts_for(*v, max_context_len);
+  const Partitioning& pt = pick_partitioning(*v, S, c.num_heads, max_context_len);
+  const int64_t mp = max_parts_for(pt, max_context_len);
   DecodeArgs a = make_args(c, out, out_dtype, query, block_tables, max_blocks_per_seq, context_lens, S, mp, scale,
                            workspace);
   const int64_t grid = (int64_t)S * c.num_heads * mp;
-  hipLaunchKernelGGL(v->kernel, dim3((unsigned)grid), dim3(v->NW * 64), 0, stream, a);
+  hipLaunchKernelGGL(pt.kernel, dim3((unsigned)grid), dim3(pt.NW * 64), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || mp <= 1 || PA_DECODE_FUSED) return err;
   hipLaunchKernelGGL(decode_reduce_kernel, dim3((unsigned)(S * c.num_heads)), dim3(64), 0, stream, a,
-                     (int32_t)c.head_dim, (int32_t)v->P);
+                     (int32_t)c.head_dim, (int32_t)pt.P);
   return hipGetLastError();
 }
 

@@ -72,8 +72,11 @@ def test_shapes(dtype, d, B):
     check_close(_run(b), _oracle(b), TOL[dtype], f"decode {dtype} d={d} B={B}")
 
 
-@pytest.mark.parametrize("case", ["mixed", "long_32k", "many_sequences"])
-def test_every_row_written_once(case):
+# (sequences x heads below the wide partitioning's minimum grid run the
+# narrow partitioning: 2 heads here; 16 and 8 heads take the wide one)
+@pytest.mark.parametrize("case,heads", [("mixed", 2), ("mixed", 16), ("long_32k", 2), ("many_sequences", 2),
+                                        ("many_sequences", 8)])
+def test_every_row_written_once(case, heads):
     # The grid covers (sequence, partition, head) items, most of them empty or
     # short in these mixes; every (sequence, head) row must come out right.
     rng = np.random.default_rng(7604)
@@ -86,9 +89,9 @@ def test_every_row_written_once(case):
         lens = np.concatenate([[32768], rng.integers(1, 32769, 15)])
     else:  # 260 sequences
         lens = rng.integers(1, 2049, 260)
-    print(f"decode rows {case}: S={len(lens)} max ctx {int(lens.max())}", flush=True)
-    b = workloads.build_decode_batch(5, lens.tolist(), num_heads=2, head_dim=128, block_size=16, dtype="f16")
-    check_close(_run(b), _oracle(b), TOL["f16"], f"decode rows {case}")
+    print(f"decode rows {case}: S={len(lens)} heads={heads} max ctx {int(lens.max())}", flush=True)
+    b = workloads.build_decode_batch(5, lens.tolist(), num_heads=heads, head_dim=128, block_size=16, dtype="f16")
+    check_close(_run(b), _oracle(b), TOL["f16"], f"decode rows {case} heads {heads}")
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
