@@ -126,9 +126,10 @@ pa_status pa_swap_blocks(const pa_kv_cache* cache, void* host_k, void* host_v, i
                          const int64_t* pairs, int32_t n, pa_swap_dir dir, void* stream);
 
 /*
- * Workspace of pa_paged_decode, in bytes, for S sequences whose longest
- * context is max_context_len tokens.  0 means "no workspace needed".
- * Returns (size_t)-1 for an unsupported cache description.
+ * Workspace of pa_paged_decode, in bytes: enough for every call with at most
+ * S sequences whose contexts are at most max_context_len tokens (the size
+ * never decreases as S or max_context_len grow).  0 means "no workspace
+ * needed".  Returns (size_t)-1 for an unsupported cache description.
  */
 size_t pa_decode_workspace_bytes(const pa_kv_cache* cache, int32_t S, int32_t max_context_len);
 

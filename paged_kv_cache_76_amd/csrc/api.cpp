@@ -188,7 +188,7 @@ pa_status pa_paged_decode(const pa_kv_cache* cache, void* out, pa_dtype out_dtyp
   st = check_decode(fn, c, out, out_dtype, query, block_tables, max_blocks_per_seq, context_lens, S,
                     max_context_len, scale);
   if (st != PA_OK) return st;
-  const size_t need = pa::decode_workspace_bytes(c, S, max_context_len);
+  const size_t need = pa::decode_workspace_needed(c, S, max_context_len);
   st = check_workspace(fn, need, workspace, workspace_bytes);
   if (st != PA_OK) return st;
   return launched(fn, pa::launch_paged_decode(c, out, out_dtype, query, block_tables, max_blocks_per_seq,

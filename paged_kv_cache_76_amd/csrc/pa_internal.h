@@ -36,7 +36,10 @@ hipError_t launch_swap_blocks(const Cache& c, void* host_k, void* host_v, int32_
 // Tokens per context partition for this cache shape, or 0 if the shape is
 // not built.
 int decode_partition_tokens(pa_dtype dtype, int head_dim, int block_size);
+// bytes to allocate (serves every launch of at most S sequences and
+// max_context_len tokens) and bytes one such launch uses
 size_t decode_workspace_bytes(const Cache& c, int32_t S, int32_t max_context_len);
+size_t decode_workspace_needed(const Cache& c, int32_t S, int32_t max_context_len);
 hipError_t launch_paged_decode(const Cache& c, void* out, pa_dtype out_dtype, const void* query,
                                const int32_t* block_tables, int32_t max_blocks_per_seq,
                                const int32_t* context_lens, int32_t S, int32_t max_context_len,

@@ -731,12 +731,29 @@ int decode_partition_tokens(pa_dtype dtype, int head_dim, int block_size) {
   return v ? v->wide.P : 0;
 }
 
+namespace {
+size_t partials_bytes(const Cache& c, int32_t S, int64_t mp) {
+  if (mp <= 1) return 0;
+  return counter_bytes(S, c.num_heads) + (size_t)S * c.num_heads * mp * (c.head_dim + 2) * sizeof(float);
+}
+}  // namespace
+
+// What the caller allocates: enough for the narrow partitioning (the one
+// with more partitions), so that one workspace serves every launch with at
+// most S sequences and max_context_len tokens, whichever partitioning each
+// launch picks.
 size_t decode_workspace_bytes(const Cache& c, int32_t S, int32_t max_context_len) {
   const Variant* v = find_variant(c.dtype, c.head_dim, c.block_size);
   if (!v) return (size_t)-1;
-  const int64_t mp = max_parts_for(pick_partitioning(*v, S, c.num_heads, max_context_len), max_context_len);
-  if (mp <= 1) return 0;
-  return counter_bytes(S, c.num_heads) + (size_t)S * c.num_heads * mp * (c.head_dim + 2) * sizeof(float);
+  return partials_bytes(c, S, max_parts_for(v->narrow, max_context_len));
+}
+
+// What one launch uses (its own partitioning), at most the size above.
+size_t decode_workspace_needed(const Cache& c, int32_t S, int32_t max_context_len) {
+  const Variant* v = find_variant(c.dtype, c.head_dim, c.block_size);
+  if (!v) return (size_t)-1;
+  return partials_bytes(c, S, max_parts_for(pick_partitioning(*v, S, c.num_heads, max_context_len),
+                                            max_context_len));
 }
 
 namespace {

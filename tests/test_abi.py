@@ -130,6 +130,20 @@ def test_workspace_size_formula():
     assert lib.pa_decode_workspace_bytes(ctypes.byref(bad), 4, 100) == ctypes.c_size_t(-1).value
 
 
+def test_one_decode_workspace_serves_every_smaller_call():
+    # the size never decreases in S or max_context_len, so a workspace sized
+    # once for the largest batch serves every step of a shrinking batch
+    lib = L.lib()
+    for heads in (1, 8, 40, 72):
+        d = _desc(num_heads=heads)
+        Ss, Ls = [1, 2, 5, 16, 20, 64, 256], [1, 16, 1024, 1025, 2048, 4096, 4097, 32768]
+        size = {(S, Lc): lib.pa_decode_workspace_bytes(ctypes.byref(d), S, Lc) for S in Ss for Lc in Ls}
+        for (S, Lc), n in size.items():
+            for (S2, L2), n2 in size.items():
+                if S2 <= S and L2 <= Lc:
+                    assert n2 <= n, (heads, S, Lc, S2, L2)
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(L, "_lib", None)
     monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "nope.so"))

@@ -187,3 +187,21 @@ def test_host_arguments_are_refused():
         L.pa_paged_decode(b.cache, out, b.q_dev.cpu(), b.tables_dev, b.lens_dev, b.max_context_len, b.scale, ws)
     with pytest.raises(ValueError, match="block_tables must be on"):
         L.pa_paged_decode(b.cache, out, b.q_dev, b.tables_dev.cpu(), b.lens_dev, b.max_context_len, b.scale, ws)
+
+
+def test_workspace_sized_once_serves_a_smaller_batch():
+    # sized for 256 sequences of up to 4096 tokens, the workspace serves a
+    # call with 20 sequences (whose small grid takes the partitioning with
+    # more partitions); the rows must come out right, and a workspace of the
+    # call's own size must also be enough
+    rng = np.random.default_rng(7607)
+    lens = np.concatenate([[3000, 2049, 1025], rng.integers(1, 4097, 17)])
+    b = workloads.build_decode_batch(5, lens.tolist(), num_heads=40, head_dim=128, block_size=16, dtype="f16")
+    big = L.decode_workspace(b.cache, 256, 4096)
+    own = L.decode_workspace(b.cache, b.S, b.max_context_len)
+    assert big.numel() >= own.numel() > 0
+    for ws in (big, own):
+        out = torch.full((b.S, 40, 128), float("nan"), dtype=torch.float32, device="cuda")
+        L.pa_paged_decode(b.cache, out, b.q_dev, b.tables_dev, b.lens_dev, b.max_context_len, b.scale, ws)
+        torch.cuda.synchronize()
+        check_close(out, _oracle(b), TOL["f16"], "decode with a workspace sized for a larger batch")
