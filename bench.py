@@ -493,7 +493,8 @@ def longdecode_bench(args) -> int:
 
     S5, C5, H5 = 16, 32768, 72
     log("building the 32K long-context cache (device-generated, 19.3 GB)")
-    ld = workloads.build_long_decode(5, S5, C5, H5, D, B, "bf16")
+    sample = ((0, 0), (0, 71), (15, 0), (15, 71)) if args.cpu_seqs > 0 else ()
+    ld = workloads.build_long_decode(5, S5, C5, H5, D, B, "bf16", samples=sample)
     ws = L.decode_workspace(ld.cache, S5, C5)
     out = torch.empty((S5, H5, D), dtype=torch.bfloat16, device="cuda")
     n = args.steps + args.warmup
@@ -510,6 +511,27 @@ def longdecode_bench(args) -> int:
     ms = sum(ev[i][0].elapsed_time(ev[i][1]) for i in range(args.warmup, n)) / args.steps
     nbytes = workloads.decode_bytes(ld.lens, H5, D, 2, B)
     gbs = nbytes / (ms * 1e-3) / 1e9
+    cpu = None
+    if sample:
+        # the float64 oracle on 2 of the 16 sequences (2 heads each), scaled to
+        # the whole step by the share of (sequence, head) pairs timed
+        import numpy as np
+        from oracle import attention as oa
+
+        data = [(np.asarray(q.to(torch.float64)), np.asarray(K.to(torch.float64)), np.asarray(V.to(torch.float64)))
+                for q, K, V in (ld.samples[k] for k in sample)]
+        times = []
+        for _ in range(3):
+            t1 = time.perf_counter()
+            for q, K, V in data:
+                oa.attend(q, K, V, ld.scale)
+            times.append(time.perf_counter() - t1)
+        dt = sorted(times)[1] * (S5 * H5) / len(sample)
+        cpu = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
+               "sample": f"sequences 0 and 15, heads 0 and 71 ({len(sample)} of {S5 * H5} (sequence, head) pairs, "
+                         f"32768 tokens each), median of 3, scaled to the whole step; float64 NumPy on "
+                         f"{os.cpu_count()} host cores ({cpu_model()})", "seconds_whole_step": round(dt, 2)}
+        log(f"cpu oracle sample: {cpu['value']} GB/s (whole step {dt:.1f} s)")
     _line("paged long-context decode HBM GB/s (16 x 32768 tokens, 72 heads, d128, bf16)", gbs, "GB/s",
           args.steps, args.warmup, elapsed / args.steps * 1e3, "bf16",
           {"workload": "long-context decode", "sequences": S5, "context": C5, "heads": H5, "head_dim": D,
@@ -517,7 +539,7 @@ def longdecode_bench(args) -> int:
           roofline={"bound": "hbm", "kernel": "pa_paged_decode (partition + merge kernels)", "achieved": round(gbs, 2),
                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
                     "avg_launch_us": round(ms * 1e3, 2), "algorithmic_bytes_per_launch": nbytes},
-          seq_steps_per_s=round(S5 / (ms * 1e-3), 1))
+          seq_steps_per_s=round(S5 / (ms * 1e-3), 1), cpu_baseline=cpu)
     return 0
 
 
