@@ -343,10 +343,10 @@ __global__ __launch_bounds__((DecodeCfg<E, D, BS, WIDE>::NW * 64)) PA_DECODE_OCC
 // softmax, so the result equals pa_paged_decode's for any grouping; only the
 // HBM traffic depends on the sharing.
 #ifndef PA_GROUP_NW
-#define PA_GROUP_NW 4  // waves per workgroup of the grouped kernel
+#define PA_GROUP_NW 8  // waves per workgroup of the grouped kernel
 #endif
 #ifndef PA_GROUP_PT
-#define PA_GROUP_PT 512  // tokens per partition of the grouped kernel
+#define PA_GROUP_PT 1024  // tokens per partition of the grouped kernel (a 64-entry table window)
 #endif
 constexpr int kGroupWaves = PA_GROUP_NW;
 constexpr float kGroupSlack = 8.0f;  // lazy-rescale slack of the grouped kernel, log2 units
