@@ -282,7 +282,9 @@ def prefill_bench(args) -> int:
     elapsed = time.perf_counter() - t0
     K = args.steps
     w_ms = sum(ev[i][0].elapsed_time(ev[i][1]) for i in range(args.warmup, n)) / K
-    p_ms = sum(ev[i][1].elapsed_time(ev[i][2]) for i in range(args.warmup, n)) / K
+    p_all = sorted(ev[i][1].elapsed_time(ev[i][2]) for i in range(args.warmup, n))
+    p_ms = sum(p_all) / K
+    p_pct = [round(p_all[min(K - 1, int(q * K))] * 1e3, 2) for q in (0.1, 0.5, 0.9)]
     tflops = flops / (p_ms * 1e-3) / 1e12
     log(f"prefill {p_ms * 1e3:.1f} us -> {tflops:.1f} TFLOP/s; write {w_ms * 1e3:.1f} us -> "
         f"{wbytes / (w_ms * 1e-3) / 1e9:.0f} GB/s")
@@ -321,7 +323,8 @@ def prefill_bench(args) -> int:
                         "achieved": round(pbytes / (p_ms * 1e-3) / 1e9, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                         "frac": round(pbytes / (p_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                         "traffic": measured_traffic(PREFILL_COUNTERS, PREFILL_SOURCES, ("prefill_kernel",)),
-                        "avg_launch_us": round(p_ms * 1e3, 2), "algorithmic_bytes_per_launch": pbytes,
+                        "avg_launch_us": round(p_ms * 1e3, 2), "launch_us_p10_p50_p90": p_pct,
+                        "algorithmic_bytes_per_launch": pbytes,
                         "arithmetic_intensity": round(flops / pbytes, 1),
                         "ridge": round(PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9), 1),
                         "mfma": {"achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
