@@ -87,17 +87,6 @@ def decode(q, K, V, scale: float | None = None) -> np.ndarray:
     return out
 
 
-def decode_batch(queries, histories, scale: float | None = None) -> np.ndarray:
-    """Decode for a batch: ``queries [S][H][d]``, ``histories`` a list of
-    ``(K_s, V_s)`` pairs with ``K_s, V_s [L_s][H][d]``.  Returns ``[S][H][d]``.
-    """
-    queries = _f64(queries)
-    if len(histories) != queries.shape[0]:
-        raise ValueError("one history per query row is required")
-    return np.stack([decode(queries[s], K, V, scale)
-                     for s, (K, V) in enumerate(histories)])
-
-
 def prefill(Q, K, V, scale: float | None = None) -> np.ndarray:
     """Causal attention for the last ``n`` positions of one sequence.
 
@@ -115,10 +104,17 @@ def prefill(Q, K, V, scale: float | None = None) -> np.ndarray:
         raise ValueError(f"shape mismatch Q{Q.shape} K{K.shape} V{V.shape}")
     if scale is None:
         scale = default_scale(d)
-    out = np.empty((n, H, d), dtype=np.float64)
+    # eq. 1 for every query row at once: a score matrix over all key
+    # positions, the keys after the row's own position removed (weight 0),
+    # each row normalised by its own sum
     first = L - n
-    for i in range(n):
-        pos = first + i
-        for h in range(H):
-            out[i, h] = attend(Q[i, h], K[: pos + 1, h, :], V[: pos + 1, h, :], scale)
+    pos = first + np.arange(n)
+    allowed = np.arange(L)[None, :] <= pos[:, None]          # [n][L]: t <= position of the row
+    out = np.empty((n, H, d), dtype=np.float64)
+    for h in range(H):
+        s = (Q[:, h, :] @ K[:, h, :].T) * float(scale)         # [n][L]
+        s = np.where(allowed, s, -np.inf)
+        e = np.exp(s - s.max(axis=1, keepdims=True))
+        a = e / e.sum(axis=1, keepdims=True)
+        out[:, h, :] = a @ V[:, h, :]
     return out

@@ -239,3 +239,40 @@ def test_planted_mistakes_fail_the_sdpa_pin(mutant, monkeypatch):
     got = oa.decode(q, K, V)[0]
     ref = _sdpa(q, K[:, 0], V[:, 0], 1 / math.sqrt(d), causal=False)[0]
     assert np.max(np.abs(got - ref)) > 1e-6
+
+
+def _prefill_mutants():
+    # whole-function copies of a causal prefill with one planted slip each
+    def masked(Q, K, V, scale, keep):
+        n, L = Q.shape[0], K.shape[0]
+        pos = L - n + np.arange(n)
+        s = (Q @ K.T) * scale
+        s = np.where(keep(np.arange(L)[None, :], pos[:, None]), s, -np.inf)
+        e = np.exp(s - s.max(axis=1, keepdims=True))
+        return (e / e.sum(axis=1, keepdims=True)) @ V
+
+    def excludes_self(Q, K, V, scale):
+        # every row but the first (which would be empty) drops its own key
+        out = masked(Q, K, V, scale, lambda t, p: t < p)
+        out[0] = V[0]
+        return out
+
+    def one_too_many(Q, K, V, scale):
+        return masked(Q, K, V, scale, lambda t, p: t <= p + 1)
+
+    def no_mask(Q, K, V, scale):
+        return masked(Q, K, V, scale, lambda t, p: t >= 0)
+
+    return [excludes_self, one_too_many, no_mask]
+
+
+@pytest.mark.parametrize("mutant", _prefill_mutants(), ids=lambda f: f.__name__)
+def test_planted_causal_mistakes_fail_the_sdpa_pin(mutant):
+    # the causal SDPA pin above separates the oracle's prefill from
+    # off-by-one and missing causal bounds
+    r = _rng(14)
+    L, d = 10, 8
+    Q, K, V = (r.standard_normal((L, d)) for _ in range(3))
+    ref = _sdpa(Q, K, V, 1 / math.sqrt(d), causal=True)
+    np.testing.assert_allclose(oa.prefill(Q[:, None], K[:, None], V[:, None])[:, 0], ref, rtol=0, atol=1e-12)
+    assert np.max(np.abs(mutant(Q, K, V, 1 / math.sqrt(d)) - ref)) > 1e-6
