@@ -105,16 +105,18 @@ def prefill(Q, K, V, scale: float | None = None) -> np.ndarray:
     if scale is None:
         scale = default_scale(d)
     # eq. 1 for every query row at once: a score matrix over all key
-    # positions, the keys after the row's own position removed (weight 0),
-    # each row normalised by its own sum
+    # positions, the keys after the row's own position removed (weight 0);
+    # row i is sum_t exp(s_it) v_t divided by sum_t exp(s_it)
     first = L - n
     pos = first + np.arange(n)
     allowed = np.arange(L)[None, :] <= pos[:, None]          # [n][L]: t <= position of the row
     out = np.empty((n, H, d), dtype=np.float64)
     for h in range(H):
-        s = (Q[:, h, :] @ K[:, h, :].T) * float(scale)         # [n][L]
+        Qh = np.ascontiguousarray(Q[:, h, :])
+        Kh = np.ascontiguousarray(K[:, h, :])
+        Vh = np.ascontiguousarray(V[:, h, :])
+        s = (Qh @ Kh.T) * float(scale)                         # [n][L]
         s = np.where(allowed, s, -np.inf)
         e = np.exp(s - s.max(axis=1, keepdims=True))
-        a = e / e.sum(axis=1, keepdims=True)
-        out[:, h, :] = a @ V[:, h, :]
+        out[:, h, :] = (e @ Vh) / e.sum(axis=1, keepdims=True)
     return out
