@@ -20,8 +20,9 @@
  * --------------------------------
  * - All data pointers are DEVICE pointers owned by the caller (the one
  *   exception: the pinned host pools of pa_swap_blocks); the library never
- *   allocates or frees memory, never synchronises, and keeps no global
- *   mutable state except a thread-local "last error" string.
+ *   allocates or frees memory, never synchronises (debug mode aside, below),
+ *   and keeps no global mutable state except a thread-local "last error"
+ *   string and the process-wide debug switch.
  * - Every compute call is asynchronous on `stream` (a hipStream_t passed as
  *   void*; NULL is the default stream).  Buffers must stay alive until the
  *   stream has executed the call.
@@ -39,6 +40,11 @@
  * - Index CONTENTS (slots, block ids, lengths) are preconditions.  The kernels
  *   skip a slot, a pair or a block id outside the pool instead of touching
  *   memory outside it, but the numerical result of such a call is undefined.
+ *   In debug mode (pa_set_debug(1), or PA_DEBUG=1 in the environment when the
+ *   library loads) every compute call first copies its index arrays to the
+ *   host -- synchronously, on its stream -- and checks them with the
+ *   pa_check_* functions below; a violated precondition returns
+ *   PA_ERR_INVALID_ARG and launches nothing.
  */
 #ifndef PAGEDATTN_H
 #define PAGEDATTN_H
@@ -241,6 +247,53 @@ pa_status pa_paged_prefill(const pa_kv_cache* cache, void* out, pa_dtype out_dty
 pa_status pa_read_stream(const void* buf, int64_t bytes, void* sink, void* stream);
 pa_status pa_read_tiles(const void* buf, int64_t tile_bytes, int32_t num_tiles, const int32_t* tiles, int32_t n,
                         void* sink, void* stream);
+
+/*
+ * Index-precondition checks (host only: every pointer below is HOST memory;
+ * nothing touches a device).  Each returns PA_OK or PA_ERR_INVALID_ARG with
+ * the first violation in pa_last_error().
+ *
+ * pa_check_copy_pairs — the pairs of pa_copy_blocks (same_pool = 1) or of
+ * pa_swap_blocks (same_pool = 0, sources and destinations in different
+ * pools).  [P1] key design 3 (a copy-on-write copy goes to a newly allocated
+ * block) and key design 5 (a step's copies run as one batch): every source in
+ * [0, src_blocks), every destination in [0, dst_blocks), destinations
+ * distinct, and with same_pool no destination is also a source -- otherwise
+ * the batch's result would depend on the order its copies run in.
+ *   pairs  int64 [n][2] = (src, dst).
+ */
+pa_status pa_check_copy_pairs(const int64_t* pairs, int32_t n, int32_t src_blocks, int32_t dst_blocks,
+                              int32_t same_pool);
+/*
+ * pa_check_slot_mapping — the slots of pa_reshape_and_cache ([P2]
+ * "PagedAttention 原理": each new token's K/V go to its own slot): every
+ * non-negative slot below num_slots (= num_blocks * block_size), no slot
+ * written by two tokens.  Negative slots (skipped tokens) may repeat.
+ */
+pa_status pa_check_slot_mapping(const int64_t* slot_mapping, int32_t T, int64_t num_slots);
+/*
+ * pa_check_block_tables — the tables and lengths of the attention calls
+ * ([P1] key design 2: logical block j of a sequence maps to a physical
+ * block): 1 <= context_lens[s] <= max_context_len, ceil(context_lens[s] /
+ * block_size) <= max_blocks_per_seq, and each of those entries of row s in
+ * [0, num_blocks).  Entries past them are not looked at.
+ *   block_tables  int32 [S][max_blocks_per_seq];  context_lens  int32 [S].
+ */
+pa_status pa_check_block_tables(const int32_t* block_tables, int32_t S, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, int32_t max_context_len, int32_t block_size,
+                                int32_t num_blocks);
+/*
+ * pa_check_prefill_rows — the query ranges of pa_paged_prefill: cu_q_lens[0]
+ * = 0, 0 <= q_len_s = cu_q_lens[s+1] - cu_q_lens[s] <= max_q_len, and q_len_s
+ * <= context_lens[s] (the queries are the last q_len_s positions).
+ *   cu_q_lens  int32 [S+1];  context_lens  int32 [S].
+ */
+pa_status pa_check_prefill_rows(const int32_t* cu_q_lens, const int32_t* context_lens, int32_t S,
+                                int32_t max_q_len);
+/* Debug mode on (non-zero) or off; process-wide. */
+void pa_set_debug(int32_t on);
+/* 1 when debug mode is on. */
+int32_t pa_get_debug(void);
 
 /* Human-readable name of a status code (static storage). */
 const char* pa_status_string(pa_status status);

@@ -26,7 +26,8 @@ TORCH_TO_PA = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_
 EXPORTS = (
     "pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_decode_workspace_bytes", "pa_paged_decode",
     "pa_decode_grouped_workspace_bytes", "pa_paged_decode_grouped", "pa_paged_prefill",
-    "pa_read_stream", "pa_read_tiles", "pa_status_string", "pa_last_error", "pa_abi_version",
+    "pa_read_stream", "pa_read_tiles", "pa_check_copy_pairs", "pa_check_slot_mapping", "pa_check_block_tables",
+    "pa_check_prefill_rows", "pa_set_debug", "pa_get_debug", "pa_status_string", "pa_last_error", "pa_abi_version",
 )
 
 
@@ -71,8 +72,18 @@ def load_library(path: str) -> ctypes.CDLL:
                                    ctypes.c_float, P]
     L.pa_read_stream.argtypes = [P, ctypes.c_int64, P, P]
     L.pa_read_tiles.argtypes = [P, ctypes.c_int64, I32, I32P, I32, P, P]
-    for fn in ("pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_paged_decode", "pa_paged_decode_grouped",
-               "pa_paged_prefill", "pa_read_stream", "pa_read_tiles"):
+    L.pa_check_copy_pairs.argtypes = [P, I32, I32, I32, I32]
+    L.pa_check_slot_mapping.argtypes = [P, I32, ctypes.c_int64]
+    L.pa_check_block_tables.argtypes = [P, I32, I32, P, I32, I32, I32]
+    L.pa_check_prefill_rows.argtypes = [P, P, I32, I32]
+    L.pa_set_debug.argtypes = [I32]
+    L.pa_set_debug.restype = None
+    L.pa_get_debug.argtypes = []
+    L.pa_get_debug.restype = I32
+    for fn in ("pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_paged_decode",
+               "pa_paged_decode_grouped",
+               "pa_paged_prefill", "pa_read_stream", "pa_read_tiles", "pa_check_copy_pairs", "pa_check_slot_mapping",
+               "pa_check_block_tables", "pa_check_prefill_rows"):
         getattr(L, fn).restype = ctypes.c_int
     L.pa_status_string.argtypes = [ctypes.c_int]
     L.pa_status_string.restype = ctypes.c_char_p
@@ -211,8 +222,11 @@ def pa_swap_blocks(cache: KVCache, host_k: torch.Tensor, host_v: torch.Tensor, p
     _contig("pairs", pairs, torch.int64)
     for name, t in (("host_k", host_k), ("host_v", host_v)):
         _contig(name, t, cache.dtype)
-        if t.shape[1:] != cache.k.shape[1:] or t.device.type != "cpu":
+        if t.dim() != 4 or t.shape[1:] != cache.k.shape[1:] or t.device.type != "cpu":
             raise ValueError(f"{name} must be a host tensor [blocks][H][B][d]")
+    if host_v.shape != host_k.shape:
+        # one block count bounds both host pools in the kernel
+        raise ValueError(f"host_k {tuple(host_k.shape)} and host_v {tuple(host_v.shape)} must have the same shape")
     if pairs.numel() and (pairs.dim() != 2 or pairs.shape[1] != 2):
         raise ValueError("pairs must be [n][2]")
     n = pairs.shape[0] if pairs.numel() else 0
@@ -349,3 +363,57 @@ def pa_read_tiles(buf: torch.Tensor, tile_bytes: int, tiles: torch.Tensor, sink:
     nbytes = buf.numel() * buf.element_size()
     _check(lib().pa_read_tiles(_ptr(buf), int(tile_bytes), nbytes // int(tile_bytes), _ptr(tiles), tiles.numel(),
                                _ptr(sink), _stream(stream)))
+
+
+# ---- index-precondition checks (host arrays; no device is touched) ---------------
+
+def _host_array(a, dtype):
+    import numpy as np
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a, a.ctypes.data_as(ctypes.c_void_p)
+
+
+def check_copy_pairs(pairs, src_blocks: int, dst_blocks: int, same_pool: bool = True) -> None:
+    """Raise if the (src, dst) pairs break pa_copy_blocks' / pa_swap_blocks'
+    preconditions (ids in range, distinct destinations, no destination that
+    is also a source when both sides are one pool)."""
+    import numpy as np
+    a, p = _host_array(np.asarray(pairs).reshape(-1, 2), np.int64)
+    _check(lib().pa_check_copy_pairs(p, a.shape[0], int(src_blocks), int(dst_blocks), int(bool(same_pool))))
+
+
+def check_slot_mapping(slots, num_slots: int) -> None:
+    """Raise if two tokens share a slot or a slot lies outside the pool."""
+    import numpy as np
+    a, p = _host_array(slots, np.int64)
+    _check(lib().pa_check_slot_mapping(p, a.size, int(num_slots)))
+
+
+def check_block_tables(tables, context_lens, max_context_len: int, block_size: int, num_blocks: int) -> None:
+    """Raise if a context length or a table entry it uses is out of range."""
+    import numpy as np
+    t, pt = _host_array(tables, np.int32)
+    lens, pl = _host_array(context_lens, np.int32)
+    if t.ndim != 2 or t.shape[0] != lens.size:
+        raise ValueError("tables must be [S][max_blocks] and context_lens [S]")
+    _check(lib().pa_check_block_tables(pt, lens.size, t.shape[1], pl, int(max_context_len), int(block_size),
+                                       int(num_blocks)))
+
+
+def check_prefill_rows(cu_q_lens, context_lens, max_q_len: int) -> None:
+    """Raise if the query ranges of a prefill call are malformed."""
+    import numpy as np
+    cu, pc = _host_array(cu_q_lens, np.int32)
+    lens, pl = _host_array(context_lens, np.int32)
+    if cu.size != lens.size + 1:
+        raise ValueError("cu_q_lens must be [S+1]")
+    _check(lib().pa_check_prefill_rows(pc, pl, lens.size, int(max_q_len)))
+
+
+def set_debug(on: bool) -> None:
+    """Check index preconditions (host copies of the index arrays) before every launch."""
+    lib().pa_set_debug(1 if on else 0)
+
+
+def get_debug() -> bool:
+    return bool(lib().pa_get_debug())

@@ -49,6 +49,11 @@ class BlockManager:
                  free_order=None, poison: int | None = None, host_blocks: int = 0):
         if block_size < 1 or num_blocks < 1:
             raise ValueError("num_blocks and block_size must be >= 1")
+        if not 0 <= host_blocks <= num_blocks:
+            # the swap space in CPU RAM is bounded by the device memory given
+            # to the KV cache ("vLLM / PagedAttention (SOSP 2023)" guide,
+            # section 05): at most one host block per device block
+            raise ValueError(f"host_blocks = {host_blocks} must lie in [0, num_blocks = {num_blocks}]")
         self.num_blocks = int(num_blocks)
         self.B = int(block_size)
         self.max_rows = int(max_rows)

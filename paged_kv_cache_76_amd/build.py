@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpagedattn.so")
 
-SOURCES = ["api.cpp", "cache_ops.hip", "paged_decode.hip", "paged_prefill.hip", "read_bench.hip"]
+SOURCES = ["api.cpp", "validate.cpp", "cache_ops.hip", "paged_decode.hip", "paged_prefill.hip", "read_bench.hip"]
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU ops.
 HIPCC_FLAGS = [

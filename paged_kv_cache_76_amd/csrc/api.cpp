@@ -5,8 +5,12 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <stdlib.h>
+
+#include <atomic>
 #include <cmath>
 #include <string>
+#include <vector>
 
 #include "pa_internal.h"
 
@@ -14,13 +18,49 @@ namespace {
 
 thread_local std::string g_last_error;
 
-pa_status fail(pa_status st, const char* fmt, ...) {
+// index-precondition checks before every launch (PA_DEBUG=1 in the
+// environment when the library loads, or pa_set_debug)
+std::atomic<int> g_debug{[] {
+  const char* e = getenv("PA_DEBUG");
+  return (e && *e && *e != '0') ? 1 : 0;
+}()};
+
+pa_status vfail(pa_status st, const char* fmt, va_list ap) {
   char buf[512];
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  g_last_error = buf;
+  return st;
+}
+
+pa_status fail(pa_status st, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(buf, sizeof buf, fmt, ap);
+  vfail(st, fmt, ap);
   va_end(ap);
-  g_last_error = buf;
+  return st;
+}
+
+// Debug mode: a synchronous copy of a device index array to the host.
+template <typename T>
+pa_status fetch(const char* fn, const T* dev, int64_t count, hipStream_t stream, std::vector<T>* host) {
+  host->assign((size_t)count, T{});
+  if (count == 0) return PA_OK;
+  if (hipMemcpyAsync(host->data(), dev, (size_t)count * sizeof(T), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(PA_ERR_INVALID_ARG, "%s: the debug check could not read an index array", fn);
+  }
+  return PA_OK;
+}
+
+// Debug mode: the table/length preconditions of the attention calls.
+pa_status debug_tables(const char* fn, const pa::Cache& c, const int32_t* tables, int32_t max_blocks,
+                       const int32_t* lens, int32_t S, int32_t max_context_len, hipStream_t stream) {
+  std::vector<int32_t> t, l;
+  pa_status st = fetch(fn, tables, (int64_t)S * max_blocks, stream, &t);
+  if (st == PA_OK) st = fetch(fn, lens, S, stream, &l);
+  if (st == PA_OK)
+    st = pa_check_block_tables(t.data(), S, max_blocks, l.data(), max_context_len, c.block_size, c.num_blocks);
   return st;
 }
 
@@ -52,6 +92,17 @@ pa_status check_cache(const char* fn, const pa_kv_cache* c, pa::Cache* out) {
   return PA_OK;
 }
 
+// Copies and swaps launch 2n x ceil(block vectors / per-workgroup vectors)
+// workgroups; each dimension's work-items must fit 32 bits.
+pa_status check_copy_grid(const char* fn, const pa::Cache& c, int32_t n) {
+  const int64_t x_items = 2 * (int64_t)n * pa::kCopyThreads;
+  const int64_t y_groups = pa::copy_grid_y(c);
+  if (x_items > (int64_t)UINT32_MAX || y_groups * pa::kCopyThreads > (int64_t)UINT32_MAX)
+    return fail(PA_ERR_INVALID_ARG, "%s: %d pairs (x %lld chunks per block) exceed the launch limit", fn, n,
+                (long long)y_groups);
+  return PA_OK;
+}
+
 pa_status launched(const char* fn, hipError_t err) {
   if (err != hipSuccess) return fail(PA_ERR_LAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(err));
   return PA_OK;
@@ -59,7 +110,21 @@ pa_status launched(const char* fn, hipError_t err) {
 
 }  // namespace
 
+namespace pa {
+pa_status check_fail(pa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vfail(st, fmt, ap);
+  va_end(ap);
+  return st;
+}
+}  // namespace pa
+
 extern "C" {
+
+void pa_set_debug(int32_t on) { g_debug.store(on ? 1 : 0); }
+
+int32_t pa_get_debug(void) { return g_debug.load(); }
 
 pa_status pa_reshape_and_cache(const pa_kv_cache* cache, const void* key, const void* value,
                                const int64_t* slot_mapping, int32_t T, void* stream) {
@@ -73,6 +138,14 @@ pa_status pa_reshape_and_cache(const pa_kv_cache* cache, const void* key, const 
   if (!aligned(key, 16) || !aligned(value, 16))
     return fail(PA_ERR_INVALID_ARG, "%s: key/value must be 16-byte aligned", fn);
   if (!aligned(slot_mapping, 8)) return fail(PA_ERR_INVALID_ARG, "%s: slot_mapping must be 8-byte aligned", fn);
+  if ((int64_t)T * pa::kWriteThreads > (int64_t)UINT32_MAX)
+    return fail(PA_ERR_INVALID_ARG, "%s: T = %d tokens exceed the launch limit", fn, T);
+  if (g_debug.load()) {
+    std::vector<int64_t> slots;
+    st = fetch(fn, slot_mapping, T, (hipStream_t)stream, &slots);
+    if (st == PA_OK) st = pa_check_slot_mapping(slots.data(), T, (int64_t)c.num_blocks * c.block_size);
+    if (st != PA_OK) return st;
+  }
   return launched(fn, pa::launch_reshape_and_cache(c, key, value, slot_mapping, T, (hipStream_t)stream));
 }
 
@@ -85,7 +158,14 @@ pa_status pa_copy_blocks(const pa_kv_cache* cache, const int64_t* pairs, int32_t
   if (n == 0) return PA_OK;
   if (!pairs) return fail(PA_ERR_INVALID_ARG, "%s: pairs is NULL", fn);
   if (!aligned(pairs, 8)) return fail(PA_ERR_INVALID_ARG, "%s: pairs must be 8-byte aligned", fn);
-  if (n > (1 << 30)) return fail(PA_ERR_INVALID_ARG, "%s: n = %d is too large", fn, n);
+  st = check_copy_grid(fn, c, n);
+  if (st != PA_OK) return st;
+  if (g_debug.load()) {
+    std::vector<int64_t> p;
+    st = fetch(fn, pairs, 2 * (int64_t)n, (hipStream_t)stream, &p);
+    if (st == PA_OK) st = pa_check_copy_pairs(p.data(), n, c.num_blocks, c.num_blocks, 1);
+    if (st != PA_OK) return st;
+  }
   return launched(fn, pa::launch_copy_blocks(c, pairs, n, (hipStream_t)stream));
 }
 
@@ -101,7 +181,8 @@ pa_status pa_swap_blocks(const pa_kv_cache* cache, void* host_k, void* host_v, i
   if (!pairs || !host_k || !host_v) return fail(PA_ERR_INVALID_ARG, "%s: NULL pairs/host pool", fn);
   if (!aligned(pairs, 8) || !aligned(host_k, 16) || !aligned(host_v, 16))
     return fail(PA_ERR_INVALID_ARG, "%s: misaligned pairs/host pool", fn);
-  if (n > (1 << 30)) return fail(PA_ERR_INVALID_ARG, "%s: n = %d is too large", fn, n);
+  st = check_copy_grid(fn, c, n);
+  if (st != PA_OK) return st;
   // the kernel dereferences the host pools: they must be pinned host memory
   // the device can address (a pageable pointer would fault the GPU)
   void* dev_ptr[2] = {nullptr, nullptr};
@@ -114,6 +195,16 @@ pa_status pa_swap_blocks(const pa_kv_cache* cache, void* host_k, void* host_v, i
       return fail(PA_ERR_INVALID_ARG, "%s: host pool %d is not pinned, device-accessible host memory", fn, i);
     }
     dev_ptr[i] = attr.devicePointer;
+  }
+  if (g_debug.load()) {
+    std::vector<int64_t> p;
+    st = fetch(fn, pairs, 2 * (int64_t)n, (hipStream_t)stream, &p);
+    if (st == PA_OK) {
+      const bool out = dir == PA_SWAP_OUT;
+      st = pa_check_copy_pairs(p.data(), n, out ? c.num_blocks : host_num_blocks, out ? host_num_blocks : c.num_blocks,
+                               0);
+    }
+    if (st != PA_OK) return st;
   }
   return launched(fn, pa::launch_swap_blocks(c, dev_ptr[0], dev_ptr[1], host_num_blocks, pairs, n,
                                              dir == PA_SWAP_OUT, (hipStream_t)stream));
@@ -191,6 +282,10 @@ pa_status pa_paged_decode(const pa_kv_cache* cache, void* out, pa_dtype out_dtyp
   const size_t need = pa::decode_workspace_needed(c, S, max_context_len);
   st = check_workspace(fn, need, workspace, workspace_bytes);
   if (st != PA_OK) return st;
+  if (g_debug.load()) {
+    st = debug_tables(fn, c, block_tables, max_blocks_per_seq, context_lens, S, max_context_len, (hipStream_t)stream);
+    if (st != PA_OK) return st;
+  }
   return launched(fn, pa::launch_paged_decode(c, out, out_dtype, query, block_tables, max_blocks_per_seq,
                                               context_lens, S, max_context_len, scale,
                                               need > 0 ? workspace : nullptr, (hipStream_t)stream));
@@ -232,6 +327,10 @@ pa_status pa_paged_decode_grouped(const pa_kv_cache* cache, void* out, pa_dtype 
   const size_t need = pa::decode_grouped_workspace_bytes(c, S, max_context_len, group_size);
   st = check_workspace(fn, need, workspace, workspace_bytes);
   if (st != PA_OK) return st;
+  if (g_debug.load()) {
+    st = debug_tables(fn, c, block_tables, max_blocks_per_seq, context_lens, S, max_context_len, (hipStream_t)stream);
+    if (st != PA_OK) return st;
+  }
   return launched(fn, pa::launch_paged_decode_grouped(c, out, out_dtype, query, block_tables, max_blocks_per_seq,
                                                       context_lens, S, max_context_len, scale, group_size,
                                                       need > 0 ? workspace : nullptr, (hipStream_t)stream));
@@ -271,6 +370,14 @@ pa_status pa_paged_prefill(const pa_kv_cache* cache, void* out, pa_dtype out_dty
   if (items > (int64_t)UINT32_MAX)
     return fail(PA_ERR_INVALID_ARG, "%s: %lld work-items (S x heads x queries) exceed the launch limit", fn,
                 (long long)items);
+  if (g_debug.load()) {
+    st = debug_tables(fn, c, block_tables, max_blocks_per_seq, context_lens, S, max_context_len, (hipStream_t)stream);
+    std::vector<int32_t> cu, l;
+    if (st == PA_OK) st = fetch(fn, cu_q_lens, (int64_t)S + 1, (hipStream_t)stream, &cu);
+    if (st == PA_OK) st = fetch(fn, context_lens, S, (hipStream_t)stream, &l);
+    if (st == PA_OK) st = pa_check_prefill_rows(cu.data(), l.data(), S, max_q_len);
+    if (st != PA_OK) return st;
+  }
   return launched(fn, pa::launch_paged_prefill(c, out, out_dtype, query, block_tables, max_blocks_per_seq,
                                                cu_q_lens, context_lens, S, max_q_len, max_context_len, scale,
                                                (hipStream_t)stream));

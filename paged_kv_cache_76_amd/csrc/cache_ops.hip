@@ -17,8 +17,6 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWriteThreads = 256;
-
 // grid.x = token t, grid.y = chunk of 256 16-byte vectors of that token's
 // [H][d] row.  The slot is loaded once per workgroup (wave-uniform).
 __global__ __launch_bounds__(kWriteThreads) void reshape_and_cache_kernel(
@@ -44,10 +42,8 @@ __global__ __launch_bounds__(kWriteThreads) void reshape_and_cache_kernel(
   vpool[dst] = vv;
 }
 
-constexpr int kCopyThreads = 256;
-constexpr int kCopyUnroll = 4;  // 16 KiB per workgroup per pool
-
-// grid.x = pair index * 2 + pool (0: keys, 1: values), grid.y = 16 KiB chunk.
+// grid.x = pair index * 2 + pool (0: keys, 1: values), grid.y = chunk of
+// kCopyThreads x kCopyUnroll 16-byte vectors (16 KiB) of the block.
 __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
     u32x4* __restrict__ kpool, u32x4* __restrict__ vpool, const int64_t* __restrict__ pairs,
     int64_t vec_per_block, int64_t num_blocks) {
@@ -103,8 +99,7 @@ hipError_t launch_swap_blocks(const Cache& c, void* host_k, void* host_v, int32_
   const int64_t block_bytes =
       (int64_t)c.num_heads * c.block_size * c.head_dim * dtype_bytes(c.dtype);
   const int64_t vec_per_block = block_bytes / 16;
-  const int64_t per_wg = kCopyThreads * kCopyUnroll;
-  dim3 grid((unsigned)(2 * n), (unsigned)((vec_per_block + per_wg - 1) / per_wg));
+  dim3 grid((unsigned)(2 * n), (unsigned)copy_grid_y(c));
   const u32x4* src_k = (const u32x4*)(to_host ? c.k : host_k);
   const u32x4* src_v = (const u32x4*)(to_host ? c.v : host_v);
   u32x4* dst_k = (u32x4*)(to_host ? host_k : c.k);
@@ -133,8 +128,7 @@ hipError_t launch_copy_blocks(const Cache& c, const int64_t* pairs, int32_t n, h
   const int64_t block_bytes =
       (int64_t)c.num_heads * c.block_size * c.head_dim * dtype_bytes(c.dtype);
   const int64_t vec_per_block = block_bytes / 16;
-  const int64_t per_wg = kCopyThreads * kCopyUnroll;
-  dim3 grid((unsigned)(2 * n), (unsigned)((vec_per_block + per_wg - 1) / per_wg));
+  dim3 grid((unsigned)(2 * n), (unsigned)copy_grid_y(c));
   hipLaunchKernelGGL(copy_blocks_kernel, grid, dim3(kCopyThreads), 0, stream, (u32x4*)c.k,
                      (u32x4*)c.v, pairs, vec_per_block, (int64_t)c.num_blocks);
   return hipGetLastError();

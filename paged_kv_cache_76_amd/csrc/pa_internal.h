@@ -24,6 +24,18 @@ struct Cache {
 inline int dtype_bytes(pa_dtype t) { return t == PA_F32 ? 4 : 2; }
 
 // ---- cache writes and copies (cache_ops.hip) ---------------------------------
+// The cache write launches T x ceil(H * vectors per row / kWriteThreads)
+// workgroups of kWriteThreads threads.
+constexpr int kWriteThreads = 256;
+// Launch shape of the copy and swap kernels: grid.x = 2 * pairs (keys and
+// values), grid.y = copy_grid_y(c) chunks per block, kCopyThreads threads.
+constexpr int kCopyThreads = 256;
+constexpr int kCopyUnroll = 4;
+inline int64_t copy_grid_y(const Cache& c) {
+  const int64_t vec_per_block = (int64_t)c.num_heads * c.block_size * c.head_dim * dtype_bytes(c.dtype) / 16;
+  const int64_t per_wg = kCopyThreads * kCopyUnroll;
+  return (vec_per_block + per_wg - 1) / per_wg;
+}
 hipError_t launch_reshape_and_cache(const Cache& c, const void* key, const void* value,
                                     const int64_t* slot_mapping, int32_t T, hipStream_t stream);
 hipError_t launch_copy_blocks(const Cache& c, const int64_t* pairs, int32_t n, hipStream_t stream);

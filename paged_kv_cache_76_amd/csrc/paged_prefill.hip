@@ -90,7 +90,7 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x3f70)
 // (wait_vmem, then a barrier, before any wave reads the buffer).
 __device__ __forceinline__ void load_to_lds(const void* src, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base)
-               : "memory");
+               : "memory", "m0");
 }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(lds_void_t*)p;
@@ -105,7 +105,7 @@ __device__ __forceinline__ void load4_to_lds(const void* src, uint32_t m0, uint3
       "s_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:2048\n\t"
       "s_mov_b32 m0, %4\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:3072" ::"v"(src),
       "s"(m0), "s"(m1), "s"(m2), "s"(m3)
-      : "memory");
+      : "memory", "m0");
 }
 
 constexpr int kD = 128;         // head_dim
@@ -691,7 +691,9 @@ __global__ __launch_bounds__(64) void prefill_generic_kernel(PrefillArgs a, int3
     const int t = t0 + lane;
     float sc = -__builtin_inff();
     int64_t row = -1;
-    if (t < nkeys) {
+    // a key whose logical block lies past the table row (a context length
+    // beyond max_blocks * B) is treated like one outside the pool
+    if (t < nkeys && t / BS < a.max_blocks) {
       const int phys = a.tables[trow + t / BS];
       if (phys >= 0 && phys < a.N) {
         row = ((int64_t)phys * a.H + h) * BS + t % BS;
@@ -723,7 +725,8 @@ __global__ __launch_bounds__(64) void prefill_generic_kernel(PrefillArgs a, int3
     m = m_new;
     __syncthreads();
   }
-  const float inv_l = 1.f / l;
+  // no usable key at all (every block outside the pool): zeros, not 0/0
+  const float inv_l = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
   for (int k = 0; k < kSlots; ++k) {
     const int d = lane + 64 * k;

@@ -213,3 +213,24 @@ def test_read_helper_argument_checks():
     assert lib.pa_read_tiles(ctypes.c_void_p(4096), 64, 4, None, 2, sink, None) == L.PA_ERR_INVALID_ARG
     assert lib.pa_read_tiles(ctypes.c_void_p(4096), 64, 4, ctypes.c_void_p(66), 2, sink, None) == L.PA_ERR_INVALID_ARG
     assert lib.pa_read_tiles(None, 64, 4, None, 0, None, None) == L.PA_OK  # no-op
+
+
+def test_copy_swap_and_write_grids_beyond_the_launch_limit_are_refused():
+    # 2n workgroups of 256 threads (copies, swaps) and T workgroups of 256
+    # (writes) must fit the 32-bit work-item count of a launch dimension
+    lib = L.lib()
+    d = _desc()
+    _err(lib.pa_copy_blocks(ctypes.byref(d), FAKE, 1 << 23, None), "launch limit")
+    _err(lib.pa_swap_blocks(ctypes.byref(d), FAKE, FAKE, 8, FAKE, 1 << 23, L.PA_SWAP_OUT, None), "launch limit")
+    _err(lib.pa_reshape_and_cache(ctypes.byref(d), FAKE, FAKE, FAKE, 1 << 24, None), "launch limit")
+
+
+def test_swap_binding_refuses_mismatched_host_pools():
+    # one host block count bounds both host pools in the kernel, so the
+    # binding refuses host pools of different sizes before any launch
+    cache = L.KVCache(torch.zeros((4, 2, 16, 128), dtype=torch.float16),
+                      torch.zeros((4, 2, 16, 128), dtype=torch.float16))
+    hk = torch.zeros((6, 2, 16, 128), dtype=torch.float16)
+    hv = torch.zeros((3, 2, 16, 128), dtype=torch.float16)
+    with pytest.raises(ValueError, match="same shape"):
+        L.pa_swap_blocks(cache, hk, hv, torch.zeros((1, 2), dtype=torch.int64), L.PA_SWAP_OUT)

@@ -267,3 +267,13 @@ def test_swap_is_all_or_nothing():
     assert m._host_free == state[2]
     with pytest.raises(KeyError):
         m.swap_in([0])
+
+
+def test_swap_space_is_bounded_by_the_device_pool():
+    # the SOSP guide, section 05: the CPU swap space is limited by the GPU
+    # memory allocated to the KV cache
+    BlockManager(16, 4, max_rows=2, max_blocks_per_seq=4, host_blocks=16)
+    with pytest.raises(ValueError, match="host_blocks"):
+        BlockManager(16, 4, max_rows=2, max_blocks_per_seq=4, host_blocks=17)
+    with pytest.raises(ValueError, match="host_blocks"):
+        BlockManager(16, 4, max_rows=2, max_blocks_per_seq=4, host_blocks=-1)

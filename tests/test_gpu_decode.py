@@ -163,19 +163,13 @@ def test_constant_values_give_that_constant():
 
 
 @pytest.mark.slow
-def test_opt13b_decode_full_size_sampled():
-    # S=64, 40 heads, d=128, fp16, contexts U[1, 2048], B=16, pool +10%
-    print("decode OPT-13B full size (sampled check)", flush=True)
+def test_opt13b_decode_full_size():
+    # S=64, 40 heads, d=128, fp16, contexts U[1, 2048], B=16, pool +10%:
+    # every (sequence, head) row against the oracle
+    print("decode OPT-13B full size (all 64 x 40 rows)", flush=True)
     lens = workloads.opt13b_decode_lengths()
     b = workloads.build_decode_batch(2, lens, num_heads=40, head_dim=128, block_size=16, dtype="f16")
-    out = _run(b)
-    assert torch.isfinite(out).all()
-    r = np.random.default_rng(0)
-    rows = sorted(set([int(np.argmax(lens)), int(np.argmin(lens))] + r.choice(64, 14, replace=False).tolist()))
-    heads = [0, 17, 39]
-    ref = _oracle(b, rows, heads)
-    got = out[rows][:, heads]
-    check_close(got, ref, TOL["f16"], "OPT-13B sampled")
+    check_close(_run(b), _oracle(b), TOL["f16"], "OPT-13B decode")
 
 
 def test_host_arguments_are_refused():

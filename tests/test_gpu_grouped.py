@@ -123,26 +123,76 @@ def test_shape_without_grouped_build_falls_back():
     check_close(out, ref, TOL["bf16"], "fallback")
 
 
+def _ramped(W, exact):
+    """Keys aligned with the query and growing along the sequence, so the
+    running max keeps moving by many powers of two (the lazy rescale path
+    runs over and over; random inputs almost never take it after the first
+    tiles).  Scores reach |q.k| ~ 480 (about 61 in log2 units after the
+    1/sqrt(128) scale).  With ``exact`` every key and query element is a
+    multiple of 1/128 of at most 8 and q has +-1 or 0 entries, so every fp32
+    product and partial sum of q.k is exact and the only rounding of a score
+    is its final scaling; otherwise the values are generic floats."""
+    gen = torch.Generator().manual_seed(7601)  # seeded inputs
+    H, d, n = 2, 128, 700
+    if exact:
+        sign = torch.where(torch.rand(generator=gen, size=(H, d)) < 0.5, -1.0, 1.0)
+        keep = torch.zeros(H, d)
+        for h in range(H):
+            keep[h, torch.randperm(d, generator=gen)[:64]] = 1.0
+        u = sign * keep / 8.0                                    # 64 entries of +-1/8: |u| = 1
+        ramp = torch.round(torch.linspace(-60.0, 60.0, n) * 16) / 16
+        noise = torch.round(torch.rand(generator=gen, size=(n, H, d)) * 32 - 16) / 64
+        k = ramp.view(n, 1, 1) * u.view(1, H, d) + noise
+    else:
+        u = torch.randn(generator=gen, size=(H, d), dtype=torch.float32)
+        u = u / u.norm(dim=-1, keepdim=True)
+        ramp = torch.linspace(-60.0, 60.0, n)
+        k = ramp.view(n, 1, 1) * u.view(1, H, d) + 0.1 * torch.randn(generator=gen, size=(n, H, d))
+    v = torch.randn(generator=gen, size=(n, H, d), dtype=torch.float32)
+    q = (u.view(1, H, d) * 8.0).repeat(W, 1, 1)
+    return k.to(torch.float32), v, q.to(torch.float32)
+
+
+def _ramped_batch(W, exact):
+    H, d, n = 2, 128, 700
+    b = workloads.build_decode_batch(11, [n] * W, num_heads=H, head_dim=d, block_size=16, dtype="f32", nan_fill=True)
+    k, v, q = _ramped(W, exact)
+    slots = np.concatenate([[b.manager.slot(s, p) for p in range(n)] for s in range(W)]).astype(np.int64)
+    L.pa_reshape_and_cache(b.cache, torch.cat([k] * W).cuda(), torch.cat([v] * W).cuda(),
+                           torch.from_numpy(slots).cuda())
+    return b, k, v, q
+
+
 @pytest.mark.parametrize("W", [2, 4])
 def test_rising_scores_force_rescales(W):
-    gen = torch.Generator().manual_seed(7601)  # seeded inputs
-    # keys aligned with the query and growing along the sequence: the running
-    # max keeps moving by many powers of two, so the lazy rescale path runs
-    # over and over (random inputs almost never take it after the first tiles)
-    H, d, B = 2, 128, 16
-    lens = [700] * W
-    b = workloads.build_decode_batch(11, lens, num_heads=H, head_dim=d, block_size=B, dtype="f32", nan_fill=True)
-    u = torch.randn(generator=gen, size=(H, d), dtype=torch.float32)
-    u = u / u.norm(dim=-1, keepdim=True)
-    ramp = torch.linspace(-60.0, 60.0, 700).view(700, 1, 1)          # score range ~ 120 / sqrt(128) * log2e
-    k = (ramp * u.view(1, H, d) + 0.1 * torch.randn(generator=gen, size=(700, H, d))).to(torch.float32)
-    v = torch.randn(generator=gen, size=(700, H, d), dtype=torch.float32)
-    slots = np.concatenate([[b.manager.slot(s, p) for p in range(700)] for s in range(W)]).astype(np.int64)
-    L.pa_reshape_and_cache(b.cache, torch.cat([k] * W).cuda(), torch.cat([v] * W).cuda(), torch.from_numpy(slots).cuda())
-    q = (u.view(1, H, d) * 8.0).repeat(W, 1, 1)
+    # fp32 at the fp32 tolerance: with exact scores the lazy rescale (weights
+    # up to 2^8 before a rescale, numerator and denominator on one reference)
+    # must not cost accuracy
+    b, k, v, q = _ramped_batch(W, exact=True)
     ws = L.decode_grouped_workspace(b.cache, W, 700, W)
-    out = torch.full((W, H, d), float("nan"), dtype=torch.float32, device="cuda")
+    out = torch.full((W, 2, 128), float("nan"), dtype=torch.float32, device="cuda")
     L.pa_paged_decode_grouped(b.cache, out, q.cuda(), b.tables_dev, b.lens_dev, 700, b.scale, W, ws)
     torch.cuda.synchronize()
     ref = np.stack([oa.decode(inputs.to_f64(q[s]), inputs.to_f64(k), inputs.to_f64(v)) for s in range(W)])
-    check_close(out, ref, TOL["f32"] * 10, f"rising scores W={W}")
+    check_close(out, ref, TOL["f32"], f"rising scores W={W}")
+
+
+@pytest.mark.parametrize("W", [2, 4])
+def test_rising_scores_grouped_equals_ungrouped(W):
+    # generic fp32 values: both kernels form the same fp32 scores, so the
+    # grouped kernel's lazy rescale must reproduce the ungrouped kernel's
+    # eager one to within the fp32 tolerance
+    b, k, v, q = _ramped_batch(W, exact=False)
+    qd = q.cuda()
+    outs = []
+    for grouped in (True, False):
+        out = torch.full((W, 2, 128), float("nan"), dtype=torch.float32, device="cuda")
+        if grouped:
+            ws = L.decode_grouped_workspace(b.cache, W, 700, W)
+            L.pa_paged_decode_grouped(b.cache, out, qd, b.tables_dev, b.lens_dev, 700, b.scale, W, ws)
+        else:
+            ws = L.decode_workspace(b.cache, W, 700)
+            L.pa_paged_decode(b.cache, out, qd, b.tables_dev, b.lens_dev, 700, b.scale, ws)
+        outs.append(out)
+    torch.cuda.synchronize()
+    check_close(outs[0], outs[1].double().cpu().numpy(), TOL["f32"], f"grouped vs ungrouped W={W}")
