@@ -165,6 +165,29 @@ pa_status pa_paged_decode(const pa_kv_cache* cache, void* out, pa_dtype out_dtyp
                           float scale, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_paged_decode_noalloc — pa_paged_decode for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  It computes exactly what pa_paged_decode computes
+ * (the same kernels, bit-identical results) but keeps the partial results of
+ * long contexts in a scratch array of PA_NOALLOC_SCRATCH_BYTES that the
+ * library holds in device memory, one per GPU, until the process ends,
+ * instead of in a caller workspace.  It calls no allocator of any kind (debug
+ * mode does not apply to it: its checks copy indices into host buffers).
+ *   Every argument is as for pa_paged_decode, without the workspace.
+ *   A call whose partials need more than PA_NOALLOC_SCRATCH_BYTES (the size
+ *   pa_decode_workspace_bytes reports bounds it) returns PA_ERR_WORKSPACE and
+ *   launches nothing.
+ *   Calls on one GPU share that GPU's array: calls that overlap in time on
+ *   one GPU (several streams or threads) race and must be serialised by the
+ *   caller.  Calls in one stream are ordered and safe.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (32u << 20)
+pa_status pa_paged_decode_noalloc(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, const void* query,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, int32_t S, int32_t max_context_len,
+                                  float scale, void* stream);
+
+/*
  * pa_paged_decode_grouped — pa_paged_decode for batches whose rows share
  * blocks (parallel samples or beam candidates over a common prefix).
  * [P1] key design 3 (several logical blocks map to one physical block) and

@@ -25,7 +25,7 @@ TORCH_TO_PA = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_
 # every symbol include/pagedattn.h declares
 EXPORTS = (
     "pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_decode_workspace_bytes", "pa_paged_decode",
-    "pa_decode_grouped_workspace_bytes", "pa_paged_decode_grouped", "pa_paged_prefill",
+    "pa_paged_decode_noalloc", "pa_decode_grouped_workspace_bytes", "pa_paged_decode_grouped", "pa_paged_prefill",
     "pa_read_stream", "pa_read_tiles", "pa_check_copy_pairs", "pa_check_slot_mapping", "pa_check_block_tables",
     "pa_check_prefill_rows", "pa_set_debug", "pa_get_debug", "pa_status_string", "pa_last_error", "pa_abi_version",
 )
@@ -64,6 +64,7 @@ def load_library(path: str) -> ctypes.CDLL:
     L.pa_decode_workspace_bytes.restype = ctypes.c_size_t
     L.pa_paged_decode.argtypes = [C, P, ctypes.c_int, P, I32P, I32, I32P, I32, I32, ctypes.c_float, P,
                                   ctypes.c_size_t, P]
+    L.pa_paged_decode_noalloc.argtypes = [C, P, ctypes.c_int, P, I32P, I32, I32P, I32, I32, ctypes.c_float, P]
     L.pa_decode_grouped_workspace_bytes.argtypes = [C, I32, I32, I32]
     L.pa_decode_grouped_workspace_bytes.restype = ctypes.c_size_t
     L.pa_paged_decode_grouped.argtypes = [C, P, ctypes.c_int, P, I32P, I32, I32P, I32, I32, ctypes.c_float, I32,
@@ -80,7 +81,7 @@ def load_library(path: str) -> ctypes.CDLL:
     L.pa_set_debug.restype = None
     L.pa_get_debug.argtypes = []
     L.pa_get_debug.restype = I32
-    for fn in ("pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_paged_decode",
+    for fn in ("pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_paged_decode", "pa_paged_decode_noalloc",
                "pa_paged_decode_grouped",
                "pa_paged_prefill", "pa_read_stream", "pa_read_tiles", "pa_check_copy_pairs", "pa_check_slot_mapping",
                "pa_check_block_tables", "pa_check_prefill_rows"):
@@ -272,6 +273,31 @@ def pa_paged_decode(cache: KVCache, out: torch.Tensor, query: torch.Tensor,
                                  _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), S,
                                  int(max_context_len), float(scale), _ptr(workspace), ws_bytes,
                                  _stream(stream)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # PA_NOALLOC_SCRATCH_BYTES of include/pagedattn.h
+
+
+def pa_paged_decode_noalloc(cache: KVCache, out: torch.Tensor, query: torch.Tensor,
+                            block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
+                            scale: float, stream=None) -> torch.Tensor:
+    """:func:`pa_paged_decode` with the library's own scratch array instead
+    of a workspace (nothing is allocated; calls overlapping on one GPU race)."""
+    _contig("query", query, cache.dtype)
+    _contig("out", out)
+    _contig("block_tables", block_tables, torch.int32)
+    _contig("context_lens", context_lens, torch.int32)
+    S = query.shape[0]
+    if query.shape != (S, cache.num_heads, cache.head_dim) or out.shape != query.shape:
+        raise ValueError("query/out must be [S][H][d]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_tables must be [S][max_blocks], context_lens [S]")
+    _device(cache, out=out, query=query, block_tables=block_tables, context_lens=context_lens)
+    d = cache.desc()
+    _check(lib().pa_paged_decode_noalloc(ctypes.byref(d), _ptr(out), TORCH_TO_PA.get(out.dtype, -1), _ptr(query),
+                                         _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), S,
+                                         int(max_context_len), float(scale), _stream(stream)))
     return out
 
 

@@ -291,6 +291,33 @@ pa_status pa_paged_decode(const pa_kv_cache* cache, void* out, pa_dtype out_dtyp
                                               need > 0 ? workspace : nullptr, (hipStream_t)stream));
 }
 
+pa_status pa_paged_decode_noalloc(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, const void* query,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, int32_t S, int32_t max_context_len, float scale,
+                                  void* stream) {
+  const char* fn = "pa_paged_decode_noalloc";
+  pa::Cache c;
+  pa_status st = check_cache(fn, cache, &c);
+  if (st != PA_OK) return st;
+  if (S < 0) return fail(PA_ERR_INVALID_ARG, "%s: S = %d < 0", fn, S);
+  if (S == 0) return PA_OK;
+  st = check_decode(fn, c, out, out_dtype, query, block_tables, max_blocks_per_seq, context_lens, S,
+                    max_context_len, scale);
+  if (st != PA_OK) return st;
+  const size_t need = pa::decode_workspace_needed(c, S, max_context_len);
+  if (need > (size_t)PA_NOALLOC_SCRATCH_BYTES)
+    return fail(PA_ERR_WORKSPACE, "%s: this call needs %zu bytes of scratch, the library's array holds %zu", fn,
+                need, (size_t)PA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipError_t err = pa::noalloc_scratch(&ws);
+    if (err != hipSuccess)
+      return fail(PA_ERR_LAUNCH, "%s: no device address for the scratch array: %s", fn, hipGetErrorString(err));
+  }
+  return launched(fn, pa::launch_paged_decode(c, out, out_dtype, query, block_tables, max_blocks_per_seq,
+                                              context_lens, S, max_context_len, scale, ws, (hipStream_t)stream));
+}
+
 size_t pa_decode_grouped_workspace_bytes(const pa_kv_cache* cache, int32_t S, int32_t max_context_len,
                                          int32_t group_size) {
   const char* fn = "pa_decode_grouped_workspace_bytes";

@@ -57,6 +57,10 @@ hipError_t launch_paged_decode(const Cache& c, void* out, pa_dtype out_dtype, co
                                const int32_t* context_lens, int32_t S, int32_t max_context_len,
                                float scale, void* workspace, hipStream_t stream);
 
+// Device address of the allocation-free decode's scratch array on the
+// current device (looked up once per device, then cached).
+hipError_t noalloc_scratch(void** ptr);
+
 // Grouped decode: rows taken group_size at a time read shared blocks once.
 // Shapes without a grouped build are served by launch_paged_decode.
 bool decode_grouped_built(pa_dtype dtype, int head_dim, int block_size, int group_size);

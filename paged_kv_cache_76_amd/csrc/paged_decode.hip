@@ -25,6 +25,8 @@
 //   table read sits off the per-block critical path.
 // * Entries of the table at or beyond ceil(ctx/B) are never read; a block id
 //   outside the pool contributes nothing (memory stays in bounds).
+#include <mutex>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -835,6 +837,40 @@ hipError_t launch_paged_decode_grouped(const Cache& c, void* out, pa_dtype out_d
   hipLaunchKernelGGL(decode_reduce_kernel, dim3((unsigned)(S * c.num_heads)), dim3(64), 0, stream, a,
                      (int32_t)c.head_dim, (int32_t)kGroupTokens);
   return hipGetLastError();
+}
+
+// ---- allocation-free decode: partials in a library-owned device array ---------
+// For callers that cannot allocate (graph capture, serving loops, harnesses
+// that forbid hipMalloc).  The array exists once per GPU (every device that
+// loads this code object holds its own copy) for the life of the process.
+// Host code never passes its name to a kernel: on the host the name is a
+// stand-in, not the device address.  Each device's address is looked up once,
+// with that device current, and kept.  Nothing in the array needs to start at
+// zero: every partial the merge kernel reads was written earlier in the same
+// call, in stream order, by the partition kernel (the arrival counters are
+// used only by the off-by-default fused merge, which this path never runs).
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace pa
