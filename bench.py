@@ -69,9 +69,10 @@ PREFILL_SOURCES = ("paged_kv_cache_76_amd/csrc/paged_prefill.hip",)
 
 
 def measured_traffic(path=COUNTERS, sources=DECODE_SOURCES, kernels=("decode_partition_kernel",
-                                                                        "decode_reduce_kernel")) -> float | None:
+                                                                        "decode_reduce_kernel")) -> dict | None:
     """HBM bytes per launch from committed rocprofv3 FETCH_SIZE / WRITE_SIZE
-    runs (scaled by the copy-kernel calibration), summed over ``kernels``, or
+    runs (scaled by the copy-kernel calibration), summed over ``kernels``, and
+    their ratio to the algorithmic bytes per launch of the same profiled run;
     None if the kernel sources changed since those counters were taken."""
     import hashlib
 
@@ -88,7 +89,8 @@ def measured_traffic(path=COUNTERS, sources=DECODE_SOURCES, kernels=("decode_par
             return None
         fs, ws = float(kv["fetch_scale"]), float(kv["write_scale"])
         kib = sum(float(kv[f"{k}_fetch_kib"]) * fs + float(kv[f"{k}_write_kib"]) * ws for k in kernels)
-        return kib * 1024.0
+        alg = float(kv["algorithmic_bytes_per_dispatch"])
+        return {"bytes": round(kib * 1024.0), "ratio": round(kib * 1024.0 / alg, 4)}
     except (OSError, KeyError, ValueError):
         return None
 
@@ -246,11 +248,14 @@ def gemm_ceiling(n: int = 8192, reps: int = 10) -> dict:
     return {"kernel": f"torch.matmul bf16 {n}x{n}x{n}", "tflops": round(2 * n ** 3 / (ms * 1e-3) / 1e12, 1)}
 
 
-def prefill_bench(args) -> int:
+PREFILL_METRIC = "paged causal prefill TFLOP/s, OPT-66B shape (8 x 1024 tokens, 72 heads, d128, bf16)"
+
+
+def prefill_measure(steps: int, warmup: int, cpu_sample: bool, gemm: bool = True) -> dict:
     """8 prompts x 1024 tokens, 72 heads, d=128, bf16, block 16 (OPT-66B
     layer shape): one step writes the prompts' K/V through their slots and runs
-    the causal paged prefill."""
-    import numpy as np
+    the causal paged prefill.  Returns the launch figures, the roofline of the
+    prefill kernel and (optionally) the float64 oracle on one sequence."""
     import torch
 
     from paged_kv_cache_76_amd import _lib as L
@@ -267,10 +272,10 @@ def prefill_bench(args) -> int:
     flops = workloads.prefill_flops(lens, lens, H5, D)
     pbytes = workloads.prefill_bytes(lens, lens, H5, D, 2, B)
     wbytes = 2 * 2 * S5 * L5 * H5 * D * 2
-    n = args.steps + args.warmup
+    n = steps + warmup
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
     for i in range(n):
-        if i == args.warmup:
+        if i == warmup:
             torch.cuda.synchronize()
             t0 = time.perf_counter()
         ev[i][0].record()
@@ -280,18 +285,20 @@ def prefill_bench(args) -> int:
         ev[i][2].record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    K = args.steps
-    w_ms = sum(ev[i][0].elapsed_time(ev[i][1]) for i in range(args.warmup, n)) / K
-    p_all = sorted(ev[i][1].elapsed_time(ev[i][2]) for i in range(args.warmup, n))
+    K = steps
+    w_ms = sum(ev[i][0].elapsed_time(ev[i][1]) for i in range(warmup, n)) / K
+    p_all = sorted(ev[i][1].elapsed_time(ev[i][2]) for i in range(warmup, n))
     p_ms = sum(p_all) / K
     p_pct = [round(p_all[min(K - 1, int(q * K))] * 1e3, 2) for q in (0.1, 0.5, 0.9)]
     tflops = flops / (p_ms * 1e-3) / 1e12
     log(f"prefill {p_ms * 1e3:.1f} us -> {tflops:.1f} TFLOP/s; write {w_ms * 1e3:.1f} us -> "
         f"{wbytes / (w_ms * 1e-3) / 1e9:.0f} GB/s")
-    gemm = gemm_ceiling()
-    log(f"dense bf16 GEMM ceiling on this GPU: {gemm['tflops']:.0f} TFLOP/s")
+    ceiling = None
+    if gemm:
+        ceiling = gemm_ceiling()
+        log(f"dense bf16 GEMM ceiling on this GPU: {ceiling['tflops']:.0f} TFLOP/s")
     cpu = None
-    if args.cpu_seqs > 0:
+    if cpu_sample:
         # the float64 oracle on a bounded sample: sequence 0, all heads, every query
         from oracle import attention as oa
 
@@ -309,30 +316,38 @@ def prefill_bench(args) -> int:
                "sample": f"sequence 0 of {S5} (all {H5} heads, {L5} causal queries), median of 3, float64 NumPy on "
                          f"{os.cpu_count()} host cores ({cpu_model()})", "seconds": dt}
         log(f"cpu oracle sample: {dt:.2f} s -> {cpu['value'] * 1e3:.3f} GFLOP/s")
-    rec = {"metric": "paged causal prefill TFLOP/s, OPT-66B shape (8 x 1024 tokens, 72 heads, d128, bf16)",
-           "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
-           "ms_per_step": round(elapsed / K * 1e3, 4), "higher_is_better": True, "scaling": "weak",
-           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-           "config": {"workload": "paged prefill step (prompt write + causal prefill)", "prompts": S5,
-                      "prompt_len": L5, "heads": H5, "head_dim": D, "block_size": B,
-                      "seed": "SeedSequence(76005)"},
-           # arithmetic intensity flops / bytes ~ 256 is below the ridge 2.5 PFLOP/s / 8 TB/s = 312.5, so the
-           # binding roof at the published peaks is HBM (attainable 256 x 8 TB/s = 2.05 PFLOP/s); the
-           # MFMA view of the same launch is given beside it
-           "roofline": {"bound": "hbm", "kernel": "pa_paged_prefill",
-                        "achieved": round(pbytes / (p_ms * 1e-3) / 1e9, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                        "frac": round(pbytes / (p_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-                        "traffic": measured_traffic(PREFILL_COUNTERS, PREFILL_SOURCES, ("prefill_kernel",)),
-                        "avg_launch_us": round(p_ms * 1e3, 2), "launch_us_p10_p50_p90": p_pct,
-                        "algorithmic_bytes_per_launch": pbytes,
-                        "arithmetic_intensity": round(flops / pbytes, 1),
-                        "ridge": round(PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9), 1),
-                        "mfma": {"achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                                 "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "algorithmic_flops_per_launch": flops}},
-           "gemm_ceiling": dict(gemm, pct_achieved=round(100 * tflops / gemm["tflops"], 2)),
-           "write": {"kernel": "pa_reshape_and_cache", "avg_launch_us": round(w_ms * 1e3, 2),
-                     "achieved_GBps": round(wbytes / (w_ms * 1e-3) / 1e9, 1), "bytes_per_launch": wbytes},
-           "cpu_baseline": cpu}
+    traffic = measured_traffic(PREFILL_COUNTERS, PREFILL_SOURCES, ("prefill_kernel",))
+    # arithmetic intensity flops / bytes ~ 256 is below the ridge 2.5 PFLOP/s / 8 TB/s = 312.5, so the
+    # binding roof at the published peaks is HBM (attainable 256 x 8 TB/s = 2.05 PFLOP/s); the MFMA
+    # view of the same launch is given beside it
+    roof = {"bound": "hbm", "kernel": "pa_paged_prefill",
+            "achieved": round(pbytes / (p_ms * 1e-3) / 1e9, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(pbytes / (p_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "traffic": traffic and traffic["bytes"], "traffic_over_algorithmic": traffic and traffic["ratio"],
+            "avg_launch_us": round(p_ms * 1e3, 2), "launch_us_p10_p50_p90": p_pct,
+            "algorithmic_bytes_per_launch": pbytes,
+            "arithmetic_intensity": round(flops / pbytes, 1),
+            "ridge": round(PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9), 1),
+            "mfma": {"achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "algorithmic_flops_per_launch": flops}}
+    return {"tflops": tflops, "elapsed": elapsed, "steps": K, "warmup": warmup, "roofline": roof,
+            "gemm_ceiling": ceiling and dict(ceiling, pct_achieved=round(100 * tflops / ceiling["tflops"], 2)),
+            "write": {"kernel": "pa_reshape_and_cache", "avg_launch_us": round(w_ms * 1e3, 2),
+                      "achieved_GBps": round(wbytes / (w_ms * 1e-3) / 1e9, 1), "bytes_per_launch": wbytes},
+            "cpu_baseline": cpu,
+            "config": {"workload": "paged prefill step (prompt write + causal prefill)", "prompts": S5,
+                       "prompt_len": L5, "heads": H5, "head_dim": D, "block_size": B,
+                       "seed": "SeedSequence(76005)"}}
+
+
+def prefill_bench(args) -> int:
+    m = prefill_measure(args.steps, args.warmup, args.cpu_seqs > 0)
+    K = m["steps"]
+    rec = {"metric": PREFILL_METRIC, "value": round(m["tflops"], 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
+           "warmup": args.warmup, "ms_per_step": round(m["elapsed"] / K * 1e3, 4), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": m["config"],
+           "roofline": m["roofline"], "gemm_ceiling": m["gemm_ceiling"], "write": m["write"],
+           "cpu_baseline": m["cpu_baseline"]}
     print(json.dumps(rec), flush=True)
     return 0
 
@@ -811,6 +826,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-seqs", type=int, default=64, help="sequences in the CPU-oracle sample (0: skip)")
+    ap.add_argument("--prefill-steps", type=int, default=10,
+                    help="decode workload: timed steps of the OPT-66B prefill sub-record (0: skip)")
     ap.add_argument("--workload", choices=["decode", "copy", "prefill", "serving", "shared", "longdecode",
                                            "blocksize", "copyablation", "accounting", "prefix", "swap"],
                     default="decode",
@@ -860,9 +877,12 @@ def main() -> int:
         return longdecode_bench(args)
     K, W = args.steps, args.warmup
     # warm-up, then K timed steps with no per-step instrumentation (the
-    # throughput), then K more with events around each decode (the launch
-    # durations of the roofline); every step appends one token per sequence
-    n_steps = W + 2 * K
+    # throughput); every step appends one token per sequence.  Then the
+    # decodes of those same K steps run again with events around each launch
+    # (the launch durations of the roofline): decode only reads the cache, and
+    # the later steps' writes went to positions past every replayed context,
+    # so a replay reads exactly the bytes its step read.
+    n_steps = W + K
 
     lens0 = workloads.opt13b_decode_lengths(2, S)
     log(f"building OPT-13B decode workload: S={S} H={H} d={D} B={B} fp16, "
@@ -897,36 +917,44 @@ def main() -> int:
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_steps)]
 
-    def step(i, timed_decode: bool):
+    def decode(i):
+        st = steps[i]
+        L.pa_paged_decode(batch.cache, out, st["q"], st["tables"], st["lens"], max_ctx, scale, ws)
+
+    def step(i):
         st = steps[i]
         if st["n_pairs"]:
             L.pa_copy_blocks(batch.cache, st["pairs"])
         L.pa_reshape_and_cache(batch.cache, st["k"], st["v"], st["slots"])
-        if timed_decode:
-            ev[i][0].record()
-        L.pa_paged_decode(batch.cache, out, st["q"], st["tables"], st["lens"], max_ctx, scale, ws)
-        if timed_decode:
-            ev[i][1].record()
+        decode(i)
 
     for i in range(W):
-        step(i, True)
+        step(i)
     torch.cuda.synchronize()
     log(f"warmup done ({W} steps); timing {K} steps")
     t0 = time.perf_counter()
     for i in range(W, W + K):
-        step(i, False)
+        step(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    log(f"timing {K} more steps with events around each decode launch")
-    for i in range(W + K, n_steps):
-        step(i, True)
+    log(f"replaying the decodes of those {K} steps with events around each launch")
+    for i in range(W, W + K):
+        ev[i][0].record()
+        decode(i)
+        ev[i][1].record()
     torch.cuda.synchronize()
 
     write_bytes = 2 * 2 * S * H * D * ELEM          # read + write, keys and values
     step_bytes = sum(workloads.decode_bytes(steps[i]["lens_host"], H, D, ELEM, B) + write_bytes
                      + 2 * 2 * steps[i]["n_pairs"] * H * B * D * ELEM for i in range(W, W + K))
-    dec_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(W + K, n_steps)]
-    dec_bytes = [workloads.decode_bytes(steps[i]["lens_host"], H, D, ELEM, B) for i in range(W + K, n_steps)]
+    dec_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(W, W + K)]
+    dec_bytes = [workloads.decode_bytes(steps[i]["lens_host"], H, D, ELEM, B) for i in range(W, W + K)]
+    # every decode dispatch of this run (warm-up, timed steps, replays), for
+    # matching rocprofv3 counter averages against algorithmic bytes
+    all_dispatch_bytes = [workloads.decode_bytes(steps[i]["lens_host"], H, D, ELEM, B)
+                          for i in list(range(W + K)) + list(range(W, W + K))]
+    log(f"algorithmic bytes per decode dispatch, averaged over all {len(all_dispatch_bytes)} of this run: "
+        f"{sum(all_dispatch_bytes) / len(all_dispatch_bytes):.0f}")
     value = step_bytes / elapsed / 1e9
     ms_per_step = elapsed / K * 1e3
     dec_avg_ms = sum(dec_ms) / K
@@ -941,6 +969,10 @@ def main() -> int:
         cpu = cpu_baseline(batch, args.cpu_seqs)
 
     traffic = measured_traffic()
+    prefill = None
+    if args.prefill_steps > 0:
+        log(f"prefill sub-record: OPT-66B 8 x 1024 prompts, {args.prefill_steps} steps")
+        prefill = prefill_measure(args.prefill_steps, 2, args.cpu_seqs > 0, gemm=False)
     last = steps[-1]
     ach = achievable_reads(batch.cache, last["tables"].cpu().numpy(), last["lens_host"])
     ach["decode_frac_of_kv_tile_read"] = round(dec_gbs / ach["kv_tile_read_GBps"], 4)
@@ -970,14 +1002,23 @@ def main() -> int:
         "roofline": {"bound": "hbm", "kernel": "pa_paged_decode (partition kernel; its merge kernel runs only for "
                                                "contexts longer than one 4096-token partition)", "achieved": round(dec_gbs, 2),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
-                     "traffic": traffic, "avg_launch_us": round(dec_avg_ms * 1e3, 2),
+                     "traffic": traffic and traffic["bytes"],
+                     "traffic_over_algorithmic": traffic and traffic["ratio"],
+                     "avg_launch_us": round(dec_avg_ms * 1e3, 2),
                      "launch_us_p10_p50_p90": [round(pct(0.1), 2), round(pct(0.5), 2), round(pct(0.9), 2)],
                      "algorithmic_bytes_per_launch": int(sum(dec_bytes) / K)},
         "cpu_baseline": cpu,
         "achievable": ach,
         "timing": (f"value and ms_per_step: {K} steps with no per-step instrumentation after {W} warm-up steps; "
-                   f"roofline launch durations: {K} further steps with events around each decode launch"),
+                   f"roofline launch durations: the decodes of the same {K} steps replayed with events around "
+                   f"each launch (decode is read-only: a replay reads the bytes of its step)"),
     }
+    if prefill is not None:
+        rec["prefill"] = {"metric": PREFILL_METRIC, "value": round(prefill["tflops"], 2), "unit": "TFLOP/s",
+                          "steps": prefill["steps"], "warmup": prefill["warmup"],
+                          "ms_per_step": round(prefill["elapsed"] / prefill["steps"] * 1e3, 4),
+                          "dtype": "bf16", "config": prefill["config"], "roofline": prefill["roofline"],
+                          "write": prefill["write"], "cpu_baseline": prefill["cpu_baseline"]}
     print(json.dumps(rec), flush=True)
     return 0
 

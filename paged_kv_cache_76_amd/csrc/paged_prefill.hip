@@ -83,14 +83,14 @@ __device__ __forceinline__ void lds_barrier() {
 // write LDS directly) have completed
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x3f70); }
 // 16 bytes per lane from global memory straight into LDS at lds_base + 16 *
-// lane (global_load_lds_dwordx4; lds_base is wave-uniform and goes to M0,
-// which nothing else in this kernel uses; one wait state after the M0 write).
+// lane (global_load_lds_dwordx4; the LDS address is wave-uniform and comes
+// from M0, which the "{m0}" operand makes the compiler set before the
+// instruction, so it knows M0's value; one wait state follows the M0 write).
 // Issued as inline assembly so the compiler does not hold every later LDS
 // read back until these loads complete: the kernel orders them itself
 // (wait_vmem, then a barrier, before any wave reads the buffer).
 __device__ __forceinline__ void load_to_lds(const void* src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base)
-               : "memory", "m0");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_base) : "memory");
 }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(lds_void_t*)p;
@@ -99,13 +99,10 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // register: the immediate offset k * 1024 advances both the global address
 // and the LDS address; M0 takes m[k] (so the LDS pieces may have gaps).
 __device__ __forceinline__ void load4_to_lds(const void* src, uint32_t m0, uint32_t m1, uint32_t m2, uint32_t m3) {
-  asm volatile(
-      "s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off\n\t"
-      "s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:1024\n\t"
-      "s_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:2048\n\t"
-      "s_mov_b32 m0, %4\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:3072" ::"v"(src),
-      "s"(m0), "s"(m1), "s"(m2), "s"(m3)
-      : "memory", "m0");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:1024" ::"v"(src), "{m0}"(m1) : "memory");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:2048" ::"v"(src), "{m0}"(m2) : "memory");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:3072" ::"v"(src), "{m0}"(m3) : "memory");
 }
 
 constexpr int kD = 128;         // head_dim
