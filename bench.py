@@ -360,63 +360,69 @@ def _line(metric, value, unit, steps, warmup, ms_per_step, dtype, config, **extr
     print(json.dumps(rec), flush=True)
 
 
-def serving_bench(args) -> int:
-    """32 consecutive steps of a 256-sequence serving loop at the OPT-13B
-    shape (fp16), block size 16 and 32.  The host block-manager work of all
+SERVING_METRIC = "paged serving-loop decode seq-steps/s, OPT-13B shape (256 seqs, 32 steps)"
+
+
+def serving_measure(bs: int, steps: int = 32, wall_pass: bool = True) -> tuple[float, float, dict, dict]:
+    """``steps`` consecutive steps of a 256-sequence serving loop at the OPT-13B
+    shape (fp16), block size ``bs``.  The host block-manager work of all
     steps runs first (timed on its own); the device loop then runs from
-    inputs already in HBM.  A second, interleaved pass (host step -> pinned
-    upload -> kernels, every step) gives the wall time per step."""
-    import numpy as np
+    inputs already in HBM.  With ``wall_pass``, a second, interleaved pass
+    (host step -> pinned upload -> kernels, every step) gives the wall time
+    per step.  Returns (seq-steps/s, ms per step, config, extra keys)."""
     import torch
 
     from paged_kv_cache_76_amd import workloads
     from paged_kv_cache_76_amd.serving import ServingLoop, opt13b_serving_lengths
 
     prompt, out, start = opt13b_serving_lengths(3, 256)
-    steps = 32
-    for bs in (16, 32):
-        log(f"serving loop: 256 seqs, B={bs}")
-        # device pass: every step's plan made ahead and resident in HBM
-        loop = ServingLoop(3, prompt, out, start, H, D, bs, DTYPE, keep_history=False)
-        counts = loop.active_counts(steps)
-        toks = [loop.tokens(n, "cuda") for n in counts]
-        prepared = []
-        for t in range(steps):
-            rows = loop.active_rows()
-            assert len(rows) == counts[t]
-            host, lens = loop.plan(rows)
-            loop.finish(rows)
-            prepared.append((rows, {k: v.cuda() for k, v in host.items()}, lens))
-        bm_ms = loop.bm_seconds / steps * 1e3
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-        from paged_kv_cache_76_amd import _lib as L
-        outs = torch.empty((256, H, D), dtype=torch.float16, device="cuda")
-        # one untimed decode of step 0's inputs (read-only): the first launch of
-        # a kernel in the process loads its code object (~2 ms), which must not
-        # land inside the timed steps
-        rows0, dev0, lens0 = prepared[0]
-        L.pa_paged_decode(loop.cache, outs[: len(rows0)], toks[0][2], dev0["tables"], dev0["lens"],
-                          int(lens0.max()), loop.scale, loop.ws)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i, (rows, dev, lens) in enumerate(prepared):
-            k, v, q = toks[i]
-            ev[i][0].record()
-            if dev["pairs"].shape[0]:
-                L.pa_copy_blocks(loop.cache, dev["pairs"])
-            L.pa_reshape_and_cache(loop.cache, k, v, dev["slots"])
-            L.pa_paged_decode(loop.cache, outs[: len(rows)], q, dev["tables"], dev["lens"],
-                              int(lens.max()), loop.scale, loop.ws)
-            ev[i][1].record()
-        torch.cuda.synchronize()
-        gpu_s = time.perf_counter() - t0
-        step_ms = [a.elapsed_time(b) for a, b in ev]
-        seq_steps = sum(len(r) for r, _, _ in prepared)
-        nbytes = sum(workloads.decode_bytes(lens, H, D, ELEM, bs) + 4 * len(rows) * H * D * ELEM
-                     for rows, _, lens in prepared)
-        stats = loop.mgr.stats()
-        finished = 256 - len(loop.active_rows())
-        del loop, prepared
+    log(f"serving loop: 256 seqs, B={bs}")
+    # device pass: every step's plan made ahead and resident in HBM
+    loop = ServingLoop(3, prompt, out, start, H, D, bs, DTYPE, keep_history=False)
+    counts = loop.active_counts(steps)
+    toks = [loop.tokens(n, "cuda") for n in counts]
+    prepared = []
+    for t in range(steps):
+        rows = loop.active_rows()
+        assert len(rows) == counts[t]
+        host, lens = loop.plan(rows)
+        loop.finish(rows)
+        prepared.append((rows, {k: v.cuda() for k, v in host.items()}, lens))
+    bm_ms = loop.bm_seconds / steps * 1e3
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    from paged_kv_cache_76_amd import _lib as L
+    outs = torch.empty((256, H, D), dtype=torch.float16, device="cuda")
+    # one untimed decode of step 0's inputs (read-only): the first launch of
+    # a kernel in the process loads its code object (~2 ms), which must not
+    # land inside the timed steps
+    rows0, dev0, lens0 = prepared[0]
+    L.pa_paged_decode(loop.cache, outs[: len(rows0)], toks[0][2], dev0["tables"], dev0["lens"],
+                      int(lens0.max()), loop.scale, loop.ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i, (rows, dev, lens) in enumerate(prepared):
+        k, v, q = toks[i]
+        ev[i][0].record()
+        if dev["pairs"].shape[0]:
+            L.pa_copy_blocks(loop.cache, dev["pairs"])
+        L.pa_reshape_and_cache(loop.cache, k, v, dev["slots"])
+        L.pa_paged_decode(loop.cache, outs[: len(rows)], q, dev["tables"], dev["lens"],
+                          int(lens.max()), loop.scale, loop.ws)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    gpu_s = time.perf_counter() - t0
+    step_ms = [a.elapsed_time(b) for a, b in ev]
+    seq_steps = sum(len(r) for r, _, _ in prepared)
+    nbytes = sum(workloads.decode_bytes(lens, H, D, ELEM, bs) + 4 * len(rows) * H * D * ELEM
+                 for rows, _, lens in prepared)
+    # tail waste (allocated but unused slots) averaged over the steps' batches
+    waste = [int(sum(-(-int(x) // bs) * bs - int(x) for x in lens)) for _, _, lens in prepared]
+    used = [int(sum(int(x) for x in lens)) for _, _, lens in prepared]
+    stats = loop.mgr.stats()
+    finished = 256 - len(loop.active_rows())
+    del loop, prepared
+    extra = {}
+    if wall_pass:
         # interleaved pass: block-manager step -> pinned upload of the plan ->
         # kernels, every step (activations already on the device, as a
         # model's projections would be)
@@ -429,20 +435,29 @@ def serving_bench(args) -> int:
         torch.cuda.synchronize()
         wall_s = time.perf_counter() - t1
         del loop2, toks2
-        kernel_s = sum(step_ms) * 1e-3
-        _line("paged serving-loop decode seq-steps/s, OPT-13B shape (256 seqs, 32 steps)", seq_steps / kernel_s,
-              "seq-steps/s", steps, 0, sum(step_ms) / steps, "f16",
-              {"workload": "serving loop (append, write, decode per step; finished sequences freed)",
-               "sequences": 256, "heads": H, "head_dim": D, "block_size": bs,
-               "lengths": "prompt lognormal(160,1)<=1024, output lognormal(300,1), total<=2048, "
-                          "uniform progress at step 0", "seed": "SeedSequence(76003)"},
-              achieved_GBps=round(nbytes / kernel_s / 1e9, 1), pct_of_peak=round(100 * nbytes / kernel_s / 1e9 / PEAK_HBM_GBS, 2),
-              seq_steps=seq_steps, finished_in_loop=finished,
-              host_block_manager_ms_per_step=round(bm_ms, 3),
-              wall_ms_per_step_interleaved=round(wall_s / steps * 1e3, 3),
-              gpu_loop_wall_ms_per_step=round(gpu_s / steps * 1e3, 3),
-              tail_waste_slots_end=stats["tail_waste_slots"],
-              slot_utilisation_end=round(stats["slot_utilisation"], 4))
+        extra["wall_ms_per_step_interleaved"] = round(wall_s / steps * 1e3, 3)
+    kernel_s = sum(step_ms) * 1e-3
+    config = {"workload": "serving loop (append, write, decode per step; finished sequences freed)",
+              "sequences": 256, "heads": H, "head_dim": D, "block_size": bs,
+              "lengths": "prompt lognormal(160,1)<=1024, output lognormal(300,1), total<=2048, "
+                         "uniform progress at step 0", "seed": "SeedSequence(76003)"}
+    extra.update(achieved_GBps=round(nbytes / kernel_s / 1e9, 1),
+                 pct_of_peak=round(100 * nbytes / kernel_s / 1e9 / PEAK_HBM_GBS, 2),
+                 seq_steps=seq_steps, finished_in_loop=finished,
+                 host_block_manager_ms_per_step=round(bm_ms, 3),
+                 gpu_loop_wall_ms_per_step=round(gpu_s / steps * 1e3, 3),
+                 tail_waste_slots_mean=round(sum(waste) / steps, 1),
+                 tail_waste_pct_mean=round(100 * sum(waste) / (sum(waste) + sum(used)), 3),
+                 tail_waste_slots_end=stats["tail_waste_slots"],
+                 slot_utilisation_end=round(stats["slot_utilisation"], 4))
+    return seq_steps / kernel_s, sum(step_ms) / steps, config, extra
+
+
+def serving_bench(args) -> int:
+    """The serving loop at block size 16 and 32 (with the interleaved wall-time pass)."""
+    for bs in (16, 32):
+        v, ms, config, extra = serving_measure(bs)
+        _line(SERVING_METRIC, v, "seq-steps/s", 32, 0, ms, "f16", config, **extra)
     return 0
 
 
@@ -476,13 +491,21 @@ def shared_bench(args) -> int:
         span = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
         loop.warm(plans[0])                             # first-launch code loading, untimed
         torch.cuda.synchronize()
+        # the timed span has no per-step instrumentation (an event pair per
+        # step costs several us); per-launch decode durations come from a
+        # replay of every step's decode with events around it afterwards
         span[0].record()
         for i in range(steps):
-            loop.launch(plans[i], ev[i])
+            loop.launch(plans[i])
         span[1].record()
         torch.cuda.synchronize()
-        ms = [a.elapsed_time(b) for a, b in ev]
         kernel_s = span[0].elapsed_time(span[1]) * 1e-3
+        for i in range(steps):
+            ev[i][0].record()
+            loop.decode_only(plans[i])
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        ms = [a.elapsed_time(b) for a, b in ev]
         cow_bytes = copies * 2 * 2 * H * B * D * 2
         name = ("beam search (width 4)" if beam else "parallel sampling (4 per prompt)") + \
             (", grouped decode" if grouped else "")
@@ -496,7 +519,10 @@ def shared_bench(args) -> int:
               seq_steps_per_s=round(128 * steps / kernel_s, 1),
               cow_pairs_per_step=round(copies / steps, 2), blocks_saved_by_sharing_mean=round(sum(saved) / steps, 1),
               logical_GB_per_step=round(logical / steps / 1e9, 4), unique_GB_per_step=round(unique / steps / 1e9, 4),
-              step_us_p10_p50_p90=[round(sorted(ms)[int(q * (steps - 1))] * 1e3, 1) for q in (0.1, 0.5, 0.9)])
+              decode_launch_us_p10_p50_p90=[round(sorted(ms)[int(q * (steps - 1))] * 1e3, 1) for q in (0.1, 0.5, 0.9)],
+              decode_launch_us_mean=round(sum(ms) / steps * 1e3, 1),
+              timing="span of the 64 steps (copy, write, decode launches) with no per-step instrumentation; "
+                     "decode launch durations from replays of every step's decode with events around each")
         del plans
     return 0
 
@@ -579,8 +605,9 @@ def accounting_bench(args) -> int:
 
 
 def blocksize_bench(args) -> int:
-    """The OPT-13B decode workload (64 x 40 heads, d=128, fp16, contexts
-    U[1,2048]) for block sizes 8..128: decode GB/s against tail waste."""
+    """Block sizes 8..128: the OPT-13B decode workload (64 x 40 heads, d=128,
+    fp16, contexts U[1,2048]) and the 256-sequence serving loop, decode GB/s
+    against tail waste."""
     import torch
 
     from paged_kv_cache_76_amd import _lib as L
@@ -613,6 +640,11 @@ def blocksize_bench(args) -> int:
               pct_of_peak=round(100 * nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2), median_us=round(ms * 1e3, 2),
               tail_waste_slots=waste, tail_waste_pct=round(100 * waste / (waste + int(lens.sum())), 3))
         del b, ws, out
+    # the same sweep on the 256-sequence serving loop (device pass only)
+    for bs in (8, 16, 32, 64, 128):
+        v, ms, config, extra = serving_measure(bs, wall_pass=False)
+        config["workload"] = "block-size sweep of the serving loop"
+        _line(SERVING_METRIC, v, "seq-steps/s", 32, 0, ms, "f16", config, **extra)
     return 0
 
 

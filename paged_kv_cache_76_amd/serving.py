@@ -327,6 +327,19 @@ class BeamLoop:
     def step(self, events=None) -> StepRecord:
         return self.launch(self.plan(), events)
 
+    def decode_only(self, plan: dict) -> torch.Tensor:
+        """The decode launch of ``plan`` alone (read-only on the cache), for
+        timing it again after the steps have run."""
+        dev = plan["dev"]
+        out = torch.empty((len(plan["rows"]), self.H, self.d), dtype=TORCH[self.dtype], device=self.device)
+        if self.grouped:
+            pa_paged_decode_grouped(self.cache, out, dev["q"], dev["tables"], dev["lens"], plan["max_ctx"],
+                                    self.scale, self.W, self.ws)
+        else:
+            pa_paged_decode(self.cache, out, dev["q"], dev["tables"], dev["lens"], plan["max_ctx"], self.scale,
+                            self.ws)
+        return out
+
     def warm(self, plan: dict) -> None:
         """Launch this loop's kernels once without changing the cache: a copy
         of block 0 onto itself and the decode of ``plan``'s inputs (read-only;

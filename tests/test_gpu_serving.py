@@ -29,7 +29,7 @@ def _check(loop, rec, dtype, what):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("B", [16, 32])
+@pytest.mark.parametrize("B", [8, 16, 32, 64, 128])
 def test_serving_loop_opt13b(B):
     # 256 sequences, OPT-13B shape (40 heads of 128), fp16, 32 steps
     print(f"serving loop B={B} (40 heads, every row at steps 0, 15, 31)", flush=True)
