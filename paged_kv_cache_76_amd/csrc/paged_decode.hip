@@ -27,6 +27,8 @@
 //   outside the pool contributes nothing (memory stays in bounds).
 #include <mutex>
 
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -439,76 +441,117 @@ void decode_grouped_kernel(DecodeArgs a, int32_t ngroups) {
     }
   };
 
+  // Steps [0, n_sh): every row of the group maps the step's block to one
+  // physical block and has all of the step's tokens -- read once for all
+  // rows.  Sharing that comes from forks forms such a prefix; the steps after
+  // it (the rows' private tails) are split into one unit per (step, row) and
+  // continue the round-robin where the shared steps left off, so a tail step
+  // (W loads) does not land on a single wave.  Any step past the prefix is
+  // read per row even if it happens to be shared, which is always correct.
   const int nsteps = min(STEPS, (maxctx - p * P + G - 1) / G);
-  for (int step = w; step < nsteps; step += NW) {
-    const int tb = p * P + step * G;
+  int n_sh = 0;
+  {
+    constexpr int NM = (STEPS + 63) / 64;  // steps judged 64 at a time, one per lane
+    bool prefix = true;
+#pragma unroll
+    for (int q = 0; q < NM; ++q) {
+      const int st = 64 * q + lane;
+      const int tb = p * P + st * G;
+      const int jl = (st * G) / BS;  // block of step st within the window (< P / BS <= 64)
+      bool sh = st < nsteps;
+      int ph0 = 0;
+#pragma unroll
+      for (int r = 0; r < W; ++r) {
+        const int ph = __shfl(tbl[r], jl);
+        if (r == 0) ph0 = ph;
+        sh = sh && (tb + G <= ctx[r]) && (ph == ph0);
+      }
+      const uint64_t mask = __ballot(sh && ph0 >= 0 && ph0 < a.N);
+      if (prefix) {
+        const int run = (~mask) ? __builtin_ctzll(~mask) : 64;  // leading shared steps of this group of 64
+        n_sh += run;
+        prefix = run == 64;
+      }
+    }
+  }
+  for (int step = w; step < n_sh; step += NW) {
     const int jl = (step * G) / BS;
     const int off0 = (step * G) % BS;
-    int phys[W];
-    bool shared = true;
+    const int phys = __builtin_amdgcn_readlane(tbl[0], jl);
+    const int64_t base = (((int64_t)phys * a.H + h) * BS + off0 + tr) * LPT + c;
+    u32x4 kc[NCH], vc[NCH];
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      kc[i] = load_kv(&a.kpool[base + i * TPL * LPT]);
+      vc[i] = load_kv(&a.vpool[base + i * TPL * LPT]);
+    }
+    // scores of every row first (the key chunks die here), then one value
+    // chunk widened at a time for all rows
+    float sc[W][NCH];
 #pragma unroll
     for (int r = 0; r < W; ++r) {
-      phys[r] = __builtin_amdgcn_readlane(tbl[r], jl);
-      shared = shared && (tb + G <= ctx[r]) && (phys[r] == phys[0]);
+      float mblk = kNegBig;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        sc[r][i] = group_sum<LPT>(dot_chunk(E{}, qc[r], kc[i])) * a.scale_log2;
+        mblk = fmaxf(mblk, sc[r][i]);
+      }
+      const bool raise = mblk > m[r] + kGroupSlack;
+      if (__any(raise)) {
+        const float m_new = raise ? mblk : m[r];
+        const float alpha = fast_exp2(m[r] - m_new);
+        l[r] *= alpha;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) o[r][e] *= alpha;
+        m[r] = m_new;
+      }
     }
-    shared = shared && phys[0] >= 0 && phys[0] < a.N;
-    u32x4 kc[NCH], vc[NCH];
-    bool valid[NCH];
-    if (shared) {
-      const int64_t base = (((int64_t)phys[0] * a.H + h) * BS + off0 + tr) * LPT + c;
 #pragma unroll
-      for (int i = 0; i < NCH; ++i) {
-        kc[i] = load_kv(&a.kpool[base + i * TPL * LPT]);
-        vc[i] = load_kv(&a.vpool[base + i * TPL * LPT]);
-        valid[i] = true;
-      }
-      // scores of every row first (the key chunks die here), then one value
-      // chunk widened at a time for all rows
-      float sc[W][NCH];
+    for (int i = 0; i < NCH; ++i) {
+      float vf[VEC];
+      widen(E{}, vc[i], vf);
 #pragma unroll
       for (int r = 0; r < W; ++r) {
-        float mblk = kNegBig;
+        const float pi = fast_exp2(sc[r][i] - m[r]);
+        l[r] += pi;
 #pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-          sc[r][i] = group_sum<LPT>(dot_chunk(E{}, qc[r], kc[i])) * a.scale_log2;
-          mblk = fmaxf(mblk, sc[r][i]);
-        }
-        const bool raise = mblk > m[r] + kGroupSlack;
-        if (__any(raise)) {
-          const float m_new = raise ? mblk : m[r];
-          const float alpha = fast_exp2(m[r] - m_new);
-          l[r] *= alpha;
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) o[r][e] *= alpha;
-          m[r] = m_new;
-        }
+        for (int e = 0; e < VEC; ++e) o[r][e] = __builtin_fmaf(pi, vf[e], o[r][e]);
       }
+    }
+  }
+  // Tail units u = (step - n_sh) * W + row go to wave (n_sh + u) % NW.  As
+  // NW is a multiple of W, every unit of a wave has the same row: R below.
+  static_assert(NW % W == 0, "the tail split gives each wave one row");
+  const int n_units = (nsteps - n_sh) * W;
+  const int u0 = ((w - n_sh) % NW + NW) % NW;  // this wave's first unit
+  auto tail = [&](auto row_tag) {
+    constexpr int R = decltype(row_tag)::value;
+    for (int u = u0; u < n_units; u += NW) {
+      const int step = n_sh + u / W;
+      const int tb = p * P + step * G;
+      if (tb >= ctx[R]) continue;  // uniform: the row has no token in this step
+      const int jl = (step * G) / BS;
+      const int off0 = (step * G) % BS;
+      const int phys = __builtin_amdgcn_readlane(tbl[R], jl);
+      const bool in_pool = phys >= 0 && phys < a.N;
+      const int64_t base = (((int64_t)(in_pool ? phys : 0) * a.H + h) * BS + off0 + tr) * LPT + c;
+      u32x4 kc[NCH], vc[NCH];
+      bool valid[NCH];
 #pragma unroll
       for (int i = 0; i < NCH; ++i) {
-        float vf[VEC];
-        widen(E{}, vc[i], vf);
-#pragma unroll
-        for (int r = 0; r < W; ++r) {
-          const float pi = fast_exp2(sc[r][i] - m[r]);
-          l[r] += pi;
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) o[r][e] = __builtin_fmaf(pi, vf[e], o[r][e]);
-        }
+        valid[i] = in_pool && (tb + i * TPL + tr < ctx[R]);
+        kc[i] = valid[i] ? load_kv(&a.kpool[base + i * TPL * LPT]) : u32x4{0, 0, 0, 0};
+        vc[i] = valid[i] ? load_kv(&a.vpool[base + i * TPL * LPT]) : u32x4{0, 0, 0, 0};
       }
-    } else {
-#pragma unroll
-      for (int r = 0; r < W; ++r) {
-        if (tb >= ctx[r]) continue;  // uniform
-        const bool in_pool = phys[r] >= 0 && phys[r] < a.N;
-        const int64_t base = (((int64_t)(in_pool ? phys[r] : 0) * a.H + h) * BS + off0 + tr) * LPT + c;
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-          valid[i] = in_pool && (tb + i * TPL + tr < ctx[r]);
-          kc[i] = valid[i] ? load_kv(&a.kpool[base + i * TPL * LPT]) : u32x4{0, 0, 0, 0};
-          vc[i] = valid[i] ? load_kv(&a.vpool[base + i * TPL * LPT]) : u32x4{0, 0, 0, 0};
-        }
-        update(r, kc, vc, valid);
-      }
+      update(R, kc, vc, valid);
+    }
+  };
+  if (n_units > u0) {
+    switch (u0 % W) {
+      case 0: tail(std::integral_constant<int, 0>{}); break;
+      case 1: tail(std::integral_constant<int, 1 % W>{}); break;
+      case 2: tail(std::integral_constant<int, 2 % W>{}); break;
+      default: tail(std::integral_constant<int, 3 % W>{}); break;
     }
   }
 
