@@ -461,73 +461,86 @@ def serving_bench(args) -> int:
     return 0
 
 
-def shared_bench(args) -> int:
+SHARED_METRIC = "paged decode with shared blocks, unique-HBM GB/s, OPT-13B shape, bf16"
+
+
+def shared_measure(beam: bool, grouped: bool, steps: int = 64) -> tuple[float, float, dict, dict]:
     """32 prompt groups of 512 tokens x 4 sequences at the OPT-13B shape in
-    bf16: parallel sampling (prompt blocks shared, reference count 4) and
-    beam search (per-step fork/free remaps, copy-on-write of shared partial
-    blocks through pa_copy_blocks), 64 decode steps each."""
+    bf16: parallel sampling (prompt blocks shared, reference count 4) or beam
+    search (per-step fork/free remaps, copy-on-write of shared partial blocks
+    through pa_copy_blocks), ``steps`` decode steps.  Returns (unique-byte
+    GB/s, ms per step, config, extra keys)."""
     import torch
 
     from paged_kv_cache_76_amd import workloads
     from paged_kv_cache_76_amd.serving import BeamLoop
 
-    steps = 64
+    log(f"shared blocks: beam={beam} grouped={grouped}")
+    loop = BeamLoop(4, 32, 4, 512, steps, H, D, B, "bf16", beam=beam, keep_history=False, grouped=grouped)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    logical = unique = copies = 0
+    saved = []
+    # host work (remaps, appends, activations, uploads) for every step first,
+    # so the timed launches find everything resident in HBM
+    plans = []
+    for i in range(steps):
+        p = loop.plan()
+        logical += workloads.decode_bytes(p["lens"], H, D, 2, B)
+        unique += loop.unique_blocks_read(p["rows"]) * B * H * D * 2 * 2
+        copies += p["n_pairs"]
+        saved.append(loop.mgr.blocks_saved_by_sharing())
+        plans.append(p)
+    span = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    loop.warm(plans[0])                             # first-launch code loading, untimed
+    torch.cuda.synchronize()
+    # the timed span has no per-step instrumentation (an event pair per
+    # step costs several us); per-launch decode durations come from a
+    # replay of every step's decode with events around it afterwards
+    span[0].record()
+    for i in range(steps):
+        loop.launch(plans[i])
+    span[1].record()
+    torch.cuda.synchronize()
+    kernel_s = span[0].elapsed_time(span[1]) * 1e-3
+    for i in range(steps):
+        ev[i][0].record()
+        loop.decode_only(plans[i])
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    cow_bytes = copies * 2 * 2 * H * B * D * 2
+    name = ("beam search (width 4)" if beam else "parallel sampling (4 per prompt)") + \
+        (", grouped decode" if grouped else "")
+    config = {"workload": f"shared-block decode: {name}", "groups": 32, "width": 4, "prompt_len": 512,
+              "heads": H, "head_dim": D, "block_size": B, "seed": "SeedSequence(76004)",
+              "decode_entry": "pa_paged_decode_grouped (group 4)" if grouped else "pa_paged_decode"}
+    extra = dict(logical_GBps=round(logical / kernel_s / 1e9, 1),
+                 pct_of_peak_unique=round(100 * (unique + cow_bytes) / kernel_s / 1e9 / PEAK_HBM_GBS, 2),
+                 seq_steps_per_s=round(128 * steps / kernel_s, 1),
+                 cow_pairs_per_step=round(copies / steps, 2), blocks_saved_by_sharing_mean=round(sum(saved) / steps, 1),
+                 logical_GB_per_step=round(logical / steps / 1e9, 4), unique_GB_per_step=round(unique / steps / 1e9, 4),
+                 decode_launch_us_p10_p50_p90=[round(sorted(ms)[int(q * (steps - 1))] * 1e3, 1) for q in (0.1, 0.5, 0.9)],
+                 decode_launch_us_mean=round(sum(ms) / steps * 1e3, 1),
+                 timing=f"span of the {steps} steps (copy, write, decode launches) with no per-step "
+                        "instrumentation; decode launch durations from replays of every step's decode with events "
+                        "around each")
+    del plans, loop
+    return (unique + cow_bytes) / kernel_s / 1e9, kernel_s / steps * 1e3, config, extra
+
+
+def shared_bench(args) -> int:
+    """Parallel sampling and beam search, each with pa_paged_decode and pa_paged_decode_grouped."""
     for beam, grouped in ((False, False), (False, True), (True, False), (True, True)):
-        log(f"shared blocks: beam={beam} grouped={grouped}")
-        loop = BeamLoop(4, 32, 4, 512, steps, H, D, B, "bf16", beam=beam, keep_history=False, grouped=grouped)
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-        logical = unique = copies = 0
-        saved = []
-        # host work (remaps, appends, activations, uploads) for every step first,
-        # so the timed launches find everything resident in HBM
-        plans = []
-        for i in range(steps):
-            p = loop.plan()
-            logical += workloads.decode_bytes(p["lens"], H, D, 2, B)
-            unique += loop.unique_blocks_read(p["rows"]) * B * H * D * 2 * 2
-            copies += p["n_pairs"]
-            saved.append(loop.mgr.blocks_saved_by_sharing())
-            plans.append(p)
-        span = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-        loop.warm(plans[0])                             # first-launch code loading, untimed
-        torch.cuda.synchronize()
-        # the timed span has no per-step instrumentation (an event pair per
-        # step costs several us); per-launch decode durations come from a
-        # replay of every step's decode with events around it afterwards
-        span[0].record()
-        for i in range(steps):
-            loop.launch(plans[i])
-        span[1].record()
-        torch.cuda.synchronize()
-        kernel_s = span[0].elapsed_time(span[1]) * 1e-3
-        for i in range(steps):
-            ev[i][0].record()
-            loop.decode_only(plans[i])
-            ev[i][1].record()
-        torch.cuda.synchronize()
-        ms = [a.elapsed_time(b) for a, b in ev]
-        cow_bytes = copies * 2 * 2 * H * B * D * 2
-        name = ("beam search (width 4)" if beam else "parallel sampling (4 per prompt)") + \
-            (", grouped decode" if grouped else "")
-        _line(f"paged decode with shared blocks, unique-HBM GB/s, OPT-13B shape, bf16, {name}",
-              (unique + cow_bytes) / kernel_s / 1e9, "GB/s", steps, 0, kernel_s / steps * 1e3, "bf16",
-              {"workload": f"shared-block decode: {name}", "groups": 32, "width": 4, "prompt_len": 512,
-               "heads": H, "head_dim": D, "block_size": B, "seed": "SeedSequence(76004)",
-               "decode_entry": "pa_paged_decode_grouped (group 4)" if grouped else "pa_paged_decode"},
-              logical_GBps=round(logical / kernel_s / 1e9, 1),
-              pct_of_peak_unique=round(100 * (unique + cow_bytes) / kernel_s / 1e9 / PEAK_HBM_GBS, 2),
-              seq_steps_per_s=round(128 * steps / kernel_s, 1),
-              cow_pairs_per_step=round(copies / steps, 2), blocks_saved_by_sharing_mean=round(sum(saved) / steps, 1),
-              logical_GB_per_step=round(logical / steps / 1e9, 4), unique_GB_per_step=round(unique / steps / 1e9, 4),
-              decode_launch_us_p10_p50_p90=[round(sorted(ms)[int(q * (steps - 1))] * 1e3, 1) for q in (0.1, 0.5, 0.9)],
-              decode_launch_us_mean=round(sum(ms) / steps * 1e3, 1),
-              timing="span of the 64 steps (copy, write, decode launches) with no per-step instrumentation; "
-                     "decode launch durations from replays of every step's decode with events around each")
-        del plans
+        v, ms, config, extra = shared_measure(beam, grouped)
+        name = config["workload"].split(": ", 1)[1]
+        _line(f"{SHARED_METRIC}, {name}", v, "GB/s", 64, 0, ms, "bf16", config, **extra)
     return 0
 
 
-def longdecode_bench(args) -> int:
+LONG_METRIC = "paged long-context decode HBM GB/s (16 x 32768 tokens, 72 heads, d128, bf16)"
+
+
+def longdecode_measure(steps: int, warmup: int, cpu_sample: bool) -> tuple[float, float, dict, dict]:
     """16 sequences x 32768 tokens, 72 heads, d=128, bf16, B=16 (19.3 GB of
     K/V read per step): repeated decode steps over the same cache."""
     import torch
@@ -537,14 +550,14 @@ def longdecode_bench(args) -> int:
 
     S5, C5, H5 = 16, 32768, 72
     log("building the 32K long-context cache (device-generated, 19.3 GB)")
-    sample = ((0, 0), (0, 71), (15, 0), (15, 71)) if args.cpu_seqs > 0 else ()
+    sample = ((0, 0), (0, 71), (15, 0), (15, 71)) if cpu_sample else ()
     ld = workloads.build_long_decode(5, S5, C5, H5, D, B, "bf16", samples=sample)
     ws = L.decode_workspace(ld.cache, S5, C5)
     out = torch.empty((S5, H5, D), dtype=torch.bfloat16, device="cuda")
-    n = args.steps + args.warmup
+    n = steps + warmup
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
     for i in range(n):
-        if i == args.warmup:
+        if i == warmup:
             torch.cuda.synchronize()
             t0 = time.perf_counter()
         ev[i][0].record()
@@ -552,9 +565,10 @@ def longdecode_bench(args) -> int:
         ev[i][1].record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    ms = sum(ev[i][0].elapsed_time(ev[i][1]) for i in range(args.warmup, n)) / args.steps
+    ms = sum(ev[i][0].elapsed_time(ev[i][1]) for i in range(warmup, n)) / steps
     nbytes = workloads.decode_bytes(ld.lens, H5, D, 2, B)
     gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"long decode {ms * 1e3:.1f} us -> {gbs:.0f} GB/s")
     cpu = None
     if sample:
         # the float64 oracle on 2 of the 16 sequences (2 heads each), scaled to
@@ -576,14 +590,20 @@ def longdecode_bench(args) -> int:
                          f"32768 tokens each), median of 3, scaled to the whole step; float64 NumPy on "
                          f"{os.cpu_count()} host cores ({cpu_model()})", "seconds_whole_step": round(dt, 2)}
         log(f"cpu oracle sample: {cpu['value']} GB/s (whole step {dt:.1f} s)")
-    _line("paged long-context decode HBM GB/s (16 x 32768 tokens, 72 heads, d128, bf16)", gbs, "GB/s",
-          args.steps, args.warmup, elapsed / args.steps * 1e3, "bf16",
-          {"workload": "long-context decode", "sequences": S5, "context": C5, "heads": H5, "head_dim": D,
-           "block_size": B, "seed": "torch.Generator(76005) on device"},
-          roofline={"bound": "hbm", "kernel": "pa_paged_decode (partition + merge kernels)", "achieved": round(gbs, 2),
-                    "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
-                    "avg_launch_us": round(ms * 1e3, 2), "algorithmic_bytes_per_launch": nbytes},
-          seq_steps_per_s=round(S5 / (ms * 1e-3), 1), cpu_baseline=cpu)
+    config = {"workload": "long-context decode", "sequences": S5, "context": C5, "heads": H5, "head_dim": D,
+              "block_size": B, "seed": "torch.Generator(76005) on device"}
+    extra = dict(roofline={"bound": "hbm", "kernel": "pa_paged_decode (partition + merge kernels)",
+                           "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                           "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                           "avg_launch_us": round(ms * 1e3, 2), "algorithmic_bytes_per_launch": nbytes},
+                 seq_steps_per_s=round(S5 / (ms * 1e-3), 1), cpu_baseline=cpu)
+    del ld, ws, out
+    return gbs, elapsed / steps * 1e3, config, extra
+
+
+def longdecode_bench(args) -> int:
+    gbs, ms, config, extra = longdecode_measure(args.steps, args.warmup, args.cpu_seqs > 0)
+    _line(LONG_METRIC, gbs, "GB/s", args.steps, args.warmup, ms, "bf16", config, **extra)
     return 0
 
 
@@ -860,6 +880,9 @@ def main() -> int:
     ap.add_argument("--cpu-seqs", type=int, default=64, help="sequences in the CPU-oracle sample (0: skip)")
     ap.add_argument("--prefill-steps", type=int, default=10,
                     help="decode workload: timed steps of the OPT-66B prefill sub-record (0: skip)")
+    ap.add_argument("--other-configs", type=int, default=1,
+                    help="decode workload: 1 adds short sub-records for the serving loop (B=16), grouped "
+                         "shared-block decoding (sampling, beam) and the 32K long-context decode; 0 skips them")
     ap.add_argument("--workload", choices=["decode", "copy", "prefill", "serving", "shared", "longdecode",
                                            "blocksize", "copyablation", "accounting", "prefix", "swap"],
                     default="decode",
@@ -1005,6 +1028,20 @@ def main() -> int:
     if args.prefill_steps > 0:
         log(f"prefill sub-record: OPT-66B 8 x 1024 prompts, {args.prefill_steps} steps")
         prefill = prefill_measure(args.prefill_steps, 2, args.cpu_seqs > 0, gemm=False)
+    others = {}
+    if args.other_configs:
+        # the other workloads of the same hot path, one short pass each
+        v, ms, config, extra = serving_measure(16, wall_pass=False)
+        others["serving"] = dict(metric=SERVING_METRIC, value=round(v, 1), unit="seq-steps/s", steps=32,
+                                 ms_per_step=round(ms, 4), dtype="f16", config=config, **extra)
+        for beam in (False, True):
+            v, ms, config, extra = shared_measure(beam, True)
+            others["shared_beam" if beam else "shared_sampling"] = dict(
+                metric=f"{SHARED_METRIC}, {config['workload'].split(': ', 1)[1]}", value=round(v, 2), unit="GB/s",
+                steps=64, ms_per_step=round(ms, 4), dtype="bf16", config=config, **extra)
+        v, ms, config, extra = longdecode_measure(5, 2, False)
+        others["longdecode"] = dict(metric=LONG_METRIC, value=round(v, 2), unit="GB/s", steps=5, warmup=2,
+                                    ms_per_step=round(ms, 4), dtype="bf16", config=config, **extra)
     last = steps[-1]
     ach = achievable_reads(batch.cache, last["tables"].cpu().numpy(), last["lens_host"])
     ach["decode_frac_of_kv_tile_read"] = round(dec_gbs / ach["kv_tile_read_GBps"], 4)
@@ -1051,6 +1088,7 @@ def main() -> int:
                           "ms_per_step": round(prefill["elapsed"] / prefill["steps"] * 1e3, 4),
                           "dtype": "bf16", "config": prefill["config"], "roofline": prefill["roofline"],
                           "write": prefill["write"], "cpu_baseline": prefill["cpu_baseline"]}
+    rec.update(others)
     print(json.dumps(rec), flush=True)
     return 0
 
