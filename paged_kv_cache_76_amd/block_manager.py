@@ -345,3 +345,74 @@ class BlockManager:
             "ref_count_histogram": {int(k): int(v) for k, v in enumerate(hist) if k > 0 and v},
             "cow_copies": self.cow_copies,
         }
+
+
+class PrefixCache:
+    """A provider's set of predefined prefixes kept in reserved physical
+    blocks ("vLLM / PagedAttention (SOSP 2023)" guide, section 04: the
+    provider reserves blocks for a set of prefixes; a request whose prompt
+    starts with one of them maps those blocks and computes only its own task
+    input, the last prefix block being copy-on-write).
+
+    Each registered prefix holds its blocks through a row of the block
+    manager reserved for it (one reference per block).  ``attach`` maps a
+    prefix into a request's row (a fork: every prefix block gains a
+    reference) and extends the row by the request's task tokens; a task
+    token landing in a partial, shared last prefix block first copies that
+    block (``extend``'s copy-on-write pair).  ``release`` drops the
+    provider's references: blocks still mapped by requests stay until those
+    requests are freed, then return to the free list.
+    """
+
+    def __init__(self, mgr: BlockManager, rows):
+        self.mgr = mgr
+        self._spare = sorted(int(r) for r in rows)   # rows reserved for prefixes, unused
+        self._row: dict[str, int] = {}                # prefix name -> its row
+        self.hits: dict[str, int] = {}                # requests attached to each prefix
+
+    @property
+    def names(self) -> list[str]:
+        return sorted(self._row)
+
+    def row(self, name: str) -> int:
+        if name not in self._row:
+            raise KeyError(f"no prefix named {name!r}")
+        return self._row[name]
+
+    def register(self, name: str, length: int) -> np.ndarray:
+        """Reserve blocks for a prefix of ``length`` tokens; returns the int64
+        slots its keys/values go to (write them with pa_reshape_and_cache
+        before any request attaches)."""
+        if name in self._row:
+            raise KeyError(f"prefix {name!r} is already registered")
+        if not self._spare:
+            raise RuntimeError("no row left for another prefix")
+        row = self._spare[0]
+        slots = self.mgr.add_prompt(row, length)      # raises OutOfBlocks before any change
+        self._spare.pop(0)
+        self._row[name] = row
+        self.hits[name] = 0
+        return slots
+
+    def attach(self, name: str, row: int, task_len: int) -> tuple[np.ndarray, np.ndarray]:
+        """Map prefix ``name`` into the empty ``row`` and extend it by
+        ``task_len`` tokens.  Returns the task tokens' slots and the
+        copy-on-write pairs to run (pa_copy_blocks) before writing them."""
+        src = self.row(name)
+        self.mgr.fork(src, row)
+        try:
+            slots, pairs = self.mgr.extend(row, task_len)
+        except Exception:
+            self.mgr.free(row)                        # undo the fork: all-or-nothing
+            raise
+        self.hits[name] += 1
+        return slots, pairs
+
+    def release(self, name: str) -> None:
+        """Drop the provider's references to a prefix's blocks."""
+        row = self.row(name)
+        self.mgr.free(row)
+        del self._row[name]
+        del self.hits[name]
+        self._spare.append(row)
+        self._spare.sort()

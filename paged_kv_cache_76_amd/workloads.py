@@ -17,7 +17,7 @@ import torch
 
 from . import inputs
 from ._lib import KVCache, pa_copy_blocks, pa_reshape_and_cache
-from .block_manager import BlockManager
+from .block_manager import BlockManager, PrefixCache
 
 TORCH = inputs.DTYPES
 
@@ -329,3 +329,76 @@ def build_shared_prefix(config_index: int, prefix_len: int, task_lens, num_heads
                        torch.from_numpy(np.ascontiguousarray(mgr.tables[1:R + 1])).to(device),
                        torch.from_numpy(cu_q).to(device), torch.from_numpy(lens.astype(np.int32)).to(device),
                        lens, task_lens, cu_q, len(pairs), 1.0 / math.sqrt(head_dim))
+
+
+@dataclass
+class PrefixSetBatch:
+    """Requests over a provider's set of cached prefixes, each prefilling only
+    its own task input ("vLLM / PagedAttention (SOSP 2023)" guide, section 04)."""
+
+    cache: KVCache
+    manager: BlockManager
+    prefixes: PrefixCache
+    prefix_k: dict             # name -> host [P][H][d]
+    prefix_v: dict
+    request_prefix: list       # prefix name of each request
+    task_k: list               # host per request [T_i][H][d]
+    task_v: list
+    q: torch.Tensor            # host [sum T_i][H][d]
+    q_dev: torch.Tensor
+    tables_dev: torch.Tensor   # int32 [R][max_blocks] (request rows)
+    cu_q_dev: torch.Tensor
+    lens_dev: torch.Tensor
+    lens: np.ndarray
+    task_lens: np.ndarray
+    cu_q: np.ndarray
+    copies: int
+    scale: float
+
+
+def build_prefix_set(config_index: int, prefix_lens: dict, requests, num_heads: int, head_dim: int,
+                     block_size: int, dtype: str, device: str = "cuda") -> PrefixSetBatch:
+    """Register the provider prefixes ``prefix_lens`` (name -> tokens) in a
+    PrefixCache and write their keys/values; then each request ``(name,
+    task_len)`` attaches its prefix, copies a shared partial last block if its
+    first task token lands there, and writes its own task keys/values.
+    Queries cover the task tokens only."""
+    R = len(requests)
+    _, r_q, r_k, r_v, r_pool, _, _ = inputs.streams(config_index, STREAMS)
+    names = sorted(prefix_lens)
+    max_len = max(prefix_lens[n] + t for n, t in requests)
+    need = sum(-(-int(prefix_lens[n]) // block_size) for n in names) + \
+        int(sum(-(-(int(t) + block_size) // block_size) for _, t in requests))
+    N = int(math.ceil(need * 1.1)) + 1
+    mgr = BlockManager(N, block_size, max_rows=R + len(names), max_blocks_per_seq=-(-max_len // block_size),
+                       free_order=inputs.pool_order(r_pool, N))
+    pc = PrefixCache(mgr, rows=range(R, R + len(names)))
+    cache = KVCache.empty(N + 1, num_heads, block_size, head_dim, TORCH[dtype], device)
+    cache.k.fill_(float("nan"))
+    cache.v.fill_(float("nan"))
+    pk, pv = {}, {}
+    for n in names:
+        pk[n] = inputs.normal(r_k, (prefix_lens[n], num_heads, head_dim), dtype)
+        pv[n] = inputs.normal(r_v, (prefix_lens[n], num_heads, head_dim), dtype)
+        slots = pc.register(n, prefix_lens[n])
+        pa_reshape_and_cache(cache, pk[n].to(device), pv[n].to(device), torch.from_numpy(slots).to(device))
+    tk, tv, all_slots, all_pairs = [], [], [], []
+    for i, (n, t) in enumerate(requests):
+        slots, pairs = pc.attach(n, i, int(t))
+        all_slots.append(slots)
+        all_pairs.append(pairs)
+        tk.append(inputs.normal(r_k, (int(t), num_heads, head_dim), dtype))
+        tv.append(inputs.normal(r_v, (int(t), num_heads, head_dim), dtype))
+    pairs = np.concatenate(all_pairs) if all_pairs else np.zeros((0, 2), np.int64)
+    if len(pairs):  # copy-on-write of shared partial prefix blocks, before any task write
+        pa_copy_blocks(cache, torch.from_numpy(pairs).to(device))
+    pa_reshape_and_cache(cache, torch.cat(tk).to(device), torch.cat(tv).to(device),
+                         torch.from_numpy(np.concatenate(all_slots)).to(device))
+    task_lens = np.array([int(t) for _, t in requests], np.int64)
+    q = inputs.normal(r_q, (int(task_lens.sum()), num_heads, head_dim), dtype)
+    lens = np.array([prefix_lens[n] + int(t) for n, t in requests], np.int64)
+    cu_q = np.concatenate([[0], np.cumsum(task_lens)]).astype(np.int32)
+    return PrefixSetBatch(cache, mgr, pc, pk, pv, [n for n, _ in requests], tk, tv, q, q.to(device),
+                          torch.from_numpy(np.ascontiguousarray(mgr.tables[:R])).to(device),
+                          torch.from_numpy(cu_q).to(device), torch.from_numpy(lens.astype(np.int32)).to(device),
+                          lens, task_lens, cu_q, len(pairs), 1.0 / math.sqrt(head_dim))

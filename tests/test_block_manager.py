@@ -277,3 +277,61 @@ def test_swap_space_is_bounded_by_the_device_pool():
         BlockManager(16, 4, max_rows=2, max_blocks_per_seq=4, host_blocks=17)
     with pytest.raises(ValueError, match="host_blocks"):
         BlockManager(16, 4, max_rows=2, max_blocks_per_seq=4, host_blocks=-1)
+
+
+def test_provider_prefix_set():
+    # the SOSP guide, section 04: blocks reserved for a set of predefined
+    # prefixes; requests map them and add their own task input
+    from oracle import cache as oc
+    from paged_kv_cache_76_amd.block_manager import PrefixCache
+    B, N = 4, 40
+    m = BlockManager(N, B, max_rows=10, max_blocks_per_seq=12, free_order=np.random.default_rng(5).permutation(N))
+    pc = PrefixCache(m, rows=[7, 8, 9])
+    pool = np.zeros((N, 1, B, 1))
+    hist = {}
+
+    def write(pool, vals, slots):
+        kv = np.asarray(vals, dtype=np.float64).reshape(-1, 1, 1)
+        return oc.reshape_and_cache(pool, pool, kv, kv, slots)[0]
+
+    for name, L, base in (("a", 8, 100), ("b", 6, 200), ("c", 3, 300)):   # 2 full, 1.5 and 0.75 blocks
+        slots = pc.register(name, L)
+        pool = write(pool, np.arange(base, base + L), slots)
+        hist[name] = list(range(base, base + L))
+    assert pc.names == ["a", "b", "c"] and m.used() == 2 + 2 + 1
+    with pytest.raises(KeyError):
+        pc.register("a", 4)
+    with pytest.raises(RuntimeError):
+        pc.register("d", 4)                               # the three reserved rows are taken
+    requests = [(0, "a", 3), (1, "b", 1), (2, "b", 5), (3, "c", 2), (4, "a", 4), (5, "c", 1)]
+    copies = []
+    for r, name, t in requests:
+        slots, pairs = pc.attach(name, r, t)
+        copies.append(len(pairs))
+        for src, dst in pairs:                            # copy-on-write before the task tokens are written
+            pool[dst] = pool[src]
+        vals = np.arange(1000 * (r + 1), 1000 * (r + 1) + t, dtype=np.float64)
+        pool = write(pool, vals, slots)
+        hist[r] = hist[name] + vals.tolist()
+    # a prefix ending on a block boundary ("a") needs no copy; partial last blocks ("b", "c") do
+    assert copies == [0, 1, 1, 1, 0, 1]
+    assert pc.hits == {"a": 2, "b": 2, "c": 2}
+    # every request reads the provider's prefix followed by its own task tokens;
+    # every prefix still reads back unchanged
+    for key, want in hist.items():
+        row = key if isinstance(key, int) else pc.row(key)
+        got = oc.gather_history(pool, m.table(row), len(want))[:, 0, 0]
+        assert got.tolist() == want
+    # full prefix blocks are shared by the provider and both of its requests
+    assert m.ref[m.table(pc.row("a"))].tolist() == [3, 3]
+    # releasing a prefix keeps the blocks its requests still map
+    used = m.used()
+    pc.release("a")
+    assert m.used() == used and m.ref[m.table(0)[:2]].tolist() == [2, 2]
+    m.free(0)
+    m.free(4)
+    assert m.used() == used - 2 - 1 - 1              # a's two blocks and the two requests' task blocks
+    assert pc.names == ["b", "c"]
+    pc.register("d", 5)                               # the released row serves a new prefix
+    with pytest.raises(KeyError):
+        pc.attach("a", 6, 1)

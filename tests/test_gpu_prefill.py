@@ -198,3 +198,32 @@ def test_generic_context_past_the_table_row_and_keys_outside_the_pool():
     ref = oa.decode(q[0], inputs.to_f64(b.k_hist[0]), inputs.to_f64(b.v_hist[0]), b.scale)
     check_close(got[0], ref, TOL["f32"], "context past the table row")
     assert torch.equal(got[1], torch.zeros_like(got[1]))
+
+
+@pytest.mark.parametrize("dtype,B", [("bf16", 16), ("f16", 32)])
+def test_provider_prefix_set_prefill(dtype, B):
+    # a provider's set of three cached prefixes (one ending on a block
+    # boundary, two with a partial last block); six requests attach to them
+    # and prefill only their task input
+    print(f"provider prefix set {dtype} B={B}", flush=True)
+    from oracle import cache as oc
+    prefixes = {"sys": 4 * B, "fewshot": 5 * B + 3, "short": B // 2 + 1}
+    requests = [("sys", 17), ("fewshot", 1), ("short", 40), ("fewshot", 70), ("sys", 3), ("short", 1)]
+    b = workloads.build_prefix_set(13, prefixes, requests, num_heads=3, head_dim=128, block_size=B, dtype=dtype)
+    assert b.copies == 4                     # one per request on a partial last prefix block
+    out = torch.full((int(b.task_lens.sum()), 3, 128), float("nan"), dtype=torch.float32, device="cuda")
+    L.pa_paged_prefill(b.cache, out, b.q_dev, b.tables_dev, b.cu_q_dev, b.lens_dev, int(b.task_lens.max()),
+                       int(b.lens.max()), b.scale)
+    torch.cuda.synchronize()
+    for i, name in enumerate(b.request_prefix):
+        K = inputs.to_f64(torch.cat([b.prefix_k[name], b.task_k[i]]))
+        V = inputs.to_f64(torch.cat([b.prefix_v[name], b.task_v[i]]))
+        Q = inputs.to_f64(b.q[b.cu_q[i]:b.cu_q[i + 1]])
+        check_close(out[b.cu_q[i]:b.cu_q[i + 1]], oa.prefill(Q, K, V, b.scale), TOL[dtype], f"request {i} ({name})")
+    # every provider prefix still holds its keys and values, bit for bit
+    kp = b.cache.k.cpu().view(torch.int16).numpy()
+    vp = b.cache.v.cpu().view(torch.int16).numpy()
+    for name, n in prefixes.items():
+        row = b.prefixes.row(name)
+        assert np.array_equal(oc.gather_history(kp, b.manager.table(row), n), b.prefix_k[name].view(torch.int16).numpy())
+        assert np.array_equal(oc.gather_history(vp, b.manager.table(row), n), b.prefix_v[name].view(torch.int16).numpy())
