@@ -212,6 +212,36 @@ pa_status pa_paged_decode_grouped(const pa_kv_cache* cache, void* out, pa_dtype 
                                   void* stream);
 
 /*
+ * pa_paged_decode_append — a decode step that also stores the step's new
+ * tokens.  For every row s, key[s] and value[s] (the K/V of its newest token,
+ * at position context_lens[s] - 1) are written into the cache slot the row's
+ * table maps that position to, and the row's attention over its whole
+ * context, that token included, is computed from them.  [P2] "PagedAttention
+ * 原理" (a new token's K/V are stored in their block, then attention reads
+ * the blocks) with [P1] key design 1 and eq. 2: pa_reshape_and_cache and the
+ * decode in one launch instead of two.
+ *   key, value   [S][num_heads][head_dim], cache dtype, 16-byte aligned.
+ *   group_size   1 (pa_paged_decode's kernels) or 2 / 4 (pa_paged_decode_grouped's).
+ *   workspace    >= pa_decode_grouped_workspace_bytes(cache, S,
+ *                max_context_len, group_size) bytes.
+ * Every other argument is as for pa_paged_decode.
+ * Precondition (the copy-on-write rule of [P1] key design 3): the rows'
+ * newest slots are distinct, and no other row of the call reads them (no
+ * other row's context reaches that offset of that block); otherwise the
+ * result depends on the order in which workgroups run.  Debug mode checks it
+ * (pa_check_append_slots).  Copy-on-write copies the write depends on
+ * (pa_copy_blocks) go before this call on the same stream.
+ * Output and cache contents are bit-identical to pa_reshape_and_cache with
+ * the slot of position context_lens[s] - 1 for row s, followed by
+ * pa_paged_decode (group_size 1) or pa_paged_decode_grouped.
+ */
+pa_status pa_paged_decode_append(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, const void* query,
+                                 const void* key, const void* value, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t S,
+                                 int32_t max_context_len, float scale, int32_t group_size, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/*
  * pa_paged_prefill — causal attention for the prompt tokens of S sequences.
  * [P1] key design 1, eq. 1 (query i attends to positions t <= i, itself
  * included) with keys/values read through the block table as in eq. 2;
@@ -305,6 +335,17 @@ pa_status pa_check_slot_mapping(const int64_t* slot_mapping, int32_t T, int64_t 
 pa_status pa_check_block_tables(const int32_t* block_tables, int32_t S, int32_t max_blocks_per_seq,
                                 const int32_t* context_lens, int32_t max_context_len, int32_t block_size,
                                 int32_t num_blocks);
+/*
+ * pa_check_append_slots — the tables and lengths of pa_paged_decode_append:
+ * the slot of each row's newest token (position context_lens[s] - 1) is
+ * distinct from every other row's and lies outside every other row's context
+ * ([P1] key design 3: a block that receives a token belongs to that sequence
+ * alone, the writer of a shared block copies it first).  Each row needs
+ * 1 <= context_lens[s] <= block_size * max_blocks_per_seq.
+ *   block_tables  int32 [S][max_blocks_per_seq];  context_lens  int32 [S].
+ */
+pa_status pa_check_append_slots(const int32_t* block_tables, int32_t S, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, int32_t block_size);
 /*
  * pa_check_prefill_rows — the query ranges of pa_paged_prefill: cu_q_lens[0]
  * = 0, 0 <= q_len_s = cu_q_lens[s+1] - cu_q_lens[s] <= max_q_len, and q_len_s

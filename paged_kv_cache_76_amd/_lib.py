@@ -25,9 +25,9 @@ TORCH_TO_PA = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_
 # every symbol include/pagedattn.h declares
 EXPORTS = (
     "pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_decode_workspace_bytes", "pa_paged_decode",
-    "pa_paged_decode_noalloc", "pa_decode_grouped_workspace_bytes", "pa_paged_decode_grouped", "pa_paged_prefill",
-    "pa_read_stream", "pa_read_tiles", "pa_check_copy_pairs", "pa_check_slot_mapping", "pa_check_block_tables",
-    "pa_check_prefill_rows", "pa_set_debug", "pa_get_debug", "pa_status_string", "pa_last_error", "pa_abi_version",
+    "pa_paged_decode_noalloc", "pa_decode_grouped_workspace_bytes", "pa_paged_decode_grouped",
+    "pa_paged_decode_append", "pa_paged_prefill", "pa_read_stream", "pa_read_tiles", "pa_check_copy_pairs",
+    "pa_check_slot_mapping", "pa_check_block_tables", "pa_check_append_slots", "pa_check_prefill_rows", "pa_set_debug", "pa_get_debug", "pa_status_string", "pa_last_error", "pa_abi_version",
 )
 
 
@@ -69,6 +69,8 @@ def load_library(path: str) -> ctypes.CDLL:
     L.pa_decode_grouped_workspace_bytes.restype = ctypes.c_size_t
     L.pa_paged_decode_grouped.argtypes = [C, P, ctypes.c_int, P, I32P, I32, I32P, I32, I32, ctypes.c_float, I32,
                                           P, ctypes.c_size_t, P]
+    L.pa_paged_decode_append.argtypes = [C, P, ctypes.c_int, P, P, P, I32P, I32, I32P, I32, I32, ctypes.c_float,
+                                         I32, P, ctypes.c_size_t, P]
     L.pa_paged_prefill.argtypes = [C, P, ctypes.c_int, P, I32P, I32, I32P, I32P, I32, I32, I32,
                                    ctypes.c_float, P]
     L.pa_read_stream.argtypes = [P, ctypes.c_int64, P, P]
@@ -76,15 +78,16 @@ def load_library(path: str) -> ctypes.CDLL:
     L.pa_check_copy_pairs.argtypes = [P, I32, I32, I32, I32]
     L.pa_check_slot_mapping.argtypes = [P, I32, ctypes.c_int64]
     L.pa_check_block_tables.argtypes = [P, I32, I32, P, I32, I32, I32]
+    L.pa_check_append_slots.argtypes = [P, I32, I32, P, I32]
     L.pa_check_prefill_rows.argtypes = [P, P, I32, I32]
     L.pa_set_debug.argtypes = [I32]
     L.pa_set_debug.restype = None
     L.pa_get_debug.argtypes = []
     L.pa_get_debug.restype = I32
     for fn in ("pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_paged_decode", "pa_paged_decode_noalloc",
-               "pa_paged_decode_grouped",
+               "pa_paged_decode_grouped", "pa_paged_decode_append",
                "pa_paged_prefill", "pa_read_stream", "pa_read_tiles", "pa_check_copy_pairs", "pa_check_slot_mapping",
-               "pa_check_block_tables", "pa_check_prefill_rows"):
+               "pa_check_block_tables", "pa_check_append_slots", "pa_check_prefill_rows"):
         getattr(L, fn).restype = ctypes.c_int
     L.pa_status_string.argtypes = [ctypes.c_int]
     L.pa_status_string.restype = ctypes.c_char_p
@@ -342,6 +345,40 @@ def pa_paged_decode_grouped(cache: KVCache, out: torch.Tensor, query: torch.Tens
     return out
 
 
+def pa_paged_decode_append(cache: KVCache, out: torch.Tensor, query: torch.Tensor, key: torch.Tensor,
+                           value: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                           max_context_len: int, scale: float, group_size: int = 1,
+                           workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Store each row's newest token (``key``/``value`` [S][H][d], position
+    ``context_lens[s] - 1``) in the cache and decode, in one launch.  Same
+    output and cache as :func:`pa_reshape_and_cache` then
+    :func:`pa_paged_decode` (``group_size`` 1) or
+    :func:`pa_paged_decode_grouped`.  ``workspace``: see
+    :func:`decode_grouped_workspace` with the same ``group_size``."""
+    _contig("query", query, cache.dtype)
+    _contig("key", key, cache.dtype)
+    _contig("value", value, cache.dtype)
+    _contig("out", out)
+    _contig("block_tables", block_tables, torch.int32)
+    _contig("context_lens", context_lens, torch.int32)
+    S = query.shape[0]
+    if query.shape != (S, cache.num_heads, cache.head_dim) or out.shape != query.shape:
+        raise ValueError("query/out must be [S][H][d]")
+    if key.shape != query.shape or value.shape != query.shape:
+        raise ValueError("key/value must be [S][H][d], one new token per row")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
+        raise ValueError("block_tables must be [S][max_blocks], context_lens [S]")
+    _device(cache, out=out, query=query, key=key, value=value, block_tables=block_tables,
+            context_lens=context_lens, workspace=workspace)
+    d = cache.desc()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().pa_paged_decode_append(ctypes.byref(d), _ptr(out), TORCH_TO_PA.get(out.dtype, -1), _ptr(query),
+                                        _ptr(key), _ptr(value), _ptr(block_tables), block_tables.shape[1],
+                                        _ptr(context_lens), S, int(max_context_len), float(scale), int(group_size),
+                                        _ptr(workspace), ws_bytes, _stream(stream)))
+    return out
+
+
 def pa_paged_prefill(cache: KVCache, out: torch.Tensor, query: torch.Tensor,
                      block_tables: torch.Tensor, cu_q_lens: torch.Tensor, context_lens: torch.Tensor,
                      max_q_len: int, max_context_len: int, scale: float, stream=None) -> torch.Tensor:
@@ -424,6 +461,16 @@ def check_block_tables(tables, context_lens, max_context_len: int, block_size: i
         raise ValueError("tables must be [S][max_blocks] and context_lens [S]")
     _check(lib().pa_check_block_tables(pt, lens.size, t.shape[1], pl, int(max_context_len), int(block_size),
                                        int(num_blocks)))
+
+
+def check_append_slots(tables, context_lens, block_size: int) -> None:
+    """Raise if two rows' newest tokens share a slot or another row reads one."""
+    import numpy as np
+    t, pt = _host_array(tables, np.int32)
+    lens, pl = _host_array(context_lens, np.int32)
+    if t.ndim != 2 or t.shape[0] != lens.size:
+        raise ValueError("tables must be [S][max_blocks] and context_lens [S]")
+    _check(lib().pa_check_append_slots(pt, lens.size, t.shape[1], pl, int(block_size)))
 
 
 def check_prefill_rows(cu_q_lens, context_lens, max_q_len: int) -> None:

@@ -363,6 +363,51 @@ pa_status pa_paged_decode_grouped(const pa_kv_cache* cache, void* out, pa_dtype 
                                                       need > 0 ? workspace : nullptr, (hipStream_t)stream));
 }
 
+pa_status pa_paged_decode_append(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, const void* query,
+                                 const void* key, const void* value, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t S,
+                                 int32_t max_context_len, float scale, int32_t group_size, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  const char* fn = "pa_paged_decode_append";
+  pa::Cache c;
+  pa_status st = check_cache(fn, cache, &c);
+  if (st != PA_OK) return st;
+  if (S < 0) return fail(PA_ERR_INVALID_ARG, "%s: S = %d < 0", fn, S);
+  if (group_size != 1 && group_size != 2 && group_size != 4)
+    return fail(PA_ERR_INVALID_ARG, "%s: group_size = %d not in {1, 2, 4}", fn, group_size);
+  if (S == 0) return PA_OK;
+  st = check_decode(fn, c, out, out_dtype, query, block_tables, max_blocks_per_seq, context_lens, S,
+                    max_context_len, scale);
+  if (st != PA_OK) return st;
+  if (!key || !value) return fail(PA_ERR_INVALID_ARG, "%s: NULL key/value", fn);
+  if (!aligned(key, 16) || !aligned(value, 16))
+    return fail(PA_ERR_INVALID_ARG, "%s: key/value must be 16-byte aligned", fn);
+  const size_t need = group_size == 1 ? pa::decode_workspace_needed(c, S, max_context_len)
+                                      : pa::decode_grouped_workspace_bytes(c, S, max_context_len, group_size);
+  st = check_workspace(fn, need, workspace, workspace_bytes);
+  if (st != PA_OK) return st;
+  if (g_debug.load()) {
+    // the tables and lengths as for a decode; new tokens in distinct slots no other row reads
+    std::vector<int32_t> t, l;
+    st = fetch(fn, block_tables, (int64_t)S * max_blocks_per_seq, (hipStream_t)stream, &t);
+    if (st == PA_OK) st = fetch(fn, context_lens, S, (hipStream_t)stream, &l);
+    if (st == PA_OK)
+      st = pa_check_block_tables(t.data(), S, max_blocks_per_seq, l.data(), max_context_len, c.block_size,
+                                 c.num_blocks);
+    if (st == PA_OK) st = pa_check_append_slots(t.data(), S, max_blocks_per_seq, l.data(), c.block_size);
+    if (st != PA_OK) return st;
+  }
+  void* ws = need > 0 ? workspace : nullptr;
+  const hipError_t err =
+      group_size == 1
+          ? pa::launch_paged_decode(c, out, out_dtype, query, block_tables, max_blocks_per_seq, context_lens, S,
+                                    max_context_len, scale, ws, (hipStream_t)stream, key, value)
+          : pa::launch_paged_decode_grouped(c, out, out_dtype, query, block_tables, max_blocks_per_seq,
+                                            context_lens, S, max_context_len, scale, group_size, ws,
+                                            (hipStream_t)stream, key, value);
+  return launched(fn, err);
+}
+
 pa_status pa_paged_prefill(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, const void* query,
                            const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* cu_q_lens,
                            const int32_t* context_lens, int32_t S, int32_t max_q_len, int32_t max_context_len,

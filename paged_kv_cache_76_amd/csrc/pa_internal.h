@@ -52,10 +52,14 @@ int decode_partition_tokens(pa_dtype dtype, int head_dim, int block_size);
 // max_context_len tokens) and bytes one such launch uses
 size_t decode_workspace_bytes(const Cache& c, int32_t S, int32_t max_context_len);
 size_t decode_workspace_needed(const Cache& c, int32_t S, int32_t max_context_len);
+// key_new / value_new ([S][H][D], cache dtype): an appending decode, which
+// first stores each row's newest token (position context_lens[s] - 1) into
+// the cache slot its table maps; NULL for a plain decode.
 hipError_t launch_paged_decode(const Cache& c, void* out, pa_dtype out_dtype, const void* query,
                                const int32_t* block_tables, int32_t max_blocks_per_seq,
                                const int32_t* context_lens, int32_t S, int32_t max_context_len,
-                               float scale, void* workspace, hipStream_t stream);
+                               float scale, void* workspace, hipStream_t stream,
+                               const void* key_new = nullptr, const void* value_new = nullptr);
 
 // Device address of the allocation-free decode's scratch array on the
 // current device (looked up once per device, then cached).
@@ -68,7 +72,8 @@ size_t decode_grouped_workspace_bytes(const Cache& c, int32_t S, int32_t max_con
 hipError_t launch_paged_decode_grouped(const Cache& c, void* out, pa_dtype out_dtype, const void* query,
                                        const int32_t* block_tables, int32_t max_blocks_per_seq,
                                        const int32_t* context_lens, int32_t S, int32_t max_context_len,
-                                       float scale, int32_t group_size, void* workspace, hipStream_t stream);
+                                       float scale, int32_t group_size, void* workspace, hipStream_t stream,
+                                       const void* key_new = nullptr, const void* value_new = nullptr);
 
 // ---- prefill (paged_prefill.hip) ----------------------------------------------
 bool prefill_supported(pa_dtype dtype, int head_dim, int block_size);

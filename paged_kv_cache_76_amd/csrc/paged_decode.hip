@@ -106,6 +106,11 @@ struct DecodeArgs {
   int32_t S, H, N, max_blocks, max_parts;
   float scale_log2;  // scale * log2(e)
   pa_dtype out_dtype;
+  // Appending decode: [S][H][D] keys/values of each row's newest token
+  // (position lens[s] - 1); NULL for a plain decode, whose tokens are all in
+  // the cache already.
+  const u32x4* knew;
+  const u32x4* vnew;
 };
 
 constexpr int cmin(int a, int b) { return a < b ? a : b; }
@@ -161,7 +166,40 @@ __device__ __forceinline__ void merge_partitions(const DecodeArgs& a, int64_t sh
   }
 }
 
-template <typename E, int D, int BS, bool WIDE>
+// An appending decode's newest token: element row_h (= row * H + head) of
+// knew/vnew, scored against q and folded into token row 0 of the calling
+// wave's running (m, l, o) state, and stored at offset `off` of block `phys`
+// of the pools (skipped for an id outside the pool, like every read), where
+// later calls read it.  Every lane loads and scores it (the dot product's lane
+// reduction needs whole lane groups); only token row 0 keeps it.
+template <typename E, int D, int BS>
+__device__ __forceinline__ void add_new_token(const DecodeArgs& a, int64_t row_h, int phys, int off, int h,
+                                              const u32x4& qc, int r, int c, float& m, float& l, float* o) {
+  using C = DecodeCfg<E, D, BS>;
+  constexpr int VEC = C::VEC, LPT = C::LPT;
+  const u32x4 kn = a.knew[row_h * LPT + c];
+  const u32x4 vn = a.vnew[row_h * LPT + c];
+  const float d = group_sum<LPT>(dot_chunk(E{}, qc, kn)) * a.scale_log2;
+  if (phys < 0 || phys >= a.N) return;  // uniform
+  if (r == 0) {
+    const int64_t dst = (((int64_t)phys * a.H + h) * BS + off) * LPT + c;
+    const_cast<u32x4*>(a.kpool)[dst] = kn;
+    const_cast<u32x4*>(a.vpool)[dst] = vn;
+    const float m_new = fmaxf(m, d);
+    const float alpha = fast_exp2(m - m_new);
+    const float pn = fast_exp2(d - m_new);
+    l = l * alpha + pn;
+    float vf[VEC];
+    widen(E{}, vn, vf);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) o[e] = __builtin_fmaf(pn, vf[e], o[e] * alpha);
+    m = m_new;
+  }
+}
+
+// APPEND: the appending decode (knew/vnew set), built apart from the plain
+// decode, whose loop it shares unchanged.
+template <typename E, int D, int BS, bool WIDE, bool APPEND>
 __global__ __launch_bounds__((DecodeCfg<E, D, BS, WIDE>::NW * 64)) PA_DECODE_OCC void decode_partition_kernel(
     DecodeArgs a) {
   using C = DecodeCfg<E, D, BS, WIDE>;
@@ -180,13 +218,18 @@ __global__ __launch_bounds__((DecodeCfg<E, D, BS, WIDE>::NW * 64)) PA_DECODE_OCC
   const int ctx = min(a.lens[s], a.max_parts * P);
   const int nparts = (ctx + P - 1) / P;
   if (p >= nparts) return;  // uniform for the whole workgroup (also ctx < 1)
+  // An appending decode reads ctx - 1 tokens from the pools and takes the
+  // newest one from its inputs after the loop (not when the length was
+  // clipped: then no token is known to be the newest and nothing is written).
+  const bool add_new = APPEND && a.lens[s] <= a.max_parts * P;
+  const int kv_ctx = add_new ? ctx - 1 : ctx;
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane / LPT;  // token row within a wave-wide load
   const int c = lane % LPT;  // 16-byte column within the row
 
-  const int nblk = (ctx + BS - 1) / BS;  // logical blocks of the sequence
+  const int nblk = (kv_ctx + BS - 1) / BS;  // logical blocks read from the pools
   const int jb = p * (P / BS);           // first logical block of the partition
   const int64_t trow = (int64_t)s * a.max_blocks;
   // table window: lane k holds logical block jb + wbase + k (-1 past the end)
@@ -204,10 +247,10 @@ __global__ __launch_bounds__((DecodeCfg<E, D, BS, WIDE>::NW * 64)) PA_DECODE_OCC
 #pragma unroll
   for (int e = 0; e < VEC; ++e) o[e] = 0.f;
 
-  const int nsteps = min(STEPS, (ctx - p * P + G - 1) / G);
+  const int nsteps = min(STEPS, (kv_ctx - p * P + G - 1) / G);  // kv_ctx >= p * P
   for (int step = w; step < nsteps; step += NW) {
     const int tb = p * P + step * G;  // first logical token of the step
-    const bool full = tb + G <= ctx;
+    const bool full = tb + G <= kv_ctx;
 
     u32x4 kc[NCH], vc[NCH];
     bool valid[NCH];
@@ -232,7 +275,7 @@ __global__ __launch_bounds__((DecodeCfg<E, D, BS, WIDE>::NW * 64)) PA_DECODE_OCC
       } else {
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
-          valid[i] = in_pool && (tb + i * TPL + r < ctx);
+          valid[i] = in_pool && (tb + i * TPL + r < kv_ctx);
           kc[i] = valid[i] ? load_kv(&a.kpool[base + i * TPL * LPT]) : u32x4{0, 0, 0, 0};
           vc[i] = valid[i] ? load_kv(&a.vpool[base + i * TPL * LPT]) : u32x4{0, 0, 0, 0};
         }
@@ -242,7 +285,7 @@ __global__ __launch_bounds__((DecodeCfg<E, D, BS, WIDE>::NW * 64)) PA_DECODE_OCC
       static_assert(NCH == 1, "multi-block steps use one load per pool");
       const int t = tb + r;
       const int phys = __shfl(tbl, (t - p * P) / BS);
-      valid[0] = t < ctx && phys >= 0 && phys < a.N;
+      valid[0] = t < kv_ctx && phys >= 0 && phys < a.N;
       const int64_t idx = (((int64_t)phys * a.H + h) * BS + (t % BS)) * LPT + c;
       kc[0] = valid[0] ? load_kv(&a.kpool[idx]) : u32x4{0, 0, 0, 0};
       vc[0] = valid[0] ? load_kv(&a.vpool[idx]) : u32x4{0, 0, 0, 0};
@@ -271,6 +314,15 @@ __global__ __launch_bounds__((DecodeCfg<E, D, BS, WIDE>::NW * 64)) PA_DECODE_OCC
       for (int e = 0; e < VEC; ++e) o[e] = __builtin_fmaf(pi, vf[e], o[e]);
     }
     m = m_new;
+  }
+
+  if constexpr (APPEND) {
+    const int pos = ctx - 1;
+    if (add_new && pos / P == p && w == 0) {
+      const int jn = pos / BS;
+      const int phys = jn < a.max_blocks ? a.tables[trow + jn] : -1;
+      add_new_token<E, D, BS>(a, (int64_t)s * a.H + h, phys, pos % BS, h, qc, r, c, m, l, o);
+    }
   }
 
   // Merge the TPL row streams of the wave (lanes with equal column c).
@@ -356,7 +408,7 @@ constexpr int kGroupWaves = PA_GROUP_NW;
 constexpr float kGroupSlack = 8.0f;  // lazy-rescale slack of the grouped kernel, log2 units
 constexpr int kGroupTokens = PA_GROUP_PT;
 
-template <typename E, int D, int BS, int W>
+template <typename E, int D, int BS, int W, bool APPEND>
 // (at B = 16 the W = 4 build fits 4 waves per SIMD without spills; at B = 32 it
 // would spill, so it keeps 3)
 __global__ __launch_bounds__(kGroupWaves * 64) __attribute__((amdgpu_waves_per_eu(BS <= 16 ? 4 : 3)))
@@ -375,12 +427,18 @@ void decode_grouped_kernel(DecodeArgs a, int32_t ngroups) {
   const int grp = rest % ngroups;
   const int p = rest / ngroups;
   const int r0 = grp * W;
-  int ctx[W];
-  int maxctx = 0;
+  // ctx: the row's tokens; kv_ctx: those read from the pools (an appending
+  // decode takes each row's newest token from its inputs after the loops,
+  // unless the length was clipped)
+  int ctx[W], kv_ctx[W];
+  int maxctx = 0, max_kv = 0;
 #pragma unroll
   for (int r = 0; r < W; ++r) {
     ctx[r] = (r0 + r < a.S) ? min(a.lens[r0 + r], a.max_parts * P) : 0;
+    const bool add_new = APPEND && r0 + r < a.S && ctx[r] > 0 && a.lens[r0 + r] <= a.max_parts * P;
+    kv_ctx[r] = add_new ? ctx[r] - 1 : ctx[r];
     maxctx = max(maxctx, ctx[r]);
+    max_kv = max(max_kv, kv_ctx[r]);
   }
   if (p * P >= maxctx) return;  // uniform for the whole workgroup
 
@@ -448,7 +506,7 @@ void decode_grouped_kernel(DecodeArgs a, int32_t ngroups) {
   // continue the round-robin where the shared steps left off, so a tail step
   // (W loads) does not land on a single wave.  Any step past the prefix is
   // read per row even if it happens to be shared, which is always correct.
-  const int nsteps = min(STEPS, (maxctx - p * P + G - 1) / G);
+  const int nsteps = min(STEPS, (max_kv - p * P + G - 1) / G);  // max_kv >= maxctx - 1 >= p * P
   int n_sh = 0;
   {
     constexpr int NM = (STEPS + 63) / 64;  // steps judged 64 at a time, one per lane
@@ -464,7 +522,7 @@ void decode_grouped_kernel(DecodeArgs a, int32_t ngroups) {
       for (int r = 0; r < W; ++r) {
         const int ph = __shfl(tbl[r], jl);
         if (r == 0) ph0 = ph;
-        sh = sh && (tb + G <= ctx[r]) && (ph == ph0);
+        sh = sh && (tb + G <= kv_ctx[r]) && (ph == ph0);
       }
       const uint64_t mask = __ballot(sh && ph0 >= 0 && ph0 < a.N);
       if (prefix) {
@@ -529,7 +587,7 @@ void decode_grouped_kernel(DecodeArgs a, int32_t ngroups) {
     for (int u = u0; u < n_units; u += NW) {
       const int step = n_sh + u / W;
       const int tb = p * P + step * G;
-      if (tb >= ctx[R]) continue;  // uniform: the row has no token in this step
+      if (tb >= kv_ctx[R]) continue;  // uniform: the row has no token in this step
       const int jl = (step * G) / BS;
       const int off0 = (step * G) % BS;
       const int phys = __builtin_amdgcn_readlane(tbl[R], jl);
@@ -539,7 +597,7 @@ void decode_grouped_kernel(DecodeArgs a, int32_t ngroups) {
       bool valid[NCH];
 #pragma unroll
       for (int i = 0; i < NCH; ++i) {
-        valid[i] = in_pool && (tb + i * TPL + tr < ctx[R]);
+        valid[i] = in_pool && (tb + i * TPL + tr < kv_ctx[R]);
         kc[i] = valid[i] ? load_kv(&a.kpool[base + i * TPL * LPT]) : u32x4{0, 0, 0, 0};
         vc[i] = valid[i] ? load_kv(&a.vpool[base + i * TPL * LPT]) : u32x4{0, 0, 0, 0};
       }
@@ -552,6 +610,18 @@ void decode_grouped_kernel(DecodeArgs a, int32_t ngroups) {
       case 1: tail(std::integral_constant<int, 1 % W>{}); break;
       case 2: tail(std::integral_constant<int, 2 % W>{}); break;
       default: tail(std::integral_constant<int, 3 % W>{}); break;
+    }
+  }
+
+  if constexpr (APPEND) {
+    // row r's newest token: wave r % NW, in the partition that holds it
+#pragma unroll
+    for (int r = 0; r < W; ++r) {
+      const int pos = ctx[r] - 1;
+      if (kv_ctx[r] < ctx[r] && pos / P == p && w == r % NW) {
+        const int phys = __builtin_amdgcn_readlane(tbl[r], (pos - p * P) / BS);
+        add_new_token<E, D, BS>(a, (int64_t)(r0 + r) * a.H + h, phys, pos % BS, h, qc[r], tr, c, m[r], l[r], o[r]);
+      }
     }
   }
 
@@ -707,6 +777,7 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeArgs a, int32_t
 struct Partitioning {
   int P, NW;
   void (*kernel)(DecodeArgs);
+  void (*append_kernel)(DecodeArgs);
 };
 struct Variant {
   pa_dtype dtype;
@@ -715,7 +786,10 @@ struct Variant {
 };
 
 #define PA_DECODE_PARTITIONING(E, D, BS, WIDE) \
-  Partitioning { DecodeCfg<E, D, BS, WIDE>::P, DecodeCfg<E, D, BS, WIDE>::NW, decode_partition_kernel<E, D, BS, WIDE> }
+  Partitioning {                                                                                       \
+    DecodeCfg<E, D, BS, WIDE>::P, DecodeCfg<E, D, BS, WIDE>::NW, decode_partition_kernel<E, D, BS, WIDE, false>, \
+        decode_partition_kernel<E, D, BS, WIDE, true>                                                    \
+  }
 #define PA_DECODE_VARIANT(E, D, BS) \
   Variant { E::id, D, BS, PA_DECODE_PARTITIONING(E, D, BS, true), PA_DECODE_PARTITIONING(E, D, BS, false) }
 
@@ -744,9 +818,11 @@ struct GroupedVariant {
   pa_dtype dtype;
   int D, BS, W;
   void (*kernel)(DecodeArgs, int32_t);
+  void (*append_kernel)(DecodeArgs, int32_t);
 };
 
-#define PA_GROUPED_VARIANT(E, D, BS, W) GroupedVariant{E::id, D, BS, W, decode_grouped_kernel<E, D, BS, W>}
+#define PA_GROUPED_VARIANT(E, D, BS, W) \
+  GroupedVariant { E::id, D, BS, W, decode_grouped_kernel<E, D, BS, W, false>, decode_grouped_kernel<E, D, BS, W, true> }
 #define PA_GROUPED_ALL(BS, W) \
   PA_GROUPED_VARIANT(F32, 128, BS, W), PA_GROUPED_VARIANT(F16, 128, BS, W), PA_GROUPED_VARIANT(BF16, 128, BS, W)
 
@@ -805,7 +881,8 @@ namespace {
 
 DecodeArgs make_args(const Cache& c, void* out, pa_dtype out_dtype, const void* query,
                      const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
-                     int32_t S, int64_t mp, float scale, void* workspace) {
+                     int32_t S, int64_t mp, float scale, void* workspace, const void* key_new,
+                     const void* value_new) {
   DecodeArgs a;
   a.q = (const u32x4*)query;
   a.kpool = (const u32x4*)c.k;
@@ -825,6 +902,8 @@ DecodeArgs make_args(const Cache& c, void* out, pa_dtype out_dtype, const void* 
   a.max_parts = (int32_t)mp;
   a.scale_log2 = scale * kLog2e;
   a.out_dtype = out_dtype;
+  a.knew = (const u32x4*)key_new;
+  a.vnew = (const u32x4*)value_new;
   return a;
 }
 
@@ -833,15 +912,16 @@ DecodeArgs make_args(const Cache& c, void* out, pa_dtype out_dtype, const void* 
 hipError_t launch_paged_decode(const Cache& c, void* out, pa_dtype out_dtype, const void* query,
                                const int32_t* block_tables, int32_t max_blocks_per_seq,
                                const int32_t* context_lens, int32_t S, int32_t max_context_len,
-                               float scale, void* workspace, hipStream_t stream) {
+                               float scale, void* workspace, hipStream_t stream, const void* key_new,
+                               const void* value_new) {
   const Variant* v = find_variant(c.dtype, c.head_dim, c.block_size);
   if (!v) return hipErrorInvalidValue;
   const Partitioning& pt = pick_partitioning(*v, S, c.num_heads, max_context_len);
   const int64_t mp = max_parts_for(pt, max_context_len);
   DecodeArgs a = make_args(c, out, out_dtype, query, block_tables, max_blocks_per_seq, context_lens, S, mp, scale,
-                           workspace);
+                           workspace, key_new, value_new);
   const int64_t grid = (int64_t)S * c.num_heads * mp;
-  hipLaunchKernelGGL(pt.kernel, dim3((unsigned)grid), dim3(pt.NW * 64), 0, stream, a);
+  hipLaunchKernelGGL(key_new ? pt.append_kernel : pt.kernel, dim3((unsigned)grid), dim3(pt.NW * 64), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || mp <= 1 || PA_DECODE_FUSED) return err;
   hipLaunchKernelGGL(decode_reduce_kernel, dim3((unsigned)(S * c.num_heads)), dim3(64), 0, stream, a,
@@ -864,17 +944,19 @@ size_t decode_grouped_workspace_bytes(const Cache& c, int32_t S, int32_t max_con
 hipError_t launch_paged_decode_grouped(const Cache& c, void* out, pa_dtype out_dtype, const void* query,
                                        const int32_t* block_tables, int32_t max_blocks_per_seq,
                                        const int32_t* context_lens, int32_t S, int32_t max_context_len,
-                                       float scale, int32_t group_size, void* workspace, hipStream_t stream) {
+                                       float scale, int32_t group_size, void* workspace, hipStream_t stream,
+                                       const void* key_new, const void* value_new) {
   const GroupedVariant* v = find_grouped(c.dtype, c.head_dim, c.block_size, group_size);
   if (!v)  // no grouped build for this shape: the ungrouped kernel gives the same result
     return launch_paged_decode(c, out, out_dtype, query, block_tables, max_blocks_per_seq, context_lens, S,
-                               max_context_len, scale, workspace, stream);
+                               max_context_len, scale, workspace, stream, key_new, value_new);
   const int64_t mp = ((int64_t)max_context_len + kGroupTokens - 1) / kGroupTokens;
   const int32_t ngroups = (S + group_size - 1) / group_size;
   DecodeArgs a = make_args(c, out, out_dtype, query, block_tables, max_blocks_per_seq, context_lens, S, mp, scale,
-                           workspace);
+                           workspace, key_new, value_new);
   const int64_t grid = (int64_t)ngroups * c.num_heads * mp;
-  hipLaunchKernelGGL(v->kernel, dim3((unsigned)grid), dim3(kGroupWaves * 64), 0, stream, a, ngroups);
+  hipLaunchKernelGGL(key_new ? v->append_kernel : v->kernel, dim3((unsigned)grid), dim3(kGroupWaves * 64), 0,
+                     stream, a, ngroups);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || mp <= 1) return err;
   hipLaunchKernelGGL(decode_reduce_kernel, dim3((unsigned)(S * c.num_heads)), dim3(64), 0, stream, a,

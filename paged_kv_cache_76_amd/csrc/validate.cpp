@@ -11,13 +11,17 @@
 //   distinct, freshly allocated blocks, never to a block another pair reads;
 // * a step's new tokens ([P2] "PagedAttention 原理": each token's K/V go to
 //   the slot the block table maps it to) occupy distinct slots;
-// * every block a table maps for a sequence's context is a block of the pool.
+// * every block a table maps for a sequence's context is a block of the pool;
+// * an appending decode's new tokens go to distinct slots that no other
+//   sequence of the batch reads (the copy-on-write rule of key design 3 makes
+//   the block that receives a token private to its sequence).
 // They run on the host over plain arrays, so they never touch a device.
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
 
 #include <algorithm>
+#include <unordered_map>
 #include <unordered_set>
 #include <vector>
 
@@ -105,6 +109,64 @@ pa_status pa_check_block_tables(const int32_t* block_tables, int32_t S, int32_t 
       if (row[j] < 0 || row[j] >= num_blocks)
         return pa::check_fail(PA_ERR_INVALID_ARG, "%s: sequence %d: logical block %lld maps to %d outside [0, %d)",
                               fn, s, (long long)j, row[j], num_blocks);
+    }
+  }
+  return PA_OK;
+}
+
+pa_status pa_check_append_slots(const int32_t* block_tables, int32_t S, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, int32_t block_size) {
+  const char* fn = "pa_check_append_slots";
+  if (S < 0 || max_blocks_per_seq < 0 || block_size < 1)
+    return pa::check_fail(PA_ERR_INVALID_ARG, "%s: bad size", fn);
+  if (S == 0) return PA_OK;
+  if (!block_tables || !context_lens) return pa::check_fail(PA_ERR_INVALID_ARG, "%s: NULL array", fn);
+  // (physical block, offset) of each row's newest token; rows with no
+  // token are the caller's error, reported by pa_check_block_tables
+  struct Slot {
+    int32_t block, off, row;
+  };
+  std::vector<Slot> fresh;
+  fresh.reserve((size_t)S);
+  for (int32_t s = 0; s < S; ++s) {
+    const int32_t L = context_lens[s];
+    if (L < 1 || (int64_t)(L - 1) / block_size >= max_blocks_per_seq)
+      return pa::check_fail(PA_ERR_INVALID_ARG, "%s: sequence %d: context length %d outside its table row", fn, s,
+                            L);
+    const int32_t pos = L - 1;
+    fresh.push_back({block_tables[(int64_t)s * max_blocks_per_seq + pos / block_size], pos % block_size, s});
+  }
+  std::sort(fresh.begin(), fresh.end(), [](const Slot& x, const Slot& y) {
+    return x.block != y.block ? x.block < y.block : x.off < y.off;
+  });
+  for (size_t i = 1; i < fresh.size(); ++i) {
+    if (fresh[i].block == fresh[i - 1].block && fresh[i].off == fresh[i - 1].off)
+      return pa::check_fail(PA_ERR_INVALID_ARG, "%s: sequences %d and %d append to the same slot (block %d, offset %d)",
+                            fn, fresh[i - 1].row, fresh[i].row, fresh[i].block, fresh[i].off);
+  }
+  // every other row's reads of a block that receives a new token: offsets
+  // below its own count of tokens in that block
+  std::unordered_map<int32_t, std::pair<size_t, size_t>> by_block;  // block -> range in fresh
+  for (size_t i = 0; i < fresh.size();) {
+    size_t j = i;
+    while (j < fresh.size() && fresh[j].block == fresh[i].block) ++j;
+    by_block[fresh[i].block] = {i, j};
+    i = j;
+  }
+  for (int32_t s = 0; s < S; ++s) {
+    const int32_t L = context_lens[s];
+    const int64_t nblk = ((int64_t)L + block_size - 1) / block_size;
+    const int32_t* row = block_tables + (int64_t)s * max_blocks_per_seq;
+    for (int64_t j = 0; j < nblk; ++j) {
+      const auto it = by_block.find(row[j]);
+      if (it == by_block.end()) continue;
+      const int64_t count = std::min<int64_t>(block_size, L - j * block_size);  // tokens of s in this block
+      for (size_t k = it->second.first; k < it->second.second; ++k) {
+        if (fresh[k].row != s && fresh[k].off < count)
+          return pa::check_fail(PA_ERR_INVALID_ARG,
+                                "%s: sequence %d appends to block %d offset %d, which sequence %d reads", fn,
+                                fresh[k].row, fresh[k].block, fresh[k].off, s);
+      }
     }
   }
   return PA_OK;

@@ -33,7 +33,7 @@ import torch
 
 from . import inputs
 from ._lib import (KVCache, decode_grouped_workspace, decode_workspace, pa_copy_blocks, pa_paged_decode,
-                   pa_paged_decode_grouped, pa_reshape_and_cache)
+                   pa_paged_decode_append, pa_paged_decode_grouped, pa_reshape_and_cache)
 from .block_manager import BlockManager
 from .workloads import STREAMS, TORCH
 
@@ -68,17 +68,20 @@ class ServingLoop:
     ``prompt_lens[s]`` tokens of prompt plus ``start[s]`` already generated
     tokens are in the cache at step 0; sequence ``s`` finishes after
     ``out_lens[s]`` generated tokens (its blocks are freed then).
+    ``fused``: each step's new tokens are written by the decode launch itself
+    (pa_paged_decode_append) instead of a pa_reshape_and_cache launch before it.
     """
 
     def __init__(self, config_index: int, prompt_lens, out_lens, start, num_heads: int, head_dim: int,
                  block_size: int, dtype: str, device: str = "cuda", keep_history: bool = True,
-                 slack: float = 1.10, out_dtype: torch.dtype | None = None):
+                 slack: float = 1.10, out_dtype: torch.dtype | None = None, fused: bool = False):
         prompt_lens = np.asarray(prompt_lens, np.int64)
         self.out_lens = np.asarray(out_lens, np.int64)
         start = np.asarray(start, np.int64)
         self.S = len(prompt_lens)
         self.H, self.d, self.B = num_heads, head_dim, block_size
         self.dtype, self.device = dtype, device
+        self.fused = fused
         self.out_dtype = out_dtype or TORCH[dtype]
         self.scale = 1.0 / math.sqrt(head_dim)
         self.generated = start.copy()
@@ -151,8 +154,13 @@ class ServingLoop:
             events[0].record()
         if host["pairs"].shape[0]:
             pa_copy_blocks(self.cache, dev["pairs"])
-        pa_reshape_and_cache(self.cache, k_new, v_new, dev["slots"])
-        pa_paged_decode(self.cache, out, q, dev["tables"], dev["lens"], max_ctx, self.scale, self.ws)
+        if self.fused:
+            # rows ascend, as in append_step: each row's new token is the newest of its table row
+            pa_paged_decode_append(self.cache, out, q, k_new, v_new, dev["tables"], dev["lens"], max_ctx,
+                                   self.scale, 1, self.ws)
+        else:
+            pa_reshape_and_cache(self.cache, k_new, v_new, dev["slots"])
+            pa_paged_decode(self.cache, out, q, dev["tables"], dev["lens"], max_ctx, self.scale, self.ws)
         if events is not None:
             events[1].record()
         return StepRecord(rows, lens, int(host["pairs"].shape[0]), out, None)
@@ -209,12 +217,15 @@ class BeamLoop:
     (children never re-parent) or beam search (every step each group's
     children fork from parents drawn with replacement, then the previous
     generation is released).  Rows alternate between two halves of the
-    table so a generation can fork into the other half."""
+    table so a generation can fork into the other half.  ``fused``: as for
+    ServingLoop (the decode launch writes the step's new tokens)."""
 
     def __init__(self, config_index: int, groups: int, width: int, prompt_len: int, steps: int,
                  num_heads: int, head_dim: int, block_size: int, dtype: str, beam: bool,
-                 device: str = "cuda", keep_history: bool = True, slack: float = 1.25, grouped: bool = False):
+                 device: str = "cuda", keep_history: bool = True, slack: float = 1.25, grouped: bool = False,
+                 fused: bool = False):
         self.G, self.W, self.beam = groups, width, beam
+        self.fused = fused
         self.H, self.d, self.B = num_heads, head_dim, block_size
         self.dtype, self.device = dtype, device
         self.scale = 1.0 / math.sqrt(head_dim)
@@ -313,6 +324,17 @@ class BeamLoop:
             events[0].record()
         if plan["n_pairs"]:
             pa_copy_blocks(self.cache, dev["pairs"])
+        if self.fused:
+            pa_paged_decode_append(self.cache, out, dev["q"], dev["k"], dev["v"], dev["tables"], dev["lens"],
+                                   plan["max_ctx"], self.scale, self.W if self.grouped else 1, self.ws)
+        else:
+            self._write_and_decode(plan, out)
+        if events is not None:
+            events[1].record()
+        return StepRecord(plan["rows"], plan["lens"], plan["n_pairs"], out, plan["q"])
+
+    def _write_and_decode(self, plan: dict, out: torch.Tensor) -> None:
+        dev = plan["dev"]
         pa_reshape_and_cache(self.cache, dev["k"], dev["v"], dev["slots"])
         if self.grouped:
             pa_paged_decode_grouped(self.cache, out, dev["q"], dev["tables"], dev["lens"], plan["max_ctx"],
@@ -320,19 +342,21 @@ class BeamLoop:
         else:
             pa_paged_decode(self.cache, out, dev["q"], dev["tables"], dev["lens"], plan["max_ctx"], self.scale,
                             self.ws)
-        if events is not None:
-            events[1].record()
-        return StepRecord(plan["rows"], plan["lens"], plan["n_pairs"], out, plan["q"])
 
     def step(self, events=None) -> StepRecord:
         return self.launch(self.plan(), events)
 
     def decode_only(self, plan: dict) -> torch.Tensor:
-        """The decode launch of ``plan`` alone (read-only on the cache), for
-        timing it again after the steps have run."""
+        """The decode launch of ``plan`` alone, for timing it again after the
+        steps have run.  It leaves the cache as it is: the plain decode only
+        reads, and a fused loop's appending decode stores each row's newest
+        token again, with the bits already there."""
         dev = plan["dev"]
         out = torch.empty((len(plan["rows"]), self.H, self.d), dtype=TORCH[self.dtype], device=self.device)
-        if self.grouped:
+        if self.fused:
+            pa_paged_decode_append(self.cache, out, dev["q"], dev["k"], dev["v"], dev["tables"], dev["lens"],
+                                   plan["max_ctx"], self.scale, self.W if self.grouped else 1, self.ws)
+        elif self.grouped:
             pa_paged_decode_grouped(self.cache, out, dev["q"], dev["tables"], dev["lens"], plan["max_ctx"],
                                     self.scale, self.W, self.ws)
         else:

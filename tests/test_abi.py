@@ -112,6 +112,25 @@ def test_decode_argument_checks():
                                None) == L.PA_ERR_UNSUPPORTED
 
 
+def test_append_decode_argument_checks():
+    lib = L.lib()
+    d = _desc()
+
+    def call(key=FAKE, value=FAKE, group=1, maxctx=100, ws=None, wsb=0, S=4, maxb=8):
+        return lib.pa_paged_decode_append(ctypes.byref(d), FAKE, L.PA_F16, FAKE, key, value, FAKE, maxb, FAKE, S,
+                                          maxctx, 0.1, group, ws, wsb, None)
+
+    _err(call(key=None), "NULL key/value")
+    _err(call(value=FAKE + 8), "key/value must be 16-byte aligned")
+    _err(call(group=3), "group_size = 3")
+    _err(call(maxb=2), "cannot hold")
+    assert call(S=0) == L.PA_OK
+    for g in (1, 2, 4):
+        need = lib.pa_decode_grouped_workspace_bytes(ctypes.byref(d), 4, 6000, g)
+        assert need > 0
+        assert call(group=g, maxb=400, maxctx=6000, ws=FAKE, wsb=need - 1) == L.PA_ERR_WORKSPACE
+
+
 def test_workspace_size_formula():
     lib = L.lib()
     d = _desc(num_heads=40)

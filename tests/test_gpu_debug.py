@@ -95,3 +95,30 @@ def test_attention_tables_and_lengths(debug_mode):
         Q = inputs.to_f64(p.q[p.cu_q[s]:p.cu_q[s + 1]])
         ref = oa.prefill(Q, inputs.to_f64(p.k_hist[s]), inputs.to_f64(p.v_hist[s]), p.scale)
         check_close(pout[p.cu_q[s]:p.cu_q[s + 1]], ref, TOL["bf16"], f"prefill in debug mode seq {s}")
+
+
+def test_append_slots_checked(debug_mode):
+    print("debug mode: appending decode", flush=True)
+    b = workloads.build_decode_batch(4, [5, 40, 17], num_heads=2, head_dim=128, block_size=16, dtype="f16")
+    ws = L.decode_workspace(b.cache, b.S, b.max_context_len)
+    out = torch.full((b.S, 2, 128), float("nan"), dtype=torch.float32, device="cuda")
+    k0, v0 = bits(b.cache.k), bits(b.cache.v)
+    key = torch.stack([b.k_hist[s][-1] for s in range(b.S)]).cuda()
+    value = torch.stack([b.v_hist[s][-1] for s in range(b.S)]).cuda()
+    # row 0 pointed at row 1's first block: its newest token (offset 4) lies
+    # inside row 1's context
+    bad = b.tables_dev.clone()
+    bad[0, 0] = bad[1, 0]
+    _refused(L.pa_paged_decode_append, b.cache, out, b.q_dev, key, value, bad, b.lens_dev, b.max_context_len,
+             b.scale, 1, ws, match="sequence 0 appends to block .* offset 4, which sequence 1 reads")
+    torch.cuda.synchronize()
+    assert torch.isnan(out).all()                                # nothing was launched
+    assert np.array_equal(bits(b.cache.k), k0) and np.array_equal(bits(b.cache.v), v0)
+    # the valid call rewrites each newest token with its own bits and decodes
+    L.pa_paged_decode_append(b.cache, out, b.q_dev, key, value, b.tables_dev, b.lens_dev, b.max_context_len,
+                             b.scale, 1, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(b.cache.k), k0) and np.array_equal(bits(b.cache.v), v0)
+    ref = np.stack([oa.decode(inputs.to_f64(b.q[s]), inputs.to_f64(b.k_hist[s]), inputs.to_f64(b.v_hist[s]), b.scale)
+                    for s in range(b.S)])
+    check_close(out, ref, TOL["f16"], "appending decode in debug mode")

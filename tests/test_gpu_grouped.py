@@ -19,10 +19,13 @@ from gpu_util import TOL, check_close
 pytestmark = pytest.mark.gpu
 
 
-def _build_shared(seed, groups, width, prompt, tails, H, d, B, dtype, share="all"):
+def _build_shared(seed, groups, width, prompt, tails, H, d, B, dtype, share="all", hold_last=False):
     """``groups`` prompts of ``prompt`` tokens; each forks into ``width`` rows
     (``share='all'``), only the first two rows share (``'pair'``) or none
-    (``'none'``); then row i of a group appends ``tails[i]`` own tokens."""
+    (``'none'``); then row i of a group appends ``tails[i]`` own tokens.
+    ``hold_last``: the last append step's copies run but its tokens are not
+    written (they are in the histories); the rows of that step are returned
+    as a sixth value."""
     r = np.random.default_rng(seed)
     S = groups * width
     need = groups * width * (-(-(prompt + max(tails)) // B) + 1)
@@ -62,11 +65,15 @@ def _build_shared(seed, groups, width, prompt, tails, H, d, B, dtype, share="all
             pairs_total += len(pairs)
         kn = inputs.normal(r, (len(rows), H, d), dtype)
         vn = inputs.normal(r, (len(rows), H, d), dtype)
-        L.pa_reshape_and_cache(cache, kn.cuda(), vn.cuda(), torch.from_numpy(slots).cuda())
+        held = sorted(rows)
+        if not (hold_last and step == max(tails) - 1):
+            L.pa_reshape_and_cache(cache, kn.cuda(), vn.cuda(), torch.from_numpy(slots).cuda())
         for i, s in enumerate(sorted(rows)):
             hist[s][0].append(kn[i:i + 1]); hist[s][1].append(vn[i:i + 1])
     q = inputs.normal(r, (S, H, d), dtype)
     lens = mgr.lens[:S].astype(np.int32)
+    if hold_last:
+        return cache, mgr, q, hist, lens, held
     return cache, mgr, q, hist, lens
 
 

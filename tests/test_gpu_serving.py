@@ -29,12 +29,14 @@ def _check(loop, rec, dtype, what):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("B", [8, 16, 32, 64, 128])
-def test_serving_loop_opt13b(B):
-    # 256 sequences, OPT-13B shape (40 heads of 128), fp16, 32 steps
-    print(f"serving loop B={B} (40 heads, every row at steps 0, 15, 31)", flush=True)
+@pytest.mark.parametrize("B,fused", [(8, False), (16, False), (32, False), (64, False), (128, False),
+                                     (16, True), (32, True)])
+def test_serving_loop_opt13b(B, fused):
+    # 256 sequences, OPT-13B shape (40 heads of 128), fp16, 32 steps; fused:
+    # each step's new tokens are written by the appending decode
+    print(f"serving loop B={B} fused={fused} (40 heads, every row at steps 0, 15, 31)", flush=True)
     prompt, out, start = opt13b_serving_lengths()
-    loop = ServingLoop(3, prompt, out, start, 40, 128, B, "f16", out_dtype=torch.float32)
+    loop = ServingLoop(3, prompt, out, start, 40, 128, B, "f16", out_dtype=torch.float32, fused=fused)
     finished = 0
     for step in range(32):
         before = len(loop.active_rows())
@@ -50,12 +52,14 @@ def test_serving_loop_opt13b(B):
 
 
 @pytest.mark.slow
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("beam,grouped", [(False, False), (True, False), (False, True), (True, True)])
-def test_shared_prompt_groups_bf16(beam, grouped):
+def test_shared_prompt_groups_bf16(beam, grouped, fused):
     # 32 groups x 4 sequences over 512-token prompts, OPT-13B shape, bf16, 64 steps
-    print(f"shared blocks beam={beam} grouped={grouped} (40 heads, every row at steps 0, 30, 63)", flush=True)
+    print(f"shared blocks beam={beam} grouped={grouped} fused={fused} (40 heads, every row at steps 0, 30, 63)",
+          flush=True)
     loop = BeamLoop(4, groups=32, width=4, prompt_len=512, steps=64, num_heads=40, head_dim=128,
-                    block_size=16, dtype="bf16", beam=beam, grouped=grouped)
+                    block_size=16, dtype="bf16", beam=beam, grouped=grouped, fused=fused)
     copies = 0
     for step in range(64):
         rec = loop.step()

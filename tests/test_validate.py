@@ -56,6 +56,23 @@ def test_block_tables():
     _refused(L.check_block_tables, t, [13, 4], 13, 4, 4, match="exceed the table row")
 
 
+def test_append_slots():
+    # B = 4: rows 0 and 1 share the full block 3 and append into blocks of
+    # their own; row 2 appends into block 7
+    t = np.array([[3, 5, 99], [3, 6, 99], [7, 99, 99]], np.int32)
+    L.check_append_slots(t, [6, 7, 2], 4)
+    # row 2 mapping block 3 would append at its offset 1, which rows 0 and 1 read
+    t_bad = np.array([[3, 5, 99], [3, 6, 99], [3, 99, 99]], np.int32)
+    _refused(L.check_append_slots, t_bad, [6, 7, 2], 4, match="sequence 2 appends to block 3 offset 1, which sequence 0 reads")
+    # a partial block shared by rows 0 and 2: row 0's new token (offset 1)
+    # lies past row 2's context, but row 2's (offset 0) is one row 0 reads
+    one = np.array([[3], [4], [3]], np.int32)
+    _refused(L.check_append_slots, one, [2, 1, 1], 4, match="sequence 2 appends to block 3 offset 0, which sequence 0 reads")
+    _refused(L.check_append_slots, np.array([[3], [3]], np.int32), [2, 2], 4, match="append to the same slot")
+    _refused(L.check_append_slots, t, [6, 0, 2], 4, match="context length 0")
+    _refused(L.check_append_slots, t, [6, 13, 2], 4, match="context length 13")
+
+
 def test_prefill_rows():
     L.check_prefill_rows([0, 3, 3, 10], [5, 1, 7], 7)           # an empty query range is allowed
     _refused(L.check_prefill_rows, [1, 3], [5], 4, match="cu_q_lens\\[0\\]")
@@ -75,6 +92,7 @@ def test_block_manager_output_passes_every_check():
     L.check_copy_pairs(pairs, 64, 64)
     L.check_slot_mapping(slots, 64 * 4)
     L.check_block_tables(mgr.tables[:4], mgr.lens[:4], 11, 4, 64)
+    L.check_append_slots(mgr.tables[:4], mgr.lens[:4], 4)
 
 
 def test_debug_switch_round_trip():
