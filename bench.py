@@ -363,22 +363,25 @@ def _line(metric, value, unit, steps, warmup, ms_per_step, dtype, config, **extr
 SERVING_METRIC = "paged serving-loop decode seq-steps/s, OPT-13B shape (256 seqs, 32 steps)"
 
 
-def serving_measure(bs: int, steps: int = 32, wall_pass: bool = True) -> tuple[float, float, dict, dict]:
+def serving_measure(bs: int, steps: int = 32, wall_pass: bool = True,
+                    fused: bool = False) -> tuple[float, float, dict, dict]:
     """``steps`` consecutive steps of a 256-sequence serving loop at the OPT-13B
     shape (fp16), block size ``bs``.  The host block-manager work of all
     steps runs first (timed on its own); the device loop then runs from
     inputs already in HBM.  With ``wall_pass``, a second, interleaved pass
     (host step -> pinned upload -> kernels, every step) gives the wall time
-    per step.  Returns (seq-steps/s, ms per step, config, extra keys)."""
+    per step.  ``fused``: the decode launch writes the new tokens
+    (pa_paged_decode_append) instead of a pa_reshape_and_cache launch.
+    Returns (seq-steps/s, ms per step, config, extra keys)."""
     import torch
 
     from paged_kv_cache_76_amd import workloads
     from paged_kv_cache_76_amd.serving import ServingLoop, opt13b_serving_lengths
 
     prompt, out, start = opt13b_serving_lengths(3, 256)
-    log(f"serving loop: 256 seqs, B={bs}")
+    log(f"serving loop: 256 seqs, B={bs}, fused={fused}")
     # device pass: every step's plan made ahead and resident in HBM
-    loop = ServingLoop(3, prompt, out, start, H, D, bs, DTYPE, keep_history=False)
+    loop = ServingLoop(3, prompt, out, start, H, D, bs, DTYPE, keep_history=False, fused=fused)
     counts = loop.active_counts(steps)
     toks = [loop.tokens(n, "cuda") for n in counts]
     prepared = []
@@ -395,9 +398,15 @@ def serving_measure(bs: int, steps: int = 32, wall_pass: bool = True) -> tuple[f
     # one untimed decode of step 0's inputs (read-only): the first launch of
     # a kernel in the process loads its code object (~2 ms), which must not
     # land inside the timed steps
+    # (a fused loop's warm-up is step 0's appending decode: it stores step
+    # 0's tokens early, into slots no row reads yet; step 0 stores them again)
     rows0, dev0, lens0 = prepared[0]
-    L.pa_paged_decode(loop.cache, outs[: len(rows0)], toks[0][2], dev0["tables"], dev0["lens"],
-                      int(lens0.max()), loop.scale, loop.ws)
+    if fused:
+        L.pa_paged_decode_append(loop.cache, outs[: len(rows0)], toks[0][2], toks[0][0], toks[0][1],
+                                 dev0["tables"], dev0["lens"], int(lens0.max()), loop.scale, 1, loop.ws)
+    else:
+        L.pa_paged_decode(loop.cache, outs[: len(rows0)], toks[0][2], dev0["tables"], dev0["lens"],
+                          int(lens0.max()), loop.scale, loop.ws)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i, (rows, dev, lens) in enumerate(prepared):
@@ -405,9 +414,13 @@ def serving_measure(bs: int, steps: int = 32, wall_pass: bool = True) -> tuple[f
         ev[i][0].record()
         if dev["pairs"].shape[0]:
             L.pa_copy_blocks(loop.cache, dev["pairs"])
-        L.pa_reshape_and_cache(loop.cache, k, v, dev["slots"])
-        L.pa_paged_decode(loop.cache, outs[: len(rows)], q, dev["tables"], dev["lens"],
-                          int(lens.max()), loop.scale, loop.ws)
+        if fused:
+            L.pa_paged_decode_append(loop.cache, outs[: len(rows)], q, k, v, dev["tables"], dev["lens"],
+                                     int(lens.max()), loop.scale, 1, loop.ws)
+        else:
+            L.pa_reshape_and_cache(loop.cache, k, v, dev["slots"])
+            L.pa_paged_decode(loop.cache, outs[: len(rows)], q, dev["tables"], dev["lens"],
+                              int(lens.max()), loop.scale, loop.ws)
         ev[i][1].record()
     torch.cuda.synchronize()
     gpu_s = time.perf_counter() - t0
@@ -426,7 +439,7 @@ def serving_measure(bs: int, steps: int = 32, wall_pass: bool = True) -> tuple[f
         # interleaved pass: block-manager step -> pinned upload of the plan ->
         # kernels, every step (activations already on the device, as a
         # model's projections would be)
-        loop2 = ServingLoop(3, prompt, out, start, H, D, bs, DTYPE, keep_history=False)
+        loop2 = ServingLoop(3, prompt, out, start, H, D, bs, DTYPE, keep_history=False, fused=fused)
         toks2 = [loop2.tokens(n, "cuda") for n in loop2.active_counts(steps)]
         torch.cuda.synchronize()
         t1 = time.perf_counter()
@@ -439,6 +452,8 @@ def serving_measure(bs: int, steps: int = 32, wall_pass: bool = True) -> tuple[f
     kernel_s = sum(step_ms) * 1e-3
     config = {"workload": "serving loop (append, write, decode per step; finished sequences freed)",
               "sequences": 256, "heads": H, "head_dim": D, "block_size": bs,
+              "step_launches": "copies, then pa_paged_decode_append" if fused
+              else "copies, pa_reshape_and_cache, pa_paged_decode",
               "lengths": "prompt lognormal(160,1)<=1024, output lognormal(300,1), total<=2048, "
                          "uniform progress at step 0", "seed": "SeedSequence(76003)"}
     extra.update(achieved_GBps=round(nbytes / kernel_s / 1e9, 1),
@@ -454,17 +469,20 @@ def serving_measure(bs: int, steps: int = 32, wall_pass: bool = True) -> tuple[f
 
 
 def serving_bench(args) -> int:
-    """The serving loop at block size 16 and 32 (with the interleaved wall-time pass)."""
+    """The serving loop at block size 16 and 32 (with the interleaved wall-time
+    pass), each with the separate write and with the appending decode."""
     for bs in (16, 32):
-        v, ms, config, extra = serving_measure(bs)
-        _line(SERVING_METRIC, v, "seq-steps/s", 32, 0, ms, "f16", config, **extra)
+        for fused in (False, True):
+            v, ms, config, extra = serving_measure(bs, fused=fused)
+            _line(SERVING_METRIC, v, "seq-steps/s", 32, 0, ms, "f16", config, **extra)
     return 0
 
 
 SHARED_METRIC = "paged decode with shared blocks, unique-HBM GB/s, OPT-13B shape, bf16"
 
 
-def shared_measure(beam: bool, grouped: bool, steps: int = 64) -> tuple[float, float, dict, dict]:
+def shared_measure(beam: bool, grouped: bool, steps: int = 64,
+                   fused: bool = False) -> tuple[float, float, dict, dict]:
     """32 prompt groups of 512 tokens x 4 sequences at the OPT-13B shape in
     bf16: parallel sampling (prompt blocks shared, reference count 4) or beam
     search (per-step fork/free remaps, copy-on-write of shared partial blocks
@@ -475,8 +493,9 @@ def shared_measure(beam: bool, grouped: bool, steps: int = 64) -> tuple[float, f
     from paged_kv_cache_76_amd import workloads
     from paged_kv_cache_76_amd.serving import BeamLoop
 
-    log(f"shared blocks: beam={beam} grouped={grouped}")
-    loop = BeamLoop(4, 32, 4, 512, steps, H, D, B, "bf16", beam=beam, keep_history=False, grouped=grouped)
+    log(f"shared blocks: beam={beam} grouped={grouped} fused={fused}")
+    loop = BeamLoop(4, 32, 4, 512, steps, H, D, B, "bf16", beam=beam, keep_history=False, grouped=grouped,
+                    fused=fused)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     logical = unique = copies = 0
     saved = []
@@ -513,7 +532,11 @@ def shared_measure(beam: bool, grouped: bool, steps: int = 64) -> tuple[float, f
         (", grouped decode" if grouped else "")
     config = {"workload": f"shared-block decode: {name}", "groups": 32, "width": 4, "prompt_len": 512,
               "heads": H, "head_dim": D, "block_size": B, "seed": "SeedSequence(76004)",
-              "decode_entry": "pa_paged_decode_grouped (group 4)" if grouped else "pa_paged_decode"}
+              "decode_entry": ("pa_paged_decode_append" if fused else
+                               "pa_paged_decode_grouped" if grouped else "pa_paged_decode")
+              + (" (group 4)" if grouped else ""),
+              "step_launches": "copies, then the appending decode (it writes the new tokens)" if fused
+              else "copies, pa_reshape_and_cache, decode"}
     extra = dict(logical_GBps=round(logical / kernel_s / 1e9, 1),
                  pct_of_peak_unique=round(100 * (unique + cow_bytes) / kernel_s / 1e9 / PEAK_HBM_GBS, 2),
                  seq_steps_per_s=round(128 * steps / kernel_s, 1),
@@ -521,19 +544,22 @@ def shared_measure(beam: bool, grouped: bool, steps: int = 64) -> tuple[float, f
                  logical_GB_per_step=round(logical / steps / 1e9, 4), unique_GB_per_step=round(unique / steps / 1e9, 4),
                  decode_launch_us_p10_p50_p90=[round(sorted(ms)[int(q * (steps - 1))] * 1e3, 1) for q in (0.1, 0.5, 0.9)],
                  decode_launch_us_mean=round(sum(ms) / steps * 1e3, 1),
-                 timing=f"span of the {steps} steps (copy, write, decode launches) with no per-step "
-                        "instrumentation; decode launch durations from replays of every step's decode with events "
-                        "around each")
+                 timing=f"span of the {steps} steps' launches with no per-step instrumentation; decode launch "
+                        "durations from replays of every step's decode with events around each (a fused loop's "
+                        "replay stores each newest token again, with the same bits)")
     del plans, loop
     return (unique + cow_bytes) / kernel_s / 1e9, kernel_s / steps * 1e3, config, extra
 
 
 def shared_bench(args) -> int:
-    """Parallel sampling and beam search, each with pa_paged_decode and pa_paged_decode_grouped."""
+    """Parallel sampling and beam search, each with pa_paged_decode and
+    pa_paged_decode_grouped, with the separate write and fused into the
+    appending decode."""
     for beam, grouped in ((False, False), (False, True), (True, False), (True, True)):
-        v, ms, config, extra = shared_measure(beam, grouped)
-        name = config["workload"].split(": ", 1)[1]
-        _line(f"{SHARED_METRIC}, {name}", v, "GB/s", 64, 0, ms, "bf16", config, **extra)
+        for fused in (False, True):
+            v, ms, config, extra = shared_measure(beam, grouped, fused=fused)
+            name = config["workload"].split(": ", 1)[1]
+            _line(f"{SHARED_METRIC}, {name}", v, "GB/s", 64, 0, ms, "bf16", config, **extra)
     return 0
 
 
@@ -604,6 +630,69 @@ def longdecode_measure(steps: int, warmup: int, cpu_sample: bool) -> tuple[float
 def longdecode_bench(args) -> int:
     gbs, ms, config, extra = longdecode_measure(args.steps, args.warmup, args.cpu_seqs > 0)
     _line(LONG_METRIC, gbs, "GB/s", args.steps, args.warmup, ms, "bf16", config, **extra)
+    return 0
+
+
+APPEND_METRIC = "decode step latency, cache write + decode in two launches vs one appending launch"
+
+
+def append_bench(args) -> int:
+    """One decode step's device work at the OPT-13B shape (fp16, B=16): the
+    new tokens' write (pa_reshape_and_cache) followed by pa_paged_decode, vs
+    pa_paged_decode_append, for batches from 1 to 256 sequences.  Each sample
+    is 20 back-to-back steps over inputs resident in HBM (the steady state of
+    a serving loop); the median of 15 interleaved samples is reported."""
+    import math
+    import statistics
+
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_76_amd import _lib as L
+    from paged_kv_cache_76_amd import workloads
+
+    for S, Ln in ((1, 512), (4, 512), (16, 512), (64, 1024), (256, 1024)):
+        log(f"appending decode: {S} x {Ln}")
+        h = workloads.host_histories(5, [Ln] * S, H, D, B, DTYPE)
+        mgr = h.manager
+        cache = L.KVCache.empty(mgr.num_blocks + 1, H, B, D, torch.float16)
+        L.pa_reshape_and_cache(cache, h.k_all.cuda(), h.v_all.cuda(), torch.from_numpy(h.slots).cuda())
+        newest = np.cumsum(h.lens) - 1
+        key, val = h.k_all[newest].cuda(), h.v_all[newest].cuda()
+        slots = torch.from_numpy(h.slots[newest]).cuda()
+        q, tables = h.q.cuda(), torch.from_numpy(mgr.tables).cuda()
+        lens = torch.from_numpy(h.lens.astype(np.int32)).cuda()
+        ws = L.decode_workspace(cache, S, Ln)
+        out = torch.empty((S, H, D), dtype=torch.float16, device="cuda")
+        scale = 1 / math.sqrt(D)
+
+        def pair():
+            L.pa_reshape_and_cache(cache, key, val, slots)
+            L.pa_paged_decode(cache, out, q, tables, lens, Ln, scale, ws)
+
+        def fused():
+            L.pa_paged_decode_append(cache, out, q, key, val, tables, lens, Ln, scale, 1, ws)
+
+        pair(), fused()
+        torch.cuda.synchronize()
+        res = {"pair": [], "fused": []}
+        for name, fn in (("pair", pair), ("fused", fused)) * 15:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(20):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            res[name].append(e0.elapsed_time(e1) * 1e3 / 20)
+        pair_us, fused_us = statistics.median(res["pair"]), statistics.median(res["fused"])
+        nbytes = workloads.decode_bytes(h.lens, H, D, ELEM, B) + 2 * S * H * D * ELEM
+        _line(APPEND_METRIC, round(fused_us, 2), "us", 20, 1, fused_us * 1e-3, "f16",
+              {"workload": "one decode step: new tokens' write and the decode", "sequences": S, "context": Ln,
+               "heads": H, "head_dim": D, "block_size": B},
+              higher_is_better=False, two_launches_us=round(pair_us, 2), one_launch_us=round(fused_us, 2),
+              saved_pct=round(100 * (1 - fused_us / pair_us), 1),
+              one_launch_GBps=round(nbytes / (fused_us * 1e-6) / 1e9, 1))
+        del cache
     return 0
 
 
@@ -884,7 +973,7 @@ def main() -> int:
                     help="decode workload: 1 adds short sub-records for the serving loop (B=16), grouped "
                          "shared-block decoding (sampling, beam) and the 32K long-context decode; 0 skips them")
     ap.add_argument("--workload", choices=["decode", "copy", "prefill", "serving", "shared", "longdecode",
-                                           "blocksize", "copyablation", "accounting", "prefix", "swap"],
+                                           "blocksize", "copyablation", "accounting", "prefix", "swap", "append"],
                     default="decode",
                     help="decode: the OPT-13B decode step (default); copy: pa_copy_blocks over 2048 "
                          "OPT-13B blocks, a plain copy of known size used to calibrate HBM counters; "
@@ -895,7 +984,9 @@ def main() -> int:
                          "sizes 8..128; copyablation: one batched pa_copy_blocks vs one memcpy per block; "
                          "accounting: KV utilisation of contiguous reservation vs paged blocks (host only); "
                          "prefix: prefill over task inputs only, with a cached 1024-token shared prefix; "
-                         "swap: a preempted group's blocks to pinned host memory and back")
+                         "swap: a preempted group's blocks to pinned host memory and back; append: one decode "
+                         "step as write + decode launches vs one pa_paged_decode_append launch, 1..256 "
+                         "sequences")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU layout is a design "
@@ -930,6 +1021,8 @@ def main() -> int:
         return shared_bench(args)
     if args.workload == "longdecode":
         return longdecode_bench(args)
+    if args.workload == "append":
+        return append_bench(args)
     K, W = args.steps, args.warmup
     # warm-up, then K timed steps with no per-step instrumentation (the
     # throughput); every step appends one token per sequence.  Then the

@@ -10,6 +10,28 @@
 namespace pa {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt vmcnt(0) only: this wave's global loads (including those that
+// write LDS directly) have completed
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x3f70); }
+// 16 bytes per lane from global memory straight into LDS at lds_base + 16 *
+// lane (global_load_lds_dwordx4; the LDS address is wave-uniform and comes
+// from M0, which the "{m0}" operand makes the compiler set before the
+// instruction, so it knows M0's value; one wait state follows the M0 write).
+// Issued as inline assembly so the compiler does not hold every later LDS
+// read back until these loads complete: the caller orders them (wait_vmem
+// before this wave reads the data, plus a barrier before other waves do).
+__device__ __forceinline__ void load_to_lds(const void* src, uint32_t lds_base) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_base) : "memory");
+}
+// 4 bytes per lane into LDS at lds_base + 4 * lane (global_load_lds_dword).
+__device__ __forceinline__ void load_dword_to_lds(const void* src, uint32_t lds_base) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds_base) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_void_t*)p;
+}
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 

@@ -166,25 +166,46 @@ __device__ __forceinline__ void merge_partitions(const DecodeArgs& a, int64_t sh
   }
 }
 
-// An appending decode's newest token: element row_h (= row * H + head) of
-// knew/vnew, scored against q and folded into token row 0 of the calling
-// wave's running (m, l, o) state, and stored at offset `off` of block `phys`
-// of the pools (skipped for an id outside the pool, like every read), where
-// later calls read it.  Every lane loads and scores it (the dot product's lane
-// reduction needs whole lane groups); only token row 0 keeps it.
+// An appending decode's newest tokens are fetched at the start of the kernel
+// straight into LDS (per row 2 x 64 chunks, K then V, lane k holding chunk
+// k % LPT; then 64 copies of the partition kernel's block id), so no
+// register is held across the loop, nothing waits for them before it, and
+// their latency hides behind it.
+template <int ROWS>
+struct NewTokenStage {
+  u32x4 kv[ROWS][2][64];
+  int32_t phys[64];
+};
+template <int ROWS>
+__device__ __forceinline__ NewTokenStage<ROWS>* new_token_stage() {
+  __shared__ NewTokenStage<ROWS> stage;
+  return &stage;
+}
+// The calling wave starts the fetch of element row_h (= row * H + head) of
+// knew/vnew into `stage`.
+template <int LPT>
+__device__ __forceinline__ void fetch_new_token(const DecodeArgs& a, int64_t row_h, int lane, u32x4* stage) {
+  const int64_t src = row_h * LPT + lane % LPT;
+  load_to_lds(a.knew + src, lds_addr(stage));
+  load_to_lds(a.vnew + src, lds_addr(stage + 64));
+}
+
+// After the loop, the wave that fetched it: the newest token from `stage`,
+// scored against q and folded into token row 0 of the wave's running
+// (m, l, o) state (skipped for a block id outside the pool, like every read).
+// Every lane scores it (the dot product's lane reduction needs whole lane
+// groups); only token row 0 keeps it.
 template <typename E, int D, int BS>
-__device__ __forceinline__ void add_new_token(const DecodeArgs& a, int64_t row_h, int phys, int off, int h,
-                                              const u32x4& qc, int r, int c, float& m, float& l, float* o) {
+__device__ __forceinline__ void add_new_token(const DecodeArgs& a, const u32x4* stage, int lane, int phys,
+                                              const u32x4& qc, int r, float& m, float& l, float* o) {
   using C = DecodeCfg<E, D, BS>;
   constexpr int VEC = C::VEC, LPT = C::LPT;
-  const u32x4 kn = a.knew[row_h * LPT + c];
-  const u32x4 vn = a.vnew[row_h * LPT + c];
+  wait_vmem();  // the fetch into LDS has landed
+  const u32x4 kn = stage[lane];
+  const u32x4 vn = stage[64 + lane];
   const float d = group_sum<LPT>(dot_chunk(E{}, qc, kn)) * a.scale_log2;
   if (phys < 0 || phys >= a.N) return;  // uniform
   if (r == 0) {
-    const int64_t dst = (((int64_t)phys * a.H + h) * BS + off) * LPT + c;
-    const_cast<u32x4*>(a.kpool)[dst] = kn;
-    const_cast<u32x4*>(a.vpool)[dst] = vn;
     const float m_new = fmaxf(m, d);
     const float alpha = fast_exp2(m - m_new);
     const float pn = fast_exp2(d - m_new);
@@ -195,6 +216,20 @@ __device__ __forceinline__ void add_new_token(const DecodeArgs& a, int64_t row_h
     for (int e = 0; e < VEC; ++e) o[e] = __builtin_fmaf(pn, vf[e], o[e] * alpha);
     m = m_new;
   }
+}
+
+// Before the loop, once the fetch has landed: the newest token from `stage`
+// into offset `off` of block `phys` of the pools, where later calls read it.
+// Non-temporal stores issued ahead of the loop: plain stores spread through
+// the launch's read stream cost a large launch 2-3x the time of a separate
+// write launch (measured), these about nothing.
+template <int LPT, int BS>
+__device__ __forceinline__ void store_new_token(const DecodeArgs& a, const u32x4* stage, int lane, int phys, int off,
+                                                int h) {
+  if (phys < 0 || phys >= a.N || lane >= LPT) return;
+  const int64_t dst = (((int64_t)phys * a.H + h) * BS + off) * LPT + lane;
+  __builtin_nontemporal_store(stage[lane], &const_cast<u32x4*>(a.kpool)[dst]);
+  __builtin_nontemporal_store(stage[64 + lane], &const_cast<u32x4*>(a.vpool)[dst]);
 }
 
 // APPEND: the appending decode (knew/vnew set), built apart from the plain
@@ -229,6 +264,19 @@ __global__ __launch_bounds__((DecodeCfg<E, D, BS, WIDE>::NW * 64)) PA_DECODE_OCC
   const int r = lane / LPT;  // token row within a wave-wide load
   const int c = lane % LPT;  // 16-byte column within the row
 
+  // wave 0 of the partition holding the newest token adds it
+  const bool new_here = add_new && (ctx - 1) / P == p && w == 0;
+  const int new_blk = (ctx - 1) / BS;  // logical block of the newest token
+  NewTokenStage<1>* stage = nullptr;
+  if constexpr (APPEND) {
+    stage = new_token_stage<1>();
+    if (new_here) {
+      fetch_new_token<LPT>(a, (int64_t)s * a.H + h, lane, &stage->kv[0][0][0]);
+      if (new_blk < a.max_blocks)
+        load_dword_to_lds(&a.tables[(int64_t)s * a.max_blocks + new_blk], lds_addr(stage->phys));
+    }
+  }
+
   const int nblk = (kv_ctx + BS - 1) / BS;  // logical blocks read from the pools
   const int jb = p * (P / BS);           // first logical block of the partition
   const int64_t trow = (int64_t)s * a.max_blocks;
@@ -246,6 +294,17 @@ __global__ __launch_bounds__((DecodeCfg<E, D, BS, WIDE>::NW * 64)) PA_DECODE_OCC
   float o[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) o[e] = 0.f;
+
+  int new_phys = -1;
+  if constexpr (APPEND) {
+    if (new_here) {
+      // the fetches into LDS have landed (with the table window and q, which
+      // the loop's first step waits for anyway)
+      wait_vmem();
+      new_phys = new_blk < a.max_blocks ? __builtin_amdgcn_readfirstlane(stage->phys[0]) : -1;
+      store_new_token<LPT, BS>(a, &stage->kv[0][0][0], lane, new_phys, (ctx - 1) % BS, h);
+    }
+  }
 
   const int nsteps = min(STEPS, (kv_ctx - p * P + G - 1) / G);  // kv_ctx >= p * P
   for (int step = w; step < nsteps; step += NW) {
@@ -317,12 +376,7 @@ __global__ __launch_bounds__((DecodeCfg<E, D, BS, WIDE>::NW * 64)) PA_DECODE_OCC
   }
 
   if constexpr (APPEND) {
-    const int pos = ctx - 1;
-    if (add_new && pos / P == p && w == 0) {
-      const int jn = pos / BS;
-      const int phys = jn < a.max_blocks ? a.tables[trow + jn] : -1;
-      add_new_token<E, D, BS>(a, (int64_t)s * a.H + h, phys, pos % BS, h, qc, r, c, m, l, o);
-    }
+    if (new_here) add_new_token<E, D, BS>(a, &stage->kv[0][0][0], lane, new_phys, qc, r, m, l, o);
   }
 
   // Merge the TPL row streams of the wave (lanes with equal column c).
@@ -430,12 +484,16 @@ void decode_grouped_kernel(DecodeArgs a, int32_t ngroups) {
   // ctx: the row's tokens; kv_ctx: those read from the pools (an appending
   // decode takes each row's newest token from its inputs after the loops,
   // unless the length was clipped)
+  // (the W lengths come in one vector load, lane r holding row r's, instead
+  // of one scalar round trip per row)
+  const int lens_w = a.lens[min(r0 + min((int)(threadIdx.x & 63), W - 1), a.S - 1)];
   int ctx[W], kv_ctx[W];
   int maxctx = 0, max_kv = 0;
 #pragma unroll
   for (int r = 0; r < W; ++r) {
-    ctx[r] = (r0 + r < a.S) ? min(a.lens[r0 + r], a.max_parts * P) : 0;
-    const bool add_new = APPEND && r0 + r < a.S && ctx[r] > 0 && a.lens[r0 + r] <= a.max_parts * P;
+    const int len = __builtin_amdgcn_readlane(lens_w, r);
+    ctx[r] = (r0 + r < a.S) ? min(len, a.max_parts * P) : 0;
+    const bool add_new = APPEND && r0 + r < a.S && len > 0 && len <= a.max_parts * P;
     kv_ctx[r] = add_new ? ctx[r] - 1 : ctx[r];
     maxctx = max(maxctx, ctx[r]);
     max_kv = max(max_kv, kv_ctx[r]);
@@ -447,6 +505,17 @@ void decode_grouped_kernel(DecodeArgs a, int32_t ngroups) {
   const int tr = lane / LPT;  // token row within a wave-wide load
   const int c = lane % LPT;   // 16-byte column within the row
   const int jb = p * (P / BS);
+
+  // row r's newest token: wave r % NW of the partition that holds it
+  NewTokenStage<W>* stage = nullptr;
+  if constexpr (APPEND) {
+    stage = new_token_stage<W>();
+#pragma unroll
+    for (int r = 0; r < W; ++r) {
+      if (kv_ctx[r] < ctx[r] && (ctx[r] - 1) / P == p && w == r % NW)
+        fetch_new_token<LPT>(a, (int64_t)(r0 + r) * a.H + h, lane, &stage->kv[r][0][0]);
+    }
+  }
 
   int tbl[W];
   u32x4 qc[W];
@@ -532,6 +601,17 @@ void decode_grouped_kernel(DecodeArgs a, int32_t ngroups) {
       }
     }
   }
+  if constexpr (APPEND) {
+#pragma unroll
+    for (int r = 0; r < W; ++r) {
+      const int pos = ctx[r] - 1;
+      if (kv_ctx[r] < ctx[r] && pos / P == p && w == r % NW) {
+        wait_vmem();  // the fetch into LDS has landed
+        store_new_token<LPT, BS>(a, &stage->kv[r][0][0], lane,
+                                 __builtin_amdgcn_readlane(tbl[r], (pos - p * P) / BS), pos % BS, h);
+      }
+    }
+  }
   for (int step = w; step < n_sh; step += NW) {
     const int jl = (step * G) / BS;
     const int off0 = (step * G) % BS;
@@ -614,13 +694,12 @@ void decode_grouped_kernel(DecodeArgs a, int32_t ngroups) {
   }
 
   if constexpr (APPEND) {
-    // row r's newest token: wave r % NW, in the partition that holds it
 #pragma unroll
     for (int r = 0; r < W; ++r) {
       const int pos = ctx[r] - 1;
       if (kv_ctx[r] < ctx[r] && pos / P == p && w == r % NW) {
         const int phys = __builtin_amdgcn_readlane(tbl[r], (pos - p * P) / BS);
-        add_new_token<E, D, BS>(a, (int64_t)(r0 + r) * a.H + h, phys, pos % BS, h, qc[r], tr, c, m[r], l[r], o[r]);
+        add_new_token<E, D, BS>(a, &stage->kv[r][0][0], lane, phys, qc[r], tr, m[r], l[r], o[r]);
       }
     }
   }

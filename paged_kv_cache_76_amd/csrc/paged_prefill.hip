@@ -50,7 +50,6 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
 // x combined with the same register of lane (l ^ 32) by a commutative op:
@@ -79,22 +78,9 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
-// s_waitcnt vmcnt(0) only: this wave's global loads (including those that
-// write LDS directly) have completed
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x3f70); }
-// 16 bytes per lane from global memory straight into LDS at lds_base + 16 *
-// lane (global_load_lds_dwordx4; the LDS address is wave-uniform and comes
-// from M0, which the "{m0}" operand makes the compiler set before the
-// instruction, so it knows M0's value; one wait state follows the M0 write).
-// Issued as inline assembly so the compiler does not hold every later LDS
-// read back until these loads complete: the kernel orders them itself
-// (wait_vmem, then a barrier, before any wave reads the buffer).
-__device__ __forceinline__ void load_to_lds(const void* src, uint32_t lds_base) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_base) : "memory");
-}
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(lds_void_t*)p;
-}
+// (wait_vmem, load_to_lds and lds_addr: the device helpers header; this
+// kernel orders its direct-to-LDS loads itself: wait_vmem, then a barrier,
+// before any wave reads the buffer)
 // Four such loads of consecutive 1 KiB global pieces from one address
 // register: the immediate offset k * 1024 advances both the global address
 // and the LDS address; M0 takes m[k] (so the LDS pieces may have gaps).

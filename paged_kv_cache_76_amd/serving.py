@@ -365,15 +365,20 @@ class BeamLoop:
         return out
 
     def warm(self, plan: dict) -> None:
-        """Launch this loop's kernels once without changing the cache: a copy
-        of block 0 onto itself and the decode of ``plan``'s inputs (read-only;
-        the cache write already ran when the prompts were written).  The
-        first launch of each kernel in a process loads its code, which must
-        not fall inside timed steps."""
+        """Launch this loop's kernels once, leaving the cache as the timed
+        steps expect it: a copy of block 0 onto itself and the decode of
+        ``plan``'s inputs (read-only; for a fused loop the appending decode
+        stores ``plan``'s new tokens early, into blocks no row reads yet, and
+        ``plan``'s own launch stores them again after its copies).  The first
+        launch of each kernel in a process loads its code, which must not
+        fall inside timed steps."""
         dev = plan["dev"]
         out = torch.empty((len(plan["rows"]), self.H, self.d), dtype=TORCH[self.dtype], device=self.device)
         pa_copy_blocks(self.cache, torch.zeros((1, 2), dtype=torch.int64, device=self.device))
-        if self.grouped:
+        if self.fused:
+            pa_paged_decode_append(self.cache, out, dev["q"], dev["k"], dev["v"], dev["tables"], dev["lens"],
+                                   plan["max_ctx"], self.scale, self.W if self.grouped else 1, self.ws)
+        elif self.grouped:
             pa_paged_decode_grouped(self.cache, out, dev["q"], dev["tables"], dev["lens"], plan["max_ctx"],
                                     self.scale, self.W, self.ws)
         else:
