@@ -218,11 +218,12 @@ __device__ __forceinline__ void add_new_token(const DecodeArgs& a, const u32x4* 
   }
 }
 
-// Before the loop, once the fetch has landed: the newest token from `stage`
-// into offset `off` of block `phys` of the pools, where later calls read it.
-// Non-temporal stores issued ahead of the loop: plain stores spread through
-// the launch's read stream cost a large launch 2-3x the time of a separate
-// write launch (measured), these about nothing.
+// The newest token from `stage` (its fetch has landed) into offset `off` of
+// block `phys` of the pools, where later calls read it.  Non-temporal
+// stores: plain stores spread through the launch's read stream cost a large
+// launch 2-3x the time of a separate write launch (measured), these about
+// nothing.  The partition kernel issues them before its loop, the grouped
+// kernel at its end.
 template <int LPT, int BS>
 __device__ __forceinline__ void store_new_token(const DecodeArgs& a, const u32x4* stage, int lane, int phys, int off,
                                                 int h) {
@@ -601,17 +602,6 @@ void decode_grouped_kernel(DecodeArgs a, int32_t ngroups) {
       }
     }
   }
-  if constexpr (APPEND) {
-#pragma unroll
-    for (int r = 0; r < W; ++r) {
-      const int pos = ctx[r] - 1;
-      if (kv_ctx[r] < ctx[r] && pos / P == p && w == r % NW) {
-        wait_vmem();  // the fetch into LDS has landed
-        store_new_token<LPT, BS>(a, &stage->kv[r][0][0], lane,
-                                 __builtin_amdgcn_readlane(tbl[r], (pos - p * P) / BS), pos % BS, h);
-      }
-    }
-  }
   for (int step = w; step < n_sh; step += NW) {
     const int jl = (step * G) / BS;
     const int off0 = (step * G) % BS;
@@ -756,6 +746,18 @@ void decode_grouped_kernel(DecodeArgs a, int32_t ngroups) {
     if (nparts > 1 && threadIdx.x == 0) {
       a.ws_ml[(sh * a.max_parts + p) * 2] = M;
       a.ws_ml[(sh * a.max_parts + p) * 2 + 1] = L;
+    }
+  }
+  // The rows' newest tokens into the pools, last (here, measured, the
+  // grouped kernel's stores cost less than before its loops, where the
+  // wave would first wait for its query loads)
+  if constexpr (APPEND) {
+#pragma unroll
+    for (int r = 0; r < W; ++r) {
+      const int pos = ctx[r] - 1;
+      if (kv_ctx[r] < ctx[r] && pos / P == p && w == r % NW)
+        store_new_token<LPT, BS>(a, &stage->kv[r][0][0], lane,
+                                 __builtin_amdgcn_readlane(tbl[r], (pos - p * P) / BS), pos % BS, h);
     }
   }
 }
