@@ -98,6 +98,12 @@ def test_grouped_kernel_on_unrelated_rows(group):
     _run_case(44, EDGE_LENS, 4, 128, 16, "bf16", group=group)
 
 
+def test_group_size_without_grouped_build_falls_back():
+    # head_dim 64 has no grouped build: group_size 4 runs the ungrouped appending kernel
+    print("append group 4 at d=64 (ungrouped fallback)", flush=True)
+    _run_case(46, [1, 16, 17, 300, 1025], 3, 64, 16, "f16", group=4)
+
+
 def test_bf16_output_rounding():
     print("append bf16 output", flush=True)
     _run_case(45, EDGE_LENS, 4, 128, 16, "bf16", out_dtype=torch.bfloat16)
