@@ -221,9 +221,9 @@ __device__ __forceinline__ void add_new_token(const DecodeArgs& a, const u32x4* 
 // The newest token from `stage` (its fetch has landed) into offset `off` of
 // block `phys` of the pools, where later calls read it.  Non-temporal
 // stores: plain stores spread through the launch's read stream cost a large
-// launch 2-3x the time of a separate write launch (measured), these about
-// nothing.  The partition kernel issues them before its loop, the grouped
-// kernel at its end.
+// launch several times what a separate write launch takes (measured), these
+// about as much as that launch.  The partition kernel issues them before its
+// loop, the grouped kernel at its end.
 template <int LPT, int BS>
 __device__ __forceinline__ void store_new_token(const DecodeArgs& a, const u32x4* stage, int lane, int phys, int off,
                                                 int h) {
