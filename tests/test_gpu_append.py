@@ -91,6 +91,14 @@ def test_wide_partitioning_and_merge():
     _run_case(43, lens, 4, 128, 16, "f16")
 
 
+@pytest.mark.slow
+def test_long_contexts_through_the_merge():
+    # 32K-token contexts at 8 heads: 32 narrow partitions per (sequence, head),
+    # the newest token in the last one, merged by the reduce kernel
+    print("append 2 x 32768 tokens, 8 heads, bf16", flush=True)
+    _run_case(47, [32768, 30001], 8, 128, 16, "bf16")
+
+
 @pytest.mark.parametrize("group", [2, 4])
 def test_grouped_kernel_on_unrelated_rows(group):
     # 13 rows (not a multiple of the group), nothing shared
