@@ -535,7 +535,9 @@ def shared_measure(beam: bool, grouped: bool, steps: int = 64,
               "decode_entry": ("pa_paged_decode_append" if fused else
                                "pa_paged_decode_grouped" if grouped else "pa_paged_decode")
               + (" (group 4)" if grouped else ""),
-              "step_launches": "copies, then the appending decode (it writes the new tokens)" if fused
+              "step_launches": ("the appending decode alone (it makes the copy-on-write copies and writes the new "
+                                "tokens)" if loop.fold_copies else
+                                "copies, then the appending decode (it writes the new tokens)") if fused
               else "copies, pa_reshape_and_cache, decode"}
     extra = dict(logical_GBps=round(logical / kernel_s / 1e9, 1),
                  pct_of_peak_unique=round(100 * (unique + cow_bytes) / kernel_s / 1e9 / PEAK_HBM_GBS, 2),
@@ -546,7 +548,7 @@ def shared_measure(beam: bool, grouped: bool, steps: int = 64,
                  decode_launch_us_mean=round(sum(ms) / steps * 1e3, 1),
                  timing=f"span of the {steps} steps' launches with no per-step instrumentation; decode launch "
                         "durations from replays of every step's decode with events around each (a fused loop's "
-                        "replay stores each newest token again, with the same bits)")
+                        "replay stores each newest token again, with the same bits, and makes no copies)")
     del plans, loop
     return (unique + cow_bytes) / kernel_s / 1e9, kernel_s / steps * 1e3, config, extra
 
@@ -693,6 +695,34 @@ def append_bench(args) -> int:
               saved_pct=round(100 * (1 - fused_us / pair_us), 1),
               one_launch_GBps=round(nbytes / (fused_us * 1e-6) / 1e9, 1))
         del cache
+    # beam search (width 4, bf16, 512-token prompts): copy-on-write copies,
+    # write and grouped decode as three launches, or all in one appending launch
+    from paged_kv_cache_76_amd.serving import BeamLoop
+    for groups in (1, 4, 32):
+        log(f"appending decode, beam search: {groups} groups of 4")
+        res = {}
+        for fused in (False, True):
+            loop = BeamLoop(4, groups, 4, 512, 40, H, D, B, "bf16", beam=True, keep_history=False, grouped=True,
+                            fused=fused)
+            plans = [loop.plan() for _ in range(40)]
+            loop.warm(plans[0])
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for p in plans:
+                loop.launch(p)
+            e1.record()
+            torch.cuda.synchronize()
+            res[fused] = (e0.elapsed_time(e1) * 1e3 / len(plans), sum(p["n_pairs"] for p in plans) / len(plans))
+            del loop, plans
+        _line(APPEND_METRIC + ", beam search", round(res[True][0], 2), "us", 40, 1, res[True][0] * 1e-3, "bf16",
+              {"workload": "beam-search step: copy-on-write copies, new tokens' write and grouped decode",
+               "groups": groups, "width": 4, "prompt_len": 512, "heads": H, "head_dim": D, "block_size": B,
+               "seed": "SeedSequence(76004)"},
+              higher_is_better=False, three_launches_us=round(res[False][0], 2), one_launch_us=round(res[True][0], 2),
+              saved_pct=round(100 * (1 - res[True][0] / res[False][0]), 1),
+              cow_pairs_per_step=round(res[False][1], 2),
+              timing="span of 40 consecutive steps planned ahead, no per-step instrumentation")
     return 0
 
 
@@ -986,7 +1016,7 @@ def main() -> int:
                          "prefix: prefill over task inputs only, with a cached 1024-token shared prefix; "
                          "swap: a preempted group's blocks to pinned host memory and back; append: one decode "
                          "step as write + decode launches vs one pa_paged_decode_append launch, 1..256 "
-                         "sequences")
+                         "sequences, and beam-search steps with their copy-on-write copies folded in")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU layout is a design "

@@ -221,6 +221,15 @@ pa_status pa_paged_decode_grouped(const pa_kv_cache* cache, void* out, pa_dtype 
  * the blocks) with [P1] key design 1 and eq. 2: pa_reshape_and_cache and the
  * decode in one launch instead of two.
  *   key, value   [S][num_heads][head_dim], cache dtype, 16-byte aligned.
+ *   cow_src      int32 [S] or NULL.  cow_src[s] >= 0: the block that holds
+ *                row s's newest token is a copy-on-write copy of block
+ *                cow_src[s] ([P1] key design 3); the call makes it one
+ *                (every slot, every head, as pa_copy_blocks would) before
+ *                the newest token lands in it, so no separate copy launch is
+ *                needed.  -1: no copy.  Supported when block_size * head_dim
+ *                * sizeof(dtype) is 1, 2 or 4 KiB (PA_ERR_UNSUPPORTED
+ *                otherwise: copy first and pass NULL).  Ids outside the pool
+ *                copy nothing, as in pa_copy_blocks.
  *   group_size   1 (pa_paged_decode's kernels) or 2 / 4 (pa_paged_decode_grouped's).
  *   workspace    >= pa_decode_grouped_workspace_bytes(cache, S,
  *                max_context_len, group_size) bytes.
@@ -228,15 +237,22 @@ pa_status pa_paged_decode_grouped(const pa_kv_cache* cache, void* out, pa_dtype 
  * Precondition (the copy-on-write rule of [P1] key design 3): the rows'
  * newest slots are distinct, and no other row of the call reads them (no
  * other row's context reaches that offset of that block); otherwise the
- * result depends on the order in which workgroups run.  Debug mode checks it
- * (pa_check_append_slots).  Copy-on-write copies the write depends on
+ * result depends on the order in which workgroups run.  With cow_src: a
+ * block that receives a copy is mapped by its row alone, no copy reads from
+ * a block that receives one, and no write of the call lands in a slot a copy
+ * reads (rows that write into a copy's source write the copying row's
+ * offset, as siblings over a shared block do).  Debug mode checks all of it
+ * (pa_check_append_slots).  Copy-on-write copies not passed in cow_src
  * (pa_copy_blocks) go before this call on the same stream.
- * Output and cache contents are bit-identical to pa_reshape_and_cache with
- * the slot of position context_lens[s] - 1 for row s, followed by
- * pa_paged_decode (group_size 1) or pa_paged_decode_grouped.
+ * Cache contents equal pa_copy_blocks with the cow_src pairs, then
+ * pa_reshape_and_cache with the slot of position context_lens[s] - 1 for
+ * row s, bit for bit; the output equals pa_paged_decode (group_size 1) or
+ * pa_paged_decode_grouped after them up to rounding (the newest token is
+ * added last).
  */
 pa_status pa_paged_decode_append(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, const void* query,
-                                 const void* key, const void* value, const int32_t* block_tables,
+                                 const void* key, const void* value, const int32_t* cow_src,
+                                 const int32_t* block_tables,
                                  int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t S,
                                  int32_t max_context_len, float scale, int32_t group_size, void* workspace,
                                  size_t workspace_bytes, void* stream);
@@ -336,16 +352,22 @@ pa_status pa_check_block_tables(const int32_t* block_tables, int32_t S, int32_t 
                                 const int32_t* context_lens, int32_t max_context_len, int32_t block_size,
                                 int32_t num_blocks);
 /*
- * pa_check_append_slots — the tables and lengths of pa_paged_decode_append:
- * the slot of each row's newest token (position context_lens[s] - 1) is
- * distinct from every other row's and lies outside every other row's context
- * ([P1] key design 3: a block that receives a token belongs to that sequence
- * alone, the writer of a shared block copies it first).  Each row needs
- * 1 <= context_lens[s] <= block_size * max_blocks_per_seq.
- *   block_tables  int32 [S][max_blocks_per_seq];  context_lens  int32 [S].
+ * pa_check_append_slots — the tables, lengths and copy sources of
+ * pa_paged_decode_append: the slot of each row's newest token (position
+ * context_lens[s] - 1) is distinct from every other row's and lies outside
+ * every other row's context ([P1] key design 3: a block that receives a
+ * token belongs to that sequence alone, the writer of a shared block copies
+ * it first); with cow_src (NULL: no copies), each copy's source is in
+ * [0, num_blocks) and is not its destination, the destination (the row's
+ * newest-token block) is mapped by no other row and receives no other copy,
+ * no copy's source receives a copy, and every write into a copy's source
+ * lands in the copying row's newest offset (the slot the copy skips).  Each
+ * row needs 1 <= context_lens[s] <= block_size * max_blocks_per_seq.
+ *   block_tables  int32 [S][max_blocks_per_seq];  context_lens, cow_src  int32 [S].
  */
 pa_status pa_check_append_slots(const int32_t* block_tables, int32_t S, int32_t max_blocks_per_seq,
-                                const int32_t* context_lens, int32_t block_size);
+                                const int32_t* context_lens, int32_t block_size, const int32_t* cow_src,
+                                int32_t num_blocks);
 /*
  * pa_check_prefill_rows — the query ranges of pa_paged_prefill: cu_q_lens[0]
  * = 0, 0 <= q_len_s = cu_q_lens[s+1] - cu_q_lens[s] <= max_q_len, and q_len_s

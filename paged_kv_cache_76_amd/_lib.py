@@ -69,8 +69,8 @@ def load_library(path: str) -> ctypes.CDLL:
     L.pa_decode_grouped_workspace_bytes.restype = ctypes.c_size_t
     L.pa_paged_decode_grouped.argtypes = [C, P, ctypes.c_int, P, I32P, I32, I32P, I32, I32, ctypes.c_float, I32,
                                           P, ctypes.c_size_t, P]
-    L.pa_paged_decode_append.argtypes = [C, P, ctypes.c_int, P, P, P, I32P, I32, I32P, I32, I32, ctypes.c_float,
-                                         I32, P, ctypes.c_size_t, P]
+    L.pa_paged_decode_append.argtypes = [C, P, ctypes.c_int, P, P, P, P, I32P, I32, I32P, I32, I32,
+                                         ctypes.c_float, I32, P, ctypes.c_size_t, P]
     L.pa_paged_prefill.argtypes = [C, P, ctypes.c_int, P, I32P, I32, I32P, I32P, I32, I32, I32,
                                    ctypes.c_float, P]
     L.pa_read_stream.argtypes = [P, ctypes.c_int64, P, P]
@@ -78,7 +78,7 @@ def load_library(path: str) -> ctypes.CDLL:
     L.pa_check_copy_pairs.argtypes = [P, I32, I32, I32, I32]
     L.pa_check_slot_mapping.argtypes = [P, I32, ctypes.c_int64]
     L.pa_check_block_tables.argtypes = [P, I32, I32, P, I32, I32, I32]
-    L.pa_check_append_slots.argtypes = [P, I32, I32, P, I32]
+    L.pa_check_append_slots.argtypes = [P, I32, I32, P, I32, P, I32]
     L.pa_check_prefill_rows.argtypes = [P, P, I32, I32]
     L.pa_set_debug.argtypes = [I32]
     L.pa_set_debug.restype = None
@@ -348,12 +348,15 @@ def pa_paged_decode_grouped(cache: KVCache, out: torch.Tensor, query: torch.Tens
 def pa_paged_decode_append(cache: KVCache, out: torch.Tensor, query: torch.Tensor, key: torch.Tensor,
                            value: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
                            max_context_len: int, scale: float, group_size: int = 1,
-                           workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+                           workspace: torch.Tensor | None = None, stream=None,
+                           cow_src: torch.Tensor | None = None) -> torch.Tensor:
     """Store each row's newest token (``key``/``value`` [S][H][d], position
-    ``context_lens[s] - 1``) in the cache and decode, in one launch.  Same
-    output and cache as :func:`pa_reshape_and_cache` then
-    :func:`pa_paged_decode` (``group_size`` 1) or
-    :func:`pa_paged_decode_grouped`.  ``workspace``: see
+    ``context_lens[s] - 1``) in the cache and decode, in one launch.  With
+    ``cow_src`` (int32 [S], -1 = none) the row's newest-token block first
+    receives a copy of block ``cow_src[s]`` in the same launch.  Same cache as
+    :func:`pa_copy_blocks` (those pairs), :func:`pa_reshape_and_cache`, and the
+    output of :func:`pa_paged_decode` (``group_size`` 1) or
+    :func:`pa_paged_decode_grouped` after them.  ``workspace``: see
     :func:`decode_grouped_workspace` with the same ``group_size``."""
     _contig("query", query, cache.dtype)
     _contig("key", key, cache.dtype)
@@ -366,14 +369,19 @@ def pa_paged_decode_append(cache: KVCache, out: torch.Tensor, query: torch.Tenso
         raise ValueError("query/out must be [S][H][d]")
     if key.shape != query.shape or value.shape != query.shape:
         raise ValueError("key/value must be [S][H][d], one new token per row")
+    if cow_src is not None:
+        _contig("cow_src", cow_src, torch.int32)
+        if cow_src.shape != (query.shape[0],):
+            raise ValueError("cow_src must be [S]")
     if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
         raise ValueError("block_tables must be [S][max_blocks], context_lens [S]")
     _device(cache, out=out, query=query, key=key, value=value, block_tables=block_tables,
-            context_lens=context_lens, workspace=workspace)
+            context_lens=context_lens, workspace=workspace, cow_src=cow_src)
     d = cache.desc()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().pa_paged_decode_append(ctypes.byref(d), _ptr(out), TORCH_TO_PA.get(out.dtype, -1), _ptr(query),
-                                        _ptr(key), _ptr(value), _ptr(block_tables), block_tables.shape[1],
+                                        _ptr(key), _ptr(value), _ptr(cow_src), _ptr(block_tables),
+                                        block_tables.shape[1],
                                         _ptr(context_lens), S, int(max_context_len), float(scale), int(group_size),
                                         _ptr(workspace), ws_bytes, _stream(stream)))
     return out
@@ -463,14 +471,24 @@ def check_block_tables(tables, context_lens, max_context_len: int, block_size: i
                                        int(num_blocks)))
 
 
-def check_append_slots(tables, context_lens, block_size: int) -> None:
-    """Raise if two rows' newest tokens share a slot or another row reads one."""
+def check_append_slots(tables, context_lens, block_size: int, cow_src=None, num_blocks: int | None = None) -> None:
+    """Raise if two rows' newest tokens share a slot or another row reads one,
+    or (with ``cow_src``, which needs ``num_blocks``) a folded-in copy breaks
+    its preconditions."""
     import numpy as np
     t, pt = _host_array(tables, np.int32)
     lens, pl = _host_array(context_lens, np.int32)
     if t.ndim != 2 or t.shape[0] != lens.size:
         raise ValueError("tables must be [S][max_blocks] and context_lens [S]")
-    _check(lib().pa_check_append_slots(pt, lens.size, t.shape[1], pl, int(block_size)))
+    pc, nb = None, 0
+    if cow_src is not None:
+        if num_blocks is None:
+            raise ValueError("num_blocks is needed with cow_src")
+        cw, pc = _host_array(cow_src, np.int32)
+        if cw.shape != (lens.size,):
+            raise ValueError("cow_src must be [S]")
+        nb = int(num_blocks)
+    _check(lib().pa_check_append_slots(pt, lens.size, t.shape[1], pl, int(block_size), pc, nb))
 
 
 def check_prefill_rows(cu_q_lens, context_lens, max_q_len: int) -> None:

@@ -364,7 +364,8 @@ pa_status pa_paged_decode_grouped(const pa_kv_cache* cache, void* out, pa_dtype 
 }
 
 pa_status pa_paged_decode_append(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, const void* query,
-                                 const void* key, const void* value, const int32_t* block_tables,
+                                 const void* key, const void* value, const int32_t* cow_src,
+                                 const int32_t* block_tables,
                                  int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t S,
                                  int32_t max_context_len, float scale, int32_t group_size, void* workspace,
                                  size_t workspace_bytes, void* stream) {
@@ -382,6 +383,12 @@ pa_status pa_paged_decode_append(const pa_kv_cache* cache, void* out, pa_dtype o
   if (!key || !value) return fail(PA_ERR_INVALID_ARG, "%s: NULL key/value", fn);
   if (!aligned(key, 16) || !aligned(value, 16))
     return fail(PA_ERR_INVALID_ARG, "%s: key/value must be 16-byte aligned", fn);
+  if (cow_src && !aligned(cow_src, 4)) return fail(PA_ERR_INVALID_ARG, "%s: cow_src must be 4-byte aligned", fn);
+  if (cow_src && !pa::append_cow_supported(c))
+    return fail(PA_ERR_UNSUPPORTED,
+                "%s: copy-on-write is folded in only when block_size * head_dim * sizeof(dtype) is 1, 2 or 4 KiB "
+                "(got %d * %d * %d); copy with pa_copy_blocks first and pass cow_src = NULL",
+                fn, c.block_size, c.head_dim, pa::dtype_bytes(c.dtype));
   const size_t need = group_size == 1 ? pa::decode_workspace_needed(c, S, max_context_len)
                                       : pa::decode_grouped_workspace_bytes(c, S, max_context_len, group_size);
   st = check_workspace(fn, need, workspace, workspace_bytes);
@@ -394,17 +401,21 @@ pa_status pa_paged_decode_append(const pa_kv_cache* cache, void* out, pa_dtype o
     if (st == PA_OK)
       st = pa_check_block_tables(t.data(), S, max_blocks_per_seq, l.data(), max_context_len, c.block_size,
                                  c.num_blocks);
-    if (st == PA_OK) st = pa_check_append_slots(t.data(), S, max_blocks_per_seq, l.data(), c.block_size);
+    std::vector<int32_t> cw;
+    if (st == PA_OK && cow_src) st = fetch(fn, cow_src, S, (hipStream_t)stream, &cw);
+    if (st == PA_OK)
+      st = pa_check_append_slots(t.data(), S, max_blocks_per_seq, l.data(), c.block_size,
+                                 cow_src ? cw.data() : nullptr, c.num_blocks);
     if (st != PA_OK) return st;
   }
   void* ws = need > 0 ? workspace : nullptr;
   const hipError_t err =
       group_size == 1
           ? pa::launch_paged_decode(c, out, out_dtype, query, block_tables, max_blocks_per_seq, context_lens, S,
-                                    max_context_len, scale, ws, (hipStream_t)stream, key, value)
+                                    max_context_len, scale, ws, (hipStream_t)stream, key, value, cow_src)
           : pa::launch_paged_decode_grouped(c, out, out_dtype, query, block_tables, max_blocks_per_seq,
                                             context_lens, S, max_context_len, scale, group_size, ws,
-                                            (hipStream_t)stream, key, value);
+                                            (hipStream_t)stream, key, value, cow_src);
   return launched(fn, err);
 }
 

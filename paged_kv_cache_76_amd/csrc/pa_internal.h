@@ -54,12 +54,17 @@ size_t decode_workspace_bytes(const Cache& c, int32_t S, int32_t max_context_len
 size_t decode_workspace_needed(const Cache& c, int32_t S, int32_t max_context_len);
 // key_new / value_new ([S][H][D], cache dtype): an appending decode, which
 // first stores each row's newest token (position context_lens[s] - 1) into
-// the cache slot its table maps; NULL for a plain decode.
+// the cache slot its table maps; NULL for a plain decode.  cow_src ([S] or
+// NULL): the copy-on-write source of each row's newest-token block (-1: none).
 hipError_t launch_paged_decode(const Cache& c, void* out, pa_dtype out_dtype, const void* query,
                                const int32_t* block_tables, int32_t max_blocks_per_seq,
                                const int32_t* context_lens, int32_t S, int32_t max_context_len,
                                float scale, void* workspace, hipStream_t stream,
-                               const void* key_new = nullptr, const void* value_new = nullptr);
+                               const void* key_new = nullptr, const void* value_new = nullptr,
+                               const int32_t* cow_src = nullptr);
+// The appending decode folds copy-on-write copies in when one (block, head)
+// slice of a pool is 64, 128 or 256 chunks of 16 bytes.
+bool append_cow_supported(const Cache& c);
 
 // Device address of the allocation-free decode's scratch array on the
 // current device (looked up once per device, then cached).
@@ -73,7 +78,8 @@ hipError_t launch_paged_decode_grouped(const Cache& c, void* out, pa_dtype out_d
                                        const int32_t* block_tables, int32_t max_blocks_per_seq,
                                        const int32_t* context_lens, int32_t S, int32_t max_context_len,
                                        float scale, int32_t group_size, void* workspace, hipStream_t stream,
-                                       const void* key_new = nullptr, const void* value_new = nullptr);
+                                       const void* key_new = nullptr, const void* value_new = nullptr,
+                                       const int32_t* cow_src = nullptr);
 
 // ---- prefill (paged_prefill.hip) ----------------------------------------------
 bool prefill_supported(pa_dtype dtype, int head_dim, int block_size);

@@ -111,6 +111,10 @@ struct DecodeArgs {
   // the cache already.
   const u32x4* knew;
   const u32x4* vnew;
+  // Appending decode with copy-on-write folded in: cow_src[s] >= 0 names the
+  // block whose copy the row's newest-token block must first receive (whole
+  // block, every head); NULL when there are no copies.
+  const int32_t* cow_src;
 };
 
 constexpr int cmin(int a, int b) { return a < b ? a : b; }
@@ -170,16 +174,51 @@ __device__ __forceinline__ void merge_partitions(const DecodeArgs& a, int64_t sh
 // straight into LDS (per row 2 x 64 chunks, K then V, lane k holding chunk
 // k % LPT; then 64 copies of the partition kernel's block id), so no
 // register is held across the loop, nothing waits for them before it, and
-// their latency hides behind it.
-template <int ROWS>
+// their latency hides behind it.  With copy-on-write folded in, the head's
+// slice of each copied block (CH chunks per pool) comes in the same way, as
+// PIECES pieces of 64 chunks (K pieces, then V pieces, per row).
+template <int ROWS, int PIECES>
 struct NewTokenStage {
   u32x4 kv[ROWS][2][64];
   int32_t phys[64];
+  u32x4 cow[ROWS * PIECES > 0 ? ROWS * PIECES : 1][64];
 };
-template <int ROWS>
-__device__ __forceinline__ NewTokenStage<ROWS>* new_token_stage() {
-  __shared__ NewTokenStage<ROWS> stage;
+template <int ROWS, int PIECES>
+__device__ __forceinline__ NewTokenStage<ROWS, PIECES>* new_token_stage() {
+  __shared__ NewTokenStage<ROWS, PIECES> stage;
   return &stage;
+}
+
+// Copy-on-write slices: a (block, head) slice of one pool is CH = BS * LPT
+// contiguous 16-byte chunks; it is folded into the appending decode when it
+// is one, two or four pieces of 64 chunks (one direct-to-LDS load per piece).
+template <int BS, int LPT>
+struct CowCfg {
+  static constexpr int CH = BS * LPT;
+  static constexpr bool OK = CH == 64 || CH == 128 || CH == 256;
+  static constexpr int PER_POOL = OK ? CH / 64 : 0;  // pieces per pool
+  static constexpr int PIECES = 2 * PER_POOL;       // K pieces, then V pieces
+};
+// Piece q of the slice (block `blk`, head h) into `dst` (64 chunks).
+template <int BS, int LPT>
+__device__ __forceinline__ void fetch_cow_piece(const DecodeArgs& a, int blk, int h, int q, int lane, u32x4* dst) {
+  using CC = CowCfg<BS, LPT>;
+  const u32x4* pool = q < CC::PER_POOL ? a.kpool : a.vpool;
+  const int64_t src = ((int64_t)blk * a.H + h) * CC::CH + (q % CC::PER_POOL) * 64 + lane;
+  load_to_lds(pool + src, lds_addr(dst));
+}
+// The fetched piece q into block `blk` (head h), every chunk but those of
+// token `skip` (the newest token's slot, which its own store fills).
+// Non-temporal stores, issued after the kernel's output writes.
+template <int BS, int LPT>
+__device__ __forceinline__ void store_cow_piece(const DecodeArgs& a, int blk, int h, int q, int lane, int skip,
+                                                const u32x4* piece) {
+  using CC = CowCfg<BS, LPT>;
+  if (blk < 0 || blk >= a.N) return;
+  const int e = (q % CC::PER_POOL) * 64 + lane;  // chunk within the slice
+  if (e / LPT == skip) return;
+  u32x4* pool = const_cast<u32x4*>(q < CC::PER_POOL ? a.kpool : a.vpool);
+  __builtin_nontemporal_store(piece[lane], &pool[((int64_t)blk * a.H + h) * CC::CH + e]);
 }
 // The calling wave starts the fetch of element row_h (= row * H + head) of
 // knew/vnew into `stage`.
@@ -266,17 +305,31 @@ __global__ __launch_bounds__((DecodeCfg<E, D, BS, WIDE>::NW * 64)) PA_DECODE_OCC
   const int c = lane % LPT;  // 16-byte column within the row
 
   // wave 0 of the partition holding the newest token adds it
-  const bool new_here = add_new && (ctx - 1) / P == p && w == 0;
+  using CC = CowCfg<BS, LPT>;
+  const bool new_part = add_new && (ctx - 1) / P == p;  // this partition holds the newest token
+  const bool new_here = new_part && w == 0;
   const int new_blk = (ctx - 1) / BS;  // logical block of the newest token
-  NewTokenStage<1>* stage = nullptr;
+  NewTokenStage<1, CC::PIECES>* stage = nullptr;
+  // copy-on-write: the newest token's block first receives a copy of `cow`;
+  // until then the row reads that block's older tokens from `cow` itself
+  int cow = -1;
   if constexpr (APPEND) {
-    stage = new_token_stage<1>();
+    stage = new_token_stage<1, CC::PIECES>();
     if (new_here) {
       fetch_new_token<LPT>(a, (int64_t)s * a.H + h, lane, &stage->kv[0][0][0]);
       if (new_blk < a.max_blocks)
         load_dword_to_lds(&a.tables[(int64_t)s * a.max_blocks + new_blk], lds_addr(stage->phys));
     }
+    if constexpr (CC::OK) {
+      if (a.cow_src && new_part) {
+        const int src = a.cow_src[s];
+        cow = src >= 0 && src < a.N ? src : -1;  // an id outside the pool copies nothing, like pa_copy_blocks
+      }
+    }
   }
+  // the pieces of the copy go to waves 1, 2, ... (wave 0 already waits for
+  // the new token before its loop)
+  const int cow_q0 = (w + NW - 1) % NW;
 
   const int nblk = (kv_ctx + BS - 1) / BS;  // logical blocks read from the pools
   const int jb = p * (P / BS);           // first logical block of the partition
@@ -284,12 +337,19 @@ __global__ __launch_bounds__((DecodeCfg<E, D, BS, WIDE>::NW * 64)) PA_DECODE_OCC
   // table window: lane k holds logical block jb + wbase + k (-1 past the end)
   auto window = [&](int wbase) {
     const int j = jb + wbase + lane;
-    return (j < nblk && j < a.max_blocks) ? a.tables[trow + j] : -1;
+    int e = (j < nblk && j < a.max_blocks) ? a.tables[trow + j] : -1;
+    if (APPEND && j == new_blk && cow >= 0) e = cow;  // (patched after the load, which does not wait for cow)
+    return e;
   };
   int wbase = 0;
   int tbl = window(0);
 
   const u32x4 qc = a.q[((int64_t)s * a.H + h) * LPT + c];
+  if constexpr (APPEND && CC::OK) {
+    if (cow >= 0) {
+      for (int q = cow_q0; q < CC::PIECES; q += NW) fetch_cow_piece<BS, LPT>(a, cow, h, q, lane, stage->cow[q]);
+    }
+  }
 
   float m = kNegBig, l = 0.f;
   float o[VEC];
@@ -428,6 +488,16 @@ __global__ __launch_bounds__((DecodeCfg<E, D, BS, WIDE>::NW * 64)) PA_DECODE_OCC
     a.ws_ml[(sh * a.max_parts + p) * 2] = M;
     a.ws_ml[(sh * a.max_parts + p) * 2 + 1] = L;
   }
+  if constexpr (APPEND && CC::OK) {
+    // the copy into the newest token's block (its id, fetched by wave 0, is
+    // in LDS since that wave's wait before its loop and the barrier above)
+    if (cow >= 0 && cow_q0 < CC::PIECES) {
+      const int dst = new_blk < a.max_blocks ? __builtin_amdgcn_readfirstlane(stage->phys[0]) : -1;
+      wait_vmem();  // this wave's pieces have landed
+      for (int q = cow_q0; q < CC::PIECES; q += NW)
+        store_cow_piece<BS, LPT>(a, dst, h, q, lane, (ctx - 1) % BS, stage->cow[q]);
+    }
+  }
 #if PA_DECODE_FUSED
   if (nparts > 1) {
     // publish this partition, count arrivals; the last one merges them all
@@ -488,6 +558,10 @@ void decode_grouped_kernel(DecodeArgs a, int32_t ngroups) {
   // (the W lengths come in one vector load, lane r holding row r's, instead
   // of one scalar round trip per row)
   const int lens_w = a.lens[min(r0 + min((int)(threadIdx.x & 63), W - 1), a.S - 1)];
+  using CC = CowCfg<BS, C::LPT>;
+  // copy-on-write sources of the rows, loaded the same way
+  const int cow_w = (APPEND && CC::OK && a.cow_src) ? a.cow_src[min(r0 + min((int)(threadIdx.x & 63), W - 1), a.S - 1)]
+                                                    : -1;
   int ctx[W], kv_ctx[W];
   int maxctx = 0, max_kv = 0;
 #pragma unroll
@@ -508,9 +582,9 @@ void decode_grouped_kernel(DecodeArgs a, int32_t ngroups) {
   const int jb = p * (P / BS);
 
   // row r's newest token: wave r % NW of the partition that holds it
-  NewTokenStage<W>* stage = nullptr;
+  NewTokenStage<W, CC::PIECES>* stage = nullptr;
   if constexpr (APPEND) {
-    stage = new_token_stage<W>();
+    stage = new_token_stage<W, CC::PIECES>();
 #pragma unroll
     for (int r = 0; r < W; ++r) {
       if (kv_ctx[r] < ctx[r] && (ctx[r] - 1) / P == p && w == r % NW)
@@ -531,6 +605,32 @@ void decode_grouped_kernel(DecodeArgs a, int32_t ngroups) {
     l[r] = 0.f;
 #pragma unroll
     for (int e = 0; e < VEC; ++e) o[r][e] = 0.f;
+  }
+
+  // Rows whose newest token is in this partition: the block that receives
+  // it (new_dst, from the table) and, with copy-on-write folded in, the
+  // block it first receives a copy of (cow).  Until the copy lands the row
+  // reads that block's older tokens from `cow`: its table lane is patched,
+  // the head's slice of `cow` is fetched into LDS (piece q by wave q), and
+  // the copy is stored at the end of the kernel.
+  int new_dst[W], cow[W];
+#pragma unroll
+  for (int r = 0; r < W; ++r) {
+    new_dst[r] = -1;
+    cow[r] = -1;
+    if (APPEND && kv_ctx[r] < ctx[r] && (ctx[r] - 1) / P == p) {
+      const int jn = (ctx[r] - 1) / BS - jb;  // lane of the newest token's block (< P / BS <= 64)
+      new_dst[r] = __builtin_amdgcn_readlane(tbl[r], jn);
+      if constexpr (CC::OK) {
+        const int src = __builtin_amdgcn_readlane(cow_w, r);
+        if (src >= 0 && src < a.N) {  // an id outside the pool copies nothing, like pa_copy_blocks
+          cow[r] = src;
+          if (lane == jn) tbl[r] = src;
+          for (int q = w; q < CC::PIECES; q += NW)
+            fetch_cow_piece<BS, LPT>(a, src, h, q, lane, stage->cow[r * CC::PIECES + q]);
+        }
+      }
+    }
   }
 
   // Online-softmax update of row r with one step's chunks; the value
@@ -687,10 +787,8 @@ void decode_grouped_kernel(DecodeArgs a, int32_t ngroups) {
 #pragma unroll
     for (int r = 0; r < W; ++r) {
       const int pos = ctx[r] - 1;
-      if (kv_ctx[r] < ctx[r] && pos / P == p && w == r % NW) {
-        const int phys = __builtin_amdgcn_readlane(tbl[r], (pos - p * P) / BS);
-        add_new_token<E, D, BS>(a, &stage->kv[r][0][0], lane, phys, qc[r], tr, m[r], l[r], o[r]);
-      }
+      if (kv_ctx[r] < ctx[r] && pos / P == p && w == r % NW)
+        add_new_token<E, D, BS>(a, &stage->kv[r][0][0], lane, new_dst[r], qc[r], tr, m[r], l[r], o[r]);
     }
   }
 
@@ -756,8 +854,14 @@ void decode_grouped_kernel(DecodeArgs a, int32_t ngroups) {
     for (int r = 0; r < W; ++r) {
       const int pos = ctx[r] - 1;
       if (kv_ctx[r] < ctx[r] && pos / P == p && w == r % NW)
-        store_new_token<LPT, BS>(a, &stage->kv[r][0][0], lane,
-                                 __builtin_amdgcn_readlane(tbl[r], (pos - p * P) / BS), pos % BS, h);
+        store_new_token<LPT, BS>(a, &stage->kv[r][0][0], lane, new_dst[r], pos % BS, h);
+      if constexpr (CC::OK) {
+        if (cow[r] >= 0 && w < CC::PIECES) {
+          wait_vmem();  // this wave's pieces have landed
+          for (int q = w; q < CC::PIECES; q += NW)
+            store_cow_piece<BS, LPT>(a, new_dst[r], h, q, lane, pos % BS, stage->cow[r * CC::PIECES + q]);
+        }
+      }
     }
   }
 }
@@ -963,7 +1067,7 @@ namespace {
 DecodeArgs make_args(const Cache& c, void* out, pa_dtype out_dtype, const void* query,
                      const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
                      int32_t S, int64_t mp, float scale, void* workspace, const void* key_new,
-                     const void* value_new) {
+                     const void* value_new, const int32_t* cow_src) {
   DecodeArgs a;
   a.q = (const u32x4*)query;
   a.kpool = (const u32x4*)c.k;
@@ -985,6 +1089,7 @@ DecodeArgs make_args(const Cache& c, void* out, pa_dtype out_dtype, const void* 
   a.out_dtype = out_dtype;
   a.knew = (const u32x4*)key_new;
   a.vnew = (const u32x4*)value_new;
+  a.cow_src = cow_src;
   return a;
 }
 
@@ -994,13 +1099,13 @@ hipError_t launch_paged_decode(const Cache& c, void* out, pa_dtype out_dtype, co
                                const int32_t* block_tables, int32_t max_blocks_per_seq,
                                const int32_t* context_lens, int32_t S, int32_t max_context_len,
                                float scale, void* workspace, hipStream_t stream, const void* key_new,
-                               const void* value_new) {
+                               const void* value_new, const int32_t* cow_src) {
   const Variant* v = find_variant(c.dtype, c.head_dim, c.block_size);
   if (!v) return hipErrorInvalidValue;
   const Partitioning& pt = pick_partitioning(*v, S, c.num_heads, max_context_len);
   const int64_t mp = max_parts_for(pt, max_context_len);
   DecodeArgs a = make_args(c, out, out_dtype, query, block_tables, max_blocks_per_seq, context_lens, S, mp, scale,
-                           workspace, key_new, value_new);
+                           workspace, key_new, value_new, cow_src);
   const int64_t grid = (int64_t)S * c.num_heads * mp;
   hipLaunchKernelGGL(key_new ? pt.append_kernel : pt.kernel, dim3((unsigned)grid), dim3(pt.NW * 64), 0, stream, a);
   hipError_t err = hipGetLastError();
@@ -1008,6 +1113,11 @@ hipError_t launch_paged_decode(const Cache& c, void* out, pa_dtype out_dtype, co
   hipLaunchKernelGGL(decode_reduce_kernel, dim3((unsigned)(S * c.num_heads)), dim3(64), 0, stream, a,
                      (int32_t)c.head_dim, (int32_t)pt.P);
   return hipGetLastError();
+}
+
+bool append_cow_supported(const Cache& c) {
+  const int64_t chunks = (int64_t)c.block_size * c.head_dim * dtype_bytes(c.dtype) / 16;  // one (block, head) slice
+  return chunks == 64 || chunks == 128 || chunks == 256;
 }
 
 bool decode_grouped_built(pa_dtype dtype, int head_dim, int block_size, int group_size) {
@@ -1026,15 +1136,15 @@ hipError_t launch_paged_decode_grouped(const Cache& c, void* out, pa_dtype out_d
                                        const int32_t* block_tables, int32_t max_blocks_per_seq,
                                        const int32_t* context_lens, int32_t S, int32_t max_context_len,
                                        float scale, int32_t group_size, void* workspace, hipStream_t stream,
-                                       const void* key_new, const void* value_new) {
+                                       const void* key_new, const void* value_new, const int32_t* cow_src) {
   const GroupedVariant* v = find_grouped(c.dtype, c.head_dim, c.block_size, group_size);
   if (!v)  // no grouped build for this shape: the ungrouped kernel gives the same result
     return launch_paged_decode(c, out, out_dtype, query, block_tables, max_blocks_per_seq, context_lens, S,
-                               max_context_len, scale, workspace, stream, key_new, value_new);
+                               max_context_len, scale, workspace, stream, key_new, value_new, cow_src);
   const int64_t mp = ((int64_t)max_context_len + kGroupTokens - 1) / kGroupTokens;
   const int32_t ngroups = (S + group_size - 1) / group_size;
   DecodeArgs a = make_args(c, out, out_dtype, query, block_tables, max_blocks_per_seq, context_lens, S, mp, scale,
-                           workspace, key_new, value_new);
+                           workspace, key_new, value_new, cow_src);
   const int64_t grid = (int64_t)ngroups * c.num_heads * mp;
   hipLaunchKernelGGL(key_new ? v->append_kernel : v->kernel, dim3((unsigned)grid), dim3(kGroupWaves * 64), 0,
                      stream, a, ngroups);

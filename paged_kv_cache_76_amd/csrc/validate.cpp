@@ -115,7 +115,8 @@ pa_status pa_check_block_tables(const int32_t* block_tables, int32_t S, int32_t 
 }
 
 pa_status pa_check_append_slots(const int32_t* block_tables, int32_t S, int32_t max_blocks_per_seq,
-                                const int32_t* context_lens, int32_t block_size) {
+                                const int32_t* context_lens, int32_t block_size, const int32_t* cow_src,
+                                int32_t num_blocks) {
   const char* fn = "pa_check_append_slots";
   if (S < 0 || max_blocks_per_seq < 0 || block_size < 1)
     return pa::check_fail(PA_ERR_INVALID_ARG, "%s: bad size", fn);
@@ -168,6 +169,47 @@ pa_status pa_check_append_slots(const int32_t* block_tables, int32_t S, int32_t 
                                 fresh[k].row, fresh[k].block, fresh[k].off, s);
       }
     }
+  }
+  if (!cow_src) return PA_OK;
+  // Copy-on-write folded in: row s's newest-token block d first receives a
+  // copy of block c = cow_src[s] (every slot but the newest token's, which
+  // its own write fills).  d must belong to s alone, and no write of the
+  // call may land in a slot of c that the copy reads.
+  std::unordered_map<int32_t, int32_t> owner;  // newest-token block -> row, for rows that copy
+  for (int32_t s = 0; s < S; ++s) {
+    const int32_t c = cow_src[s];
+    if (c < 0) continue;
+    const int32_t pos = context_lens[s] - 1;
+    const int32_t d = block_tables[(int64_t)s * max_blocks_per_seq + pos / block_size];
+    if (c >= num_blocks)
+      return pa::check_fail(PA_ERR_INVALID_ARG, "%s: sequence %d: copy source %d outside [0, %d)", fn, s, c,
+                            num_blocks);
+    if (c == d) return pa::check_fail(PA_ERR_INVALID_ARG, "%s: sequence %d copies block %d onto itself", fn, s, c);
+    owner[d] = s;
+  }
+  for (int32_t s = 0; s < S; ++s) {  // nobody else maps a block that receives a copy
+    const int64_t nblk = ((int64_t)context_lens[s] + block_size - 1) / block_size;
+    const int32_t* row = block_tables + (int64_t)s * max_blocks_per_seq;
+    for (int64_t j = 0; j < nblk; ++j) {
+      const auto it = owner.find(row[j]);
+      if (it != owner.end() && it->second != s)
+        return pa::check_fail(PA_ERR_INVALID_ARG, "%s: block %d receives sequence %d's copy but sequence %d maps it",
+                              fn, row[j], it->second, s);
+    }
+  }
+  for (const Slot& f : fresh) {  // every write of the call against every copy's source
+    for (int32_t s = 0; s < S; ++s) {
+      if (cow_src[s] != f.block) continue;
+      if (f.off != (context_lens[s] - 1) % block_size)
+        return pa::check_fail(PA_ERR_INVALID_ARG,
+                              "%s: sequence %d writes block %d offset %d, which sequence %d's copy reads", fn, f.row,
+                              f.block, f.off, s);
+    }
+  }
+  for (int32_t s = 0; s < S; ++s) {  // a copy's source is no other copy's destination
+    if (cow_src[s] >= 0 && owner.count(cow_src[s]))
+      return pa::check_fail(PA_ERR_INVALID_ARG, "%s: sequence %d copies from block %d, which receives a copy", fn, s,
+                            cow_src[s]);
   }
   return PA_OK;
 }

@@ -226,6 +226,12 @@ class BeamLoop:
                  fused: bool = False):
         self.G, self.W, self.beam = groups, width, beam
         self.fused = fused
+        # fused steps also fold their copy-on-write copies into the decode
+        # launch when the library does that for this shape: a (block, head)
+        # slice of one pool of 1, 2 or 4 KiB
+        elem = 4 if dtype == "f32" else 2
+        self.fold_copies = fused and block_size * head_dim * elem in (1024, 2048, 4096)
+        self.copy_launches = 0  # pa_copy_blocks launches made by the steps
         self.H, self.d, self.B = num_heads, head_dim, block_size
         self.dtype, self.device = dtype, device
         self.scale = 1.0 / math.sqrt(head_dim)
@@ -303,16 +309,32 @@ class BeamLoop:
         v_new = inputs.normal(self.r_step, (n, self.H, self.d), self.dtype)
         q = inputs.normal(self.r_step, (n, self.H, self.d), self.dtype)
         lens = self.mgr.lens[rows_sorted].astype(np.int32)
-        dev = {"pairs": torch.from_numpy(pairs), "k": k_new, "v": v_new, "slots": torch.from_numpy(slots),
-               "q": q, "tables": torch.from_numpy(np.ascontiguousarray(self.mgr.tables[rows_sorted])),
-               "lens": torch.from_numpy(lens)}
+        tables = np.ascontiguousarray(self.mgr.tables[rows_sorted])
+        copy_pairs, cow = pairs, None
+        if self.fold_copies:
+            # each copy's destination is the newest-token block of the row that
+            # appends into it: that row takes the copy's source instead
+            newest = tables[np.arange(n), (lens - 1) // self.B]
+            cow = np.full(n, -1, np.int32)
+            left = []
+            for src, dst in pairs:
+                hit = np.nonzero(newest == dst)[0]
+                if len(hit) == 1:
+                    cow[hit[0]] = src
+                else:
+                    left.append((src, dst))
+            copy_pairs = np.asarray(left, np.int64).reshape(-1, 2)
+        dev = {"pairs": torch.from_numpy(copy_pairs), "k": k_new, "v": v_new, "slots": torch.from_numpy(slots),
+               "q": q, "tables": torch.from_numpy(tables), "lens": torch.from_numpy(lens)}
+        if cow is not None:
+            dev["cow"] = torch.from_numpy(cow)
         dev = {k: t.to(self.device) for k, t in dev.items()}
         if self.keep_history:
             for i, s in enumerate(rows_sorted):
                 self.hist[int(s)].k.append(k_new[i:i + 1])
                 self.hist[int(s)].v.append(v_new[i:i + 1])
-        return {"rows": rows_sorted, "lens": lens, "n_pairs": len(pairs), "dev": dev, "q": q,
-                "max_ctx": int(lens.max())}
+        return {"rows": rows_sorted, "lens": lens, "n_pairs": len(pairs), "n_copy_launch": len(copy_pairs),
+                "dev": dev, "q": q, "max_ctx": int(lens.max())}
 
     def launch(self, plan: dict, events=None) -> StepRecord:
         """Device half of a step: copy-on-write copies, the new tokens' cache
@@ -322,11 +344,13 @@ class BeamLoop:
         out = torch.empty((n, self.H, self.d), dtype=TORCH[self.dtype], device=self.device)
         if events is not None:
             events[0].record()
-        if plan["n_pairs"]:
+        if plan["n_copy_launch"]:
             pa_copy_blocks(self.cache, dev["pairs"])
+            self.copy_launches += 1
         if self.fused:
             pa_paged_decode_append(self.cache, out, dev["q"], dev["k"], dev["v"], dev["tables"], dev["lens"],
-                                   plan["max_ctx"], self.scale, self.W if self.grouped else 1, self.ws)
+                                   plan["max_ctx"], self.scale, self.W if self.grouped else 1, self.ws,
+                                   cow_src=dev.get("cow"))
         else:
             self._write_and_decode(plan, out)
         if events is not None:

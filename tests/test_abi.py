@@ -116,12 +116,16 @@ def test_append_decode_argument_checks():
     lib = L.lib()
     d = _desc()
 
-    def call(key=FAKE, value=FAKE, group=1, maxctx=100, ws=None, wsb=0, S=4, maxb=8):
-        return lib.pa_paged_decode_append(ctypes.byref(d), FAKE, L.PA_F16, FAKE, key, value, FAKE, maxb, FAKE, S,
-                                          maxctx, 0.1, group, ws, wsb, None)
+    def call(key=FAKE, value=FAKE, group=1, maxctx=100, ws=None, wsb=0, S=4, maxb=8, cow=None, desc=d):
+        return lib.pa_paged_decode_append(ctypes.byref(desc), FAKE, L.PA_F16, FAKE, key, value, cow, FAKE, maxb,
+                                          FAKE, S, maxctx, 0.1, group, ws, wsb, None)
 
     _err(call(key=None), "NULL key/value")
     _err(call(value=FAKE + 8), "key/value must be 16-byte aligned")
+    _err(call(cow=FAKE + 2), "cow_src must be 4-byte aligned")
+    # copy-on-write folds in for 1, 2 or 4 KiB (block, head) slices only
+    assert call(cow=FAKE, desc=_desc(block_size=32)) == L.PA_ERR_UNSUPPORTED   # 8 KiB
+    _err(L.PA_ERR_UNSUPPORTED, "pa_copy_blocks first")
     _err(call(group=3), "group_size = 3")
     _err(call(maxb=2), "cannot hold")
     assert call(S=0) == L.PA_OK

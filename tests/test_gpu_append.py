@@ -153,3 +153,48 @@ def test_grouped_over_shared_blocks(share, W, dtype, B, prompt, tails):
     ref = np.stack([oa.decode(inputs.to_f64(q[s]), inputs.to_f64(torch.cat(hist[s][0])),
                               inputs.to_f64(torch.cat(hist[s][1])), scale) for s in range(S)])
     check_close(out, ref, TOL[dtype], f"append grouped {share} W={W}")
+
+
+@pytest.mark.parametrize("W,dtype,B,prompt,tails", [
+    (4, "bf16", 16, 300, [1, 1, 1, 1]),      # 4 siblings over a partial prompt block: 3 copy, 1 writes in place
+    (4, "f16", 16, 1007, [1, 1, 1, 1]),      # the copied block holds 15 of 16 tokens
+    (2, "bf16", 16, 1030, [1, 1, 1, 1]),     # the copied block in the second partition
+    (1, "f16", 16, 300, [1, 1, 1, 1]),       # the ungrouped kernel (group_size 1) folds the copies too
+    (4, "f16", 8, 300, [1, 1, 1, 1]),        # a 2 KiB slice (B = 8: the ungrouped kernel)
+])
+def test_copy_on_write_folded_in(W, dtype, B, prompt, tails):
+    # the builder's last step runs neither its copies nor its writes: the
+    # appending decode receives the copies as cow_src and does both
+    print(f"append + copy-on-write W={W} {dtype} B={B} prompt={prompt} tails={tails}", flush=True)
+    H, d = 4, 128
+    width = 4
+    cache, mgr, q, hist, lens, held, pairs = _build_shared(W * 1000 + B + prompt, 3, width, prompt, tails, H, d, B,
+                                                           dtype, "all", hold_last=True, hold_copies=True)
+    S = q.shape[0]
+    assert len(pairs) > 0, "the held step copies shared blocks"
+    key = torch.stack([torch.cat(hist[s][0])[-1] for s in range(S)])
+    value = torch.stack([torch.cat(hist[s][1])[-1] for s in range(S)])
+    newest_blk = np.array([mgr.tables[s][(lens[s] - 1) // B] for s in range(S)])
+    slots = newest_blk.astype(np.int64) * B + (lens - 1) % B
+    cow = np.full(S, -1, np.int32)
+    for src, dst in pairs:
+        (hit,) = np.nonzero(newest_blk == dst)
+        assert len(hit) == 1, "every copy goes to one row's newest-token block"
+        cow[hit[0]] = src
+    L.check_append_slots(mgr.tables[:S], lens, B, cow, cache.num_blocks)
+    k0, v0 = bits(cache.k), bits(cache.v)
+    scale = 1 / math.sqrt(d)
+    ws = L.decode_grouped_workspace(cache, S, int(lens.max()), W)
+    out = torch.full((S, H, d), float("nan"), dtype=torch.float32, device="cuda")
+    L.pa_paged_decode_append(cache, out, q.cuda(), key.cuda(), value.cuda(), torch.from_numpy(mgr.tables[:S]).cuda(),
+                             torch.from_numpy(lens).cuda(), int(lens.max()), scale, W, ws,
+                             cow_src=torch.from_numpy(cow).cuda())
+    torch.cuda.synchronize()
+    # the oracle: the held copies, then every row's newest token
+    ek, ev = oc.copy_blocks(k0, v0, pairs)
+    ek, ev = oc.reshape_and_cache(ek, ev, bits(key), bits(value), slots)
+    assert np.array_equal(bits(cache.k), ek), "K pool differs from copy + write"
+    assert np.array_equal(bits(cache.v), ev), "V pool differs from copy + write"
+    ref = np.stack([oa.decode(inputs.to_f64(q[s]), inputs.to_f64(torch.cat(hist[s][0])),
+                              inputs.to_f64(torch.cat(hist[s][1])), scale) for s in range(S)])
+    check_close(out, ref, TOL[dtype], f"append + copy-on-write W={W}")

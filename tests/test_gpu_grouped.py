@@ -19,13 +19,16 @@ from gpu_util import TOL, check_close
 pytestmark = pytest.mark.gpu
 
 
-def _build_shared(seed, groups, width, prompt, tails, H, d, B, dtype, share="all", hold_last=False):
+def _build_shared(seed, groups, width, prompt, tails, H, d, B, dtype, share="all", hold_last=False,
+                  hold_copies=False):
     """``groups`` prompts of ``prompt`` tokens; each forks into ``width`` rows
     (``share='all'``), only the first two rows share (``'pair'``) or none
     (``'none'``); then row i of a group appends ``tails[i]`` own tokens.
     ``hold_last``: the last append step's copies run but its tokens are not
     written (they are in the histories); the rows of that step are returned
-    as a sixth value."""
+    as a sixth value.  ``hold_copies`` (with ``hold_last``): that step's
+    copy-on-write copies do not run either; its pairs come back as a seventh
+    value."""
     r = np.random.default_rng(seed)
     S = groups * width
     need = groups * width * (-(-(prompt + max(tails)) // B) + 1)
@@ -57,10 +60,13 @@ def _build_shared(seed, groups, width, prompt, tails, H, d, B, dtype, share="all
     L.pa_reshape_and_cache(cache, torch.cat(k_writes).cuda(), torch.cat(v_writes).cuda(),
                            torch.from_numpy(np.concatenate(slot_writes)).cuda())
     pairs_total = 0
+    held_pairs = np.zeros((0, 2), np.int64)
     for step in range(max(tails)):
         rows = [s for s in range(S) if tails[s % width] > step]
         slots, pairs = mgr.append_step(rows)
-        if len(pairs):
+        if hold_copies and step == max(tails) - 1:
+            held_pairs = pairs
+        elif len(pairs):
             L.pa_copy_blocks(cache, torch.from_numpy(pairs).cuda())
             pairs_total += len(pairs)
         kn = inputs.normal(r, (len(rows), H, d), dtype)
@@ -72,6 +78,8 @@ def _build_shared(seed, groups, width, prompt, tails, H, d, B, dtype, share="all
             hist[s][0].append(kn[i:i + 1]); hist[s][1].append(vn[i:i + 1])
     q = inputs.normal(r, (S, H, d), dtype)
     lens = mgr.lens[:S].astype(np.int32)
+    if hold_last and hold_copies:
+        return cache, mgr, q, hist, lens, held, held_pairs
     if hold_last:
         return cache, mgr, q, hist, lens, held
     return cache, mgr, q, hist, lens

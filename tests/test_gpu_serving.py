@@ -68,6 +68,8 @@ def test_shared_prompt_groups_bf16(beam, grouped, fused):
             _check(loop, rec, "bf16", f"shared beam={beam} step {step}")
     if beam:
         assert copies > 0            # shared partial blocks were copied before writes
+        if fused:
+            assert loop.copy_launches == 0   # every copy went into the decode launch
     else:
         assert copies == 0           # 512-token prompts end on a block boundary
         # the prompt blocks are still shared by all 4 samples of each group

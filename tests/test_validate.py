@@ -73,6 +73,30 @@ def test_append_slots():
     _refused(L.check_append_slots, t, [6, 13, 2], 4, match="context length 13")
 
 
+def test_append_slots_with_copies():
+    # B = 4, four siblings over the shared partial block 3 (3 tokens): rows 0-2
+    # copy it into blocks 5, 6, 7 and append at offset 3; row 3 appends in
+    # place into block 3 at the same offset
+    t = np.array([[3], [5], [6], [7]], np.int32)
+    t[3, 0] = 3
+    t[0, 0], t[1, 0], t[2, 0] = 5, 6, 7
+    lens = [4, 4, 4, 4]
+    cow = [3, 3, 3, -1]
+    L.check_append_slots(t, lens, 4, cow, 8)
+    _refused(L.check_append_slots, t, lens, 4, [3, 3, 9, -1], 8, match="copy source 9 outside")
+    _refused(L.check_append_slots, t, lens, 4, [5, 3, 3, -1], 8, match="copies block 5 onto itself")
+    # row 3 writes block 3 at offset 2 while row 0's copy of block 3 reads it
+    _refused(L.check_append_slots, np.array([[5], [6], [7], [3]], np.int32), [4, 4, 4, 3], 4, [3, 3, 3, -1], 8,
+             match="sequence 3 writes block 3 offset 2, which sequence 0's copy reads")
+    # (a copy's destination mapped by another row always shows up first as a
+    # newest slot that another row reads, which the check above refuses)
+    # a copy's source that receives another copy
+    _refused(L.check_append_slots, np.array([[5], [6]], np.int32), [2, 2], 4, [6, 1], 8,
+             match="copies from block 6, which receives a copy")
+    with pytest.raises(ValueError, match="num_blocks"):
+        L.check_append_slots(t, lens, 4, cow)
+
+
 def test_prefill_rows():
     L.check_prefill_rows([0, 3, 3, 10], [5, 1, 7], 7)           # an empty query range is allowed
     _refused(L.check_prefill_rows, [1, 3], [5], 4, match="cu_q_lens\\[0\\]")
