@@ -497,7 +497,7 @@ def shared_measure(beam: bool, grouped: bool, steps: int = 64,
     loop = BeamLoop(4, 32, 4, 512, steps, H, D, B, "bf16", beam=beam, keep_history=False, grouped=grouped,
                     fused=fused)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    logical = unique = copies = 0
+    logical = unique = copies = cow_tokens = 0
     saved = []
     # host work (remaps, appends, activations, uploads) for every step first,
     # so the timed launches find everything resident in HBM
@@ -507,6 +507,7 @@ def shared_measure(beam: bool, grouped: bool, steps: int = 64,
         logical += workloads.decode_bytes(p["lens"], H, D, 2, B)
         unique += loop.unique_blocks_read(p["rows"]) * B * H * D * 2 * 2
         copies += p["n_pairs"]
+        cow_tokens += p["cow_tokens"]
         saved.append(loop.mgr.blocks_saved_by_sharing())
         plans.append(p)
     span = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -527,7 +528,9 @@ def shared_measure(beam: bool, grouped: bool, steps: int = 64,
         ev[i][1].record()
     torch.cuda.synchronize()
     ms = [a.elapsed_time(b) for a, b in ev]
-    cow_bytes = copies * 2 * 2 * H * B * D * 2
+    # the copies' algorithmic bytes: each copy carries the appending row's
+    # tokens before its newest (read once, written once, K and V)
+    cow_bytes = cow_tokens * 2 * 2 * H * D * 2
     name = ("beam search (width 4)" if beam else "parallel sampling (4 per prompt)") + \
         (", grouped decode" if grouped else "")
     config = {"workload": f"shared-block decode: {name}", "groups": 32, "width": 4, "prompt_len": 512,
@@ -542,7 +545,8 @@ def shared_measure(beam: bool, grouped: bool, steps: int = 64,
     extra = dict(logical_GBps=round(logical / kernel_s / 1e9, 1),
                  pct_of_peak_unique=round(100 * (unique + cow_bytes) / kernel_s / 1e9 / PEAK_HBM_GBS, 2),
                  seq_steps_per_s=round(128 * steps / kernel_s, 1),
-                 cow_pairs_per_step=round(copies / steps, 2), blocks_saved_by_sharing_mean=round(sum(saved) / steps, 1),
+                 cow_pairs_per_step=round(copies / steps, 2), cow_tokens_per_step=round(cow_tokens / steps, 1),
+                 cow_GB_per_step=round(cow_bytes / steps / 1e9, 4), blocks_saved_by_sharing_mean=round(sum(saved) / steps, 1),
                  logical_GB_per_step=round(logical / steps / 1e9, 4), unique_GB_per_step=round(unique / steps / 1e9, 4),
                  decode_launch_us_p10_p50_p90=[round(sorted(ms)[int(q * (steps - 1))] * 1e3, 1) for q in (0.1, 0.5, 0.9)],
                  decode_launch_us_mean=round(sum(ms) / steps * 1e3, 1),

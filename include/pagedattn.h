@@ -224,9 +224,11 @@ pa_status pa_paged_decode_grouped(const pa_kv_cache* cache, void* out, pa_dtype 
  *   cow_src      int32 [S] or NULL.  cow_src[s] >= 0: the block that holds
  *                row s's newest token is a copy-on-write copy of block
  *                cow_src[s] ([P1] key design 3); the call makes it one
- *                (every slot, every head, as pa_copy_blocks would) before
- *                the newest token lands in it, so no separate copy launch is
- *                needed.  -1: no copy.  Supported when block_size * head_dim
+ *                before the newest token lands in it, so no separate copy
+ *                launch is needed: every head's slots before the newest
+ *                token's offset are copied (the row's tokens in that block);
+ *                the slots after it hold no token of any row and keep what
+ *                they held.  -1: no copy.  Supported when block_size * head_dim
  *                * sizeof(dtype) is 1, 2 or 4 KiB (PA_ERR_UNSUPPORTED
  *                otherwise: copy first and pass NULL).  Ids outside the pool
  *                copy nothing, as in pa_copy_blocks.
@@ -240,13 +242,14 @@ pa_status pa_paged_decode_grouped(const pa_kv_cache* cache, void* out, pa_dtype 
  * result depends on the order in which workgroups run.  With cow_src: a
  * block that receives a copy is mapped by its row alone, no copy reads from
  * a block that receives one, and no write of the call lands in a slot a copy
- * reads (rows that write into a copy's source write the copying row's
- * offset, as siblings over a shared block do).  Debug mode checks all of it
+ * reads (rows that write into a copy's source write at or past the copying
+ * row's offset, as siblings over a shared block do).  Debug mode checks all of it
  * (pa_check_append_slots).  Copy-on-write copies not passed in cow_src
  * (pa_copy_blocks) go before this call on the same stream.
  * Cache contents equal pa_copy_blocks with the cow_src pairs, then
  * pa_reshape_and_cache with the slot of position context_lens[s] - 1 for
- * row s, bit for bit; the output equals pa_paged_decode (group_size 1) or
+ * row s, bit for bit, in every slot but those after a copied block's newest
+ * token (no row holds a token there); the output equals pa_paged_decode (group_size 1) or
  * pa_paged_decode_grouped after them up to rounding (the newest token is
  * added last).
  */
@@ -361,7 +364,8 @@ pa_status pa_check_block_tables(const int32_t* block_tables, int32_t S, int32_t 
  * [0, num_blocks) and is not its destination, the destination (the row's
  * newest-token block) is mapped by no other row and receives no other copy,
  * no copy's source receives a copy, and every write into a copy's source
- * lands in the copying row's newest offset (the slot the copy skips).  Each
+ * lands at or past the copying row's newest offset (the copy reads the
+ * slots before it).  Each
  * row needs 1 <= context_lens[s] <= block_size * max_blocks_per_seq.
  *   block_tables  int32 [S][max_blocks_per_seq];  context_lens, cow_src  int32 [S].
  */

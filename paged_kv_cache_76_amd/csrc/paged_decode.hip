@@ -176,7 +176,8 @@ __device__ __forceinline__ void merge_partitions(const DecodeArgs& a, int64_t sh
 // register is held across the loop, nothing waits for them before it, and
 // their latency hides behind it.  With copy-on-write folded in, the head's
 // slice of each copied block (CH chunks per pool) comes in the same way, as
-// PIECES pieces of 64 chunks (K pieces, then V pieces, per row).
+// PIECES pieces of 64 chunks (K pieces, then V pieces, per row), of which
+// only those holding the row's tokens before its newest are fetched.
 template <int ROWS, int PIECES>
 struct NewTokenStage {
   u32x4 kv[ROWS][2][64];
@@ -199,24 +200,29 @@ struct CowCfg {
   static constexpr int PER_POOL = OK ? CH / 64 : 0;  // pieces per pool
   static constexpr int PIECES = 2 * PER_POOL;       // K pieces, then V pieces
 };
-// Piece q of the slice (block `blk`, head h) into `dst` (64 chunks).
+// Piece q of the slice (block `blk`, head h) into `dst` (64 chunks), unless
+// the piece starts at or past token `keep` (the newest token's slot): the
+// copy carries only the tokens the row holds before its newest one.
 template <int BS, int LPT>
-__device__ __forceinline__ void fetch_cow_piece(const DecodeArgs& a, int blk, int h, int q, int lane, u32x4* dst) {
+__device__ __forceinline__ void fetch_cow_piece(const DecodeArgs& a, int blk, int h, int q, int lane, int keep,
+                                                u32x4* dst) {
   using CC = CowCfg<BS, LPT>;
+  if ((q % CC::PER_POOL) * (64 / LPT) >= keep) return;  // uniform
   const u32x4* pool = q < CC::PER_POOL ? a.kpool : a.vpool;
   const int64_t src = ((int64_t)blk * a.H + h) * CC::CH + (q % CC::PER_POOL) * 64 + lane;
   load_to_lds(pool + src, lds_addr(dst));
 }
-// The fetched piece q into block `blk` (head h), every chunk but those of
-// token `skip` (the newest token's slot, which its own store fills).
-// Non-temporal stores, issued after the kernel's output writes.
+// The fetched piece q into block `blk` (head h): the chunks of tokens
+// before `keep` (the newest token's slot, which its own store fills; the
+// slots after it hold no token of any row).  Non-temporal stores, issued
+// after the kernel's output writes.
 template <int BS, int LPT>
-__device__ __forceinline__ void store_cow_piece(const DecodeArgs& a, int blk, int h, int q, int lane, int skip,
+__device__ __forceinline__ void store_cow_piece(const DecodeArgs& a, int blk, int h, int q, int lane, int keep,
                                                 const u32x4* piece) {
   using CC = CowCfg<BS, LPT>;
   if (blk < 0 || blk >= a.N) return;
   const int e = (q % CC::PER_POOL) * 64 + lane;  // chunk within the slice
-  if (e / LPT == skip) return;
+  if (e / LPT >= keep) return;
   u32x4* pool = const_cast<u32x4*>(q < CC::PER_POOL ? a.kpool : a.vpool);
   __builtin_nontemporal_store(piece[lane], &pool[((int64_t)blk * a.H + h) * CC::CH + e]);
 }
@@ -347,7 +353,8 @@ __global__ __launch_bounds__((DecodeCfg<E, D, BS, WIDE>::NW * 64)) PA_DECODE_OCC
   const u32x4 qc = a.q[((int64_t)s * a.H + h) * LPT + c];
   if constexpr (APPEND && CC::OK) {
     if (cow >= 0) {
-      for (int q = cow_q0; q < CC::PIECES; q += NW) fetch_cow_piece<BS, LPT>(a, cow, h, q, lane, stage->cow[q]);
+      for (int q = cow_q0; q < CC::PIECES; q += NW)
+        fetch_cow_piece<BS, LPT>(a, cow, h, q, lane, (ctx - 1) % BS, stage->cow[q]);
     }
   }
 
@@ -627,7 +634,7 @@ void decode_grouped_kernel(DecodeArgs a, int32_t ngroups) {
           cow[r] = src;
           if (lane == jn) tbl[r] = src;
           for (int q = w; q < CC::PIECES; q += NW)
-            fetch_cow_piece<BS, LPT>(a, src, h, q, lane, stage->cow[r * CC::PIECES + q]);
+            fetch_cow_piece<BS, LPT>(a, src, h, q, lane, (ctx[r] - 1) % BS, stage->cow[r * CC::PIECES + q]);
         }
       }
     }

@@ -172,9 +172,10 @@ pa_status pa_check_append_slots(const int32_t* block_tables, int32_t S, int32_t 
   }
   if (!cow_src) return PA_OK;
   // Copy-on-write folded in: row s's newest-token block d first receives a
-  // copy of block c = cow_src[s] (every slot but the newest token's, which
-  // its own write fills).  d must belong to s alone, and no write of the
-  // call may land in a slot of c that the copy reads.
+  // copy of block c = cow_src[s] (the slots before the newest token's, which
+  // its own write fills; the slots after it hold no token).  d must belong to
+  // s alone, and no write of the call may land in a slot of c that the copy
+  // reads.
   std::unordered_map<int32_t, int32_t> owner;  // newest-token block -> row, for rows that copy
   for (int32_t s = 0; s < S; ++s) {
     const int32_t c = cow_src[s];
@@ -200,7 +201,7 @@ pa_status pa_check_append_slots(const int32_t* block_tables, int32_t S, int32_t 
   for (const Slot& f : fresh) {  // every write of the call against every copy's source
     for (int32_t s = 0; s < S; ++s) {
       if (cow_src[s] != f.block) continue;
-      if (f.off != (context_lens[s] - 1) % block_size)
+      if (f.off < (context_lens[s] - 1) % block_size)
         return pa::check_fail(PA_ERR_INVALID_ARG,
                               "%s: sequence %d writes block %d offset %d, which sequence %d's copy reads", fn, f.row,
                               f.block, f.off, s);

@@ -311,10 +311,16 @@ class BeamLoop:
         lens = self.mgr.lens[rows_sorted].astype(np.int32)
         tables = np.ascontiguousarray(self.mgr.tables[rows_sorted])
         copy_pairs, cow = pairs, None
+        newest = tables[np.arange(n), (lens - 1) // self.B]
+        # tokens the copies carry: each copy's destination is the newest-token
+        # block of the row that appends into it, which holds (len - 1) % B
+        # of that row's tokens before the newest
+        cow_tokens = 0
+        for _, dst in pairs:
+            hit = np.nonzero(newest == dst)[0]
+            cow_tokens += int(lens[hit[0]] - 1) % self.B if len(hit) else self.B
         if self.fold_copies:
-            # each copy's destination is the newest-token block of the row that
-            # appends into it: that row takes the copy's source instead
-            newest = tables[np.arange(n), (lens - 1) // self.B]
+            # that row takes the copy's source instead
             cow = np.full(n, -1, np.int32)
             left = []
             for src, dst in pairs:
@@ -333,7 +339,8 @@ class BeamLoop:
             for i, s in enumerate(rows_sorted):
                 self.hist[int(s)].k.append(k_new[i:i + 1])
                 self.hist[int(s)].v.append(v_new[i:i + 1])
-        return {"rows": rows_sorted, "lens": lens, "n_pairs": len(pairs), "n_copy_launch": len(copy_pairs),
+        return {"rows": rows_sorted, "lens": lens, "n_pairs": len(pairs), "cow_tokens": cow_tokens,
+                "n_copy_launch": len(copy_pairs),
                 "dev": dev, "q": q, "max_ctx": int(lens.max())}
 
     def launch(self, plan: dict, events=None) -> StepRecord:

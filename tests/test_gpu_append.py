@@ -190,9 +190,15 @@ def test_copy_on_write_folded_in(W, dtype, B, prompt, tails):
                              torch.from_numpy(lens).cuda(), int(lens.max()), scale, W, ws,
                              cow_src=torch.from_numpy(cow).cuda())
     torch.cuda.synchronize()
-    # the oracle: the held copies, then every row's newest token
+    # the oracle: the held copies, then every row's newest token; a copied
+    # block's slots after the row's newest token hold no token, and the call
+    # leaves them as they were (it copies the row's tokens only)
     ek, ev = oc.copy_blocks(k0, v0, pairs)
     ek, ev = oc.reshape_and_cache(ek, ev, bits(key), bits(value), slots)
+    for s in np.nonzero(cow >= 0)[0]:
+        blk, off = newest_blk[s], (lens[s] - 1) % B
+        ek[blk, :, off + 1:] = k0[blk, :, off + 1:]
+        ev[blk, :, off + 1:] = v0[blk, :, off + 1:]
     assert np.array_equal(bits(cache.k), ek), "K pool differs from copy + write"
     assert np.array_equal(bits(cache.v), ev), "V pool differs from copy + write"
     ref = np.stack([oa.decode(inputs.to_f64(q[s]), inputs.to_f64(torch.cat(hist[s][0])),

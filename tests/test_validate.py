@@ -88,6 +88,9 @@ def test_append_slots_with_copies():
     # row 3 writes block 3 at offset 2 while row 0's copy of block 3 reads it
     _refused(L.check_append_slots, np.array([[5], [6], [7], [3]], np.int32), [4, 4, 4, 3], 4, [3, 3, 3, -1], 8,
              match="sequence 3 writes block 3 offset 2, which sequence 0's copy reads")
+    # a write into the source past the copying row's tokens is no conflict
+    # (B = 8: row 0 copies block 3's first 3 slots, row 1 writes its offset 5)
+    L.check_append_slots(np.array([[5], [3]], np.int32), [4, 6], 8, [3, -1], 8)
     # (a copy's destination mapped by another row always shows up first as a
     # newest slot that another row reads, which the check above refuses)
     # a copy's source that receives another copy
