@@ -228,10 +228,8 @@ pa_status pa_paged_decode_grouped(const pa_kv_cache* cache, void* out, pa_dtype 
  *                launch is needed: every head's slots before the newest
  *                token's offset are copied (the row's tokens in that block);
  *                the slots after it hold no token of any row and keep what
- *                they held.  -1: no copy.  Supported when block_size * head_dim
- *                * sizeof(dtype) is 1, 2 or 4 KiB (PA_ERR_UNSUPPORTED
- *                otherwise: copy first and pass NULL).  Ids outside the pool
- *                copy nothing, as in pa_copy_blocks.
+ *                they held.  -1: no copy.  Ids outside the pool copy
+ *                nothing, as in pa_copy_blocks.
  *   group_size   1 (pa_paged_decode's kernels) or 2 / 4 (pa_paged_decode_grouped's).
  *   workspace    >= pa_decode_grouped_workspace_bytes(cache, S,
  *                max_context_len, group_size) bytes.
@@ -243,15 +241,17 @@ pa_status pa_paged_decode_grouped(const pa_kv_cache* cache, void* out, pa_dtype 
  * block that receives a copy is mapped by its row alone, no copy reads from
  * a block that receives one, and no write of the call lands in a slot a copy
  * reads (rows that write into a copy's source write at or past the copying
- * row's offset, as siblings over a shared block do).  Debug mode checks all of it
- * (pa_check_append_slots).  Copy-on-write copies not passed in cow_src
+ * row's offset, as siblings over a shared block do).  Debug mode checks all
+ * of it (pa_check_append_slots).  Copy-on-write copies not passed in cow_src
  * (pa_copy_blocks) go before this call on the same stream.
  * Cache contents equal pa_copy_blocks with the cow_src pairs, then
  * pa_reshape_and_cache with the slot of position context_lens[s] - 1 for
  * row s, bit for bit, in every slot but those after a copied block's newest
- * token (no row holds a token there); the output equals pa_paged_decode (group_size 1) or
- * pa_paged_decode_grouped after them up to rounding (the newest token is
- * added last).
+ * token (no row holds a token there); the output equals pa_paged_decode
+ * (group_size 1) or pa_paged_decode_grouped after them up to rounding (the
+ * newest token is added last).  The writes are made by extra workgroups at
+ * the end of the decode's grid (ceil(S * num_heads / (4 * waves)) of them);
+ * the launch's work-items must fit 32 bits (PA_ERR_INVALID_ARG otherwise).
  */
 pa_status pa_paged_decode_append(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, const void* query,
                                  const void* key, const void* value, const int32_t* cow_src,

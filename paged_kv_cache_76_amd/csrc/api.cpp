@@ -230,7 +230,8 @@ namespace {
 // Checks shared by the decode entry points (everything but the workspace).
 pa_status check_decode(const char* fn, const pa::Cache& c, const void* out, pa_dtype out_dtype, const void* query,
                        const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
-                       int32_t S, int32_t max_context_len, float scale) {
+                       int32_t S, int32_t max_context_len, float scale, int32_t group_size = 1,
+                       bool append = false) {
   if (out_dtype != c.dtype && out_dtype != PA_F32)
     return fail(PA_ERR_INVALID_ARG, "%s: out_dtype must be the cache dtype or PA_F32", fn);
   if (!out || !query || !block_tables || !context_lens)
@@ -248,10 +249,9 @@ pa_status check_decode(const char* fn, const pa::Cache& c, const void* out, pa_d
   if (P == 0)
     return fail(PA_ERR_UNSUPPORTED, "%s: (dtype %d, head_dim %d, block_size %d) not built", fn, (int)c.dtype,
                 c.head_dim, c.block_size);
-  // the smallest partition any decode kernel uses bounds the grid
-  const int64_t parts = ((int64_t)max_context_len + 63) / 64;
-  if ((int64_t)S * c.num_heads * parts >= (int64_t)1 << 31)
-    return fail(PA_ERR_INVALID_ARG, "%s: grid of S*H*partitions does not fit", fn);
+  // a launch's work-items are counted in 32 bits
+  if (S > 0 && pa::decode_work_items(c, S, max_context_len, group_size, append) > (int64_t)UINT32_MAX)
+    return fail(PA_ERR_INVALID_ARG, "%s: the launch of S*H*partitions workgroups does not fit", fn);
   return PA_OK;
 }
 
@@ -349,7 +349,7 @@ pa_status pa_paged_decode_grouped(const pa_kv_cache* cache, void* out, pa_dtype 
     return fail(PA_ERR_INVALID_ARG, "%s: group_size = %d not in {1, 2, 4}", fn, group_size);
   if (S == 0) return PA_OK;
   st = check_decode(fn, c, out, out_dtype, query, block_tables, max_blocks_per_seq, context_lens, S,
-                    max_context_len, scale);
+                    max_context_len, scale, group_size);
   if (st != PA_OK) return st;
   const size_t need = pa::decode_grouped_workspace_bytes(c, S, max_context_len, group_size);
   st = check_workspace(fn, need, workspace, workspace_bytes);
@@ -378,17 +378,12 @@ pa_status pa_paged_decode_append(const pa_kv_cache* cache, void* out, pa_dtype o
     return fail(PA_ERR_INVALID_ARG, "%s: group_size = %d not in {1, 2, 4}", fn, group_size);
   if (S == 0) return PA_OK;
   st = check_decode(fn, c, out, out_dtype, query, block_tables, max_blocks_per_seq, context_lens, S,
-                    max_context_len, scale);
+                    max_context_len, scale, group_size, true);
   if (st != PA_OK) return st;
   if (!key || !value) return fail(PA_ERR_INVALID_ARG, "%s: NULL key/value", fn);
   if (!aligned(key, 16) || !aligned(value, 16))
     return fail(PA_ERR_INVALID_ARG, "%s: key/value must be 16-byte aligned", fn);
   if (cow_src && !aligned(cow_src, 4)) return fail(PA_ERR_INVALID_ARG, "%s: cow_src must be 4-byte aligned", fn);
-  if (cow_src && !pa::append_cow_supported(c))
-    return fail(PA_ERR_UNSUPPORTED,
-                "%s: copy-on-write is folded in only when block_size * head_dim * sizeof(dtype) is 1, 2 or 4 KiB "
-                "(got %d * %d * %d); copy with pa_copy_blocks first and pass cow_src = NULL",
-                fn, c.block_size, c.head_dim, pa::dtype_bytes(c.dtype));
   const size_t need = group_size == 1 ? pa::decode_workspace_needed(c, S, max_context_len)
                                       : pa::decode_grouped_workspace_bytes(c, S, max_context_len, group_size);
   st = check_workspace(fn, need, workspace, workspace_bytes);

@@ -29,6 +29,24 @@ __device__ __forceinline__ void load_to_lds(const void* src, uint32_t lds_base) 
 __device__ __forceinline__ void load_dword_to_lds(const void* src, uint32_t lds_base) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds_base) : "memory");
 }
+// A wave-uniform 32-bit value read through the scalar data cache (a load;
+// the kernel that uses this never writes `p`).  The compiler picks scalar
+// loads by itself only when it can prove that no store of the kernel reaches
+// the address; kernels that also write the pools lose that proof, and their
+// vector loads of such metadata queue behind the wave's streaming loads.
+// Returns after the value has arrived.
+__device__ __forceinline__ int32_t scalar_load(const int32_t* p) {
+  int32_t v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
+}
+// Two such values in one round trip.
+__device__ __forceinline__ void scalar_load2(const int32_t* p, const int32_t* q, int32_t& x, int32_t& y) {
+  asm volatile("s_load_dword %0, %2, 0x0\n\ts_load_dword %1, %3, 0x0\n\ts_waitcnt lgkmcnt(0)"
+               : "=&s"(x), "=&s"(y)
+               : "s"(p), "s"(q)
+               : "memory");
+}
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(lds_void_t*)p;
 }

@@ -52,6 +52,9 @@ int decode_partition_tokens(pa_dtype dtype, int head_dim, int block_size);
 // max_context_len tokens) and bytes one such launch uses
 size_t decode_workspace_bytes(const Cache& c, int32_t S, int32_t max_context_len);
 size_t decode_workspace_needed(const Cache& c, int32_t S, int32_t max_context_len);
+// The most work-items a decode launch of this shape may take (0 when the
+// shape is not built).
+int64_t decode_work_items(const Cache& c, int32_t S, int32_t max_context_len, int32_t group_size, bool append);
 // key_new / value_new ([S][H][D], cache dtype): an appending decode, which
 // first stores each row's newest token (position context_lens[s] - 1) into
 // the cache slot its table maps; NULL for a plain decode.  cow_src ([S] or
@@ -62,9 +65,6 @@ hipError_t launch_paged_decode(const Cache& c, void* out, pa_dtype out_dtype, co
                                float scale, void* workspace, hipStream_t stream,
                                const void* key_new = nullptr, const void* value_new = nullptr,
                                const int32_t* cow_src = nullptr);
-// The appending decode folds copy-on-write copies in when one (block, head)
-// slice of a pool is 64, 128 or 256 chunks of 16 bytes.
-bool append_cow_supported(const Cache& c);
 
 // Device address of the allocation-free decode's scratch array on the
 // current device (looked up once per device, then cached).

@@ -25,6 +25,7 @@
 //   table read sits off the per-block critical path.
 // * Entries of the table at or beyond ceil(ctx/B) are never read; a block id
 //   outside the pool contributes nothing (memory stays in bounds).
+#include <algorithm>
 #include <mutex>
 
 #include <type_traits>
@@ -174,58 +175,117 @@ __device__ __forceinline__ void merge_partitions(const DecodeArgs& a, int64_t sh
 // straight into LDS (per row 2 x 64 chunks, K then V, lane k holding chunk
 // k % LPT; then 64 copies of the partition kernel's block id), so no
 // register is held across the loop, nothing waits for them before it, and
-// their latency hides behind it.  With copy-on-write folded in, the head's
-// slice of each copied block (CH chunks per pool) comes in the same way, as
-// PIECES pieces of 64 chunks (K pieces, then V pieces, per row), of which
-// only those holding the row's tokens before its newest are fetched.
-template <int ROWS, int PIECES>
+// their latency hides behind it.
+template <int ROWS>
 struct NewTokenStage {
   u32x4 kv[ROWS][2][64];
   int32_t phys[64];
-  u32x4 cow[ROWS * PIECES > 0 ? ROWS * PIECES : 1][64];
 };
-template <int ROWS, int PIECES>
-__device__ __forceinline__ NewTokenStage<ROWS, PIECES>* new_token_stage() {
-  __shared__ NewTokenStage<ROWS, PIECES> stage;
+template <int ROWS>
+__device__ __forceinline__ NewTokenStage<ROWS>* new_token_stage() {
+  __shared__ NewTokenStage<ROWS> stage;
   return &stage;
 }
 
-// Copy-on-write slices: a (block, head) slice of one pool is CH = BS * LPT
-// contiguous 16-byte chunks; it is folded into the appending decode when it
-// is one, two or four pieces of 64 chunks (one direct-to-LDS load per piece).
-template <int BS, int LPT>
-struct CowCfg {
-  static constexpr int CH = BS * LPT;
-  static constexpr bool OK = CH == 64 || CH == 128 || CH == 256;
-  static constexpr int PER_POOL = OK ? CH / 64 : 0;  // pieces per pool
-  static constexpr int PIECES = 2 * PER_POOL;       // K pieces, then V pieces
-};
-// Piece q of the slice (block `blk`, head h) into `dst` (64 chunks), unless
-// the piece starts at or past token `keep` (the newest token's slot): the
-// copy carries only the tokens the row holds before its newest one.
-template <int BS, int LPT>
-__device__ __forceinline__ void fetch_cow_piece(const DecodeArgs& a, int blk, int h, int q, int lane, int keep,
-                                                u32x4* dst) {
-  using CC = CowCfg<BS, LPT>;
-  if ((q % CC::PER_POOL) * (64 / LPT) >= keep) return;  // uniform
-  const u32x4* pool = q < CC::PER_POOL ? a.kpool : a.vpool;
-  const int64_t src = ((int64_t)blk * a.H + h) * CC::CH + (q % CC::PER_POOL) * 64 + lane;
-  load_to_lds(pool + src, lds_addr(dst));
+// The cache writes of an appending decode are made by writer workgroups
+// appended to the decode grid: each takes 4 * NW (row, head) items (item =
+// row * H + head) and stores the row's newest token of that head into its
+// slot and, for a row with a copy-on-write source, first copies the row's
+// tokens before the newest (slots [0, off) of the head's slice) from the
+// source into the newest-token block.  Dispatched last, they run while the
+// decode workgroups drain: measured, the same stores issued by the decode
+// workgroups, spread through the read stream, cost several times as much.
+// Nothing the decode workgroups read is written: a row reads its copied
+// block's older tokens from the source (its table entry is patched) and its
+// newest token from the inputs, and no other row maps either slot.
+__host__ __device__ constexpr int writer_items(int nw) { return 4 * nw; }
+inline int64_t writer_groups(int64_t S, int64_t H, int nw) {
+  return (S * H + writer_items(nw) - 1) / writer_items(nw);
 }
-// The fetched piece q into block `blk` (head h): the chunks of tokens
-// before `keep` (the newest token's slot, which its own store fills; the
-// slots after it hold no token of any row).  Non-temporal stores, issued
-// after the kernel's output writes.
-template <int BS, int LPT>
-__device__ __forceinline__ void store_cow_piece(const DecodeArgs& a, int blk, int h, int q, int lane, int keep,
-                                                const u32x4* piece) {
-  using CC = CowCfg<BS, LPT>;
-  if (blk < 0 || blk >= a.N) return;
-  const int e = (q % CC::PER_POOL) * 64 + lane;  // chunk within the slice
-  if (e / LPT >= keep) return;
-  u32x4* pool = const_cast<u32x4*>(q < CC::PER_POOL ? a.kpool : a.vpool);
-  __builtin_nontemporal_store(piece[lane], &pool[((int64_t)blk * a.H + h) * CC::CH + e]);
+// Writer workgroup `wid`; `max_len`: the longest context whose newest token
+// the decode adds (longer ones were clipped: nothing is written for them).
+// (S * H and the item ids fit 32 bits: the launch's work-items do.)
+template <int BS, int LPT, int NW>
+__device__ __forceinline__ void write_step(const DecodeArgs& a, int wid, int64_t max_len) {
+  constexpr int IPW = writer_items(NW), NT = NW * 64;
+  __shared__ int32_t lds_dst[IPW], lds_off[IPW], lds_src[IPW];
+  const int item0 = wid * IPW;
+  if (threadIdx.x < IPW) {
+    const int item = item0 + threadIdx.x;
+    int dst = -1, off = 0, src = -1;
+    if (item < a.S * a.H) {
+      const int row = item / a.H;
+      const int len = a.lens[row];
+      if (len >= 1 && len <= max_len && (len - 1) / BS < a.max_blocks) {
+        const int d = a.tables[(int64_t)row * a.max_blocks + (len - 1) / BS];
+        if (d >= 0 && d < a.N) {
+          dst = d;
+          off = (len - 1) % BS;
+          // a source outside the pool copies nothing, like pa_copy_blocks
+          if (a.cow_src) {
+            const int c = a.cow_src[row];
+            src = c >= 0 && c < a.N ? c : -1;
+          }
+        }
+      }
+    }
+    lds_dst[threadIdx.x] = dst;
+    lds_off[threadIdx.x] = off;
+    lds_src[threadIdx.x] = src;
+  }
+  __syncthreads();
+  // the newest tokens: (item, pool, chunk) spread over the threads, all
+  // loads first, then the stores
+  constexpr int TOK = IPW * 2 * LPT, KT = (TOK + NT - 1) / NT;
+  u32x4 val[KT];
+  int64_t at[KT];
+#pragma unroll
+  for (int k = 0; k < KT; ++k) {
+    const int e = threadIdx.x + k * NT;
+    const int i = e / (2 * LPT), pool = (e / LPT) % 2, c = e % LPT;
+    at[k] = -1;
+    if (e < TOK && lds_dst[i] >= 0) {
+      const int item = item0 + i;
+      const int h = item % a.H;
+      val[k] = (pool ? a.vnew : a.knew)[(int64_t)item * LPT + c];
+      at[k] = ((((int64_t)lds_dst[i] * a.H + h) * BS + lds_off[i]) * LPT + c) * 2 + pool;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < KT; ++k) {
+    if (at[k] >= 0)
+      __builtin_nontemporal_store(val[k], &const_cast<u32x4*>((at[k] & 1) ? a.vpool : a.kpool)[at[k] >> 1]);
+  }
+  // the copies: one item per wave at a time; a slice's tokens before the
+  // newest are one contiguous run of off * LPT chunks per pool
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  for (int i = w; i < IPW; i += NW) {
+    const int src = __builtin_amdgcn_readfirstlane(lds_src[i]);
+    if (src < 0) continue;
+    const int dst = __builtin_amdgcn_readfirstlane(lds_dst[i]);
+    const int per_pool = __builtin_amdgcn_readfirstlane(lds_off[i]) * LPT;
+    const int h = (item0 + i) % a.H;
+    const int64_t s0 = ((int64_t)src * a.H + h) * BS * LPT, d0 = ((int64_t)dst * a.H + h) * BS * LPT;
+    constexpr int KC = 8;  // loads in flight per lane
+    for (int b = 0; b < 2 * per_pool; b += KC * 64) {
+      u32x4 v[KC];
+#pragma unroll
+      for (int k = 0; k < KC; ++k) {
+        const int e = b + k * 64 + lane;
+        if (e < 2 * per_pool) v[k] = (e < per_pool ? a.kpool : a.vpool)[s0 + (e < per_pool ? e : e - per_pool)];
+      }
+#pragma unroll
+      for (int k = 0; k < KC; ++k) {
+        const int e = b + k * 64 + lane;
+        if (e < 2 * per_pool)
+          __builtin_nontemporal_store(v[k], &const_cast<u32x4*>(e < per_pool ? a.kpool : a.vpool)
+                                                [d0 + (e < per_pool ? e : e - per_pool)]);
+      }
+    }
+  }
 }
+
 // The calling wave starts the fetch of element row_h (= row * H + head) of
 // knew/vnew into `stage`.
 template <int LPT>
@@ -263,21 +323,6 @@ __device__ __forceinline__ void add_new_token(const DecodeArgs& a, const u32x4* 
   }
 }
 
-// The newest token from `stage` (its fetch has landed) into offset `off` of
-// block `phys` of the pools, where later calls read it.  Non-temporal
-// stores: plain stores spread through the launch's read stream cost a large
-// launch several times what a separate write launch takes (measured), these
-// about as much as that launch.  The partition kernel issues them before its
-// loop, the grouped kernel at its end.
-template <int LPT, int BS>
-__device__ __forceinline__ void store_new_token(const DecodeArgs& a, const u32x4* stage, int lane, int phys, int off,
-                                                int h) {
-  if (phys < 0 || phys >= a.N || lane >= LPT) return;
-  const int64_t dst = (((int64_t)phys * a.H + h) * BS + off) * LPT + lane;
-  __builtin_nontemporal_store(stage[lane], &const_cast<u32x4*>(a.kpool)[dst]);
-  __builtin_nontemporal_store(stage[64 + lane], &const_cast<u32x4*>(a.vpool)[dst]);
-}
-
 // APPEND: the appending decode (knew/vnew set), built apart from the plain
 // decode, whose loop it shares unchanged.
 template <typename E, int D, int BS, bool WIDE, bool APPEND>
@@ -291,18 +336,36 @@ __global__ __launch_bounds__((DecodeCfg<E, D, BS, WIDE>::NW * 64)) PA_DECODE_OCC
   __shared__ float lds_l[NW];
 
   const int bid = blockIdx.x;
+  if constexpr (APPEND) {
+    // the writer workgroups follow the S * H * max_parts decode workgroups
+    const int64_t ndec = (int64_t)a.S * a.H * a.max_parts;
+    if (__builtin_expect(bid >= ndec, 0)) {
+      write_step<BS, LPT, NW>(a, (int)(bid - ndec), (int64_t)a.max_parts * P);
+      return;
+    }
+  }
   const int h = bid % a.H;
   const int rest = bid / a.H;
   const int s = rest % a.S;
   const int p = rest / a.S;
   // a length beyond the grid's partitions is clipped (memory stays in bounds)
-  const int ctx = min(a.lens[s], a.max_parts * P);
+  // (an appending decode also reads the row's copy-on-write source, in the
+  // same round trip: the lengths again when there is none)
+  int len, cow_in = -1;
+  if constexpr (APPEND) {
+    scalar_load2(a.lens + s, a.cow_src ? a.cow_src + s : a.lens + s, len, cow_in);
+    if (!a.cow_src) cow_in = -1;
+  } else {
+    len = a.lens[s];
+  }
+  const int ctx = min(len, a.max_parts * P);
   const int nparts = (ctx + P - 1) / P;
   if (p >= nparts) return;  // uniform for the whole workgroup (also ctx < 1)
   // An appending decode reads ctx - 1 tokens from the pools and takes the
   // newest one from its inputs after the loop (not when the length was
-  // clipped: then no token is known to be the newest and nothing is written).
-  const bool add_new = APPEND && a.lens[s] <= a.max_parts * P;
+  // clipped: then no token is known to be the newest and nothing is written;
+  // the writer workgroups make the same choice).
+  const bool add_new = APPEND && len <= a.max_parts * P;
   const int kv_ctx = add_new ? ctx - 1 : ctx;
 
   const int lane = threadIdx.x & 63;
@@ -311,31 +374,22 @@ __global__ __launch_bounds__((DecodeCfg<E, D, BS, WIDE>::NW * 64)) PA_DECODE_OCC
   const int c = lane % LPT;  // 16-byte column within the row
 
   // wave 0 of the partition holding the newest token adds it
-  using CC = CowCfg<BS, LPT>;
   const bool new_part = add_new && (ctx - 1) / P == p;  // this partition holds the newest token
   const bool new_here = new_part && w == 0;
   const int new_blk = (ctx - 1) / BS;  // logical block of the newest token
-  NewTokenStage<1, CC::PIECES>* stage = nullptr;
-  // copy-on-write: the newest token's block first receives a copy of `cow`;
-  // until then the row reads that block's older tokens from `cow` itself
-  int cow = -1;
+  NewTokenStage<1>* stage = nullptr;
+  // copy-on-write: the newest token's block receives a copy of `cow` (made
+  // by a writer workgroup); the row reads that block's older tokens from
+  // `cow` itself (an id outside the pool copies nothing, like pa_copy_blocks)
+  const int cow = new_part && cow_in >= 0 && cow_in < a.N ? cow_in : -1;
   if constexpr (APPEND) {
-    stage = new_token_stage<1, CC::PIECES>();
+    stage = new_token_stage<1>();
     if (new_here) {
       fetch_new_token<LPT>(a, (int64_t)s * a.H + h, lane, &stage->kv[0][0][0]);
       if (new_blk < a.max_blocks)
         load_dword_to_lds(&a.tables[(int64_t)s * a.max_blocks + new_blk], lds_addr(stage->phys));
     }
-    if constexpr (CC::OK) {
-      if (a.cow_src && new_part) {
-        const int src = a.cow_src[s];
-        cow = src >= 0 && src < a.N ? src : -1;  // an id outside the pool copies nothing, like pa_copy_blocks
-      }
-    }
   }
-  // the pieces of the copy go to waves 1, 2, ... (wave 0 already waits for
-  // the new token before its loop)
-  const int cow_q0 = (w + NW - 1) % NW;
 
   const int nblk = (kv_ctx + BS - 1) / BS;  // logical blocks read from the pools
   const int jb = p * (P / BS);           // first logical block of the partition
@@ -344,35 +398,18 @@ __global__ __launch_bounds__((DecodeCfg<E, D, BS, WIDE>::NW * 64)) PA_DECODE_OCC
   auto window = [&](int wbase) {
     const int j = jb + wbase + lane;
     int e = (j < nblk && j < a.max_blocks) ? a.tables[trow + j] : -1;
-    if (APPEND && j == new_blk && cow >= 0) e = cow;  // (patched after the load, which does not wait for cow)
+    if (APPEND && j == new_blk && cow >= 0) e = cow;
     return e;
   };
   int wbase = 0;
   int tbl = window(0);
 
   const u32x4 qc = a.q[((int64_t)s * a.H + h) * LPT + c];
-  if constexpr (APPEND && CC::OK) {
-    if (cow >= 0) {
-      for (int q = cow_q0; q < CC::PIECES; q += NW)
-        fetch_cow_piece<BS, LPT>(a, cow, h, q, lane, (ctx - 1) % BS, stage->cow[q]);
-    }
-  }
 
   float m = kNegBig, l = 0.f;
   float o[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) o[e] = 0.f;
-
-  int new_phys = -1;
-  if constexpr (APPEND) {
-    if (new_here) {
-      // the fetches into LDS have landed (with the table window and q, which
-      // the loop's first step waits for anyway)
-      wait_vmem();
-      new_phys = new_blk < a.max_blocks ? __builtin_amdgcn_readfirstlane(stage->phys[0]) : -1;
-      store_new_token<LPT, BS>(a, &stage->kv[0][0][0], lane, new_phys, (ctx - 1) % BS, h);
-    }
-  }
 
   const int nsteps = min(STEPS, (kv_ctx - p * P + G - 1) / G);  // kv_ctx >= p * P
   for (int step = w; step < nsteps; step += NW) {
@@ -444,7 +481,11 @@ __global__ __launch_bounds__((DecodeCfg<E, D, BS, WIDE>::NW * 64)) PA_DECODE_OCC
   }
 
   if constexpr (APPEND) {
-    if (new_here) add_new_token<E, D, BS>(a, &stage->kv[0][0][0], lane, new_phys, qc, r, m, l, o);
+    if (new_here) {
+      wait_vmem();  // the fetches into LDS have landed
+      const int new_phys = new_blk < a.max_blocks ? __builtin_amdgcn_readfirstlane(stage->phys[0]) : -1;
+      add_new_token<E, D, BS>(a, &stage->kv[0][0][0], lane, new_phys, qc, r, m, l, o);
+    }
   }
 
   // Merge the TPL row streams of the wave (lanes with equal column c).
@@ -495,16 +536,6 @@ __global__ __launch_bounds__((DecodeCfg<E, D, BS, WIDE>::NW * 64)) PA_DECODE_OCC
     a.ws_ml[(sh * a.max_parts + p) * 2] = M;
     a.ws_ml[(sh * a.max_parts + p) * 2 + 1] = L;
   }
-  if constexpr (APPEND && CC::OK) {
-    // the copy into the newest token's block (its id, fetched by wave 0, is
-    // in LDS since that wave's wait before its loop and the barrier above)
-    if (cow >= 0 && cow_q0 < CC::PIECES) {
-      const int dst = new_blk < a.max_blocks ? __builtin_amdgcn_readfirstlane(stage->phys[0]) : -1;
-      wait_vmem();  // this wave's pieces have landed
-      for (int q = cow_q0; q < CC::PIECES; q += NW)
-        store_cow_piece<BS, LPT>(a, dst, h, q, lane, (ctx - 1) % BS, stage->cow[q]);
-    }
-  }
 #if PA_DECODE_FUSED
   if (nparts > 1) {
     // publish this partition, count arrivals; the last one merges them all
@@ -554,6 +585,14 @@ void decode_grouped_kernel(DecodeArgs a, int32_t ngroups) {
   __shared__ float lds_l[NW][W];
 
   const int bid = blockIdx.x;
+  if constexpr (APPEND) {
+    // the writer workgroups follow the ngroups * H * max_parts decode workgroups
+    const int64_t ndec = (int64_t)ngroups * a.H * a.max_parts;
+    if (__builtin_expect(bid >= ndec, 0)) {
+      write_step<BS, C::LPT, NW>(a, (int)(bid - ndec), (int64_t)a.max_parts * P);
+      return;
+    }
+  }
   const int h = bid % a.H;
   const int rest = bid / a.H;
   const int grp = rest % ngroups;
@@ -565,10 +604,8 @@ void decode_grouped_kernel(DecodeArgs a, int32_t ngroups) {
   // (the W lengths come in one vector load, lane r holding row r's, instead
   // of one scalar round trip per row)
   const int lens_w = a.lens[min(r0 + min((int)(threadIdx.x & 63), W - 1), a.S - 1)];
-  using CC = CowCfg<BS, C::LPT>;
   // copy-on-write sources of the rows, loaded the same way
-  const int cow_w = (APPEND && CC::OK && a.cow_src) ? a.cow_src[min(r0 + min((int)(threadIdx.x & 63), W - 1), a.S - 1)]
-                                                    : -1;
+  const int cow_w = (APPEND && a.cow_src) ? a.cow_src[min(r0 + min((int)(threadIdx.x & 63), W - 1), a.S - 1)] : -1;
   int ctx[W], kv_ctx[W];
   int maxctx = 0, max_kv = 0;
 #pragma unroll
@@ -589,9 +626,9 @@ void decode_grouped_kernel(DecodeArgs a, int32_t ngroups) {
   const int jb = p * (P / BS);
 
   // row r's newest token: wave r % NW of the partition that holds it
-  NewTokenStage<W, CC::PIECES>* stage = nullptr;
+  NewTokenStage<W>* stage = nullptr;
   if constexpr (APPEND) {
-    stage = new_token_stage<W, CC::PIECES>();
+    stage = new_token_stage<W>();
 #pragma unroll
     for (int r = 0; r < W; ++r) {
       if (kv_ctx[r] < ctx[r] && (ctx[r] - 1) / P == p && w == r % NW)
@@ -616,27 +653,19 @@ void decode_grouped_kernel(DecodeArgs a, int32_t ngroups) {
 
   // Rows whose newest token is in this partition: the block that receives
   // it (new_dst, from the table) and, with copy-on-write folded in, the
-  // block it first receives a copy of (cow).  Until the copy lands the row
-  // reads that block's older tokens from `cow`: its table lane is patched,
-  // the head's slice of `cow` is fetched into LDS (piece q by wave q), and
-  // the copy is stored at the end of the kernel.
-  int new_dst[W], cow[W];
+  // block it receives a copy of (made by a writer workgroup): the row reads
+  // that block's older tokens from the copy's source (its table lane is
+  // patched).
+  int new_dst[W];
 #pragma unroll
   for (int r = 0; r < W; ++r) {
     new_dst[r] = -1;
-    cow[r] = -1;
     if (APPEND && kv_ctx[r] < ctx[r] && (ctx[r] - 1) / P == p) {
       const int jn = (ctx[r] - 1) / BS - jb;  // lane of the newest token's block (< P / BS <= 64)
       new_dst[r] = __builtin_amdgcn_readlane(tbl[r], jn);
-      if constexpr (CC::OK) {
-        const int src = __builtin_amdgcn_readlane(cow_w, r);
-        if (src >= 0 && src < a.N) {  // an id outside the pool copies nothing, like pa_copy_blocks
-          cow[r] = src;
-          if (lane == jn) tbl[r] = src;
-          for (int q = w; q < CC::PIECES; q += NW)
-            fetch_cow_piece<BS, LPT>(a, src, h, q, lane, (ctx[r] - 1) % BS, stage->cow[r * CC::PIECES + q]);
-        }
-      }
+      const int src = __builtin_amdgcn_readlane(cow_w, r);
+      // an id outside the pool copies nothing, like pa_copy_blocks
+      if (src >= 0 && src < a.N && lane == jn) tbl[r] = src;
     }
   }
 
@@ -853,24 +882,6 @@ void decode_grouped_kernel(DecodeArgs a, int32_t ngroups) {
       a.ws_ml[(sh * a.max_parts + p) * 2 + 1] = L;
     }
   }
-  // The rows' newest tokens into the pools, last (here, measured, the
-  // grouped kernel's stores cost less than before its loops, where the
-  // wave would first wait for its query loads)
-  if constexpr (APPEND) {
-#pragma unroll
-    for (int r = 0; r < W; ++r) {
-      const int pos = ctx[r] - 1;
-      if (kv_ctx[r] < ctx[r] && pos / P == p && w == r % NW)
-        store_new_token<LPT, BS>(a, &stage->kv[r][0][0], lane, new_dst[r], pos % BS, h);
-      if constexpr (CC::OK) {
-        if (cow[r] >= 0 && w < CC::PIECES) {
-          wait_vmem();  // this wave's pieces have landed
-          for (int q = w; q < CC::PIECES; q += NW)
-            store_cow_piece<BS, LPT>(a, new_dst[r], h, q, lane, pos % BS, stage->cow[r * CC::PIECES + q]);
-        }
-      }
-    }
-  }
 }
 
 // Merge of the partitions of each (sequence, head) split into several:
@@ -1061,6 +1072,28 @@ size_t decode_workspace_bytes(const Cache& c, int32_t S, int32_t max_context_len
   return partials_bytes(c, S, max_parts_for(v->narrow, max_context_len));
 }
 
+// The most work-items a decode launch of this shape may take (whichever
+// partitioning it picks, the grouped kernel's for group_size > 1, plus an
+// appending decode's writer workgroups): the caller refuses launches whose
+// count does not fit the 32-bit grid size.
+int64_t decode_work_items(const Cache& c, int32_t S, int32_t max_context_len, int32_t group_size, bool append) {
+  const Variant* v = find_variant(c.dtype, c.head_dim, c.block_size);
+  if (!v) return 0;
+  int64_t most = 0;
+  for (const Partitioning* pt : {&v->wide, &v->narrow}) {
+    const int64_t wg = (int64_t)S * c.num_heads * max_parts_for(*pt, max_context_len) +
+                       (append ? writer_groups(S, c.num_heads, pt->NW) : 0);
+    most = std::max(most, wg * pt->NW * 64);
+  }
+  if (group_size > 1 && find_grouped(c.dtype, c.head_dim, c.block_size, group_size)) {
+    const int64_t mp = ((int64_t)max_context_len + kGroupTokens - 1) / kGroupTokens;
+    const int64_t wg = (int64_t)(S + group_size - 1) / group_size * c.num_heads * mp +
+                       (append ? writer_groups(S, c.num_heads, kGroupWaves) : 0);
+    most = std::max(most, wg * kGroupWaves * 64);
+  }
+  return most;
+}
+
 // What one launch uses (its own partitioning), at most the size above.
 size_t decode_workspace_needed(const Cache& c, int32_t S, int32_t max_context_len) {
   const Variant* v = find_variant(c.dtype, c.head_dim, c.block_size);
@@ -1113,18 +1146,14 @@ hipError_t launch_paged_decode(const Cache& c, void* out, pa_dtype out_dtype, co
   const int64_t mp = max_parts_for(pt, max_context_len);
   DecodeArgs a = make_args(c, out, out_dtype, query, block_tables, max_blocks_per_seq, context_lens, S, mp, scale,
                            workspace, key_new, value_new, cow_src);
-  const int64_t grid = (int64_t)S * c.num_heads * mp;
+  // an appending decode's writer workgroups come after the decode's
+  const int64_t grid = (int64_t)S * c.num_heads * mp + (key_new ? writer_groups(S, c.num_heads, pt.NW) : 0);
   hipLaunchKernelGGL(key_new ? pt.append_kernel : pt.kernel, dim3((unsigned)grid), dim3(pt.NW * 64), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || mp <= 1 || PA_DECODE_FUSED) return err;
   hipLaunchKernelGGL(decode_reduce_kernel, dim3((unsigned)(S * c.num_heads)), dim3(64), 0, stream, a,
                      (int32_t)c.head_dim, (int32_t)pt.P);
   return hipGetLastError();
-}
-
-bool append_cow_supported(const Cache& c) {
-  const int64_t chunks = (int64_t)c.block_size * c.head_dim * dtype_bytes(c.dtype) / 16;  // one (block, head) slice
-  return chunks == 64 || chunks == 128 || chunks == 256;
 }
 
 bool decode_grouped_built(pa_dtype dtype, int head_dim, int block_size, int group_size) {
@@ -1152,7 +1181,8 @@ hipError_t launch_paged_decode_grouped(const Cache& c, void* out, pa_dtype out_d
   const int32_t ngroups = (S + group_size - 1) / group_size;
   DecodeArgs a = make_args(c, out, out_dtype, query, block_tables, max_blocks_per_seq, context_lens, S, mp, scale,
                            workspace, key_new, value_new, cow_src);
-  const int64_t grid = (int64_t)ngroups * c.num_heads * mp;
+  const int64_t grid =
+      (int64_t)ngroups * c.num_heads * mp + (key_new ? writer_groups(S, c.num_heads, kGroupWaves) : 0);
   hipLaunchKernelGGL(key_new ? v->append_kernel : v->kernel, dim3((unsigned)grid), dim3(kGroupWaves * 64), 0,
                      stream, a, ngroups);
   hipError_t err = hipGetLastError();

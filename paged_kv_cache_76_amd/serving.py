@@ -226,11 +226,8 @@ class BeamLoop:
                  fused: bool = False):
         self.G, self.W, self.beam = groups, width, beam
         self.fused = fused
-        # fused steps also fold their copy-on-write copies into the decode
-        # launch when the library does that for this shape: a (block, head)
-        # slice of one pool of 1, 2 or 4 KiB
-        elem = 4 if dtype == "f32" else 2
-        self.fold_copies = fused and block_size * head_dim * elem in (1024, 2048, 4096)
+        # fused steps also fold their copy-on-write copies into the decode launch
+        self.fold_copies = fused
         self.copy_launches = 0  # pa_copy_blocks launches made by the steps
         self.H, self.d, self.B = num_heads, head_dim, block_size
         self.dtype, self.device = dtype, device

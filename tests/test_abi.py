@@ -123,9 +123,9 @@ def test_append_decode_argument_checks():
     _err(call(key=None), "NULL key/value")
     _err(call(value=FAKE + 8), "key/value must be 16-byte aligned")
     _err(call(cow=FAKE + 2), "cow_src must be 4-byte aligned")
-    # copy-on-write folds in for 1, 2 or 4 KiB (block, head) slices only
-    assert call(cow=FAKE, desc=_desc(block_size=32)) == L.PA_ERR_UNSUPPORTED   # 8 KiB
-    _err(L.PA_ERR_UNSUPPORTED, "pa_copy_blocks first")
+    # a launch whose work-items (decode and writer workgroups) overflow the
+    # 32-bit grid size is refused before anything runs
+    _err(call(S=1 << 22), "does not fit")
     _err(call(group=3), "group_size = 3")
     _err(call(maxb=2), "cannot hold")
     assert call(S=0) == L.PA_OK

@@ -161,6 +161,9 @@ def test_grouped_over_shared_blocks(share, W, dtype, B, prompt, tails):
     (2, "bf16", 16, 1030, [1, 1, 1, 1]),     # the copied block in the second partition
     (1, "f16", 16, 300, [1, 1, 1, 1]),       # the ungrouped kernel (group_size 1) folds the copies too
     (4, "f16", 8, 300, [1, 1, 1, 1]),        # a 2 KiB slice (B = 8: the ungrouped kernel)
+    (4, "bf16", 32, 300, [1, 1, 1, 1]),      # an 8 KiB slice
+    (1, "f32", 16, 200, [1, 1, 1, 1]),       # f32, 8 KiB
+    (2, "f16", 128, 700, [1, 1, 1, 1]),      # B = 128: 32 KiB slices, copies of 60 tokens per pool
 ])
 def test_copy_on_write_folded_in(W, dtype, B, prompt, tails):
     # the builder's last step runs neither its copies nor its writes: the
