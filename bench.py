@@ -42,6 +42,29 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+SETTLE_MS = 60.0
+
+
+def settle(launch, ms: float = SETTLE_MS) -> int:
+    """Repeat ``launch`` (one read-only kernel launch) until ``ms`` of
+    sustained GPU work have passed, right before a timed loop.  Measured on
+    the MI355X: after an idle phase (building a workload on the host) the
+    clocks take some 10-30 ms of load to reach their steady state (a 5 ms
+    pass of shared-block decode steps ran at 82-84 us per step cold and at
+    74 us after 30 ms of load), so a short timed loop would otherwise measure
+    the ramp.  Returns the number of launches made."""
+    import torch
+
+    t0 = time.perf_counter()
+    n = 0
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(8):
+            launch()
+        torch.cuda.synchronize()
+        n += 8
+    return n
+
+
 def cpu_model() -> str:
     try:
         out = subprocess.run(["lscpu"], capture_output=True, text=True).stdout
@@ -274,6 +297,8 @@ def prefill_measure(steps: int, warmup: int, cpu_sample: bool, gemm: bool = True
     wbytes = 2 * 2 * S5 * L5 * H5 * D * 2
     n = steps + warmup
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+    L.pa_reshape_and_cache(b.cache, k_all, v_all, slots)
+    settle(lambda: L.pa_paged_prefill(b.cache, out, b.q_dev, b.tables_dev, b.cu_q_dev, b.lens_dev, L5, L5, b.scale))
     for i in range(n):
         if i == warmup:
             torch.cuda.synchronize()
@@ -407,7 +432,9 @@ def serving_measure(bs: int, steps: int = 32, wall_pass: bool = True,
     else:
         L.pa_paged_decode(loop.cache, outs[: len(rows0)], toks[0][2], dev0["tables"], dev0["lens"],
                           int(lens0.max()), loop.scale, loop.ws)
-    torch.cuda.synchronize()
+    # (then step 0's plain decode, read-only, until the clocks have settled)
+    settle(lambda: L.pa_paged_decode(loop.cache, outs[: len(rows0)], toks[0][2], dev0["tables"], dev0["lens"],
+                                     int(lens0.max()), loop.scale, loop.ws))
     t0 = time.perf_counter()
     for i, (rows, dev, lens) in enumerate(prepared):
         k, v, q = toks[i]
@@ -512,7 +539,16 @@ def shared_measure(beam: bool, grouped: bool, steps: int = 64,
         plans.append(p)
     span = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     loop.warm(plans[0])                             # first-launch code loading, untimed
-    torch.cuda.synchronize()
+    # the first step's plain decode, read-only, until the clocks have settled
+    out0 = torch.empty((len(plans[0]["rows"]), H, D), dtype=torch.bfloat16, device="cuda")
+    d0 = plans[0]["dev"]
+    from paged_kv_cache_76_amd import _lib as L
+    if grouped:
+        settle(lambda: L.pa_paged_decode_grouped(loop.cache, out0, d0["q"], d0["tables"], d0["lens"],
+                                                 plans[0]["max_ctx"], loop.scale, 4, loop.ws))
+    else:
+        settle(lambda: L.pa_paged_decode(loop.cache, out0, d0["q"], d0["tables"], d0["lens"], plans[0]["max_ctx"],
+                                         loop.scale, loop.ws))
     # the timed span has no per-step instrumentation (an event pair per
     # step costs several us); per-launch decode durations come from a
     # replay of every step's decode with events around it afterwards
@@ -588,6 +624,7 @@ def longdecode_measure(steps: int, warmup: int, cpu_sample: bool) -> tuple[float
     out = torch.empty((S5, H5, D), dtype=torch.bfloat16, device="cuda")
     n = steps + warmup
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    settle(lambda: L.pa_paged_decode(ld.cache, out, ld.q_dev, ld.tables_dev, ld.lens_dev, C5, ld.scale, ws))
     for i in range(n):
         if i == warmup:
             torch.cuda.synchronize()
@@ -680,7 +717,7 @@ def append_bench(args) -> int:
             L.pa_paged_decode_append(cache, out, q, key, val, tables, lens, Ln, scale, 1, ws)
 
         pair(), fused()
-        torch.cuda.synchronize()
+        settle(lambda: L.pa_paged_decode(cache, out, q, tables, lens, Ln, scale, ws))
         res = {"pair": [], "fused": []}
         for name, fn in (("pair", pair), ("fused", fused)) * 15:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -710,7 +747,9 @@ def append_bench(args) -> int:
                             fused=fused)
             plans = [loop.plan() for _ in range(40)]
             loop.warm(plans[0])
-            torch.cuda.synchronize()
+            d0, out0 = plans[0]["dev"], torch.empty((4 * groups, H, D), dtype=torch.bfloat16, device="cuda")
+            settle(lambda: L.pa_paged_decode_grouped(loop.cache, out0, d0["q"], d0["tables"], d0["lens"],
+                                                     plans[0]["max_ctx"], loop.scale, 4, loop.ws))
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             for p in plans:
@@ -1112,8 +1151,9 @@ def main() -> int:
 
     for i in range(W):
         step(i)
-    torch.cuda.synchronize()
-    log(f"warmup done ({W} steps); timing {K} steps")
+    # then the last warm-up step's decode, read-only, until the clocks settle
+    n_settle = settle(lambda: decode(max(W - 1, 0)))
+    log(f"warmup done ({W} steps, then {n_settle} read-only decodes over {SETTLE_MS:.0f} ms); timing {K} steps")
     t0 = time.perf_counter()
     for i in range(W, W + K):
         step(i)
@@ -1135,6 +1175,7 @@ def main() -> int:
     # matching rocprofv3 counter averages against algorithmic bytes
     all_dispatch_bytes = [workloads.decode_bytes(steps[i]["lens_host"], H, D, ELEM, B)
                           for i in list(range(W + K)) + list(range(W, W + K))]
+    all_dispatch_bytes += [workloads.decode_bytes(steps[max(W - 1, 0)]["lens_host"], H, D, ELEM, B)] * n_settle
     log(f"algorithmic bytes per decode dispatch, averaged over all {len(all_dispatch_bytes)} of this run: "
         f"{sum(all_dispatch_bytes) / len(all_dispatch_bytes):.0f}")
     value = step_bytes / elapsed / 1e9
@@ -1157,12 +1198,14 @@ def main() -> int:
         prefill = prefill_measure(args.prefill_steps, 2, args.cpu_seqs > 0, gemm=False)
     others = {}
     if args.other_configs:
-        # the other workloads of the same hot path, one short pass each
-        v, ms, config, extra = serving_measure(16, wall_pass=False)
+        # the other workloads of the same hot path, one short pass each (the
+        # serving and shared-block steps in one appending launch each, the
+        # faster form; --workload serving / shared time both forms)
+        v, ms, config, extra = serving_measure(16, wall_pass=False, fused=True)
         others["serving"] = dict(metric=SERVING_METRIC, value=round(v, 1), unit="seq-steps/s", steps=32,
                                  ms_per_step=round(ms, 4), dtype="f16", config=config, **extra)
         for beam in (False, True):
-            v, ms, config, extra = shared_measure(beam, True)
+            v, ms, config, extra = shared_measure(beam, True, fused=True)
             others["shared_beam" if beam else "shared_sampling"] = dict(
                 metric=f"{SHARED_METRIC}, {config['workload'].split(': ', 1)[1]}", value=round(v, 2), unit="GB/s",
                 steps=64, ms_per_step=round(ms, 4), dtype="bf16", config=config, **extra)
