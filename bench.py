@@ -62,6 +62,7 @@ def settle(launch, ms: float = SETTLE_MS) -> int:
             launch()
         torch.cuda.synchronize()
         n += 8
+    log(f"clocks settled: {n} read-only launches over {ms:.0f} ms")
     return n
 
 

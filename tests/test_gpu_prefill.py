@@ -38,7 +38,7 @@ def _oracle(b, s, rows=None, heads=None):
 @pytest.mark.parametrize("dtype,B", [("bf16", 16), ("f16", 16), ("bf16", 32), ("f16", 64), ("bf16", 128)])
 def test_prompt_lengths(dtype, B):
     print(f"prefill {dtype} B={B}", flush=True)
-    lens = [1, 63, 64, 65, 127, 128, 129, 300]
+    lens = [1, 63, 64, 65, 127, 128, 129, 255, 256, 257, 300, 511, 513]
     b = workloads.build_prefill_batch(5, lens, lens, num_heads=2, head_dim=128, block_size=B, dtype=dtype)
     out = _run(b)
     for s in range(len(lens)):
