@@ -250,7 +250,7 @@ pa_status pa_paged_decode_grouped(const pa_kv_cache* cache, void* out, pa_dtype 
  * token (no row holds a token there); the output equals pa_paged_decode
  * (group_size 1) or pa_paged_decode_grouped after them up to rounding (the
  * newest token is added last).  The writes are made by extra workgroups at
- * the end of the decode's grid (ceil(S * num_heads / (4 * waves)) of them);
+ * the end of the decode's grid (ceil(S * num_heads / waves) of them);
  * the launch's work-items must fit 32 bits (PA_ERR_INVALID_ARG otherwise).
  */
 pa_status pa_paged_decode_append(const pa_kv_cache* cache, void* out, pa_dtype out_dtype, const void* query,
