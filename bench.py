@@ -948,22 +948,36 @@ def swap_bench(args) -> int:
     host_k = torch.empty((nblk, H, B, D), dtype=torch.float16, pin_memory=True)
     host_v = torch.empty((nblk, H, B, D), dtype=torch.float16, pin_memory=True)
     t_host = time.perf_counter()
-    out_pairs = torch.from_numpy(m.swap_out(range(S16))).cuda()
-    in_pairs = torch.from_numpy(m.swap_in(range(S16))).cuda()
+    out_np = m.swap_out(range(S16))
+    in_np = m.swap_in(range(S16))
     bm_ms = (time.perf_counter() - t_host) * 1e3 / 2
+    out_pairs, in_pairs = torch.from_numpy(out_np).cuda(), torch.from_numpy(in_np).cuda()
     moved = 2 * nblk * H * B * D * 2                 # keys and values, one direction
+    staging = L.swap_staging(cache, 256)             # 80 MiB: the 1024-block group moves in 4 chunks
+
+    def swap(form, pairs_dev, pairs_np, direction, stream=None):
+        # the kernel form takes device pairs, the copy-engine form host pairs
+        if form == "kernel":
+            L.pa_swap_blocks(cache, host_k, host_v, pairs_dev, direction, stream=stream)
+        else:
+            L.pa_swap_blocks_dma(cache, host_k, host_v, pairs_np, direction, staging, stream=stream,
+                                 pairs_dev=pairs_dev)
+
     res = {}
-    for name, pairs, direction in (("out", out_pairs, L.PA_SWAP_OUT), ("in", in_pairs, L.PA_SWAP_IN)):
-        for _ in range(args.warmup):
-            L.pa_swap_blocks(cache, host_k, host_v, pairs, direction)
-        torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-        for e0, e1 in ev:
-            e0.record()
-            L.pa_swap_blocks(cache, host_k, host_v, pairs, direction)
-            e1.record()
-        torch.cuda.synchronize()
-        res[name] = sorted(e0.elapsed_time(e1) for e0, e1 in ev)[args.steps // 2]
+    for form in ("kernel", "dma"):
+        for name, pairs, pairs_np, direction in (("out", out_pairs, out_np, L.PA_SWAP_OUT),
+                                                 ("in", in_pairs, in_np, L.PA_SWAP_IN)):
+            for _ in range(args.warmup):
+                swap(form, pairs, pairs_np, direction)
+            torch.cuda.synchronize()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(args.steps)]
+            for e0, e1 in ev:
+                e0.record()
+                swap(form, pairs, pairs_np, direction)
+                e1.record()
+            torch.cuda.synchronize()
+            res[(form, name)] = sorted(e0.elapsed_time(e1) for e0, e1 in ev)[args.steps // 2]
     # reference: one plain host<->device copy of the same number of bytes
     flat_dev = cache.k.view(-1)[: nblk * H * B * D]
     flat_host = host_k.view(-1)
@@ -991,13 +1005,13 @@ def swap_bench(args) -> int:
 
     side = torch.cuda.Stream()
 
-    def run(with_swap: bool, with_decode: bool):
+    def run(with_swap: bool, with_decode: bool, form: str = "kernel"):
         es = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
         ed = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
         torch.cuda.synchronize()
         if with_swap:
             es[0].record(side)
-            L.pa_swap_blocks(cache, host_k, host_v, out_pairs, L.PA_SWAP_OUT, stream=side)
+            swap(form, out_pairs, out_np, L.PA_SWAP_OUT, stream=side)
             es[1].record(side)
         if with_decode:
             ed[0].record()
@@ -1008,30 +1022,36 @@ def swap_bench(args) -> int:
         return (ed[0].elapsed_time(ed[1]) * 1e3 / n_dec if with_decode else None,
                 es[0].elapsed_time(es[1]) * 1e-3 if with_swap else None)
 
-    for _ in range(2):
-        run(True, True)
-    alone = [run(False, True)[0] for _ in range(5)]
-    swap_alone = [run(True, False)[1] for _ in range(5)]
-    both = [run(True, True) for _ in range(5)]
+    settle(decode)
     med = lambda v: sorted(v)[len(v) // 2]
     dec_bytes = workloads.decode_bytes(lens0, H, D, 2, B)
-    overlap = {"decode_alone_us": round(med(alone), 1),
-               "decode_during_swap_us": round(med([b[0] for b in both]), 1),
-               "decode_alone_GBps": round(dec_bytes / (med(alone) * 1e-6) / 1e9, 1),
-               "decode_during_swap_GBps": round(dec_bytes / (med([b[0] for b in both]) * 1e-6) / 1e9, 1),
-               "swap_out_alone_GBps": round(moved / med(swap_alone) / 1e9, 1),
-               "swap_out_during_decode_GBps": round(moved / med([b[1] for b in both]) / 1e9, 1),
-               "decodes_per_swap": n_dec}
-    log(f"overlap: decode {overlap['decode_alone_us']} us alone, {overlap['decode_during_swap_us']} us during the "
-        f"swap; swap-out {overlap['swap_out_alone_GBps']} GB/s alone, {overlap['swap_out_during_decode_GBps']} "
-        "GB/s during the decodes")
-    _line("preemption swap GB/s (device -> pinned host), 16 x 1024 OPT-13B tokens", moved / (res["out"] * 1e-3) / 1e9,
-          "GB/s", args.steps, args.warmup, res["out"], "f16",
-          {"workload": "swap out / swap in of a 16-sequence group", "blocks": nblk, "heads": H, "block_size": B,
-           "head_dim": D, "bytes_each_way": moved},
-          swap_in_GBps=round(moved / (res["in"] * 1e-3) / 1e9, 1), swap_out_us=round(res["out"] * 1e3, 1),
-          swap_in_us=round(res["in"] * 1e3, 1), contiguous_memcpy_d2h_GBps=round(memcpy_gbs, 1),
-          host_block_manager_ms=round(bm_ms, 3), overlap_with_decode=overlap)
+    overlaps = {}
+    for form in ("kernel", "dma"):
+        for _ in range(2):
+            run(True, True, form)
+        alone = [run(False, True)[0] for _ in range(5)]
+        swap_alone = [run(True, False, form)[1] for _ in range(5)]
+        both = [run(True, True, form) for _ in range(5)]
+        overlap = {"decode_alone_us": round(med(alone), 1),
+                   "decode_during_swap_us": round(med([b[0] for b in both]), 1),
+                   "decode_alone_GBps": round(dec_bytes / (med(alone) * 1e-6) / 1e9, 1),
+                   "decode_during_swap_GBps": round(dec_bytes / (med([b[0] for b in both]) * 1e-6) / 1e9, 1),
+                   "swap_out_alone_GBps": round(moved / med(swap_alone) / 1e9, 1),
+                   "swap_out_during_decode_GBps": round(moved / med([b[1] for b in both]) / 1e9, 1),
+                   "decodes_per_swap": n_dec}
+        log(f"overlap ({form}): decode {overlap['decode_alone_us']} us alone, {overlap['decode_during_swap_us']} us "
+            f"during the swap; swap-out {overlap['swap_out_alone_GBps']} GB/s alone, "
+            f"{overlap['swap_out_during_decode_GBps']} GB/s during the decodes")
+        overlaps[form] = overlap
+    for form, entry in (("kernel", "pa_swap_blocks (a kernel)"), ("dma", "pa_swap_blocks_dma (copy engines)")):
+        _line(f"preemption swap GB/s (device -> pinned host), 16 x 1024 OPT-13B tokens, {entry}",
+              moved / (res[(form, "out")] * 1e-3) / 1e9, "GB/s", args.steps, args.warmup, res[(form, "out")], "f16",
+              {"workload": "swap out / swap in of a 16-sequence group", "blocks": nblk, "heads": H,
+               "block_size": B, "head_dim": D, "bytes_each_way": moved, "entry": entry},
+              swap_in_GBps=round(moved / (res[(form, "in")] * 1e-3) / 1e9, 1),
+              swap_out_us=round(res[(form, "out")] * 1e3, 1), swap_in_us=round(res[(form, "in")] * 1e3, 1),
+              contiguous_memcpy_d2h_GBps=round(memcpy_gbs, 1), host_block_manager_ms=round(bm_ms, 3),
+              overlap_with_decode=overlaps[form])
     return 0
 
 

@@ -132,6 +132,37 @@ pa_status pa_swap_blocks(const pa_kv_cache* cache, void* host_k, void* host_v, i
                          const int64_t* pairs, int32_t n, pa_swap_dir dir, void* stream);
 
 /*
+ * pa_swap_blocks_dma — the moves of pa_swap_blocks with the host link driven
+ * by the copy engines instead of a kernel.  Swap-out: a short kernel gathers
+ * the device blocks into consecutive staging slots (device to device), then
+ * one DMA copy per pool moves every run of pairs whose host ids are
+ * consecutive; swap-in: the DMA copies first, then a kernel scatters the
+ * staging slots into their device blocks.  No compute unit then waits on the
+ * host link, which matters when the swap runs beside decode launches
+ * (measured at the OPT-13B shape: the kernel form slows a concurrent decode
+ * by ~50 %).  [P2] 调度和抢占, [P3] section 05, [P1] key design 4, as
+ * pa_swap_blocks.
+ *
+ *   host_k, host_v   as pa_swap_blocks (pinned host memory, checked).
+ *   pairs            int64 [n][2] on the device, (src, dst) as for
+ *                    pa_swap_blocks; destinations distinct.  A pair with an
+ *                    id outside its pool moves nothing.
+ *   pairs_host       the same pairs in host memory (the copies are planned on
+ *                    the host); reusable once the call returns.  Debug mode
+ *                    checks that the two agree.
+ *   staging          device memory, 16-byte aligned, caller-owned: slots of
+ *                    one key and one value block (pa_swap_staging_bytes);
+ *                    a swap larger than the staging runs in chunks of its
+ *                    size, in order on `stream`.  Too small for one block:
+ *                    PA_ERR_WORKSPACE.
+ * Effect: as pa_swap_blocks, bit-exact; everything is queued on `stream`.
+ */
+size_t pa_swap_staging_bytes(const pa_kv_cache* cache, int32_t blocks);
+pa_status pa_swap_blocks_dma(const pa_kv_cache* cache, void* host_k, void* host_v, int32_t host_num_blocks,
+                             const int64_t* pairs, const int64_t* pairs_host, int32_t n, pa_swap_dir dir,
+                             void* staging, size_t staging_bytes, void* stream);
+
+/*
  * Workspace of pa_paged_decode, in bytes: enough for every call with at most
  * S sequences whose contexts are at most max_context_len tokens (the size
  * never decreases as S or max_context_len grow).  0 means "no workspace

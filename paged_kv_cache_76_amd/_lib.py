@@ -24,7 +24,8 @@ TORCH_TO_PA = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_
 
 # every symbol include/pagedattn.h declares
 EXPORTS = (
-    "pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_decode_workspace_bytes", "pa_paged_decode",
+    "pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_swap_blocks_dma", "pa_swap_staging_bytes",
+    "pa_decode_workspace_bytes", "pa_paged_decode",
     "pa_paged_decode_noalloc", "pa_decode_grouped_workspace_bytes", "pa_paged_decode_grouped",
     "pa_paged_decode_append", "pa_paged_prefill", "pa_read_stream", "pa_read_tiles", "pa_check_copy_pairs",
     "pa_check_slot_mapping", "pa_check_block_tables", "pa_check_append_slots", "pa_check_prefill_rows", "pa_set_debug", "pa_get_debug", "pa_status_string", "pa_last_error", "pa_abi_version",
@@ -60,6 +61,9 @@ def load_library(path: str) -> ctypes.CDLL:
     L.pa_reshape_and_cache.argtypes = [C, P, P, I64P, I32, P]
     L.pa_copy_blocks.argtypes = [C, I64P, I32, P]
     L.pa_swap_blocks.argtypes = [C, P, P, I32, I64P, I32, ctypes.c_int, P]
+    L.pa_swap_blocks_dma.argtypes = [C, P, P, I32, I64P, I64P, I32, ctypes.c_int, P, ctypes.c_size_t, P]
+    L.pa_swap_staging_bytes.argtypes = [C, I32]
+    L.pa_swap_staging_bytes.restype = ctypes.c_size_t
     L.pa_decode_workspace_bytes.argtypes = [C, I32, I32]
     L.pa_decode_workspace_bytes.restype = ctypes.c_size_t
     L.pa_paged_decode.argtypes = [C, P, ctypes.c_int, P, I32P, I32, I32P, I32, I32, ctypes.c_float, P,
@@ -84,8 +88,8 @@ def load_library(path: str) -> ctypes.CDLL:
     L.pa_set_debug.restype = None
     L.pa_get_debug.argtypes = []
     L.pa_get_debug.restype = I32
-    for fn in ("pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_paged_decode", "pa_paged_decode_noalloc",
-               "pa_paged_decode_grouped", "pa_paged_decode_append",
+    for fn in ("pa_reshape_and_cache", "pa_copy_blocks", "pa_swap_blocks", "pa_swap_blocks_dma", "pa_paged_decode",
+               "pa_paged_decode_noalloc", "pa_paged_decode_grouped", "pa_paged_decode_append",
                "pa_paged_prefill", "pa_read_stream", "pa_read_tiles", "pa_check_copy_pairs", "pa_check_slot_mapping",
                "pa_check_block_tables", "pa_check_append_slots", "pa_check_prefill_rows"):
         getattr(L, fn).restype = ctypes.c_int
@@ -238,6 +242,49 @@ def pa_swap_blocks(cache: KVCache, host_k: torch.Tensor, host_v: torch.Tensor, p
     d = cache.desc()
     _check(lib().pa_swap_blocks(ctypes.byref(d), _ptr(host_k), _ptr(host_v), host_k.shape[0],
                                 _ptr(pairs) if n else None, n, int(direction), _stream(stream)))
+
+
+def swap_staging(cache: KVCache, blocks: int) -> torch.Tensor:
+    """A device staging buffer for pa_swap_blocks_dma with room for
+    ``blocks`` blocks of keys and values."""
+    n = lib().pa_swap_staging_bytes(ctypes.byref(cache.desc()), blocks)
+    if n == 0:
+        raise ValueError(f"no staging size for {blocks} blocks")
+    return torch.empty(n, dtype=torch.uint8, device=cache.k.device)
+
+
+def pa_swap_blocks_dma(cache: KVCache, host_k: torch.Tensor, host_v: torch.Tensor, pairs, direction: int,
+                       staging: torch.Tensor, stream=None, pairs_dev: torch.Tensor | None = None) -> None:
+    """pa_swap_blocks with the host link driven by the copy engines:
+    ``pairs int64 [n][2]`` in host memory (a numpy array or a CPU tensor),
+    (device, host) for PA_SWAP_OUT and (host, device) for PA_SWAP_IN; their
+    device copy ``pairs_dev`` is made here (synchronously) when not given.
+    ``staging``: a device buffer from swap_staging()."""
+    import numpy as np
+    p = np.ascontiguousarray(pairs.numpy() if isinstance(pairs, torch.Tensor) else pairs, dtype=np.int64)
+    if p.size and (p.ndim != 2 or p.shape[1] != 2):
+        raise ValueError("pairs must be [n][2]")
+    for name, t in (("host_k", host_k), ("host_v", host_v)):
+        _contig(name, t, cache.dtype)
+        if t.dim() != 4 or t.shape[1:] != cache.k.shape[1:] or t.device.type != "cpu":
+            raise ValueError(f"{name} must be a host tensor [blocks][H][B][d]")
+    if host_v.shape != host_k.shape:
+        raise ValueError(f"host_k {tuple(host_k.shape)} and host_v {tuple(host_v.shape)} must have the same shape")
+    _contig("staging", staging, torch.uint8)
+    n = p.shape[0] if p.size else 0
+    if pairs_dev is None:
+        pairs_dev = torch.from_numpy(p.reshape(-1, 2)).to(cache.k.device)  # synchronous copy
+        if stream is not None:
+            pairs_dev.record_stream(stream)
+    _contig("pairs_dev", pairs_dev, torch.int64)
+    if tuple(pairs_dev.shape) != (n, 2) and n:
+        raise ValueError("pairs_dev must match pairs")
+    _device(cache, pairs_dev=pairs_dev, staging=staging)
+    d = cache.desc()
+    _check(lib().pa_swap_blocks_dma(ctypes.byref(d), _ptr(host_k), _ptr(host_v), host_k.shape[0],
+                                    _ptr(pairs_dev) if n else None,
+                                    p.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)) if n else None, n,
+                                    int(direction), _ptr(staging), staging.numel(), _stream(stream)))
 
 
 def pa_decode_workspace_bytes(cache: KVCache, S: int, max_context_len: int) -> int:

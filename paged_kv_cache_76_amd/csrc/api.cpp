@@ -7,6 +7,7 @@
 
 #include <stdlib.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <string>
@@ -208,6 +209,98 @@ pa_status pa_swap_blocks(const pa_kv_cache* cache, void* host_k, void* host_v, i
   }
   return launched(fn, pa::launch_swap_blocks(c, dev_ptr[0], dev_ptr[1], host_num_blocks, pairs, n,
                                              dir == PA_SWAP_OUT, (hipStream_t)stream));
+}
+
+size_t pa_swap_staging_bytes(const pa_kv_cache* cache, int32_t blocks) {
+  pa::Cache c;
+  if (check_cache("pa_swap_staging_bytes", cache, &c) != PA_OK || blocks < 1) return 0;
+  return (size_t)2 * blocks * c.num_heads * c.block_size * c.head_dim * pa::dtype_bytes(c.dtype);
+}
+
+pa_status pa_swap_blocks_dma(const pa_kv_cache* cache, void* host_k, void* host_v, int32_t host_num_blocks,
+                             const int64_t* pairs, const int64_t* pairs_host, int32_t n, pa_swap_dir dir,
+                             void* staging, size_t staging_bytes, void* stream) {
+  const char* fn = "pa_swap_blocks_dma";
+  pa::Cache c;
+  pa_status st = check_cache(fn, cache, &c);
+  if (st != PA_OK) return st;
+  if (dir != PA_SWAP_OUT && dir != PA_SWAP_IN) return fail(PA_ERR_INVALID_ARG, "%s: bad direction %d", fn, (int)dir);
+  if (n < 0 || host_num_blocks < 0) return fail(PA_ERR_INVALID_ARG, "%s: negative size", fn);
+  if (n == 0) return PA_OK;
+  if (!pairs || !pairs_host || !host_k || !host_v || !staging)
+    return fail(PA_ERR_INVALID_ARG, "%s: NULL pairs/host pool/staging", fn);
+  if (!aligned(pairs, 8) || !aligned(host_k, 16) || !aligned(host_v, 16) || !aligned(staging, 16))
+    return fail(PA_ERR_INVALID_ARG, "%s: misaligned pairs/host pool/staging", fn);
+  const size_t block_bytes = (size_t)c.num_heads * c.block_size * c.head_dim * pa::dtype_bytes(c.dtype);
+  // staging slots: a key block and a value block each
+  const int64_t slots = (int64_t)(staging_bytes / (2 * block_bytes));
+  if (slots < 1)
+    return fail(PA_ERR_WORKSPACE, "%s: staging of %zu bytes holds no block (%zu needed per block)", fn, staging_bytes,
+                2 * block_bytes);
+  const int32_t chunk = (int32_t)std::min<int64_t>(slots, n);
+  st = check_copy_grid(fn, c, chunk);
+  if (st != PA_OK) return st;
+  // the copy engines read or write the host pools directly: pinned memory
+  void* host_ptr[2] = {host_k, host_v};
+  for (int i = 0; i < 2; ++i) {
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, host_ptr[i]) != hipSuccess || attr.type != hipMemoryTypeHost) {
+      (void)hipGetLastError();
+      return fail(PA_ERR_INVALID_ARG, "%s: host pool %d is not pinned host memory", fn, i);
+    }
+  }
+  const bool out = dir == PA_SWAP_OUT;
+  const int64_t src_blocks = out ? c.num_blocks : host_num_blocks;
+  const int64_t dst_blocks = out ? host_num_blocks : c.num_blocks;
+  if (g_debug.load()) {
+    std::vector<int64_t> p;
+    st = fetch(fn, pairs, 2 * (int64_t)n, (hipStream_t)stream, &p);
+    if (st != PA_OK) return st;
+    for (int64_t i = 0; i < 2 * (int64_t)n; ++i)
+      if (p[i] != pairs_host[i])
+        return fail(PA_ERR_INVALID_ARG, "%s: pairs and pairs_host differ at pair %lld", fn, (long long)(i / 2));
+    st = pa_check_copy_pairs(pairs_host, n, (int32_t)src_blocks, (int32_t)dst_blocks, 0);
+    if (st != PA_OK) return st;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  char* stage[2] = {(char*)staging, (char*)staging + slots * block_bytes};
+  char* host[2] = {(char*)host_k, (char*)host_v};
+  auto valid = [&](int64_t i) {
+    const int64_t a = pairs_host[2 * i], b = pairs_host[2 * i + 1];
+    return a >= 0 && a < src_blocks && b >= 0 && b < dst_blocks;
+  };
+  for (int64_t i0 = 0; i0 < n; i0 += chunk) {
+    const int32_t cnt = (int32_t)std::min<int64_t>(chunk, n - i0);
+    if (out) {
+      hipError_t err = pa::launch_stage_blocks(c, stage[0], stage[1], pairs, i0, cnt, src_blocks, dst_blocks, true, s);
+      if (err != hipSuccess) return launched(fn, err);
+    }
+    // one copy per pool for each run of valid pairs whose host ids are
+    // consecutive (their staging slots always are)
+    for (int64_t j = 0; j < cnt;) {
+      if (!valid(i0 + j)) {
+        ++j;
+        continue;
+      }
+      const int64_t host_id = pairs_host[2 * (i0 + j) + (out ? 1 : 0)];
+      int64_t len = 1;
+      while (j + len < cnt && valid(i0 + j + len) && pairs_host[2 * (i0 + j + len) + (out ? 1 : 0)] == host_id + len)
+        ++len;
+      for (int pool = 0; pool < 2; ++pool) {
+        char* h = host[pool] + host_id * block_bytes;
+        char* g = stage[pool] + j * block_bytes;
+        const hipError_t err = out ? hipMemcpyAsync(h, g, len * block_bytes, hipMemcpyDeviceToHost, s)
+                                   : hipMemcpyAsync(g, h, len * block_bytes, hipMemcpyHostToDevice, s);
+        if (err != hipSuccess) return launched(fn, err);
+      }
+      j += len;
+    }
+    if (!out) {
+      hipError_t err = pa::launch_stage_blocks(c, stage[0], stage[1], pairs, i0, cnt, src_blocks, dst_blocks, false, s);
+      if (err != hipSuccess) return launched(fn, err);
+    }
+  }
+  return PA_OK;
 }
 
 size_t pa_decode_workspace_bytes(const pa_kv_cache* cache, int32_t S, int32_t max_context_len) {

@@ -92,7 +92,51 @@ __global__ __launch_bounds__(kCopyThreads) void swap_blocks_kernel(
   }
 }
 
+// Staging of a swap through the copy engines: gather = the device blocks of
+// pairs i0 .. i0 + count - 1 into consecutive staging slots (swap-out),
+// scatter = consecutive staging slots into their device blocks (swap-in).
+// A pair with an id outside its pool moves nothing.  grid.x = item * 2 +
+// pool, grid.y = chunk of the block, as copy_blocks_kernel.
+__global__ __launch_bounds__(kCopyThreads) void stage_blocks_kernel(
+    u32x4* __restrict__ kpool, u32x4* __restrict__ vpool, u32x4* __restrict__ stage_k, u32x4* __restrict__ stage_v,
+    const int64_t* __restrict__ pairs, int64_t i0, int64_t vec_per_block, int64_t src_blocks, int64_t dst_blocks,
+    int32_t gather) {
+  const int64_t j = blockIdx.x >> 1;
+  u32x4* __restrict__ pool = (blockIdx.x & 1) ? vpool : kpool;
+  u32x4* __restrict__ stage = (blockIdx.x & 1) ? stage_v : stage_k;
+  const int64_t s = pairs[2 * (i0 + j)];
+  const int64_t d = pairs[2 * (i0 + j) + 1];
+  if (s < 0 || s >= src_blocks || d < 0 || d >= dst_blocks) return;
+  const int64_t blk = gather ? s : d;  // the device block
+  const u32x4* __restrict__ from = gather ? pool + blk * vec_per_block : stage + j * vec_per_block;
+  u32x4* __restrict__ to = gather ? stage + j * vec_per_block : pool + blk * vec_per_block;
+  const int64_t base = (int64_t)blockIdx.y * (kCopyThreads * kCopyUnroll) + threadIdx.x;
+  u32x4 buf[kCopyUnroll];
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const int64_t e = base + u * kCopyThreads;
+    if (e < vec_per_block) buf[u] = __builtin_nontemporal_load(&from[e]);
+  }
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const int64_t e = base + u * kCopyThreads;
+    if (e < vec_per_block) to[e] = buf[u];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_stage_blocks(const Cache& c, void* stage_k, void* stage_v, const int64_t* pairs, int64_t i0,
+                               int32_t count, int64_t src_blocks, int64_t dst_blocks, bool gather,
+                               hipStream_t stream) {
+  const int64_t block_bytes =
+      (int64_t)c.num_heads * c.block_size * c.head_dim * dtype_bytes(c.dtype);
+  dim3 grid((unsigned)(2 * count), (unsigned)copy_grid_y(c));
+  hipLaunchKernelGGL(stage_blocks_kernel, grid, dim3(kCopyThreads), 0, stream, (u32x4*)c.k, (u32x4*)c.v,
+                     (u32x4*)stage_k, (u32x4*)stage_v, pairs, i0, block_bytes / 16, src_blocks, dst_blocks,
+                     gather ? 1 : 0);
+  return hipGetLastError();
+}
 
 hipError_t launch_swap_blocks(const Cache& c, void* host_k, void* host_v, int32_t host_blocks,
                               const int64_t* pairs, int32_t n, bool to_host, hipStream_t stream) {

@@ -43,6 +43,12 @@ hipError_t launch_copy_blocks(const Cache& c, const int64_t* pairs, int32_t n, h
 // host_blocks blocks; to_host: device -> host (pairs = (device, host)).
 hipError_t launch_swap_blocks(const Cache& c, void* host_k, void* host_v, int32_t host_blocks,
                               const int64_t* pairs, int32_t n, bool to_host, hipStream_t stream);
+// Swap staging for pa_swap_blocks_dma: pairs i0 .. i0 + count - 1 between
+// their device blocks and consecutive staging slots (gather: device ->
+// staging; otherwise staging -> device).
+hipError_t launch_stage_blocks(const Cache& c, void* stage_k, void* stage_v, const int64_t* pairs, int64_t i0,
+                               int32_t count, int64_t src_blocks, int64_t dst_blocks, bool gather,
+                               hipStream_t stream);
 
 // ---- decode (paged_decode.hip) ------------------------------------------------
 // Tokens per context partition for this cache shape, or 0 if the shape is

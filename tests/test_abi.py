@@ -257,3 +257,32 @@ def test_swap_binding_refuses_mismatched_host_pools():
     hv = torch.zeros((3, 2, 16, 128), dtype=torch.float16)
     with pytest.raises(ValueError, match="same shape"):
         L.pa_swap_blocks(cache, hk, hv, torch.zeros((1, 2), dtype=torch.int64), L.PA_SWAP_OUT)
+
+
+def test_swap_dma_argument_checks():
+    # the copy-engine swap: bad arguments are refused before any HIP call
+    lib = L.lib()
+    d = _desc()
+    pairs = (ctypes.c_int64 * 2)(0, 0)
+    per_block = 2 * 2 * 16 * 128 * 2                        # a key and a value block of the description
+    assert lib.pa_swap_staging_bytes(ctypes.byref(d), 3) == 3 * per_block
+    assert lib.pa_swap_staging_bytes(ctypes.byref(d), 0) == 0
+
+    def call(n=1, direction=L.PA_SWAP_OUT, hk=FAKE, dev_pairs=FAKE, staging=FAKE, nbytes=per_block):
+        return lib.pa_swap_blocks_dma(ctypes.byref(d), hk, FAKE, 8, dev_pairs, pairs, n, direction, staging, nbytes,
+                                      None)
+
+    assert call(n=0) == L.PA_OK                               # no-op
+    _err(call(direction=7), "bad direction")
+    _err(call(n=-1), "negative size")
+    _err(call(hk=None), "NULL pairs/host pool/staging")
+    _err(call(staging=None), "NULL pairs/host pool/staging")
+    _err(call(hk=FAKE + 4), "misaligned")
+    _err(call(dev_pairs=FAKE + 4), "misaligned")
+    assert call(nbytes=per_block - 1) == L.PA_ERR_WORKSPACE
+    cache = L.KVCache(torch.zeros((4, 2, 16, 128), dtype=torch.float16),
+                      torch.zeros((4, 2, 16, 128), dtype=torch.float16))
+    with pytest.raises(ValueError, match="same shape"):
+        L.pa_swap_blocks_dma(cache, torch.zeros((6, 2, 16, 128), dtype=torch.float16),
+                             torch.zeros((3, 2, 16, 128), dtype=torch.float16), [[0, 0]], L.PA_SWAP_OUT,
+                             torch.zeros(per_block, dtype=torch.uint8))

@@ -47,18 +47,62 @@ def test_swap_round_trip_bit_exact(dtype, N, NH, H, B, d, n):
     assert np.array_equal(bits(cache.k), fk) and np.array_equal(bits(cache.v), fv)
 
 
+@pytest.mark.parametrize("dtype,N,NH,H,B,d,n", [("f16", 40, 30, 40, 16, 128, 17), ("bf16", 9, 12, 3, 32, 64, 5),
+                                                ("f32", 16, 16, 1, 4, 8, 16)])
+def test_swap_dma_round_trip_bit_exact(dtype, N, NH, H, B, d, n):
+    # the copy-engine form: runs of consecutive pairs become single copies,
+    # a pair with an id outside its pool moves nothing
+    print(f"swap dma {dtype} N={N} NH={NH} n={n}", flush=True)
+    t = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+    r = np.random.default_rng(7 * N + n)
+    dk, dv = random_bits(r, (N, H, B, d), t), random_bits(r, (N, H, B, d), t)
+    hk, hv = random_bits(r, (NH, H, B, d), t), random_bits(r, (NH, H, B, d), t)
+    cache = L.KVCache(from_bits(dk, t), from_bits(dv, t))
+    host_k, host_v = _pinned_from_bits(hk, t), _pinned_from_bits(hv, t)
+    # device blocks: a sorted sample (consecutive ids form runs), host blocks
+    # consecutive except one jump
+    src = np.sort(r.choice(N, n, replace=False))
+    dst = np.arange(n) + (NH - n) // 2
+    dst[n // 2:] = (dst[n // 2:] + (NH - n) - (NH - n) // 2) if NH > n else dst[n // 2:]
+    out_pairs = np.stack([src, dst], axis=1).astype(np.int64)
+    bad = np.array([[N + 3, 0], [0, -1]], np.int64)            # moves nothing
+    # staging for 3 blocks: the swap runs in chunks of 3 pairs
+    staging = L.swap_staging(cache, 3)
+    L.pa_swap_blocks_dma(cache, host_k, host_v, np.concatenate([out_pairs[:2], bad, out_pairs[2:]]), L.PA_SWAP_OUT,
+                         staging)
+    torch.cuda.synchronize()
+    ek, ev = oc.swap_blocks(dk, dv, hk, hv, out_pairs)
+    assert np.array_equal(bits(host_k), ek) and np.array_equal(bits(host_v), ev)
+    assert np.array_equal(bits(cache.k), dk)                # the source is untouched
+    in_pairs = np.stack([out_pairs[:, 1], np.roll(out_pairs[:, 0], 1)], axis=1)
+    L.pa_swap_blocks_dma(cache, host_k, host_v, torch.from_numpy(in_pairs), L.PA_SWAP_IN, L.swap_staging(cache, n))
+    torch.cuda.synchronize()
+    fk, fv = oc.swap_blocks(ek, ev, dk, dv, in_pairs)
+    assert np.array_equal(bits(cache.k), fk) and np.array_equal(bits(cache.v), fv)
+
+
 def test_swap_rejects_pageable_host_memory():
     cache = L.KVCache.empty(4, 1, 4, 8, torch.float32)
     host = torch.zeros((4, 1, 4, 8), dtype=torch.float32)        # not pinned
     with pytest.raises(L.PagedAttnError, match="not pinned"):
         L.pa_swap_blocks(cache, host, host, torch.zeros((1, 2), dtype=torch.int64, device="cuda"), L.PA_SWAP_OUT)
+    with pytest.raises(L.PagedAttnError, match="not pinned"):
+        L.pa_swap_blocks_dma(cache, host, host, np.zeros((1, 2), np.int64), L.PA_SWAP_OUT, L.swap_staging(cache, 1))
 
 
-def test_preemption_round_trip_then_decode():
+@pytest.mark.parametrize("dma", [False, True])
+def test_preemption_round_trip_then_decode(dma):
     # rows 0 and 3 share a prompt and diverge by one copy-on-write append; the
     # pair is swapped out, a new sequence overwrites every free device block,
     # then the pair is swapped back in (to different blocks) and decoded
-    print("preemption round trip", flush=True)
+    print(f"preemption round trip dma={dma}", flush=True)
+
+    def swap(pairs, direction):
+        if dma:
+            L.pa_swap_blocks_dma(cache, host_k, host_v, pairs, direction, L.swap_staging(cache, 4))
+        else:
+            L.pa_swap_blocks(cache, host_k, host_v, torch.from_numpy(pairs).cuda(), direction)
+
     H, d, B, N, NH = 4, 128, 16, 160, 128
     r_len, r_q, r_k, r_v, r_pool = inputs.streams(40, 5)
     m = BlockManager(N, B, max_rows=5, max_blocks_per_seq=N, free_order=inputs.pool_order(r_pool, N),
@@ -81,14 +125,14 @@ def test_preemption_round_trip_then_decode():
     host_k = torch.empty((NH, H, B, d), dtype=torch.float16, pin_memory=True)
     host_v = torch.empty((NH, H, B, d), dtype=torch.float16, pin_memory=True)
     before = m.used()
-    L.pa_swap_blocks(cache, host_k, host_v, torch.from_numpy(m.swap_out([0, 3])).cuda(), L.PA_SWAP_OUT)
+    swap(m.swap_out([0, 3]), L.PA_SWAP_OUT)
     assert m.used() == before - len(set(m.swapped[0][0].tolist()) | set(m.swapped[3][0].tolist()))
     n_free = m.num_free
     gen = torch.Generator(device="cuda").manual_seed(7603)
     junk = torch.randn((n_free * B, H, d), device="cuda", generator=gen).to(torch.float16)
     L.pa_reshape_and_cache(cache, junk, junk, torch.from_numpy(m.add_prompt(4, n_free * B)).cuda())
     m.free(4)
-    L.pa_swap_blocks(cache, host_k, host_v, torch.from_numpy(m.swap_in([3, 0])).cuda(), L.PA_SWAP_IN)
+    swap(m.swap_in([3, 0]), L.PA_SWAP_IN)
     rows = [0, 1, 2, 3]
     ctx = m.lens[rows].astype(np.int32)
     tables = torch.from_numpy(np.ascontiguousarray(m.tables[rows])).cuda()
