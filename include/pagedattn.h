@@ -299,7 +299,10 @@ pa_status pa_paged_decode_append(const pa_kv_cache* cache, void* out, pa_dtype o
  * mapped slots — call pa_reshape_and_cache before this).
  *
  *   query, out     [sum_s q_len_s][num_heads][head_dim]; rows of sequence s
- *                  are cu_q_lens[s] .. cu_q_lens[s+1]-1.
+ *                  are cu_q_lens[s] .. cu_q_lens[s+1]-1.  The call is not
+ *                  given their row count: both must hold cu_q_lens[S] rows
+ *                  (a precondition; the Python binding checks it in debug
+ *                  mode).
  *   block_tables   int32 [S][max_blocks_per_seq] as for pa_paged_decode, except
  *                  that entries at or beyond ceil(context_lens[s]/B) may be
  *                  read (the first tiles' entries are fetched before the

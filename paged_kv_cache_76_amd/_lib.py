@@ -131,6 +131,15 @@ def _stream(stream) -> int | None:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _i32(**sizes) -> None:
+    """Sizes the C-ABI takes as int32: refuse one that does not fit (ctypes
+    would wrap it silently into another, smaller size, and the call would
+    then cover only part of the caller's tensors)."""
+    for name, v in sizes.items():
+        if not -(1 << 31) <= int(v) < (1 << 31):
+            raise ValueError(f"{name} = {int(v)} does not fit the C-ABI's int32")
+
+
 @dataclass
 class KVCache:
     """Caller-owned key/value pools ``[num_blocks][H][B][d]`` (torch tensors)."""
@@ -163,6 +172,8 @@ class KVCache:
             raise ValueError("k and v pools must both be [num_blocks][H][B][d] of one dtype")
         if not (self.k.is_contiguous() and self.v.is_contiguous()):
             raise ValueError("pools must be contiguous")
+        _i32(num_blocks=self.num_blocks, num_heads=self.num_heads, head_dim=self.head_dim,
+             block_size=self.block_size)
         return PaKVCache(self.k.data_ptr(), self.v.data_ptr(), self.num_blocks, self.num_heads,
                          self.head_dim, self.block_size, TORCH_TO_PA.get(self.dtype, -1))
 
@@ -205,6 +216,7 @@ def pa_reshape_and_cache(cache: KVCache, key: torch.Tensor, value: torch.Tensor,
     T = slot_mapping.numel()
     if key.shape != (T, cache.num_heads, cache.head_dim) or value.shape != key.shape:
         raise ValueError(f"key/value must be [{T}][{cache.num_heads}][{cache.head_dim}]")
+    _i32(T=T)
     _device(cache, key=key, value=value, slot_mapping=slot_mapping)
     d = cache.desc()
     _check(lib().pa_reshape_and_cache(ctypes.byref(d), _ptr(key), _ptr(value), _ptr(slot_mapping),
@@ -217,6 +229,7 @@ def pa_copy_blocks(cache: KVCache, pairs: torch.Tensor, stream=None) -> None:
     n = pairs.shape[0] if pairs.numel() else 0
     if pairs.numel() and (pairs.dim() != 2 or pairs.shape[1] != 2):
         raise ValueError("pairs must be [n][2]")
+    _i32(pairs=n)
     _device(cache, pairs=pairs)
     d = cache.desc()
     _check(lib().pa_copy_blocks(ctypes.byref(d), _ptr(pairs) if n else None, n, _stream(stream)))
@@ -238,6 +251,7 @@ def pa_swap_blocks(cache: KVCache, host_k: torch.Tensor, host_v: torch.Tensor, p
     if pairs.numel() and (pairs.dim() != 2 or pairs.shape[1] != 2):
         raise ValueError("pairs must be [n][2]")
     n = pairs.shape[0] if pairs.numel() else 0
+    _i32(pairs=n, host_blocks=host_k.shape[0])
     _device(cache, pairs=pairs)
     d = cache.desc()
     _check(lib().pa_swap_blocks(ctypes.byref(d), _ptr(host_k), _ptr(host_v), host_k.shape[0],
@@ -247,6 +261,7 @@ def pa_swap_blocks(cache: KVCache, host_k: torch.Tensor, host_v: torch.Tensor, p
 def swap_staging(cache: KVCache, blocks: int) -> torch.Tensor:
     """A device staging buffer for pa_swap_blocks_dma with room for
     ``blocks`` blocks of keys and values."""
+    _i32(blocks=blocks)
     n = lib().pa_swap_staging_bytes(ctypes.byref(cache.desc()), blocks)
     if n == 0:
         raise ValueError(f"no staging size for {blocks} blocks")
@@ -276,6 +291,7 @@ def pa_swap_blocks_dma(cache: KVCache, host_k: torch.Tensor, host_v: torch.Tenso
         pairs_dev = torch.from_numpy(p.reshape(-1, 2)).to(cache.k.device)  # synchronous copy
         if stream is not None:
             pairs_dev.record_stream(stream)
+    _i32(pairs=n, host_blocks=host_k.shape[0])
     _contig("pairs_dev", pairs_dev, torch.int64)
     if tuple(pairs_dev.shape) != (n, 2) and n:
         raise ValueError("pairs_dev must match pairs")
@@ -288,6 +304,7 @@ def pa_swap_blocks_dma(cache: KVCache, host_k: torch.Tensor, host_v: torch.Tenso
 
 
 def pa_decode_workspace_bytes(cache: KVCache, S: int, max_context_len: int) -> int:
+    _i32(S=S, max_context_len=max_context_len)
     d = cache.desc()
     n = lib().pa_decode_workspace_bytes(ctypes.byref(d), S, max_context_len)
     if n == ctypes.c_size_t(-1).value:
@@ -316,6 +333,7 @@ def pa_paged_decode(cache: KVCache, out: torch.Tensor, query: torch.Tensor,
         raise ValueError("query/out must be [S][H][d]")
     if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
         raise ValueError("block_tables must be [S][max_blocks], context_lens [S]")
+    _i32(S=S, max_blocks_per_seq=block_tables.shape[1], max_context_len=max_context_len)
     _device(cache, out=out, query=query, block_tables=block_tables, context_lens=context_lens, workspace=workspace)
     d = cache.desc()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -343,6 +361,7 @@ def pa_paged_decode_noalloc(cache: KVCache, out: torch.Tensor, query: torch.Tens
         raise ValueError("query/out must be [S][H][d]")
     if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
         raise ValueError("block_tables must be [S][max_blocks], context_lens [S]")
+    _i32(S=S, max_blocks_per_seq=block_tables.shape[1], max_context_len=max_context_len)
     _device(cache, out=out, query=query, block_tables=block_tables, context_lens=context_lens)
     d = cache.desc()
     _check(lib().pa_paged_decode_noalloc(ctypes.byref(d), _ptr(out), TORCH_TO_PA.get(out.dtype, -1), _ptr(query),
@@ -352,6 +371,7 @@ def pa_paged_decode_noalloc(cache: KVCache, out: torch.Tensor, query: torch.Tens
 
 
 def pa_decode_grouped_workspace_bytes(cache: KVCache, S: int, max_context_len: int, group_size: int) -> int:
+    _i32(S=S, max_context_len=max_context_len, group_size=group_size)
     d = cache.desc()
     n = lib().pa_decode_grouped_workspace_bytes(ctypes.byref(d), S, max_context_len, group_size)
     if n == ctypes.c_size_t(-1).value:
@@ -382,6 +402,7 @@ def pa_paged_decode_grouped(cache: KVCache, out: torch.Tensor, query: torch.Tens
         raise ValueError("query/out must be [S][H][d]")
     if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
         raise ValueError("block_tables must be [S][max_blocks], context_lens [S]")
+    _i32(S=S, max_blocks_per_seq=block_tables.shape[1], max_context_len=max_context_len)
     _device(cache, out=out, query=query, block_tables=block_tables, context_lens=context_lens, workspace=workspace)
     d = cache.desc()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -422,6 +443,7 @@ def pa_paged_decode_append(cache: KVCache, out: torch.Tensor, query: torch.Tenso
             raise ValueError("cow_src must be [S]")
     if block_tables.dim() != 2 or block_tables.shape[0] != S or context_lens.shape != (S,):
         raise ValueError("block_tables must be [S][max_blocks], context_lens [S]")
+    _i32(S=S, max_blocks_per_seq=block_tables.shape[1], max_context_len=max_context_len)
     _device(cache, out=out, query=query, key=key, value=value, block_tables=block_tables,
             context_lens=context_lens, workspace=workspace, cow_src=cow_src)
     d = cache.desc()
@@ -449,7 +471,17 @@ def pa_paged_prefill(cache: KVCache, out: torch.Tensor, query: torch.Tensor,
     if (cu_q_lens.shape != (S + 1,) or out.shape != query.shape or block_tables.dim() != 2
             or block_tables.shape[0] != S):
         raise ValueError("cu_q_lens must be [S+1], block_tables [S][max_blocks], out like query")
+    _i32(S=S, max_blocks_per_seq=block_tables.shape[1], max_q_len=max_q_len,
+         max_context_len=max_context_len, rows=query.shape[0])
     _device(cache, out=out, query=query, block_tables=block_tables, cu_q_lens=cu_q_lens, context_lens=context_lens)
+    if S and get_debug():
+        # the rows of sequence s are cu_q_lens[s] .. cu_q_lens[s+1]-1 of query
+        # and out; the C-ABI is not given their count, so it is checked here
+        # (a device read, like the library's own debug-mode index checks)
+        total = int(cu_q_lens[S].item())
+        if total > query.shape[0]:
+            raise PagedAttnError(PA_ERR_INVALID_ARG, f"cu_q_lens[S] = {total} exceeds the {query.shape[0]} "
+                                 "rows of query and out")
     d = cache.desc()
     _check(lib().pa_paged_prefill(ctypes.byref(d), _ptr(out), TORCH_TO_PA.get(out.dtype, -1), _ptr(query),
                                   _ptr(block_tables), block_tables.shape[1], _ptr(cu_q_lens),
@@ -479,7 +511,9 @@ def pa_read_tiles(buf: torch.Tensor, tile_bytes: int, tiles: torch.Tensor, sink:
     _contig("buf", buf)
     tiles = _contig("tiles", tiles, torch.int32)
     nbytes = buf.numel() * buf.element_size()
-    _check(lib().pa_read_tiles(_ptr(buf), int(tile_bytes), nbytes // int(tile_bytes), _ptr(tiles), tiles.numel(),
+    _i32(tiles=tiles.numel())
+    num_tiles = min(nbytes // int(tile_bytes), (1 << 31) - 1)  # a bound on the (int32) tile ids
+    _check(lib().pa_read_tiles(_ptr(buf), int(tile_bytes), num_tiles, _ptr(tiles), tiles.numel(),
                                _ptr(sink), _stream(stream)))
 
 

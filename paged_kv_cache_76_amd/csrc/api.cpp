@@ -80,9 +80,10 @@ pa_status check_cache(const char* fn, const pa_kv_cache* c, pa::Cache* out) {
                 c->num_blocks, c->num_heads, c->head_dim, c->block_size);
   if (!pow2(c->block_size))
     return fail(PA_ERR_INVALID_ARG, "%s: block_size %d is not a power of two", fn, c->block_size);
-  if ((c->head_dim * pa::dtype_bytes(c->dtype)) % 16 != 0)
-    return fail(PA_ERR_UNSUPPORTED, "%s: head_dim*sizeof(dtype) = %d is not a multiple of 16 bytes", fn,
-                c->head_dim * pa::dtype_bytes(c->dtype));
+  const int64_t row_bytes = (int64_t)c->head_dim * pa::dtype_bytes(c->dtype);
+  if (row_bytes % 16 != 0)
+    return fail(PA_ERR_UNSUPPORTED, "%s: head_dim*sizeof(dtype) = %lld is not a multiple of 16 bytes", fn,
+                (long long)row_bytes);
   out->k = c->k;
   out->v = c->v;
   out->num_blocks = c->num_blocks;

@@ -220,6 +220,28 @@ def test_binding_refuses_host_tensors():
         L.pa_paged_prefill(cache, q[:, :1].clone(), q[:, :1].clone(), tables, cu, lens, 1, 1, 0.1)
 
 
+def test_binding_refuses_sizes_beyond_int32():
+    # ctypes would wrap a size past int32 into another, smaller one (2**32 + 5
+    # arrives as 5), so a call would silently cover part of the tensors: the
+    # binding refuses such sizes before anything else sees them
+    assert ctypes.CFUNCTYPE(ctypes.c_int32, ctypes.c_int32)(lambda x: x)((1 << 32) + 5) == 5
+    with pytest.raises(ValueError, match="does not fit"):
+        L._i32(T=(1 << 32) + 5)
+    L._i32(T=(1 << 31) - 1, S=0, n=-(1 << 31))
+    cache = L.KVCache(torch.zeros((4, 2, 16, 128), dtype=torch.float16),
+                      torch.zeros((4, 2, 16, 128), dtype=torch.float16))
+    q = torch.zeros((2, 2, 128), dtype=torch.float16)
+    tables = torch.zeros((2, 4), dtype=torch.int32)
+    lens = torch.ones(2, dtype=torch.int32)
+    with pytest.raises(ValueError, match="max_context_len = 4294967297 does not fit"):
+        L.pa_paged_decode(cache, q.clone(), q, tables, lens, (1 << 32) + 1, 0.1)
+    cu = torch.tensor([0, 1, 2], dtype=torch.int32)
+    with pytest.raises(ValueError, match="max_q_len = 4294967297 does not fit"):
+        L.pa_paged_prefill(cache, q.clone(), q, tables, cu, lens, (1 << 32) + 1, (1 << 32) + 1, 0.1)
+    with pytest.raises(ValueError, match="does not fit"):
+        L.pa_decode_workspace_bytes(cache, 1 << 31, 16)
+
+
 def test_read_helper_argument_checks():
     lib = L.lib()
     sink = ctypes.c_void_p(16)

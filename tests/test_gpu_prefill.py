@@ -227,3 +227,20 @@ def test_provider_prefix_set_prefill(dtype, B):
         row = b.prefixes.row(name)
         assert np.array_equal(oc.gather_history(kp, b.manager.table(row), n), b.prefix_k[name].view(torch.int16).numpy())
         assert np.array_equal(oc.gather_history(vp, b.manager.table(row), n), b.prefix_v[name].view(torch.int16).numpy())
+
+
+def test_debug_mode_refuses_query_rows_beyond_the_buffers():
+    # the rows of sequence s are cu_q_lens[s] .. cu_q_lens[s+1]-1 of query and
+    # out; with debug checks on, a cu_q_lens whose total exceeds the rows the
+    # caller passed is refused before any launch
+    b = workloads.build_prefill_batch(5, [40, 30], [40, 30], num_heads=2, head_dim=128, block_size=16, dtype="bf16")
+    q = b.q_dev[:60].contiguous()   # 70 rows are addressed, 60 given
+    out = torch.empty((60, 2, 128), dtype=torch.float32, device="cuda")
+    before = L.get_debug()
+    try:
+        L.set_debug(True)
+        with pytest.raises(L.PagedAttnError, match="exceeds the 60 rows") as e:
+            L.pa_paged_prefill(b.cache, out, q, b.tables_dev, b.cu_q_dev, b.lens_dev, 40, 40, b.scale)
+        assert e.value.status == L.PA_ERR_INVALID_ARG
+    finally:
+        L.set_debug(before)
