@@ -94,6 +94,28 @@ def test_every_row_written_once(case, heads):
     check_close(_run(b), _oracle(b), TOL["f16"], f"decode rows {case} heads {heads}")
 
 
+@pytest.mark.parametrize("scale", [0.0, -0.0883])
+@pytest.mark.parametrize("lens,heads", [([1, 17, 700, 1500, 2100], 2), (list(range(5, 5 + 32 * 9, 9)), 32)])
+def test_zero_and_negative_scale(scale, lens, heads):
+    # Decode takes any finite score scale.  Scale 0 weighs every key alike, so
+    # the output is the plain mean of the values (checked against that closed
+    # form as well); a negative scale reverses the order of the scores, which
+    # the running max must follow.  2 heads: the narrow partitioning, with
+    # merges (up to 3 partitions); 32 rows x 32 heads: the wide one.
+    print(f"decode scale {scale} S={len(lens)} heads={heads}", flush=True)
+    b = workloads.build_decode_batch(12, lens, num_heads=heads, head_dim=128, block_size=16, dtype="bf16")
+    ws = L.decode_workspace(b.cache, b.S, b.max_context_len)
+    out = torch.full((b.S, heads, 128), float("nan"), dtype=torch.float32, device="cuda")
+    L.pa_paged_decode(b.cache, out, b.q_dev, b.tables_dev, b.lens_dev, b.max_context_len, scale, ws)
+    torch.cuda.synchronize()
+    ref = np.stack([oa.decode(inputs.to_f64(b.q[s]), inputs.to_f64(b.k_hist[s]), inputs.to_f64(b.v_hist[s]), scale)
+                    for s in range(b.S)])
+    check_close(out, ref, TOL["bf16"], f"decode scale {scale}")
+    if scale == 0.0:
+        mean = np.stack([inputs.to_f64(b.v_hist[s]).mean(axis=0) for s in range(b.S)])
+        check_close(out, mean, TOL["bf16"], "decode at scale 0 against the mean of the values")
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_storage_dtype_output(dtype):
     # output rounded to the cache dtype: within tolerance + half an ULP

@@ -112,6 +112,23 @@ def test_grouped_matches_oracle(share, W, dtype, B, prompt, tails):
     check_close(out, _oracle(q, hist, scale), TOL[dtype], f"grouped {share} W={W}")
 
 
+@pytest.mark.parametrize("scale", [0.0, -0.0883])
+def test_grouped_zero_and_negative_scale(scale):
+    # any finite scale: the grouped kernel's running max and lazy rescale work
+    # on scaled scores, so a negative scale (scores in reverse order) and
+    # scale 0 (equal weights) come out like the oracle
+    print(f"grouped scale {scale}", flush=True)
+    H, d, W = 4, 128, 4
+    cache, mgr, q, hist, lens = _build_shared(7700, 3, W, 300, [1, 2, 3, 17], H, d, 16, "bf16", "all")
+    S = q.shape[0]
+    ws = L.decode_grouped_workspace(cache, S, int(lens.max()), W)
+    out = torch.full((S, H, d), float("nan"), dtype=torch.float32, device="cuda")
+    L.pa_paged_decode_grouped(cache, out, q.cuda(), torch.from_numpy(mgr.tables).cuda(),
+                              torch.from_numpy(lens).cuda(), int(lens.max()), scale, W, ws)
+    torch.cuda.synchronize()
+    check_close(out, _oracle(q, hist, scale), TOL["bf16"], f"grouped scale {scale}")
+
+
 @pytest.mark.parametrize("W", [1, 2, 4])
 def test_any_grouping_of_unrelated_rows(W):
     # 7 unrelated sequences (S not a multiple of W), contexts over several partitions
