@@ -27,3 +27,15 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture
+def release_mode():
+    """For tests of how the kernels themselves treat indices outside their
+    ranges (skipped, clamped): the debug-mode checks would refuse those
+    calls before any launch, so they are off for the test."""
+    from paged_kv_cache_76_amd import _lib as L
+    before = L.get_debug()
+    L.set_debug(False)
+    yield
+    L.set_debug(before)

@@ -1,5 +1,7 @@
 """Helpers shared by the GPU parity tests (no arithmetic of the method here)."""
 
+import contextlib
+
 import numpy as np
 import torch
 
@@ -44,3 +46,16 @@ def check_close(got: torch.Tensor, ref: np.ndarray, tol: float, what: str = "") 
     bad = err > allowed
     assert not bad.any(), f"{what}: max err {err.max():.3e} at {np.unravel_index(err.argmax(), err.shape)}"
     return float(err.max())
+
+
+@contextlib.contextmanager
+def debug_checks(on: bool):
+    """The library's index-precondition checks on or off for the block
+    (restored afterwards, whatever PA_DEBUG set for the process)."""
+    from paged_kv_cache_76_amd import _lib as L
+    before = L.get_debug()
+    L.set_debug(on)
+    try:
+        yield
+    finally:
+        L.set_debug(before)

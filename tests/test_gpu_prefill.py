@@ -9,7 +9,7 @@ from oracle import attention as oa
 from paged_kv_cache_76_amd import _lib as L
 from paged_kv_cache_76_amd import inputs, workloads
 
-from gpu_util import TOL, check_close
+from gpu_util import TOL, check_close, debug_checks
 
 pytestmark = pytest.mark.gpu
 
@@ -180,7 +180,7 @@ def test_shared_prefix_prefill_over_task_input_only(dtype, B, prefix, tasks):
     assert np.array_equal(got, b.prefix_k.view(torch.int16).numpy())
 
 
-def test_generic_context_past_the_table_row_and_keys_outside_the_pool():
+def test_generic_context_past_the_table_row_and_keys_outside_the_pool(release_mode):
     # The generic kernel (fp32, d=8, B=4) reads no table entry past the row:
     # a context length beyond max_blocks * B (a broken precondition) attends
     # over the keys the row covers.  A row whose blocks all lie outside the
@@ -191,6 +191,11 @@ def test_generic_context_past_the_table_row_and_keys_outside_the_pool():
     tables[1].fill_(1 << 30)                                     # every block of sequence 1 outside the pool
     lens_dev = torch.tensor([60, 12], dtype=torch.int32, device="cuda")  # 60 > 40 = max_blocks * B
     out = torch.full((2, 1, 8), float("nan"), dtype=torch.float32, device="cuda")
+    # debug mode refuses the broken precondition before any launch
+    with debug_checks(True), pytest.raises(L.PagedAttnError, match="context length 60 outside"):
+        L.pa_paged_prefill(b.cache, out, b.q_dev, tables, b.cu_q_dev, lens_dev, 1, 40, b.scale)
+    torch.cuda.synchronize()
+    assert torch.isnan(out).all()
     L.pa_paged_prefill(b.cache, out, b.q_dev, tables, b.cu_q_dev, lens_dev, 1, 40, b.scale)
     torch.cuda.synchronize()
     got = out.cpu()

@@ -49,7 +49,7 @@ def test_swap_round_trip_bit_exact(dtype, N, NH, H, B, d, n):
 
 @pytest.mark.parametrize("dtype,N,NH,H,B,d,n", [("f16", 40, 30, 40, 16, 128, 17), ("bf16", 9, 12, 3, 32, 64, 5),
                                                 ("f32", 16, 16, 1, 4, 8, 16)])
-def test_swap_dma_round_trip_bit_exact(dtype, N, NH, H, B, d, n):
+def test_swap_dma_round_trip_bit_exact(dtype, N, NH, H, B, d, n, release_mode):
     # the copy-engine form: runs of consecutive pairs become single copies,
     # a pair with an id outside its pool moves nothing
     print(f"swap dma {dtype} N={N} NH={NH} n={n}", flush=True)
