@@ -1,0 +1,104 @@
+"""Seeded random configurations against the float64 oracle: the decode, the
+appending decode (group 1, 2 or 4) and the prefill over every built
+(dtype, head_dim, block_size), with the batch size, head count, context
+lengths and query lengths drawn per case.  Lengths mix block, partition and
+query-tile boundaries with uniform draws.  Every case is fixed by its index
+(numpy's seeded generator) and prints its parameters before it runs.
+
+What each must equal: [P1] key design 1, eq. 1 (softmax-weighted sum over the
+positions up to the query's own, scale 1/sqrt(d)), computed by the oracle over
+the logically contiguous histories; the appending decode's pools must also
+equal the oracle's cache write bit for bit."""
+
+import numpy as np
+import pytest
+
+from paged_kv_cache_76_amd import workloads
+
+from gpu_util import TOL, check_close
+from test_gpu_append import _run_case
+from test_gpu_decode import _oracle as _decode_oracle
+from test_gpu_decode import _run as _decode_run
+from test_gpu_prefill import _oracle as _prefill_oracle
+from test_gpu_prefill import _run as _prefill_run
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = ["f32", "f16", "bf16"]
+# (head_dim, block_size) pairs the decode is built for
+DECODE_SHAPES = [(8, 4), (8, 8), (8, 16), (64, 16), (64, 32), (128, 8), (128, 16), (128, 32), (128, 64),
+                 (128, 128), (256, 16), (256, 32)]
+
+
+def _lengths(rng, S, B, hi):
+    """S context lengths in [1, hi]: about half from the boundaries of a
+    block, a narrow partition (1024) and a wide one (4096), the rest uniform."""
+    special = np.array([1, 2, B - 1, B, B + 1, 2 * B + 1, 1023, 1024, 1025, 4095, 4096, 4097])
+    special = special[(special >= 1) & (special <= hi)]
+    uniform = rng.integers(1, hi + 1, S)
+    pick = rng.random(S) < 0.5
+    return [int(x) for x in np.where(pick, rng.choice(special, S), uniform)]
+
+
+def _decode_case(i):
+    rng = np.random.default_rng(7690 + i)
+    dtype = DTYPES[i % 3]
+    d, B = DECODE_SHAPES[(i // 3 + i) % len(DECODE_SHAPES)]
+    if i % 4 == 3:
+        # 32 rows x 32 heads of short contexts: the wide partitioning
+        d = min(d, 128)
+        return dtype, d, B, 32, 32, _lengths(rng, 32, B, 200)
+    S = int(rng.integers(1, 9))
+    H = int(rng.integers(1, 7))
+    return dtype, d, B, S, H, _lengths(rng, S, B, 5000)
+
+
+@pytest.mark.parametrize("i", range(48))
+def test_random_decode(i):
+    dtype, d, B, S, H, lens = _decode_case(i)
+    print(f"random decode {i}: {dtype} d={d} B={B} S={S} H={H} lens={lens}", flush=True)
+    b = workloads.build_decode_batch(8000 + i, lens, num_heads=H, head_dim=d, block_size=B, dtype=dtype)
+    check_close(_decode_run(b), _decode_oracle(b), TOL[dtype], f"random decode {i}")
+
+
+@pytest.mark.parametrize("i", range(36))
+def test_random_appending_decode(i):
+    rng = np.random.default_rng(7790 + i)
+    dtype = DTYPES[i % 3]
+    if i % 2 == 0:
+        # the grouped builds: head_dim 128, blocks of 16 or 32, groups of 2 or 4
+        d, B, group = 128, (16, 32)[(i // 2) % 2], (2, 4)[(i // 4) % 2]
+    else:
+        d, B = DECODE_SHAPES[(i * 5) % len(DECODE_SHAPES)]
+        group = 1
+    S = int(rng.integers(1, 11))
+    H = int(rng.integers(1, 6))
+    lens = _lengths(rng, S, B, 4500)
+    print(f"random appending decode {i}: {dtype} d={d} B={B} group={group} S={S} H={H} lens={lens}", flush=True)
+    _run_case(8100 + i, lens, H, d, B, dtype, group=group)
+
+
+@pytest.mark.parametrize("i", range(36))
+def test_random_prefill(i):
+    rng = np.random.default_rng(7890 + i)
+    if i % 2 == 0:
+        # the MFMA kernel: head_dim 128, bf16 or f16, blocks of 16 to 128
+        dtype, d, B = ("bf16", "f16")[(i // 2) % 2], 128, (16, 32, 64, 128)[(i // 2) % 4]
+    else:
+        # the generic kernel: any other description
+        dtype = DTYPES[(i // 2) % 3]
+        d, B = ((8, 4), (64, 16), (256, 32), (128, 16), (32, 8), (96, 2))[(i // 2) % 6]
+        if d == 128 and dtype != "f32":
+            dtype = "f32"
+    S = int(rng.integers(1, 5))
+    H = int(rng.integers(1, 5))
+    special = np.array([1, 2, B - 1, B, B + 1, 63, 64, 65, 127, 128, 129, 255, 257, 640])
+    special = special[special >= 1]
+    lens = [int(x) for x in np.where(rng.random(S) < 0.5, rng.choice(special, S), rng.integers(1, 700, S))]
+    # the queries: the whole prompt, or its last q_len positions
+    q_lens = [int(n) if rng.random() < 0.5 else int(rng.integers(1, n + 1)) for n in lens]
+    print(f"random prefill {i}: {dtype} d={d} B={B} S={S} H={H} lens={lens} q_lens={q_lens}", flush=True)
+    b = workloads.build_prefill_batch(8200 + i, lens, q_lens, num_heads=H, head_dim=d, block_size=B, dtype=dtype)
+    out = _prefill_run(b).cpu()
+    for s in range(S):
+        check_close(out[b.cu_q[s]:b.cu_q[s + 1]], _prefill_oracle(b, s), TOL[dtype], f"random prefill {i} seq {s}")
