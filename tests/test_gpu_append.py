@@ -169,9 +169,15 @@ def test_copy_on_write_folded_in(W, dtype, B, prompt, tails):
     # the builder's last step runs neither its copies nor its writes: the
     # appending decode receives the copies as cow_src and does both
     print(f"append + copy-on-write W={W} {dtype} B={B} prompt={prompt} tails={tails}", flush=True)
-    H, d = 4, 128
-    width = 4
-    cache, mgr, q, hist, lens, held, pairs = _build_shared(W * 1000 + B + prompt, 3, width, prompt, tails, H, d, B,
+    cow_case(W * 1000 + B + prompt, W, dtype, B, prompt, tails)
+
+
+def cow_case(seed, W, dtype, B, prompt, tails, H=4, d=128, groups=3):
+    """``groups`` prompts forked into ``len(tails)`` rows each; the last
+    append step's copies and writes are left to one appending decode (group
+    size ``W``) with ``cow_src``; pools and outputs against the oracle."""
+    width = len(tails)
+    cache, mgr, q, hist, lens, held, pairs = _build_shared(seed, groups, width, prompt, tails, H, d, B,
                                                            dtype, "all", hold_last=True, hold_copies=True)
     S = q.shape[0]
     assert len(pairs) > 0, "the held step copies shared blocks"

@@ -8,7 +8,9 @@ query-tile boundaries with uniform draws.  Every case is fixed by its index
 What each must equal: [P1] key design 1, eq. 1 (softmax-weighted sum over the
 positions up to the query's own, scale 1/sqrt(d)), computed by the oracle over
 the logically contiguous histories; the appending decode's pools must also
-equal the oracle's cache write bit for bit."""
+equal the oracle's cache write bit for bit, and with copy-on-write folded in
+the oracle's copy then write ([P1] key design 3: a write into a shared block
+first copies it to a fresh block)."""
 
 import numpy as np
 import pytest
@@ -16,7 +18,7 @@ import pytest
 from paged_kv_cache_76_amd import workloads
 
 from gpu_util import TOL, check_close
-from test_gpu_append import _run_case
+from test_gpu_append import _run_case, cow_case
 from test_gpu_decode import _oracle as _decode_oracle
 from test_gpu_decode import _run as _decode_run
 from test_gpu_prefill import _oracle as _prefill_oracle
@@ -102,3 +104,29 @@ def test_random_prefill(i):
     out = _prefill_run(b).cpu()
     for s in range(S):
         check_close(out[b.cu_q[s]:b.cu_q[s + 1]], _prefill_oracle(b, s), TOL[dtype], f"random prefill {i} seq {s}")
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_copy_on_write_in_the_appending_decode(i):
+    # prompts forked into 2-4 rows each; the first append after the fork
+    # writes into the shared partial last block, so all rows but the last
+    # sharer copy it (cow_src) and the appending decode does copies, writes
+    # and decode in one launch
+    rng = np.random.default_rng(7990 + i)
+    dtype = DTYPES[i % 3]
+    d = 64 if i % 4 == 0 else 128
+    B = (16, 32)[(i // 4) % 2] if d == 64 else (8, 16, 32, 64, 128)[(i // 3) % 5]
+    W = (1, 2, 4)[(i // 2) % 3]
+    width = int(rng.integers(2, 5))
+    groups = int(rng.integers(1, 5))
+    H = int(rng.integers(1, 6))
+    kind = i % 3
+    if kind == 0:      # anywhere, at any offset within the last block
+        prompt = int(rng.integers(1, 1200 // B)) * B + int(rng.integers(1, B))
+    elif kind == 1:    # the copied block one token short of full
+        prompt = int(rng.integers(1, 1200 // B)) * B + B - 1
+    else:              # the copied block just past the first narrow partition
+        prompt = 1024 + int(rng.integers(1, B))
+    print(f"random copy-on-write {i}: {dtype} d={d} B={B} W={W} width={width} groups={groups} H={H} "
+          f"prompt={prompt}", flush=True)
+    cow_case(8300 + i, W, dtype, B, prompt, [1] * width, H=H, d=d, groups=groups)
