@@ -66,6 +66,49 @@ def settle(launch, ms: float = SETTLE_MS) -> int:
     return n
 
 
+FLUSH_BYTES = 1 << 30
+
+
+class CacheFlush:
+    """Evicts the GPU's caches between timed launches: a plain read (a sum
+    over int32 words, temporal loads) of 1 GiB, four times the MI355X's
+    256 MB Infinity Cache and far more than the XCDs' L2s.  Reads allocate
+    in the Infinity Cache (measured: such a pass also evicts lines a previous
+    write left dirty), and the pass leaves no dirty lines of its own; a
+    read-modify-write flush would, and their write-back would slow the timed
+    launch (by ~5 us on a 75 us decode, measured).  A launch timed right
+    after the pass reads its bytes from HBM, whatever the previous launch
+    left cached."""
+
+    def __init__(self):
+        import torch
+
+        self.buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
+        self.sink = None
+
+    def __call__(self) -> None:
+        self.sink = self.buf.sum()
+
+
+def flushed_replays(launch, n: int) -> list[float]:
+    """Durations (ms) of launch(i) for i < n, each timed with events right
+    after a cache flush."""
+    import torch
+
+    flush = CacheFlush()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for _ in range(20):   # keeps the clocks up after the host-side set-up
+        flush()
+    for i in range(n):
+        flush()
+        ev[i][0].record()
+        launch(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    del flush
+    return [a.elapsed_time(b) for a, b in ev]
+
+
 def cpu_model() -> str:
     try:
         out = subprocess.run(["lscpu"], capture_output=True, text=True).stdout
@@ -526,14 +569,15 @@ def shared_measure(beam: bool, grouped: bool, steps: int = 64,
                     fused=fused)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     logical = unique = copies = cow_tokens = 0
-    saved = []
+    saved, uniq_steps = [], []
     # host work (remaps, appends, activations, uploads) for every step first,
     # so the timed launches find everything resident in HBM
     plans = []
     for i in range(steps):
         p = loop.plan()
         logical += workloads.decode_bytes(p["lens"], H, D, 2, B)
-        unique += loop.unique_blocks_read(p["rows"]) * B * H * D * 2 * 2
+        uniq_steps.append(loop.unique_blocks_read(p["rows"]) * B * H * D * 2 * 2)
+        unique += uniq_steps[-1]
         copies += p["n_pairs"]
         cow_tokens += p["cow_tokens"]
         saved.append(loop.mgr.blocks_saved_by_sharing())
@@ -565,6 +609,10 @@ def shared_measure(beam: bool, grouped: bool, steps: int = 64,
         ev[i][1].record()
     torch.cuda.synchronize()
     ms = [a.elapsed_time(b) for a, b in ev]
+    # the same replays, each right after a cache flush: a step's unique bytes
+    # (its prompt blocks above all, re-read every step) fit in part in the
+    # 256 MB Infinity Cache, which back-to-back steps could otherwise hit
+    cold = flushed_replays(lambda i: loop.decode_only(plans[i]), steps)
     # the copies' algorithmic bytes: each copy carries the appending row's
     # tokens before its newest (read once, written once, K and V)
     cow_bytes = cow_tokens * 2 * 2 * H * D * 2
@@ -587,6 +635,12 @@ def shared_measure(beam: bool, grouped: bool, steps: int = 64,
                  logical_GB_per_step=round(logical / steps / 1e9, 4), unique_GB_per_step=round(unique / steps / 1e9, 4),
                  decode_launch_us_p10_p50_p90=[round(sorted(ms)[int(q * (steps - 1))] * 1e3, 1) for q in (0.1, 0.5, 0.9)],
                  decode_launch_us_mean=round(sum(ms) / steps * 1e3, 1),
+                 decode_unique_GBps=round(sum(uniq_steps) / (sum(ms) * 1e-3) / 1e9, 1),
+                 after_cache_flush=dict(
+                     decode_launch_us_mean=round(sum(cold) / steps * 1e3, 1),
+                     decode_unique_GBps=round(sum(uniq_steps) / (sum(cold) * 1e-3) / 1e9, 1),
+                     pct_of_peak_unique=round(100 * sum(uniq_steps) / (sum(cold) * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+                     flush="a 1 GiB read pass before each replayed decode"),
                  timing=f"span of the {steps} steps' launches with no per-step instrumentation; decode launch "
                         "durations from replays of every step's decode with events around each (a fused loop's "
                         "replay stores each newest token again, with the same bits, and makes no copies)")
@@ -1206,6 +1260,12 @@ def main() -> int:
     pct = lambda q: dec_sorted[min(K - 1, int(q * K))] * 1e3
     dec_gbs = (sum(dec_bytes) / K) / (dec_avg_ms * 1e-3) / 1e9
     log(f"step {ms_per_step:.3f} ms, decode {dec_avg_ms * 1e3:.1f} us -> {dec_gbs:.0f} GB/s")
+    # the same decodes again, each right after a cache flush: what a launch
+    # reaches when nothing it reads is left in the Infinity Cache or the L2s
+    cold_ms = flushed_replays(lambda j: decode(W + j), K)
+    cold_avg_ms = sum(cold_ms) / K
+    cold_gbs = (sum(dec_bytes) / K) / (cold_avg_ms * 1e-3) / 1e9
+    log(f"decode after a cache flush: {cold_avg_ms * 1e3:.1f} us -> {cold_gbs:.0f} GB/s")
 
     cpu = None
     if args.cpu_seqs > 0:
@@ -1266,12 +1326,17 @@ def main() -> int:
                      "traffic_over_algorithmic": traffic and traffic["ratio"],
                      "avg_launch_us": round(dec_avg_ms * 1e3, 2),
                      "launch_us_p10_p50_p90": [round(pct(0.1), 2), round(pct(0.5), 2), round(pct(0.9), 2)],
-                     "algorithmic_bytes_per_launch": int(sum(dec_bytes) / K)},
+                     "algorithmic_bytes_per_launch": int(sum(dec_bytes) / K),
+                     "after_cache_flush": {"avg_launch_us": round(cold_avg_ms * 1e3, 2),
+                                           "achieved": round(cold_gbs, 2),
+                                           "frac": round(cold_gbs / PEAK_HBM_GBS, 4),
+                                           "flush": "a 1 GiB read pass before each launch"}},
         "cpu_baseline": cpu,
         "achievable": ach,
         "timing": (f"value and ms_per_step: {K} steps with no per-step instrumentation after {W} warm-up steps; "
                    f"roofline launch durations: the decodes of the same {K} steps replayed with events around "
-                   f"each launch (decode is read-only: a replay reads the bytes of its step)"),
+                   f"each launch (decode is read-only: a replay reads the bytes of its step); after_cache_flush: "
+                   f"the same replays, each after a 1 GiB read pass that evicts the Infinity Cache and L2s"),
     }
     if prefill is not None:
         rec["prefill"] = {"metric": PREFILL_METRIC, "value": round(prefill["tflops"], 2), "unit": "TFLOP/s",
