@@ -885,6 +885,99 @@ def blocksize_bench(args) -> int:
     return 0
 
 
+def paging_cost_bench(args) -> int:
+    """What scattering the blocks costs the decode: the OPT-13B decode (64 x
+    40 heads, d=128, fp16, contexts U[1,2048], B=16) on its seeded-shuffled
+    pool, and on a copy of that pool in which every sequence's blocks sit at
+    consecutive physical ids in logical order (the layout a contiguous,
+    unpaged cache would have).  The kernel, the lengths, the queries and the
+    arithmetic are the same, so the outputs must be bit-identical; the time
+    difference is the cost of the scattered block placement ("vLLM /
+    PagedAttention", awesome.papernotes.org, key design 5, puts the kernel
+    overhead of paging at 20-26 %).  Both layouts are also
+    read with no arithmetic (their K/V tiles in the decode's order), the
+    achievable rate of each access pattern."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_76_amd import _lib as L
+    from paged_kv_cache_76_amd import workloads
+
+    lens = workloads.opt13b_decode_lengths(2, S)
+    b = workloads.build_decode_batch(2, lens, H, D, B, DTYPE, nan_fill=False)
+    tables = b.manager.tables[:S]
+    nblk = [-(-int(n) // B) for n in lens]
+    first = np.concatenate([[0], np.cumsum(nblk)[:-1]]).astype(np.int64)
+    src_ids = np.concatenate([tables[s, :nblk[s]] for s in range(S)]).astype(np.int64)
+    total = int(src_ids.size)
+    contig = L.KVCache.empty(total + 1, H, B, D, torch.float16)
+    idx = torch.from_numpy(src_ids).cuda()
+    contig.k[:total] = b.cache.k[idx]
+    contig.v[:total] = b.cache.v[idx]
+    ct = np.full_like(tables, total)        # unused entries: the spare block past the sequences
+    for s in range(S):
+        ct[s, :nblk[s]] = first[s] + np.arange(nblk[s])
+    ctables = torch.from_numpy(np.ascontiguousarray(ct)).cuda()
+    ws = L.decode_workspace(b.cache, S, b.max_context_len)
+    outs = {n: torch.empty((S, H, D), dtype=torch.float16, device="cuda") for n in ("scattered", "contiguous")}
+    runs = {"scattered": lambda: L.pa_paged_decode(b.cache, outs["scattered"], b.q_dev, b.tables_dev, b.lens_dev,
+                                                   b.max_context_len, b.scale, ws),
+            "contiguous": lambda: L.pa_paged_decode(contig, outs["contiguous"], b.q_dev, ctables, b.lens_dev,
+                                                    b.max_context_len, b.scale, ws)}
+    for fn in runs.values():
+        fn()
+    torch.cuda.synchronize()
+    same = torch.equal(outs["scattered"].view(torch.int16), outs["contiguous"].view(torch.int16))
+    log(f"decode output on the two layouts bit-identical: {same}")
+    settle(runs["scattered"])
+    # layouts alternating back to back, an event pair around each launch, no
+    # host synchronisation between launches (the GPU never idles)
+    ev = {n: [] for n in runs}
+    for _ in range(max(args.steps, 5)):
+        for n, fn in runs.items():
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            ev[n].append((e0, e1))
+    torch.cuda.synchronize()
+    times = {n: [a.elapsed_time(z) for a, z in e] for n, e in ev.items()}
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    tile_bytes = B * D * ELEM
+
+    def tile_list(tab):
+        ids = [(tab[s, :nblk[s]][None, :].astype(np.int64) * H + np.arange(H)[:, None]).reshape(-1) for s in range(S)]
+        return torch.from_numpy(np.concatenate(ids).astype(np.int32)).cuda()
+
+    reads = {}
+    for n, (cache, tab) in {"scattered": (b.cache, tables), "contiguous": (contig, ct)}.items():
+        tl = tile_list(tab)
+        evs = []
+        for _ in range(max(args.steps, 5)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            L.pa_read_tiles(cache.k, tile_bytes, tl, sink)
+            L.pa_read_tiles(cache.v, tile_bytes, tl, sink)
+            e1.record()
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        ts = [a.elapsed_time(z) for a, z in evs]
+        reads[n] = 2 * tl.numel() * tile_bytes / (sorted(ts)[len(ts) // 2] * 1e-3) / 1e9
+    nbytes = workloads.decode_bytes(lens, H, D, ELEM, B)
+    med = {n: sorted(t)[len(t) // 2] for n, t in times.items()}
+    for n in runs:
+        gbs = nbytes / (med[n] * 1e-3) / 1e9
+        _line("paged decode HBM GB/s, scattered vs contiguous block placement, OPT-13B shape", gbs, "GB/s",
+              len(times[n]), 0, med[n], "f16",
+              {"workload": f"OPT-13B decode, {n} block placement", "sequences": S, "heads": H, "head_dim": D,
+               "block_size": B, "seed": "SeedSequence(76002)"},
+              pct_of_peak=round(100 * gbs / PEAK_HBM_GBS, 2), median_us=round(med[n] * 1e3, 2),
+              plain_tile_read_GBps=round(reads[n], 1), outputs_bit_identical=same)
+    log(f"scattered {med['scattered'] * 1e3:.1f} us, contiguous {med['contiguous'] * 1e3:.1f} us: "
+        f"scattered placement costs {100 * (med['scattered'] / med['contiguous'] - 1):.1f} %")
+    return 0
+
+
 def copy_ablation_bench(args) -> int:
     """Copy-on-write copies issued as one batched pa_copy_blocks launch versus
     one device-to-device memcpy per block and pool (the alternative the pages
@@ -1121,7 +1214,8 @@ def main() -> int:
                     help="decode workload: 1 adds short sub-records for the serving loop (B=16), grouped "
                          "shared-block decoding (sampling, beam) and the 32K long-context decode; 0 skips them")
     ap.add_argument("--workload", choices=["decode", "copy", "prefill", "serving", "shared", "longdecode",
-                                           "blocksize", "copyablation", "accounting", "prefix", "swap", "append"],
+                                           "blocksize", "copyablation", "accounting", "prefix", "swap", "append",
+                                           "pagingcost"],
                     default="decode",
                     help="decode: the OPT-13B decode step (default); copy: pa_copy_blocks over 2048 "
                          "OPT-13B blocks, a plain copy of known size used to calibrate HBM counters; "
@@ -1134,7 +1228,9 @@ def main() -> int:
                          "prefix: prefill over task inputs only, with a cached 1024-token shared prefix; "
                          "swap: a preempted group's blocks to pinned host memory and back; append: one decode "
                          "step as write + decode launches vs one pa_paged_decode_append launch, 1..256 "
-                         "sequences, and beam-search steps with their copy-on-write copies folded in")
+                         "sequences, and beam-search steps with their copy-on-write copies folded in; "
+                         "pagingcost: the OPT-13B decode on its shuffled pool vs the same blocks placed "
+                         "contiguously per sequence")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU layout is a design "
@@ -1155,6 +1251,8 @@ def main() -> int:
         return blocksize_bench(args)
     if args.workload == "copyablation":
         return copy_ablation_bench(args)
+    if args.workload == "pagingcost":
+        return paging_cost_bench(args)
     if args.workload == "prefix":
         return prefix_bench(args)
     if args.workload == "swap":
