@@ -930,18 +930,26 @@ def paging_cost_bench(args) -> int:
     same = torch.equal(outs["scattered"].view(torch.int16), outs["contiguous"].view(torch.int16))
     log(f"decode output on the two layouts bit-identical: {same}")
     settle(runs["scattered"])
-    # layouts alternating back to back, an event pair around each launch, no
-    # host synchronisation between launches (the GPU never idles)
-    ev = {n: [] for n in runs}
-    for _ in range(max(args.steps, 5)):
+    # the layouts in alternating blocks of back-to-back launches (a block of
+    # one layout, then one of the other, five rounds), an event pair around
+    # each launch, no host synchronisation inside a block; a block starts with
+    # a few untimed launches, so no launch is timed right after the other
+    # layout's
+    times = {n: [] for n in runs}
+    per_block = max(args.steps, 5)
+    for _ in range(5):
         for n, fn in runs.items():
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            fn()
-            e1.record()
-            ev[n].append((e0, e1))
-    torch.cuda.synchronize()
-    times = {n: [a.elapsed_time(z) for a, z in e] for n, e in ev.items()}
+            for _ in range(3):
+                fn()
+            ev = []
+            for _ in range(per_block):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                ev.append((e0, e1))
+            torch.cuda.synchronize()
+            times[n] += [a.elapsed_time(z) for a, z in ev]
     sink = torch.zeros(4, dtype=torch.int32, device="cuda")
     tile_bytes = B * D * ELEM
 
