@@ -1,7 +1,7 @@
 """CPU oracle for paged KV-cache attention — TEST INFRASTRUCTURE ONLY.
 
-This package is the independent judge of the HIP path in
-``paged_kv_cache_76_amd``.  It is plain, slow, obviously-correct NumPy in
+This package is the independent reference the HIP path in
+``paged_kv_cache_76_amd`` is checked against.  It is plain, slow, obviously-correct NumPy in
 float64 and shares no code with the GPU library: it never sees a kernel, a
 header, a helper or a constant generator of the product, and the product never
 imports it.  Only ``tests/``, ``__graft_entry__.smoke()`` and the

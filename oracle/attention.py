@@ -1,6 +1,6 @@
 """Exact attention over a logically contiguous history, in float64.
 
-TEST INFRASTRUCTURE ONLY (see the package docstring): the judge of the HIP
+TEST INFRASTRUCTURE ONLY (see the package docstring): the reference for the HIP
 decode and prefill kernels, never called by the product.
 
 Definition followed ("vLLM / PagedAttention", awesome.papernotes.org,

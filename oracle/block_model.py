@@ -1,6 +1,6 @@
 """Dictionary model of the KV block manager.
 
-TEST INFRASTRUCTURE ONLY (see the package docstring): the judge of the host
+TEST INFRASTRUCTURE ONLY (see the package docstring): the reference for the host
 block manager in ``paged_kv_cache_76_amd.block_manager``; it shares no code
 with it.
 
